@@ -1,0 +1,196 @@
+"""CPU oracle for the Q4_0 x Q8_0 quantized matrix product.
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the CPU-baseline leg
+of the benchmark use it; the HIP library never imports, links or calls it, and
+this package imports nothing from the HIP side.
+
+The arithmetic lives in ``q4bq_oracle.c`` (plain C loops, fp64 accumulation,
+built with ``gcc -O2 -ffp-contract=off``); this module only loads it with
+ctypes and converts between NumPy arrays and raw pointers.  Every function
+follows "llama.cpp 深度解读" (luoboask.github.io) section 2 (the Q4_0 block and
+its encode/decode) and section 3 (ggml_vec_dot_q4_0_q8_0), with the readings
+R1-R6 / G1 / G5 stated at the top of the C file.
+
+Layouts (all row-major, innermost dimension contiguous):
+  W  : rows x K fp32            Wq : rows x (K/32) blocks of 18 bytes
+  X  : N x K fp32               Xq : N x (K/32) blocks of 34 bytes
+  Y  : N x rows                 D  : N x rows x (K/32) int32
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+QK = 32
+Q4_BYTES = 18
+Q8_BYTES = 34
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "q4bq_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the C oracle with gcc into ``oracle/liboracle.so``."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-Wall",
+               "-fPIC", "-shared", "-o", tmp, _SRC, "-lm", "-lpthread"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    sig = {
+        "orc_f32_to_f16": (ctypes.c_uint16, [ctypes.c_float]),
+        "orc_f16_to_f32": (ctypes.c_float, [ctypes.c_uint16]),
+        "orc_f32_to_f16_array": (None, [P, I64, P]),
+        "orc_q4_0_quantize": (None, [P, I64, I64, P]),
+        "orc_q4_0_dequantize": (None, [P, I64, I64, P]),
+        "orc_q8_0_quantize": (None, [P, I64, I64, P]),
+        "orc_block_dot": (ctypes.c_int32, [P, P]),
+        "orc_block_dots": (None, [P, I64, I64, P, I64, P]),
+        "orc_mul_mat_ref": (None, [P, I64, I64, P, I64, P]),
+        "orc_mul_mat_pages_f32": (None, [P, I64, I64, P, I64, P]),
+        "orc_mul_mat": (ctypes.c_int, [P, I64, I64, P, I64, P, ctypes.c_int]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data
+
+
+def _check_k(K: int) -> int:
+    if K <= 0 or K % QK != 0:
+        raise ValueError("K must be a positive multiple of 32, got %d" % K)
+    return K // QK
+
+
+# --- scalar conversions (R6) -------------------------------------------------
+
+def f32_to_f16_bits(x: float) -> int:
+    return int(_load().orc_f32_to_f16(ctypes.c_float(x)))
+
+
+def f16_bits_to_f32(h: int) -> float:
+    return float(_load().orc_f16_to_f32(ctypes.c_uint16(h)))
+
+
+def f32_to_f16_bits_array(x: np.ndarray) -> np.ndarray:
+    """Element-wise fp32 -> fp16 bits by the oracle's converter."""
+    flat = np.ascontiguousarray(x, dtype=np.float32).ravel()
+    out = np.empty(flat.size, dtype=np.uint16)
+    _load().orc_f32_to_f16_array(_ptr(flat), flat.size, _ptr(out))
+    return out.reshape(np.shape(x))
+
+
+# --- encoders / decoder --------------------------------------------------------
+
+def q4_0_quantize(W: np.ndarray) -> np.ndarray:
+    """fp32 rows x K -> uint8 rows x (K/32*18), the page's block layout."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    rows, K = W.shape
+    nb = _check_k(K)
+    out = np.empty((rows, nb * Q4_BYTES), dtype=np.uint8)
+    _load().orc_q4_0_quantize(_ptr(W), rows, K, _ptr(out))
+    return out
+
+
+def q4_0_dequantize(Wq: np.ndarray, K: int) -> np.ndarray:
+    Wq = np.ascontiguousarray(Wq, dtype=np.uint8)
+    nb = _check_k(K)
+    rows = Wq.size // (nb * Q4_BYTES)
+    out = np.empty((rows, K), dtype=np.float32)
+    _load().orc_q4_0_dequantize(_ptr(Wq), rows, K, _ptr(out))
+    return out
+
+
+def q8_0_quantize(X: np.ndarray) -> np.ndarray:
+    """fp32 N x K -> uint8 N x (K/32*34), natural element order."""
+    X = np.ascontiguousarray(X, dtype=np.float32)
+    N, K = X.shape
+    nb = _check_k(K)
+    out = np.empty((N, nb * Q8_BYTES), dtype=np.uint8)
+    _load().orc_q8_0_quantize(_ptr(X), N, K, _ptr(out))
+    return out
+
+
+# --- dots and products ------------------------------------------------------------
+
+def block_dot(wblk: np.ndarray, xblk: np.ndarray) -> int:
+    wblk = np.ascontiguousarray(wblk, dtype=np.uint8)
+    xblk = np.ascontiguousarray(xblk, dtype=np.uint8)
+    assert wblk.size == Q4_BYTES and xblk.size == Q8_BYTES
+    return int(_load().orc_block_dot(_ptr(wblk), _ptr(xblk)))
+
+
+def block_dots(Wq: np.ndarray, Xq: np.ndarray, K: int) -> np.ndarray:
+    """int32 N x rows x (K/32): every per-block integer dot."""
+    Wq = np.ascontiguousarray(Wq, dtype=np.uint8)
+    Xq = np.ascontiguousarray(Xq, dtype=np.uint8)
+    nb = _check_k(K)
+    rows = Wq.size // (nb * Q4_BYTES)
+    N = Xq.size // (nb * Q8_BYTES)
+    D = np.empty((N, rows, nb), dtype=np.int32)
+    _load().orc_block_dots(_ptr(Wq), rows, K, _ptr(Xq), N, _ptr(D))
+    return D
+
+
+def mul_mat_ref(Wq: np.ndarray, Xq: np.ndarray, K: int) -> np.ndarray:
+    """fp64 N x rows: exact per-block terms summed in fp64 (the parity target)."""
+    Wq = np.ascontiguousarray(Wq, dtype=np.uint8)
+    Xq = np.ascontiguousarray(Xq, dtype=np.uint8)
+    nb = _check_k(K)
+    rows = Wq.size // (nb * Q4_BYTES)
+    N = Xq.size // (nb * Q8_BYTES)
+    Y = np.empty((N, rows), dtype=np.float64)
+    _load().orc_mul_mat_ref(_ptr(Wq), rows, K, _ptr(Xq), N, _ptr(Y))
+    return Y
+
+
+def mul_mat_pages_f32(Wq: np.ndarray, Xq: np.ndarray, K: int) -> np.ndarray:
+    """fp32 N x rows with the page's own sequential fp32 accumulation."""
+    Wq = np.ascontiguousarray(Wq, dtype=np.uint8)
+    Xq = np.ascontiguousarray(Xq, dtype=np.uint8)
+    nb = _check_k(K)
+    rows = Wq.size // (nb * Q4_BYTES)
+    N = Xq.size // (nb * Q8_BYTES)
+    Y = np.empty((N, rows), dtype=np.float32)
+    _load().orc_mul_mat_pages_f32(_ptr(Wq), rows, K, _ptr(Xq), N, _ptr(Y))
+    return Y
+
+
+def mul_mat(Wq: np.ndarray, X: np.ndarray, nthreads: int = 1) -> np.ndarray:
+    """Whole operator from fp32 activations: Q8_0-quantize X, then the fp64
+    reference product.  Returns fp64 N x rows."""
+    Wq = np.ascontiguousarray(Wq, dtype=np.uint8)
+    X = np.ascontiguousarray(X, dtype=np.float32)
+    N, K = X.shape
+    nb = _check_k(K)
+    rows = Wq.size // (nb * Q4_BYTES)
+    Y = np.empty((N, rows), dtype=np.float64)
+    rc = _load().orc_mul_mat(_ptr(Wq), rows, K, _ptr(X), N, _ptr(Y), int(nthreads))
+    if rc != 0:
+        raise MemoryError("oracle scratch allocation failed")
+    return Y

@@ -1,0 +1,368 @@
+/*
+ * CPU oracle for the Q4_0-weight x Q8_0-activation quantized matrix product.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link,
+ * load or call this file: only the tests, the smoke check and the CPU-baseline
+ * leg of the benchmark do.  It shares no code, header, table or constant with
+ * the HIP library.
+ *
+ * Plain, slow, obviously correct loops.  Built with `gcc -O2 -ffp-contract=off`
+ * so that every fp32 operation below is one IEEE binary32 operation.
+ *
+ * Sources (the pages the method is taken from):
+ *   [P3-2]  "llama.cpp 深度解读" (luoboask.github.io), section 2
+ *           "量化数据结构 — Q4_0 格式详解": the block_q4_0 struct (fp16 d + 16 bytes
+ *           of nibbles, 32 weights), its 4-step encode and its decode
+ *           (value = (nibble - 8) * d, low nibble = even element).
+ *   [P3-3]  same page, section 3 "量化矩阵乘法 — 核心算子": ggml_vec_dot_q4_0_q8_0,
+ *           per block d = d_x * d_y (both fp16 widened to fp32), integer sum of
+ *           nibble * int8 products, then sumf += d * sumi.  Activations are
+ *           Q8_0-quantized so the dot runs in the integer domain.
+ *   [P2-mm] "解锁模型适配能力：Llama.cpp 框架下新架构开发全流程指南" (tahou.com),
+ *           section "GGML 的特性与注意事项", item 2: ggml's mul_mat contracts the
+ *           innermost dimension of both operands.
+ *
+ * Readings where the pages are silent (each is listed in the design notes):
+ *   R1 nibble order: byte j = element 2j (low) | element 2j+1 (high), as printed.
+ *   R2 the weights are divided by the STORED scale (fp16, widened to fp32).
+ *   R3 round() is C roundf: half away from zero.
+ *   R4 an all-zero block stores d = 0 and every nibble 8 (Q8_0: every q = 0).
+ *   R5 Q8_0: d = fp16(amax / 127), q = clamp(roundf(x / d), -127, 127).
+ *   R6 fp32 -> fp16 is IEEE round-to-nearest-even, subnormals kept.
+ *   G1 the printed dot loop multiplies the raw nibble; the page itself flags
+ *      that real code handles the offset.  The decode formula fixes it: the
+ *      dot uses (nibble - 8).
+ *   G5 q is clamped to [0, 15] (w = +amax gives round(8) + 8 = 16).
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_QK 32            /* weights per block, [P3-2] QK4_0 */
+#define ORC_Q4_BYTES 18      /* 2-byte fp16 d + 16 bytes of nibbles, [P3-2] */
+#define ORC_Q8_BYTES 34      /* 2-byte fp16 d + 32 int8 (inferred block_q8_0) */
+
+/* ------------------------------------------------------------------------ */
+/* IEEE binary16 <-> binary32 (R6).                                          */
+/* ------------------------------------------------------------------------ */
+
+/* m / 2^sh rounded to nearest, ties to even.  sh >= 1. */
+static uint32_t orc_shift_rne(uint32_t m, int sh)
+{
+    uint32_t q = m >> sh;
+    uint32_t rem = m & ((1u << sh) - 1u);
+    uint32_t half = 1u << (sh - 1);
+    if (rem > half || (rem == half && (q & 1u)))
+        q += 1u;
+    return q;
+}
+
+uint16_t orc_f32_to_f16(float f)
+{
+    uint32_t x;
+    memcpy(&x, &f, 4);
+    uint16_t sign = (uint16_t)((x >> 16) & 0x8000u);
+    uint32_t ax = x & 0x7fffffffu;
+    if (ax >= 0x7f800000u) /* inf or nan */
+        return (uint16_t)(sign | 0x7c00u | (ax > 0x7f800000u ? 0x0200u : 0u));
+    int be = (int)(ax >> 23);          /* biased fp32 exponent */
+    if (be < 127 - 25)                 /* |f| < 2^-25: rounds to zero */
+        return sign;
+    uint32_t m = (ax & 0x7fffffu) | 0x800000u; /* |f| = m * 2^(be - 150) */
+    int e = be - 127;                  /* floor(log2 |f|) */
+    if (e < -14) {
+        /* fp16 subnormal: the result counts units of 2^-24.
+         * |f| / 2^-24 = m * 2^(be - 126).  A count of 1024 is the smallest
+         * normal number, whose encoding is exactly 0x0400. */
+        return (uint16_t)(sign | orc_shift_rne(m, 126 - be));
+    }
+    uint32_t q = orc_shift_rne(m, 13);   /* 11-bit significand, in [1024, 2048] */
+    int e16 = e + 15;
+    if (q == 2048u) {
+        q = 1024u;
+        e16 += 1;
+    }
+    if (e16 >= 31)
+        return (uint16_t)(sign | 0x7c00u);
+    return (uint16_t)(sign | ((uint32_t)e16 << 10) | (q - 1024u));
+}
+
+float orc_f16_to_f32(uint16_t h)
+{
+    int sign = h >> 15;
+    int e = (h >> 10) & 31;
+    int m = h & 1023;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24);
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(m + 1024), e - 25);
+    return (float)(sign ? -v : v);
+}
+
+void orc_f32_to_f16_array(const float *x, int64_t n, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = orc_f32_to_f16(x[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Q4_0 encode / decode, [P3-2].                                            */
+/* ------------------------------------------------------------------------ */
+
+/* One block of 32 weights -> 18 bytes. */
+void orc_q4_0_quantize_block(const float *w, uint8_t *out)
+{
+    /* step 1: largest magnitude in the block */
+    float amax = 0.0f;
+    for (int k = 0; k < ORC_QK; ++k) {
+        float a = fabsf(w[k]);
+        if (a > amax)
+            amax = a;
+    }
+    /* step 2: scale = amax / 8, stored as fp16 (R6); divide by the stored value (R2) */
+    float scale = amax / 8.0f;
+    uint16_t dh = orc_f32_to_f16(scale);
+    float d = orc_f16_to_f32(dh);
+    /* step 3: q = round(w / d) + 8, clamped into the nibble range (R3, R4, G5) */
+    int q[ORC_QK];
+    for (int k = 0; k < ORC_QK; ++k) {
+        if (d == 0.0f) {
+            q[k] = 8;
+        } else {
+            float t = w[k] / d;
+            int v = (int)roundf(t) + 8;
+            if (v < 0)
+                v = 0;
+            if (v > 15)
+                v = 15;
+            q[k] = v;
+        }
+    }
+    /* step 4: two nibbles per byte, even element in the low nibble (R1) */
+    out[0] = (uint8_t)(dh & 0xffu);
+    out[1] = (uint8_t)(dh >> 8);
+    for (int j = 0; j < ORC_QK / 2; ++j)
+        out[2 + j] = (uint8_t)(q[2 * j] | (q[2 * j + 1] << 4));
+}
+
+/* rows x K fp32 (row-major) -> rows x (K/32) blocks of 18 bytes. */
+void orc_q4_0_quantize(const float *W, int64_t rows, int64_t K, uint8_t *Wq)
+{
+    int64_t nb = K / ORC_QK;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < nb; ++b)
+            orc_q4_0_quantize_block(W + r * K + b * ORC_QK,
+                                    Wq + (r * nb + b) * ORC_Q4_BYTES);
+}
+
+/* Decode: element j of a block is (nibble - 8) * d, nibble j taken from byte
+ * j/2, low nibble for even j. */
+void orc_q4_0_dequantize(const uint8_t *Wq, int64_t rows, int64_t K, float *W)
+{
+    int64_t nb = K / ORC_QK;
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t b = 0; b < nb; ++b) {
+            const uint8_t *blk = Wq + (r * nb + b) * ORC_Q4_BYTES;
+            float d = orc_f16_to_f32((uint16_t)(blk[0] | (blk[1] << 8)));
+            for (int j = 0; j < ORC_QK; ++j) {
+                uint8_t byte = blk[2 + j / 2];
+                int nib = (j % 2 == 0) ? (byte & 0x0f) : (byte >> 4);
+                W[r * K + b * ORC_QK + j] = (float)(nib - 8) * d;
+            }
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Q8_0 encode (R5).                                                         */
+/* ------------------------------------------------------------------------ */
+
+void orc_q8_0_quantize_block(const float *x, uint8_t *out)
+{
+    float amax = 0.0f;
+    for (int k = 0; k < ORC_QK; ++k) {
+        float a = fabsf(x[k]);
+        if (a > amax)
+            amax = a;
+    }
+    float scale = amax / 127.0f;
+    uint16_t dh = orc_f32_to_f16(scale);
+    float d = orc_f16_to_f32(dh);
+    out[0] = (uint8_t)(dh & 0xffu);
+    out[1] = (uint8_t)(dh >> 8);
+    for (int k = 0; k < ORC_QK; ++k) {
+        int v = 0;
+        if (d != 0.0f) {
+            v = (int)roundf(x[k] / d);
+            if (v < -127)
+                v = -127;
+            if (v > 127)
+                v = 127;
+        }
+        out[2 + k] = (uint8_t)(int8_t)v;
+    }
+}
+
+void orc_q8_0_quantize(const float *X, int64_t N, int64_t K, uint8_t *Xq)
+{
+    int64_t nb = K / ORC_QK;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t b = 0; b < nb; ++b)
+            orc_q8_0_quantize_block(X + n * K + b * ORC_QK,
+                                    Xq + (n * nb + b) * ORC_Q8_BYTES);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Per-block integer dot, [P3-3] with the offset of [P3-2] (G1).             */
+/* ------------------------------------------------------------------------ */
+
+int32_t orc_block_dot(const uint8_t *wblk, const uint8_t *xblk)
+{
+    const uint8_t *qs = wblk + 2;
+    const int8_t *y = (const int8_t *)(xblk + 2);
+    int32_t sumi = 0;
+    for (int j = 0; j < ORC_QK / 2; ++j) {
+        int v0 = (qs[j] & 0x0f) - 8; /* element 2j   */
+        int v1 = (qs[j] >> 4) - 8;   /* element 2j+1 */
+        sumi += v0 * y[2 * j] + v1 * y[2 * j + 1];
+    }
+    return sumi;
+}
+
+/* D[(n * rows + r) * nb + b] = dot of weight block (r, b) with activation
+ * block (n, b). */
+void orc_block_dots(const uint8_t *Wq, int64_t rows, int64_t K,
+                    const uint8_t *Xq, int64_t N, int32_t *D)
+{
+    int64_t nb = K / ORC_QK;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t r = 0; r < rows; ++r)
+            for (int64_t b = 0; b < nb; ++b)
+                D[(n * rows + r) * nb + b] =
+                    orc_block_dot(Wq + (r * nb + b) * ORC_Q4_BYTES,
+                                  Xq + (n * nb + b) * ORC_Q8_BYTES);
+}
+
+static float orc_block_d(const uint8_t *blk)
+{
+    return orc_f16_to_f32((uint16_t)(blk[0] | (blk[1] << 8)));
+}
+
+/* ------------------------------------------------------------------------ */
+/* The product.  Y is N x rows, rows contiguous ([P2-mm]: the output of       */
+/* mul_mat(W[K, rows], X[K, N]) is [rows, N] in ggml's innermost-first order). */
+/* ------------------------------------------------------------------------ */
+
+/* Reference: Y[n][r] = sum_b d_w * d_x * s, every term exact in fp64, summed
+ * in fp64 in increasing b. */
+void orc_mul_mat_ref(const uint8_t *Wq, int64_t rows, int64_t K,
+                     const uint8_t *Xq, int64_t N, double *Y)
+{
+    int64_t nb = K / ORC_QK;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t r = 0; r < rows; ++r) {
+            double acc = 0.0;
+            for (int64_t b = 0; b < nb; ++b) {
+                const uint8_t *wb = Wq + (r * nb + b) * ORC_Q4_BYTES;
+                const uint8_t *xb = Xq + (n * nb + b) * ORC_Q8_BYTES;
+                double dw = (double)orc_block_d(wb);
+                double dx = (double)orc_block_d(xb);
+                acc += dw * dx * (double)orc_block_dot(wb, xb);
+            }
+            Y[n * rows + r] = acc;
+        }
+    }
+}
+
+/* The page's own fp32 accumulation: d = d0 * d1 in fp32, sumf += d * sumi in
+ * fp32, increasing block order ([P3-3] steps 3 and 5). */
+void orc_mul_mat_pages_f32(const uint8_t *Wq, int64_t rows, int64_t K,
+                           const uint8_t *Xq, int64_t N, float *Y)
+{
+    int64_t nb = K / ORC_QK;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t r = 0; r < rows; ++r) {
+            float sumf = 0.0f;
+            for (int64_t b = 0; b < nb; ++b) {
+                const uint8_t *wb = Wq + (r * nb + b) * ORC_Q4_BYTES;
+                const uint8_t *xb = Xq + (n * nb + b) * ORC_Q8_BYTES;
+                float d = orc_block_d(wb) * orc_block_d(xb);
+                int32_t sumi = orc_block_dot(wb, xb);
+                sumf += d * (float)sumi;
+            }
+            Y[n * rows + r] = sumf;
+        }
+    }
+}
+
+/* Whole operator with fp32 activations: quantize X to Q8_0, then the
+ * reference product.  Rows are split evenly over `nthreads` threads (the only
+ * concession to speed; it changes no arithmetic).  Returns 0, or -1 when the
+ * scratch allocation fails. */
+struct orc_job {
+    const uint8_t *Wq;
+    const uint8_t *Xq;
+    int64_t rows, K, N, r0, r1;
+    double *Y;
+};
+
+static void *orc_job_run(void *arg)
+{
+    struct orc_job *j = (struct orc_job *)arg;
+    int64_t nb = j->K / ORC_QK;
+    for (int64_t n = 0; n < j->N; ++n) {
+        for (int64_t r = j->r0; r < j->r1; ++r) {
+            double acc = 0.0;
+            for (int64_t b = 0; b < nb; ++b) {
+                const uint8_t *wb = j->Wq + (r * nb + b) * ORC_Q4_BYTES;
+                const uint8_t *xb = j->Xq + (n * nb + b) * ORC_Q8_BYTES;
+                double dw = (double)orc_block_d(wb);
+                double dx = (double)orc_block_d(xb);
+                acc += dw * dx * (double)orc_block_dot(wb, xb);
+            }
+            j->Y[n * j->rows + r] = acc;
+        }
+    }
+    return NULL;
+}
+
+int orc_mul_mat(const uint8_t *Wq, int64_t rows, int64_t K, const float *X,
+                int64_t N, double *Y, int nthreads)
+{
+    int64_t nb = K / ORC_QK;
+    uint8_t *Xq = (uint8_t *)malloc((size_t)(N * nb * ORC_Q8_BYTES) + 1);
+    if (!Xq)
+        return -1;
+    orc_q8_0_quantize(X, N, K, Xq);
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > 256)
+        nthreads = 256;
+    pthread_t tid[256];
+    int running[256];
+    struct orc_job jobs[256];
+    for (int t = 0; t < nthreads; ++t) {
+        jobs[t].Wq = Wq;
+        jobs[t].Xq = Xq;
+        jobs[t].rows = rows;
+        jobs[t].K = K;
+        jobs[t].N = N;
+        jobs[t].r0 = rows * t / nthreads;
+        jobs[t].r1 = rows * (t + 1) / nthreads;
+        jobs[t].Y = Y;
+        running[t] = nthreads > 1 &&
+                     pthread_create(&tid[t], NULL, orc_job_run, &jobs[t]) == 0;
+        if (!running[t])
+            orc_job_run(&jobs[t]); /* single thread, or a thread failed to start */
+    }
+    for (int t = 0; t < nthreads; ++t)
+        if (running[t])
+            pthread_join(tid[t], NULL);
+    free(Xq);
+    return 0;
+}

@@ -1,0 +1,393 @@
+"""Pins for the CPU oracle: checks against what the pages and the mathematics
+fix, never against the oracle's own formulas retyped.
+
+Sources:
+  "llama.cpp 深度解读" (luoboask.github.io)
+     section 2 "量化数据结构 — Q4_0 格式详解": block_q4_0 (18 bytes per 32 weights,
+       7.1x compression from 128 bytes), encode steps, decode v = (nibble-8)*d;
+     section 3 "量化矩阵乘法 — 核心算子": the per-block integer dot and the fp32
+       d_w * d_x scaling.
+  "解锁模型适配能力：Llama.cpp 框架下新架构开发全流程指南" (tahou.com),
+     "GGML 的特性与注意事项" item 2: mul_mat contracts the innermost dimension.
+
+Each pin is chosen so a plausible slip (swapped nibbles, dropped -8, half-even
+rounding, unclamped 16, transposed output, wrong fp16 rounding) fails one.
+"""
+import ctypes
+import ctypes.util
+
+import numpy as np
+import pytest
+
+from conftest import hexbytes, read_golden
+from q4_block_quantized_amd import inputs
+
+
+# ---------------------------------------------------------------------------
+# P1: layout and sizes
+# ---------------------------------------------------------------------------
+
+def test_p1_block_sizes_and_compression(orc):
+    W = inputs.random_matrix(1, 3, 96)
+    Wq = orc.q4_0_quantize(W)
+    assert Wq.shape == (3, 3 * 18)              # 18 bytes per 32 weights
+    Xq = orc.q8_0_quantize(W)
+    assert Xq.shape == (3, 3 * 34)              # fp16 d + 32 int8
+    # the page's "32 floats (128 bytes) -> 18 bytes = 7.1x"
+    assert round(32 * 4 / 18, 1) == 7.1
+    assert 18 * 8 / 32 == 4.5                   # bits per weight used for byte accounting
+
+
+def test_p1_rows_are_independent_blocks(orc):
+    """Block (r, b) occupies bytes [(r*nb + b)*18, +18): quantizing one row or
+    one block alone gives the same bytes as the whole matrix."""
+    W = inputs.random_matrix(2, 5, 128, 0.02)
+    Wq = orc.q4_0_quantize(W)
+    for r in range(5):
+        row = orc.q4_0_quantize(W[r:r + 1])
+        assert np.array_equal(row[0], Wq[r])
+        for b in range(4):
+            blk = orc.q4_0_quantize(W[r:r + 1, 32 * b:32 * b + 32])
+            assert np.array_equal(blk[0], Wq[r, 18 * b:18 * b + 18])
+
+
+# ---------------------------------------------------------------------------
+# P2 / P3: hand-worked blocks
+# ---------------------------------------------------------------------------
+
+def _ramp():
+    return np.array([((k % 16) - 8) / 8 for k in range(32)], dtype=np.float32)
+
+
+def test_p2_ramp_block_bytes(orc):
+    g = read_golden("q4_0_ramp_block.txt")
+    got = orc.q4_0_quantize(_ramp()[None, :])[0]
+    assert got.tobytes().hex(" ").upper() == g["bytes"][0]
+
+
+def test_p2_ones_activation_bytes(orc):
+    g = read_golden("q8_0_ones_block.txt")
+    got = orc.q8_0_quantize(np.ones((1, 32), np.float32))[0]
+    assert np.array_equal(got, hexbytes(g["bytes"][0]))
+
+
+def test_p2_ramp_dot_ones(orc):
+    g = read_golden("ramp_dot_ones.txt")
+    wq = hexbytes(read_golden("q4_0_ramp_block.txt")["bytes"][0])
+    xq = hexbytes(read_golden("q8_0_ones_block.txt")["bytes"][0])
+    assert orc.block_dot(wq, xq) == int(g["sumi"][0])
+    y = orc.mul_mat_ref(wq[None], xq[None], 32)
+    assert y.shape == (1, 1)
+    assert y[0, 0] == float(g["y"][0])
+    yf = orc.mul_mat_pages_f32(wq[None], xq[None], 32)
+    assert yf[0, 0] == np.float32(float(g["y"][0]))
+    # unquantized dot of the two fp32 blocks
+    assert float(np.dot(_ramp().astype(np.float64), np.ones(32))) == float(g["unquantized"][0])
+
+
+def test_p3_tie_and_clip_block(orc):
+    g = read_golden("q4_0_tie_clip_block.txt")
+    w = np.zeros(32, np.float32)
+    w[:6] = [-1.0, 0.0625, -0.0625, 0.1875, 0.3125, 1.0]
+    got = orc.q4_0_quantize(w[None])[0]
+    assert np.array_equal(got, hexbytes(g["bytes"][0]))
+    assert not np.array_equal(got, hexbytes(g["half_even_bytes_rejected"][0]))
+
+
+def test_p3_q8_tie_block(orc):
+    g = read_golden("q8_0_tie_block.txt")
+    x = np.zeros(32, np.float32)
+    x[:5] = [0.9921875, 2.0 ** -8, -1.5 * 2.0 ** -7, 2.5 * 2.0 ** -7, -0.5 * 2.0 ** -7]
+    got = orc.q8_0_quantize(x[None])[0]
+    assert np.array_equal(got, hexbytes(g["bytes"][0]))
+    assert not np.array_equal(got, hexbytes(g["half_even_bytes_rejected"][0]))
+
+
+def test_p3_tie_rounding_matches_libm_round():
+    """The reading of round() is C round(): check libm's roundf on the ties and
+    their neighbours (half away from zero, not half to even)."""
+    libm = ctypes.CDLL(ctypes.util.find_library("m"))
+    libm.roundf.restype = ctypes.c_float
+    libm.roundf.argtypes = [ctypes.c_float]
+    for k in range(-9, 9):
+        t = k + 0.5
+        want = k + 1 if t > 0 else k
+        assert libm.roundf(t) == want
+    assert libm.roundf(np.nextafter(np.float32(0.5), np.float32(0))) == 0.0
+    assert libm.roundf(np.float32(0.49999997)) == 0.0
+
+
+def test_p9_zero_blocks(orc):
+    g = read_golden("zero_blocks.txt")
+    assert np.array_equal(orc.q4_0_quantize(np.zeros((1, 32), np.float32))[0],
+                          hexbytes(g["q4_0_bytes"][0]))
+    assert np.array_equal(orc.q8_0_quantize(np.zeros((1, 32), np.float32))[0],
+                          hexbytes(g["q8_0_bytes"][0]))
+    # negative zero behaves like zero
+    assert np.array_equal(orc.q4_0_quantize(-np.zeros((1, 32), np.float32))[0],
+                          hexbytes(g["q4_0_bytes"][0]))
+
+
+# ---------------------------------------------------------------------------
+# P4: decode table
+# ---------------------------------------------------------------------------
+
+def test_p4_decode_table(orc):
+    for case in read_golden("q4_0_decode_table.txt")["case"]:
+        dbits, dval, qs, vals = [c.strip() for c in case.split("|")]
+        h = int(dbits, 16)
+        blk = np.concatenate([np.array([h & 0xFF, h >> 8], np.uint8), hexbytes(qs)])
+        got = orc.q4_0_dequantize(blk[None], 32)[0].astype(np.float64)
+        want = np.array([int(v) for v in vals.split()], np.float64) * float(dval)
+        assert np.array_equal(got, want), case
+        assert orc.f16_bits_to_f32(h) == float(dval)
+
+
+# ---------------------------------------------------------------------------
+# P5: round-trip invariants
+# ---------------------------------------------------------------------------
+
+def _edge_blocks():
+    rng = np.random.default_rng(5)
+    blocks = [
+        inputs.random_matrix(51, 64, 32, 0.02),
+        inputs.random_matrix(52, 64, 32, 1.0),
+        inputs.random_matrix(53, 16, 32, 1e-6),      # fp16-subnormal scales
+        inputs.random_matrix(54, 16, 32, 1e-9),      # scale underflows to zero
+        inputs.random_matrix(55, 16, 32, 3000.0),    # large but in range
+    ]
+    spiky = inputs.random_matrix(56, 32, 32, 0.02)
+    spiky[np.arange(32), rng.integers(0, 32, 32)] *= 10.0
+    blocks.append(spiky)
+    one_hot = np.zeros((8, 32), np.float32)
+    one_hot[np.arange(8), np.arange(8) * 4] = np.array([1, -1, 0.5, -0.25, 3, -7, 1e-5, -1e-5], np.float32)
+    blocks.append(one_hot)
+    return np.concatenate(blocks, axis=0)
+
+
+def test_p5_q4_0_round_trip(orc):
+    W = _edge_blocks()
+    Wq = orc.q4_0_quantize(W)
+    What = orc.q4_0_dequantize(Wq, 32).astype(np.float64)
+    d = Wq[:, 0:2].copy().view(np.float16)[:, 0].astype(np.float64)  # numpy's fp16 decode
+    amax = np.abs(W).max(axis=1).astype(np.float64)
+    nib = np.stack([Wq[:, 2:] & 15, Wq[:, 2:] >> 4], axis=2).reshape(-1, 32)
+    w = W.astype(np.float64)
+    for i in range(W.shape[0]):
+        if d[i] == 0:
+            assert np.all(What[i] == 0) and amax[i] / 8 < 2.0 ** -24
+            continue
+        # the stored scale is the fp16 nearest to amax/8
+        assert abs(d[i] - amax[i] / 8) <= 2.0 ** -11 * amax[i] / 8 + 2.0 ** -25
+        ratio = w[i] / d[i]
+        hi_clip = (nib[i] == 15) & (ratio >= 7.5)
+        lo_clip = (nib[i] == 0) & (ratio < -8.5)
+        clamped = hi_clip | lo_clip
+        err = np.abs(w[i] - What[i])
+        bound = d[i] / 2 + 2.0 ** -24 * np.abs(w[i])
+        assert np.all(err[~clamped] <= bound[~clamped]), i
+        # a clamped element is off by at most amax - 7d = d + 8 * (amax/8 - d)
+        assert np.all(err[clamped] <= d[i] + 8 * abs(amax[i] / 8 - d[i]))
+        if d[i] >= 2.0 ** -14:
+            # normal-range scale: only +amax-side weights clip, the most
+            # negative weight maps to nibble 0 when it is -amax
+            assert not np.any(lo_clip)
+            if w[i].min() == -amax[i]:
+                assert nib[i][np.argmin(w[i])] == 0
+
+
+def test_p5_q8_0_round_trip(orc):
+    X = _edge_blocks()
+    Xq = orc.q8_0_quantize(X)
+    d = Xq[:, 0:2].copy().view(np.float16)[:, 0].astype(np.float64)
+    q = Xq[:, 2:].view(np.int8).astype(np.float64)
+    x = X.astype(np.float64)
+    amax = np.abs(x).max(axis=1)
+    for i in range(X.shape[0]):
+        if d[i] == 0:
+            assert np.all(q[i] == 0)
+            continue
+        assert abs(d[i] - amax[i] / 127) <= 2.0 ** -11 * amax[i] / 127 + 2.0 ** -25
+        err = np.abs(x[i] - q[i] * d[i])
+        clamped = (np.abs(q[i]) == 127) & (np.abs(x[i] / d[i]) >= 127.5)
+        if d[i] >= 2.0 ** -14:
+            # a normal-range d is within 2^-11 of amax/127, so |x/d| < 127.07
+            assert not np.any(clamped)
+        assert np.all(err[~clamped] <= d[i] / 2 + 2.0 ** -24 * np.abs(x[i][~clamped])), i
+        assert np.all(np.sign(q[i][clamped]) == np.sign(x[i][clamped]))
+        assert np.abs(q[i]).max() == 127 or amax[i] / d[i] < 126.5
+
+
+# ---------------------------------------------------------------------------
+# P6: fp32 -> fp16 conversion against numpy.float16 (IEEE RNE)
+# ---------------------------------------------------------------------------
+
+def _np_f16_bits(x):
+    with np.errstate(over="ignore"):
+        return x.astype(np.float16).view(np.uint16)
+
+
+def test_p6_fp16_conversion_exhaustive_critical_exponents(orc):
+    """Every fp32 bit pattern whose exponent sits at a rounding boundary of
+    binary16: the zero / subnormal threshold, the subnormal/normal seam, the
+    ordinary range and the overflow edge, both signs."""
+    mant = np.arange(1 << 23, dtype=np.uint32)
+    for be in (101, 102, 103, 110, 111, 112, 113, 127, 141, 142, 143):
+        for sign in (0, 1):
+            bits = (np.uint32(sign) << 31) | (np.uint32(be) << 23) | mant
+            x = bits.view(np.float32)
+            assert np.array_equal(orc.f32_to_f16_bits_array(x), _np_f16_bits(x)), (be, sign)
+
+
+def test_p6_fp16_conversion_random_and_specials(orc):
+    rng = np.random.default_rng(6)
+    bits = rng.integers(0, 1 << 32, size=1 << 22, dtype=np.uint64).astype(np.uint32)
+    x = bits.view(np.float32)
+    x = x[np.isfinite(x)]
+    assert np.array_equal(orc.f32_to_f16_bits_array(x), _np_f16_bits(x))
+    # every fp16 value, the midpoints between neighbours and one fp32 ulp either side
+    h = np.arange(0, 0x7C00, dtype=np.uint16)
+    v = h.view(np.float16).astype(np.float32)
+    mid = ((v[:-1].astype(np.float64) + v[1:].astype(np.float64)) / 2).astype(np.float32)
+    cand = np.concatenate([v, mid, np.nextafter(mid, np.float32(np.inf)),
+                           np.nextafter(mid, np.float32(0)), np.float32([65504, 65519.996, 65520, 1e30])])
+    cand = np.concatenate([cand, -cand])
+    assert np.array_equal(orc.f32_to_f16_bits_array(cand), _np_f16_bits(cand))
+    # decode of every finite fp16 agrees with numpy
+    assert all(orc.f16_bits_to_f32(int(b)) == float(np.uint16(b).view(np.float16))
+               for b in range(0, 0x7C00, 7))
+
+
+# ---------------------------------------------------------------------------
+# P8: brute force in fp64 on tiny shapes (dequantize, then a dense matmul)
+# ---------------------------------------------------------------------------
+
+def _np_dequant_q4(Wq, K):
+    """Decode with NumPy only: fp16 d via numpy.float16, nibbles unpacked
+    with the low half first, minus 8."""
+    nb = K // 32
+    blk = Wq.reshape(-1, nb, 18)
+    d = blk[:, :, 0:2].copy().view(np.float16)[:, :, 0].astype(np.float64)
+    qs = blk[:, :, 2:]
+    nib = np.stack([qs & 15, qs >> 4], axis=3).reshape(-1, nb, 32).astype(np.float64)
+    return ((nib - 8.0) * d[:, :, None]).reshape(-1, K)
+
+
+def _np_dequant_q8(Xq, K):
+    nb = K // 32
+    blk = Xq.reshape(-1, nb, 34)
+    d = blk[:, :, 0:2].copy().view(np.float16)[:, :, 0].astype(np.float64)
+    q = blk[:, :, 2:].copy().view(np.int8).astype(np.float64)
+    return (q * d[:, :, None]).reshape(-1, K)
+
+
+@pytest.mark.parametrize("rows,K,N", [(1, 32, 1), (3, 64, 2), (8, 96, 4), (5, 256, 3), (7, 32, 4)])
+def test_p8_brute_force_fp64(orc, rows, K, N):
+    W = inputs.random_matrix(800 + rows * K, rows, K, 0.02)
+    W[0, 0] *= 10.0
+    X = inputs.random_matrix(900 + N * K, N, K)
+    Wq = orc.q4_0_quantize(W)
+    Xq = orc.q8_0_quantize(X)
+    Y = orc.mul_mat_ref(Wq, Xq, K)
+    assert Y.shape == (N, rows)                         # output is N x rows, rows contiguous
+    Yb = _np_dequant_q8(Xq, K) @ _np_dequant_q4(Wq, K).T
+    assert np.allclose(Y, Yb, rtol=1e-12, atol=1e-15)
+    # per-block dots reproduce the decoded products exactly
+    D = orc.block_dots(Wq, Xq, K)
+    nb = K // 32
+    Wn = (_np_dequant_q4(Wq, K) / np.repeat(Wq.reshape(rows, nb, 18)[:, :, 0:2].copy()
+                                             .view(np.float16)[:, :, 0].astype(np.float64), 32, axis=1))
+    Xn = _np_dequant_q8(Xq, K) / np.repeat(Xq.reshape(N, nb, 34)[:, :, 0:2].copy()
+                                            .view(np.float16)[:, :, 0].astype(np.float64), 32, axis=1)
+    for b in range(nb):
+        sl = slice(32 * b, 32 * b + 32)
+        want = np.rint(Xn[:, sl] @ Wn[:, sl].T).astype(np.int64)
+        assert np.array_equal(D[:, :, b].astype(np.int64), want)
+
+
+def test_p8_against_unquantized_product(orc):
+    """The quantized product approximates X @ W^T within the sum of the
+    element-wise round-trip errors."""
+    W = inputs.random_matrix(71, 6, 256, 0.02)
+    X = inputs.random_matrix(72, 3, 256)
+    Wq, Xq = orc.q4_0_quantize(W), orc.q8_0_quantize(X)
+    Y = orc.mul_mat_ref(Wq, Xq, 256)
+    exact = X.astype(np.float64) @ W.astype(np.float64).T
+    What, Xhat = _np_dequant_q4(Wq, 256), _np_dequant_q8(Xq, 256)
+    bound = np.abs(X) @ np.abs(W.astype(np.float64) - What).T + np.abs(Xhat - X) @ np.abs(What).T
+    assert np.all(np.abs(Y - exact) <= bound * (1 + 1e-9) + 1e-15)
+
+
+# ---------------------------------------------------------------------------
+# P9: special cases
+# ---------------------------------------------------------------------------
+
+def test_p9_zero_operands(orc):
+    W = inputs.random_matrix(91, 4, 64, 0.02)
+    X = inputs.random_matrix(92, 2, 64)
+    Z = np.zeros_like
+    assert np.all(orc.mul_mat_ref(orc.q4_0_quantize(Z(W)), orc.q8_0_quantize(X), 64) == 0)
+    assert np.all(orc.mul_mat_ref(orc.q4_0_quantize(W), orc.q8_0_quantize(Z(X)), 64) == 0)
+
+
+def test_p9_single_nonzero_weight(orc):
+    """One nonzero weight w at element k: the block's d is fp16(|w|/8) and the
+    element decodes to -8d (w < 0) or 7d (w > 0, clamped from 16)."""
+    X = inputs.random_matrix(93, 2, 64)
+    Xq = orc.q8_0_quantize(X)
+    xd = Xq.reshape(2, 2, 34)[:, :, 0:2].copy().view(np.float16)[:, :, 0].astype(np.float64)
+    xq = Xq.reshape(2, 2, 34)[:, :, 2:].view(np.int8).astype(np.float64)
+    for w, k in [(0.5, 3), (-0.5, 40), (0.013, 63), (-3.0, 0)]:
+        W = np.zeros((1, 64), np.float32)
+        W[0, k] = w
+        Y = orc.mul_mat_ref(orc.q4_0_quantize(W), Xq, 64)
+        d = float(np.float16(abs(w) / 8))
+        v = (7 if w > 0 else -8) * d
+        b, j = divmod(k, 32)
+        assert np.array_equal(Y[:, 0], v * xd[:, b] * xq[:, b, j])
+
+
+def test_p9_permuting_tokens_permutes_outputs(orc):
+    W = inputs.random_matrix(94, 5, 96, 0.02)
+    X = inputs.random_matrix(95, 4, 96)
+    Wq = orc.q4_0_quantize(W)
+    perm = np.array([2, 0, 3, 1])
+    Y = orc.mul_mat_ref(Wq, orc.q8_0_quantize(X), 96)
+    Yp = orc.mul_mat_ref(Wq, orc.q8_0_quantize(X[perm]), 96)
+    assert np.array_equal(Yp, Y[perm])
+
+
+def test_p9_k32_single_block(orc):
+    W = inputs.random_matrix(96, 9, 32, 0.02)
+    X = inputs.random_matrix(97, 3, 32)
+    Wq, Xq = orc.q4_0_quantize(W), orc.q8_0_quantize(X)
+    D = orc.block_dots(Wq, Xq, 32)
+    dw = Wq[:, 0:2].copy().view(np.float16)[:, 0].astype(np.float64)
+    dx = Xq[:, 0:2].copy().view(np.float16)[:, 0].astype(np.float64)
+    assert np.array_equal(orc.mul_mat_ref(Wq, Xq, 32), dx[:, None] * dw[None, :] * D[:, :, 0])
+
+
+# ---------------------------------------------------------------------------
+# Internal consistency of the oracle's entry points
+# ---------------------------------------------------------------------------
+
+def test_fused_path_equals_prequantized_path(orc):
+    W = inputs.random_matrix(101, 33, 160, 0.02)
+    X = inputs.random_matrix(102, 5, 160)
+    Wq = orc.q4_0_quantize(W)
+    Y1 = orc.mul_mat(Wq, X, nthreads=1)
+    Y4 = orc.mul_mat(Wq, X, nthreads=4)
+    Yr = orc.mul_mat_ref(Wq, orc.q8_0_quantize(X), 160)
+    assert np.array_equal(Y1, Yr) and np.array_equal(Y4, Yr)
+
+
+def test_pages_f32_loop_within_tolerance(orc):
+    """The page's sequential fp32 accumulation stays inside the parity
+    tolerance of the fp64 reference (1e-4 relative + 1e-5 absolute)."""
+    W = inputs.random_matrix(103, 256, 4096, 0.02)
+    W[inputs.random_matrix(105, 256, 4096) > 2.33] *= 10.0    # ~1 % outliers
+    X = inputs.random_matrix(104, 2, 4096)
+    Wq, Xq = orc.q4_0_quantize(W), orc.q8_0_quantize(X)
+    Yr = orc.mul_mat_ref(Wq, Xq, 4096)
+    Yf = orc.mul_mat_pages_f32(Wq, Xq, 4096).astype(np.float64)
+    assert np.all(np.abs(Yf - Yr) <= 1e-4 * np.abs(Yr) + 1e-5)
