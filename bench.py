@@ -1,0 +1,216 @@
+"""Benchmark of the Q4_0 x Q8_0 product on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload c4]
+
+A step is one whole operator call (activation quantization + product) on
+inputs already resident in device memory.  The headline workload is the
+Llama-3-8B vocabulary projection (128256 x 4096 Q4_0 weights, one token),
+where the throughput metric is HBM bandwidth: value = algorithmic bytes per
+step (Q4_0 weights + fp32 activations + fp32 output) / time per step.  The
+line also carries the 512-token prefill (14336 x 4096) in int8 TOPS, the
+roofline fraction of the dominant kernel (timed alone with HIP events on the
+stream it runs on) and the CPU oracle timed on a bounded sample.
+
+Weights rotate over enough copies (>= 1 GiB) that each step reads them from
+HBM, not from the 256 MB last-level cache.  Prints ONE JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 matrix peak (5.0 POP/s)
+ROTATE_BYTES = 1 << 30
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="c4", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
+    return ap.parse_args()
+
+
+def q4_bytes(rows, K):
+    return rows * (K // 32) * 18
+
+
+def step_bytes(rows, K, N):
+    """Algorithmic bytes of one operator call: weights + fp32 X + fp32 Y."""
+    return q4_bytes(rows, K) + N * K * 4 + N * rows * 4
+
+
+def kernel_bytes(rows, K, N):
+    """Algorithmic bytes of the product kernel alone: weights + the quantized
+    activations it reads (32 int8 + 8-byte scale record per block) + fp32 Y."""
+    return q4_bytes(rows, K) + N * (K // 32) * 40 + N * rows * 4
+
+
+class Mats:
+    """Device copies of one workload's weights (rotated) and activations."""
+
+    def __init__(self, hip, torch, cid, N):
+        from q4_block_quantized_amd import inputs
+        wl = inputs.WORKLOADS[cid]
+        self.wl, self.N = wl, N
+        self.items = []
+        for m, (rows, K) in enumerate(wl.mats):
+            W = torch.from_numpy(inputs.weights(cid, m, rows, K, outliers=wl.outliers)).cuda()
+            Wq = hip.q4_0_quantize(W)
+            del W
+            X = torch.from_numpy(inputs.activations(cid, m, max(wl.ns), K)[:N].copy()).cuda()
+            Y = torch.empty((N, rows), dtype=torch.float32, device="cuda")
+            ws = hip.workspace(rows, K, N)
+            self.items.append([rows, K, [Wq], X, Y, ws])
+        total = sum(q4_bytes(r, k) for r, k, *_ in self.items)
+        copies = max(1, -(-ROTATE_BYTES // total))
+        for it in self.items:
+            it[2] += [it[2][0].clone() for _ in range(copies - 1)]
+        self.copies = copies
+        torch.cuda.synchronize()
+
+    def step(self, hip, i):
+        for rows, K, Wqs, X, Y, ws in self.items:
+            hip.mul_mat_q4_0_q8_0_ex(Wqs[i % self.copies], X, ws, Y)
+
+    def kernel_only(self, hip, i):
+        for rows, K, Wqs, X, Y, ws in self.items:
+            hip.mul_mat_q4_0_q8_0_prepared(Wqs[i % self.copies], ws, self.N, K, Y)
+
+    def prepare(self, hip):
+        for rows, K, Wqs, X, Y, ws in self.items:
+            hip.q4bq_quantize_activations(X, ws)
+
+    def bytes_step(self):
+        return sum(step_bytes(r, k, self.N) for r, k, *_ in self.items)
+
+    def bytes_kernel(self):
+        return sum(kernel_bytes(r, k, self.N) for r, k, *_ in self.items)
+
+    def ops(self):
+        return sum(2 * r * k * self.N for r, k, *_ in self.items)
+
+
+def timed(torch, fn, steps, warmup):
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        fn(i)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps  # ms
+
+
+def cpu_baseline(cid, N):
+    """The oracle, as it stands, on a bounded row sample of the workload."""
+    import oracle
+    from q4_block_quantized_amd import inputs
+    wl = inputs.WORKLOADS[cid]
+    rows, K = wl.mats[0]
+    take = min(rows, 16384)
+    W = inputs.weights(cid, 0, rows, K, outliers=wl.outliers, row_slice=slice(0, take))
+    X = inputs.activations(cid, 0, max(wl.ns), K)[:N].copy()
+    Wq = oracle.q4_0_quantize(W)
+    threads = min(os.cpu_count() or 1, 16)
+    runs, t0 = 0, time.perf_counter()
+    while True:
+        oracle.mul_mat(Wq, X, nthreads=threads)
+        runs += 1
+        el = time.perf_counter() - t0
+        if el >= 10.0 or runs >= 200:
+            break
+    per = el / runs
+    return {"value": round(step_bytes(take, K, N) / per / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "rows 0..%d of the %dx%d matrix, N=%d, %d runs in %.1f s (%.1f ms each), fp64 oracle"
+                      % (take - 1, rows, K, N, runs, el, per * 1e3)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (got --gpus %d)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from q4_block_quantized_amd import binding as hip
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP device", file=sys.stderr)
+        sys.exit(2)
+    hip.lib()
+    cid = int(args.workload[1])
+    from q4_block_quantized_amd import inputs
+    wl = inputs.WORKLOADS[cid]
+    N = wl.ns[0]
+
+    log("workload %s N=%d: preparing" % (wl.name, N))
+    mats = Mats(hip, torch, cid, N)
+    ms_step = timed(torch, lambda i: mats.step(hip, i), args.steps, args.warmup)
+    mats.prepare(hip)
+    ms_kernel = timed(torch, lambda i: mats.kernel_only(hip, i), args.steps, args.warmup)
+    n_launch = len(mats.items)
+    gbs = mats.bytes_step() / (ms_step * 1e-3) / 1e9
+    kern_gbs = mats.bytes_kernel() / (ms_kernel * 1e-3) / 1e9
+    log("step %.2f us -> %.1f GB/s; product kernel %.2f us/launch -> %.1f GB/s"
+        % (ms_step * 1e3, gbs, ms_kernel * 1e3 / n_launch, kern_gbs))
+    per_launch_bytes = mats.bytes_kernel() // n_launch
+    del mats
+    torch.cuda.empty_cache()
+
+    prefill = None
+    if not args.no_prefill:
+        log("prefill: preparing")
+        pm = Mats(hip, torch, 5, 512)
+        ms_p = timed(torch, lambda i: pm.step(hip, i), max(10, args.steps // 4), max(3, args.warmup // 4))
+        pm.prepare(hip)
+        ms_pk = timed(torch, lambda i: pm.kernel_only(hip, i), max(10, args.steps // 4), max(3, args.warmup // 4))
+        tops = pm.ops() / (ms_p * 1e-3) / 1e12
+        ktops = pm.ops() / (ms_pk * 1e-3) / 1e12
+        log("prefill step %.2f us -> %.1f TOPS; kernel %.2f us -> %.1f TOPS" % (ms_p * 1e3, tops, ms_pk * 1e3, ktops))
+        prefill = {"workload": "llama3_8b_prefill", "rows": 14336, "K": 4096, "N": 512,
+                   "ms_per_step": round(ms_p, 5), "value": round(tops, 2), "unit": "TOPS (int8)",
+                   "roofline": {"bound": "mfma", "achieved": round(ktops, 2), "peak": INT8_PEAK_TOPS,
+                                "unit": "TOPS", "frac": round(ktops / INT8_PEAK_TOPS, 4), "traffic": None}}
+        del pm
+        torch.cuda.empty_cache()
+
+    cpu = None if args.no_cpu else cpu_baseline(cid, N)
+
+    out = {
+        "metric": "Q4_0xQ8_0 mul_mat HBM bandwidth (GB/s, N=1 decode)",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int4xint8->int32, fp32 scale/accumulate", "data": "synthetic (seeded N(0,0.02) weights, N(0,1) activations)",
+        "config": {"workload": wl.name, "matrices": [list(m) for m in wl.mats], "N": N,
+                   "weights_cold": "rotating copies >= 1 GiB"},
+        "roofline": {"bound": "hbm", "achieved": round(kern_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(kern_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "k_gemv (product kernel alone)", "bytes_per_launch": per_launch_bytes,
+                     "us_per_launch": round(ms_kernel * 1e3 / n_launch, 3)},
+        "prefill": prefill,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,155 @@
+/*
+ * q4bq -- Q4_0-weight x Q8_0-activation quantized matrix product on MI355X.
+ *
+ * C ABI of libq4bq.so.  Every pointer argument is a DEVICE pointer (memory the
+ * caller allocated on the current HIP device), every size is an element count,
+ * and `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ * calls are asynchronous on `stream`: they validate their arguments on the host,
+ * enqueue kernels and return; buffers must stay alive until the stream has
+ * passed them.  The library keeps no pointer after a call returns and holds no
+ * state other than per-device launch parameters, so calls are reentrant.
+ *
+ * Formats (as defined in "llama.cpp 深度解读", luoboask.github.io):
+ *   Q4_0 block, section 2 "量化数据结构 — Q4_0 格式详解": 18 bytes for 32
+ *     consecutive weights -- bytes 0-1 the scale d (IEEE binary16,
+ *     little-endian), bytes 2-17 the nibbles; byte 2+j holds element 2j in its
+ *     low 4 bits and element 2j+1 in its high 4 bits; element value
+ *     (nibble - 8) * d.
+ *   Q8_0 block, the activation operand of ggml_vec_dot_q4_0_q8_0 in section 3
+ *     "量化矩阵乘法 — 核心算子": 34 bytes -- bytes 0-1 the scale d (binary16),
+ *     bytes 2-33 the 32 int8 values in element order; element value q * d.
+ *
+ * Matrix layouts (row-major, innermost dimension contiguous, as in ggml where
+ * mul_mat contracts the innermost dimension -- "解锁模型适配能力：Llama.cpp 框架下
+ * 新架构开发全流程指南", tahou.com, "GGML 的特性与注意事项" item 2):
+ *   W  fp32 rows x K            Wq  rows x (K/32) Q4_0 blocks; block (r, b) at
+ *                                   byte offset (r * K/32 + b) * 18
+ *   X  fp32 N x K               Xq  N x (K/32) Q8_0 blocks; block (n, b) at
+ *                                   byte offset (n * K/32 + b) * 34
+ *   Y  fp32 N x rows            Y[n * rows + r] = sum over k of
+ *                                   W~[r][k] * X~[n][k] (~ = quantized values)
+ *
+ * Errors: every entry point returns Q4BQ_OK (0) or a negative status and never
+ * aborts.  Arguments are checked before anything is enqueued; on Q4BQ_EINVAL
+ * nothing was launched and no output was touched.  Q4BQ_EHIP reports a HIP
+ * runtime or launch failure (outputs then undefined).  Inputs are assumed
+ * finite, with |W| / 8 and |X| / 127 below 65504 (the binary16 range); outside
+ * that the results are unspecified but the call still returns normally.
+ */
+#ifndef Q4BQ_H
+#define Q4BQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define Q4BQ_OK 0
+#define Q4BQ_EINVAL (-1) /* bad argument: null, size < 1, K % 32 != 0, misaligned, overlap */
+#define Q4BQ_EHIP (-2)   /* HIP runtime / launch failure */
+#define Q4BQ_ENOMEM (-3) /* scratch allocation failed, or workspace too small */
+
+#define Q4BQ_QK 32
+#define Q4BQ_Q4_0_BYTES 18
+#define Q4BQ_Q8_0_BYTES 34
+
+/*
+ * Q4_0 encode, "llama.cpp 深度解读" section 2, encode steps 1-4: per block of
+ * 32 weights, amax = max |w|; the scale amax / 8 is stored as binary16
+ * (round to nearest even, subnormals kept); q = round(w / d) + 8 with d the
+ * stored scale widened to fp32, round() half away from zero, clamped to
+ * [0, 15]; an all-zero block stores d = 0 and nibbles 8.
+ *   W   fp32 rows x K, 4-byte aligned.        Wq  rows*(K/32)*18 bytes, 2-byte aligned.
+ * Requires rows >= 1, K >= 32, K % 32 == 0.  Bit-exact; deterministic.
+ */
+int q4_0_quantize(const float *W, int64_t rows, int64_t K, void *Wq, void *stream);
+
+/*
+ * Q8_0 encode of activations (the rule the pages leave implicit, read as the
+ * Q4_0 rule with 127 levels): per block, d = binary16(amax / 127),
+ * q = round(x / d) clamped to [-127, 127], q = 0 when d == 0.
+ *   X   fp32 N x K, 4-byte aligned.           Xq  N*(K/32)*34 bytes, 2-byte aligned.
+ * Requires N >= 1, K >= 32, K % 32 == 0.  Bit-exact; deterministic.
+ */
+int q8_0_quantize(const float *X, int64_t N, int64_t K, void *Xq, void *stream);
+
+/*
+ * The operator: Y = mul_mat(Wq, X), "llama.cpp 深度解读" section 3 (Q4_0
+ * weights times Q8_0 activations, one fp32 scale d_w * d_x per 32-block, the
+ * block's integer dot of (nibble - 8) with the int8 activations accumulated in
+ * int32, the scaled block terms summed in fp32).  X is fp32; it is quantized
+ * to Q8_0 by exactly the rule of q8_0_quantize inside the call.
+ *   Wq  rows x (K/32) Q4_0 blocks, 2-byte aligned.
+ *   X   fp32 N x K, 4-byte aligned.
+ *   Y   fp32 N x rows, 4-byte aligned, overwritten; must not overlap Wq or X.
+ * N <= 8 runs the streaming decode kernel; larger N the int8 matrix-core
+ * kernel.  Needs stream-ordered scratch of q4bq_workspace_size(rows, K, N)
+ * bytes, taken with hipMallocAsync on `stream` (Q4BQ_ENOMEM if that fails).
+ * The summation order is fixed for a given (rows, K, N, device), so repeated
+ * calls give bitwise-identical Y.
+ */
+int mul_mat_q4_0_q8_0(const void *Wq, int64_t rows, int64_t K, const float *X,
+                      int64_t N, float *Y, void *stream);
+
+/* Scratch bytes the operator needs for these sizes (0 on invalid sizes). */
+size_t q4bq_workspace_size(int64_t rows, int64_t K, int64_t N);
+
+/*
+ * mul_mat_q4_0_q8_0 with caller-owned scratch: `workspace` is a device buffer
+ * of ws_bytes >= q4bq_workspace_size(rows, K, N), 16-byte aligned, not
+ * overlapping the other arguments (Q4BQ_ENOMEM if too small).  No allocation
+ * happens inside.  Same results as mul_mat_q4_0_q8_0, bit for bit.
+ */
+int mul_mat_q4_0_q8_0_ex(const void *Wq, int64_t rows, int64_t K, const float *X,
+                         int64_t N, float *Y, void *workspace, size_t ws_bytes,
+                         void *stream);
+
+/*
+ * Two-phase form of mul_mat_q4_0_q8_0_ex, for several products that share one
+ * activation matrix (for example the projections that read the same token
+ * vector).  q4bq_quantize_activations runs the Q8_0 rule of q8_0_quantize on
+ * X (fp32 N x K, 4-byte aligned) and leaves the result in `workspace` (16-byte
+ * aligned, ws_bytes >= q4bq_workspace_size(1, K, N); its contents are private
+ * to the library).  mul_mat_q4_0_q8_0_prepared then computes Y from Wq and
+ * that workspace; it may be called any number of times, for different Wq with
+ * the same K, while the workspace is left untouched.  Running the two in
+ * sequence gives exactly the Y of mul_mat_q4_0_q8_0.
+ */
+int q4bq_quantize_activations(const float *X, int64_t N, int64_t K, void *workspace,
+                              size_t ws_bytes, void *stream);
+int mul_mat_q4_0_q8_0_prepared(const void *Wq, int64_t rows, int64_t K,
+                               const void *workspace, int64_t N, float *Y, void *stream);
+
+/*
+ * The operator with pre-quantized activations: Xq holds N x (K/32) Q8_0 blocks
+ * (2-byte aligned), otherwise as mul_mat_q4_0_q8_0.  Feeding it the output of
+ * q8_0_quantize(X) gives exactly the Y of mul_mat_q4_0_q8_0(X).
+ */
+int mul_mat_q4_0_q8_0_pq(const void *Wq, int64_t rows, int64_t K, const void *Xq,
+                         int64_t N, float *Y, void *stream);
+
+/*
+ * Test export: every per-block integer dot, "llama.cpp 深度解读" section 3
+ * step 4 with the (nibble - 8) offset of section 2's decode:
+ *   D[(n * rows + r) * (K/32) + b] = sum_j (nibble_j(r, b) - 8) * q_j(n, b)
+ * (int32, exact).  Computed by the same block-dot code as the operator's
+ * kernel for this N (the decode kernel for N <= 8, the matrix-core kernel
+ * otherwise).  D: N*rows*(K/32) int32, 4-byte aligned, must not overlap the
+ * inputs.  Xq as in mul_mat_q4_0_q8_0_pq.
+ */
+int q4_0_q8_0_block_dots(const void *Wq, int64_t rows, int64_t K, const void *Xq,
+                         int64_t N, int32_t *D, void *stream);
+
+/* Static text for a status code. */
+const char *q4bq_status_string(int status);
+
+/* Library ABI version (major * 10000 + minor * 100 + patch). */
+int q4bq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4BQ_H */

@@ -1,0 +1,218 @@
+"""Python binding of libq4bq.so: argument marshalling only.
+
+Every function has the name of the C entry point it calls (include/q4bq.h),
+takes torch tensors that live on the current HIP device, passes their raw
+pointers and the current torch stream, and raises ``Q4BQError`` on a non-zero
+status.  All arithmetic happens in the library's HIP kernels; a missing or
+unloadable library raises -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libq4bq.so")
+
+QK = 32
+Q4_0_BYTES = 18
+Q8_0_BYTES = 34
+
+Q4BQ_OK = 0
+Q4BQ_EINVAL = -1
+Q4BQ_EHIP = -2
+Q4BQ_ENOMEM = -3
+
+EXPORTS = (
+    "q4_0_quantize", "q8_0_quantize", "mul_mat_q4_0_q8_0", "q4bq_workspace_size",
+    "mul_mat_q4_0_q8_0_ex", "mul_mat_q4_0_q8_0_pq", "q4_0_q8_0_block_dots",
+    "q4bq_status_string", "q4bq_version", "q4bq_quantize_activations", "mul_mat_q4_0_q8_0_prepared",
+)
+
+
+class Q4BQError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s failed: %d (%s)" % (where, status, status_string(status)))
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library, with argument and result types declared."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libq4bq.so is not built (%s); run `python -m q4_block_quantized_amd.build`" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    sigs = {
+        "q4_0_quantize": (I, [P, I64, I64, P, P]),
+        "q8_0_quantize": (I, [P, I64, I64, P, P]),
+        "mul_mat_q4_0_q8_0": (I, [P, I64, I64, P, I64, P, P]),
+        "q4bq_workspace_size": (ctypes.c_size_t, [I64, I64, I64]),
+        "mul_mat_q4_0_q8_0_ex": (I, [P, I64, I64, P, I64, P, P, ctypes.c_size_t, P]),
+        "mul_mat_q4_0_q8_0_pq": (I, [P, I64, I64, P, I64, P, P]),
+        "q4_0_q8_0_block_dots": (I, [P, I64, I64, P, I64, P, P]),
+        "q4bq_quantize_activations": (I, [P, I64, I64, P, ctypes.c_size_t, P]),
+        "mul_mat_q4_0_q8_0_prepared": (I, [P, I64, I64, P, I64, P, P]),
+        "q4bq_status_string": (ctypes.c_char_p, [I]),
+        "q4bq_version": (I, []),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().q4bq_status_string(int(status)).decode()
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != Q4BQ_OK:
+        raise Q4BQError(rc, where)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _dev(t: torch.Tensor, dtype, name: str) -> int:
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t.data_ptr()
+
+
+def _nb(K: int) -> int:
+    if K < QK or K % QK:
+        raise ValueError("K must be a positive multiple of 32, got %d" % K)
+    return K // QK
+
+
+# --- entry points -------------------------------------------------------------
+
+def q4_0_quantize(W: torch.Tensor, Wq: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """fp32 rows x K -> uint8 rows x (K/32*18) Q4_0 blocks."""
+    rows, K = W.shape
+    nb = _nb(K)
+    if Wq is None:
+        Wq = torch.empty((rows, nb * Q4_0_BYTES), dtype=torch.uint8, device=W.device)
+    _check(lib().q4_0_quantize(_dev(W, torch.float32, "W"), rows, K, _dev(Wq, torch.uint8, "Wq"),
+                               _stream(stream)), "q4_0_quantize")
+    return Wq
+
+
+def q8_0_quantize(X: torch.Tensor, Xq: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """fp32 N x K -> uint8 N x (K/32*34) Q8_0 blocks."""
+    N, K = X.shape
+    nb = _nb(K)
+    if Xq is None:
+        Xq = torch.empty((N, nb * Q8_0_BYTES), dtype=torch.uint8, device=X.device)
+    _check(lib().q8_0_quantize(_dev(X, torch.float32, "X"), N, K, _dev(Xq, torch.uint8, "Xq"),
+                               _stream(stream)), "q8_0_quantize")
+    return Xq
+
+
+def _rows(Wq: torch.Tensor, K: int) -> int:
+    nb = _nb(K)
+    if Wq.numel() % (nb * Q4_0_BYTES):
+        raise ValueError("Wq size %d is not a whole number of rows of K=%d" % (Wq.numel(), K))
+    return Wq.numel() // (nb * Q4_0_BYTES)
+
+
+def mul_mat_q4_0_q8_0(Wq: torch.Tensor, X: torch.Tensor, Y: torch.Tensor | None = None,
+                      stream=None) -> torch.Tensor:
+    """Y (N x rows, fp32) = Q4_0 weights Wq times fp32 activations X (N x K)."""
+    N, K = X.shape
+    rows = _rows(Wq, K)
+    if Y is None:
+        Y = torch.empty((N, rows), dtype=torch.float32, device=X.device)
+    _check(lib().mul_mat_q4_0_q8_0(_dev(Wq, torch.uint8, "Wq"), rows, K, _dev(X, torch.float32, "X"), N,
+                                   _dev(Y, torch.float32, "Y"), _stream(stream)), "mul_mat_q4_0_q8_0")
+    return Y
+
+
+def q4bq_workspace_size(rows: int, K: int, N: int) -> int:
+    return int(lib().q4bq_workspace_size(rows, K, N))
+
+
+def workspace(rows: int, K: int, N: int, device=None) -> torch.Tensor:
+    """A device buffer big enough for mul_mat_q4_0_q8_0_ex at these sizes."""
+    n = q4bq_workspace_size(rows, K, N)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device or "cuda")
+
+
+def mul_mat_q4_0_q8_0_ex(Wq: torch.Tensor, X: torch.Tensor, ws: torch.Tensor, Y: torch.Tensor | None = None,
+                         stream=None) -> torch.Tensor:
+    N, K = X.shape
+    rows = _rows(Wq, K)
+    if Y is None:
+        Y = torch.empty((N, rows), dtype=torch.float32, device=X.device)
+    _check(lib().mul_mat_q4_0_q8_0_ex(_dev(Wq, torch.uint8, "Wq"), rows, K, _dev(X, torch.float32, "X"), N,
+                                      _dev(Y, torch.float32, "Y"), _dev(ws, torch.uint8, "workspace"),
+                                      ws.numel(), _stream(stream)), "mul_mat_q4_0_q8_0_ex")
+    return Y
+
+
+def q4bq_quantize_activations(X: torch.Tensor, ws: torch.Tensor, stream=None) -> torch.Tensor:
+    """Quantize X (N x K fp32) into the workspace for mul_mat_q4_0_q8_0_prepared."""
+    N, K = X.shape
+    _nb(K)
+    _check(lib().q4bq_quantize_activations(_dev(X, torch.float32, "X"), N, K, _dev(ws, torch.uint8, "workspace"),
+                                           ws.numel(), _stream(stream)), "q4bq_quantize_activations")
+    return ws
+
+
+def mul_mat_q4_0_q8_0_prepared(Wq: torch.Tensor, ws: torch.Tensor, N: int, K: int, Y: torch.Tensor | None = None,
+                               stream=None) -> torch.Tensor:
+    rows = _rows(Wq, K)
+    if Y is None:
+        Y = torch.empty((N, rows), dtype=torch.float32, device=Wq.device)
+    _check(lib().mul_mat_q4_0_q8_0_prepared(_dev(Wq, torch.uint8, "Wq"), rows, K, _dev(ws, torch.uint8, "workspace"),
+                                            N, _dev(Y, torch.float32, "Y"), _stream(stream)),
+           "mul_mat_q4_0_q8_0_prepared")
+    return Y
+
+
+def mul_mat_q4_0_q8_0_pq(Wq: torch.Tensor, Xq: torch.Tensor, K: int, Y: torch.Tensor | None = None,
+                         stream=None) -> torch.Tensor:
+    nb = _nb(K)
+    if Xq.numel() % (nb * Q8_0_BYTES):
+        raise ValueError("Xq size is not a whole number of Q8_0 rows")
+    N = Xq.numel() // (nb * Q8_0_BYTES)
+    rows = _rows(Wq, K)
+    if Y is None:
+        Y = torch.empty((N, rows), dtype=torch.float32, device=Xq.device)
+    _check(lib().mul_mat_q4_0_q8_0_pq(_dev(Wq, torch.uint8, "Wq"), rows, K, _dev(Xq, torch.uint8, "Xq"), N,
+                                      _dev(Y, torch.float32, "Y"), _stream(stream)), "mul_mat_q4_0_q8_0_pq")
+    return Y
+
+
+def q4_0_q8_0_block_dots(Wq: torch.Tensor, Xq: torch.Tensor, K: int, D: torch.Tensor | None = None,
+                         stream=None) -> torch.Tensor:
+    """int32 N x rows x (K/32): every per-block integer dot."""
+    nb = _nb(K)
+    N = Xq.numel() // (nb * Q8_0_BYTES)
+    rows = _rows(Wq, K)
+    if D is None:
+        D = torch.empty((N, rows, nb), dtype=torch.int32, device=Xq.device)
+    _check(lib().q4_0_q8_0_block_dots(_dev(Wq, torch.uint8, "Wq"), rows, K, _dev(Xq, torch.uint8, "Xq"), N,
+                                      _dev(D, torch.int32, "D"), _stream(stream)), "q4_0_q8_0_block_dots")
+    return D
+
+
+def q4bq_version() -> int:
+    return int(lib().q4bq_version())

@@ -1,0 +1,238 @@
+// C ABI of libq4bq.so: argument checks, dispatch, scratch handling.
+// See include/q4bq.h for the contract of each entry point.
+#include "q4bq.h"
+
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+
+#include "q4bq_internal.h"
+
+namespace q4bq {
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_once[kMaxDevices];
+DeviceInfo g_dev[kMaxDevices];
+hipError_t g_dev_err[kMaxDevices];
+
+// Largest sizes accepted: keep every byte offset far inside int64 and every
+// per-row block index inside int32.
+constexpr int64_t kMaxDim = int64_t(1) << 40;
+constexpr int64_t kMaxBlocksPerRow = int64_t(1) << 30;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool overlap(const void* a, size_t an, const void* b, size_t bn) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + bn && y < x + an;
+}
+
+bool bad_k(int64_t K) { return K < kQK || K % kQK != 0 || K / kQK > kMaxBlocksPerRow; }
+bool bad_dim(int64_t n) { return n < 1 || n > kMaxDim; }
+
+int status_of(hipError_t e) { return e == hipSuccess ? Q4BQ_OK : Q4BQ_EHIP; }
+
+// Sizes whose products could overflow the byte arithmetic are rejected.
+bool too_big(int64_t a, int64_t b, int64_t bytes_per) {
+    // a * b * bytes_per < 2^62
+    const double v = static_cast<double>(a) * static_cast<double>(b) * static_cast<double>(bytes_per);
+    return v >= 4.0e18;
+}
+
+int run_product(const uint8_t* Wq, int64_t rows, int64_t K, const float* X, const uint8_t* Xq, int64_t N,
+                float* Y, int32_t* D, void* ws, hipStream_t s) {
+    hipError_t err = hipSuccess;
+    const DeviceInfo* dev = current_device(&err);
+    if (!dev) return Q4BQ_EHIP;
+    const int64_t nb = K / kQK;
+    err = X ? launch_act_from_f32(X, N, nb, ws, s) : launch_act_from_q8(Xq, N, nb, ws, s);
+    if (err != hipSuccess) return Q4BQ_EHIP;
+    if (N <= kGemvMaxN)
+        err = launch_gemv(dev, Wq, rows, nb, ws, N, Y, D, s);
+    else
+        err = launch_gemm(dev, Wq, rows, nb, ws, N, Y, D, s);
+    return status_of(err);
+}
+
+// Runs the product with stream-ordered scratch taken from the device pool.
+int run_with_scratch(const uint8_t* Wq, int64_t rows, int64_t K, const float* X, const uint8_t* Xq, int64_t N,
+                     float* Y, int32_t* D, hipStream_t s) {
+    hipError_t err = hipSuccess;
+    if (!current_device(&err)) return Q4BQ_EHIP;
+    const size_t bytes = q4bq_workspace_size(rows, K, N);
+    void* ws = nullptr;
+    if (hipMallocAsync(&ws, bytes, s) != hipSuccess || ws == nullptr) {
+        (void)hipGetLastError();
+        return Q4BQ_ENOMEM;
+    }
+    const int rc = run_product(Wq, rows, K, X, Xq, N, Y, D, ws, s);
+    if (hipFreeAsync(ws, s) != hipSuccess) return Q4BQ_EHIP;
+    return rc;
+}
+
+}  // namespace
+
+const DeviceInfo* current_device(hipError_t* err) {
+    int id = 0;
+    hipError_t e = hipGetDevice(&id);
+    if (e != hipSuccess || id < 0 || id >= kMaxDevices) {
+        *err = e != hipSuccess ? e : hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::call_once(g_once[id], [id] {
+        DeviceInfo d{id, 0, 1};
+        hipError_t r = hipDeviceGetAttribute(&d.num_cu, hipDeviceAttributeMultiprocessorCount, id);
+        if (r == hipSuccess && d.num_cu <= 0) r = hipErrorInvalidDevice;
+        d.num_xcd = 8;
+        g_dev[id] = d;
+        g_dev_err[id] = r;
+    });
+    if (g_dev_err[id] != hipSuccess) {
+        *err = g_dev_err[id];
+        return nullptr;
+    }
+    return &g_dev[id];
+}
+
+}  // namespace q4bq
+
+using namespace q4bq;
+
+extern "C" {
+
+int q4_0_quantize(const float* W, int64_t rows, int64_t K, void* Wq, void* stream) {
+    if (!W || !Wq || bad_dim(rows) || bad_k(K) || too_big(rows, K, 4)) return Q4BQ_EINVAL;
+    if (!aligned(W, 4) || !aligned(Wq, 2)) return Q4BQ_EINVAL;
+    const int64_t nblocks = rows * (K / kQK);
+    if (overlap(W, static_cast<size_t>(rows * K) * 4, Wq, static_cast<size_t>(nblocks) * kQ4Bytes))
+        return Q4BQ_EINVAL;
+    return status_of(launch_q4_0_quantize(W, nblocks, static_cast<uint8_t*>(Wq), static_cast<hipStream_t>(stream)));
+}
+
+int q8_0_quantize(const float* X, int64_t N, int64_t K, void* Xq, void* stream) {
+    if (!X || !Xq || bad_dim(N) || bad_k(K) || too_big(N, K, 4)) return Q4BQ_EINVAL;
+    if (!aligned(X, 4) || !aligned(Xq, 2)) return Q4BQ_EINVAL;
+    const int64_t nblocks = N * (K / kQK);
+    if (overlap(X, static_cast<size_t>(N * K) * 4, Xq, static_cast<size_t>(nblocks) * kQ8Bytes))
+        return Q4BQ_EINVAL;
+    return status_of(launch_q8_0_quantize(X, nblocks, static_cast<uint8_t*>(Xq), static_cast<hipStream_t>(stream)));
+}
+
+size_t q4bq_workspace_size(int64_t rows, int64_t K, int64_t N) {
+    if (bad_dim(rows) || bad_dim(N) || bad_k(K) || too_big(N, K, 4)) return 0;
+    const size_t b = act_bytes(N, K / kQK);
+    return (b + 255) & ~static_cast<size_t>(255);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Common checks of the product entry points.  The activation operand is one
+// of: fp32 X (kF32, 4-byte aligned), Q8_0 blocks (kQ8, 2-byte aligned) or the
+// library's prepared workspace (kPrepared, 16-byte aligned).  dots: the output
+// is the int32 block-dot array (N * rows * K/32) instead of Y (N * rows).
+enum ActKind { kF32, kQ8, kPrepared };
+
+int check_product(const void* Wq, int64_t rows, int64_t K, const void* Xany, ActKind kind, int64_t N,
+                  const void* out, bool dots) {
+    if (!Wq || !Xany || !out || bad_dim(rows) || bad_dim(N) || bad_k(K)) return Q4BQ_EINVAL;
+    const int64_t nb = K / kQK;
+    if (too_big(rows, K, 1) || too_big(N, K, 4) || too_big(N, rows, 4)) return Q4BQ_EINVAL;
+    if (dots && too_big(N * rows, nb, 4)) return Q4BQ_EINVAL;
+    const uintptr_t x_align = kind == kF32 ? 4 : kind == kQ8 ? 2 : 16;
+    if (!aligned(Wq, 2) || !aligned(Xany, x_align) || !aligned(out, 4)) return Q4BQ_EINVAL;
+    const size_t w_bytes = static_cast<size_t>(rows * nb) * kQ4Bytes;
+    const size_t x_bytes = kind == kF32 ? static_cast<size_t>(N * K) * 4
+                           : kind == kQ8 ? static_cast<size_t>(N * nb) * kQ8Bytes
+                                         : act_bytes(N, nb);
+    const size_t o_bytes = static_cast<size_t>(N * rows) * 4 * static_cast<size_t>(dots ? nb : 1);
+    if (overlap(out, o_bytes, Wq, w_bytes) || overlap(out, o_bytes, Xany, x_bytes)) return Q4BQ_EINVAL;
+    return Q4BQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mul_mat_q4_0_q8_0(const void* Wq, int64_t rows, int64_t K, const float* X, int64_t N, float* Y, void* stream) {
+    const int rc = check_product(Wq, rows, K, X, kF32, N, Y, false);
+    if (rc != Q4BQ_OK) return rc;
+    return run_with_scratch(static_cast<const uint8_t*>(Wq), rows, K, X, nullptr, N, Y, nullptr,
+                            static_cast<hipStream_t>(stream));
+}
+
+int mul_mat_q4_0_q8_0_ex(const void* Wq, int64_t rows, int64_t K, const float* X, int64_t N, float* Y,
+                         void* workspace, size_t ws_bytes, void* stream) {
+    const int rc = check_product(Wq, rows, K, X, kF32, N, Y, false);
+    if (rc != Q4BQ_OK) return rc;
+    if (!workspace || !aligned(workspace, 16)) return Q4BQ_EINVAL;
+    const size_t need = q4bq_workspace_size(rows, K, N);
+    if (ws_bytes < need) return Q4BQ_ENOMEM;
+    const int64_t nb = K / kQK;
+    if (overlap(workspace, need, Y, static_cast<size_t>(N * rows) * 4) ||
+        overlap(workspace, need, X, static_cast<size_t>(N * K) * 4) ||
+        overlap(workspace, need, Wq, static_cast<size_t>(rows * nb) * kQ4Bytes))
+        return Q4BQ_EINVAL;
+    return run_product(static_cast<const uint8_t*>(Wq), rows, K, X, nullptr, N, Y, nullptr, workspace,
+                       static_cast<hipStream_t>(stream));
+}
+
+int mul_mat_q4_0_q8_0_pq(const void* Wq, int64_t rows, int64_t K, const void* Xq, int64_t N, float* Y,
+                         void* stream) {
+    const int rc = check_product(Wq, rows, K, Xq, kQ8, N, Y, false);
+    if (rc != Q4BQ_OK) return rc;
+    return run_with_scratch(static_cast<const uint8_t*>(Wq), rows, K, nullptr, static_cast<const uint8_t*>(Xq), N,
+                            Y, nullptr, static_cast<hipStream_t>(stream));
+}
+
+int q4_0_q8_0_block_dots(const void* Wq, int64_t rows, int64_t K, const void* Xq, int64_t N, int32_t* D,
+                         void* stream) {
+    const int rc = check_product(Wq, rows, K, Xq, kQ8, N, D, true);
+    if (rc != Q4BQ_OK) return rc;
+    return run_with_scratch(static_cast<const uint8_t*>(Wq), rows, K, nullptr, static_cast<const uint8_t*>(Xq), N,
+                            nullptr, D, static_cast<hipStream_t>(stream));
+}
+
+int q4bq_quantize_activations(const float* X, int64_t N, int64_t K, void* workspace, size_t ws_bytes,
+                              void* stream) {
+    if (!X || !workspace || bad_dim(N) || bad_k(K) || too_big(N, K, 4)) return Q4BQ_EINVAL;
+    if (!aligned(X, 4) || !aligned(workspace, 16)) return Q4BQ_EINVAL;
+    const size_t need = q4bq_workspace_size(1, K, N);
+    if (ws_bytes < need) return Q4BQ_ENOMEM;
+    if (overlap(workspace, need, X, static_cast<size_t>(N * K) * 4)) return Q4BQ_EINVAL;
+    hipError_t err = hipSuccess;
+    if (!current_device(&err)) return Q4BQ_EHIP;
+    return status_of(launch_act_from_f32(X, N, K / kQK, workspace, static_cast<hipStream_t>(stream)));
+}
+
+int mul_mat_q4_0_q8_0_prepared(const void* Wq, int64_t rows, int64_t K, const void* workspace, int64_t N, float* Y,
+                               void* stream) {
+    const int rc = check_product(Wq, rows, K, workspace, kPrepared, N, Y, false);
+    if (rc != Q4BQ_OK) return rc;
+    hipError_t err = hipSuccess;
+    const DeviceInfo* dev = current_device(&err);
+    if (!dev) return Q4BQ_EHIP;
+    const int64_t nb = K / kQK;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    err = N <= kGemvMaxN ? launch_gemv(dev, static_cast<const uint8_t*>(Wq), rows, nb, workspace, N, Y, nullptr, s)
+                         : launch_gemm(dev, static_cast<const uint8_t*>(Wq), rows, nb, workspace, N, Y, nullptr, s);
+    return status_of(err);
+}
+
+const char* q4bq_status_string(int status) {
+    switch (status) {
+        case Q4BQ_OK: return "ok";
+        case Q4BQ_EINVAL: return "invalid argument (null pointer, size < 1, K not a positive multiple of 32, "
+                                 "misaligned pointer or overlapping buffers)";
+        case Q4BQ_EHIP: return "HIP runtime or kernel launch failure";
+        case Q4BQ_ENOMEM: return "scratch allocation failed or workspace too small";
+        default: return "unknown status";
+    }
+}
+
+int q4bq_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,237 @@
+// Decode product, N = 1..8 tokens: Y[n][r] = sum_b d_w(r,b) * d_x(n,b) * s(r,n,b).
+//
+// The per-block integer dot s follows ggml_vec_dot_q4_0_q8_0 as described in
+// "llama.cpp 深度解读" (luoboask.github.io) section 3 "量化矩阵乘法 — 核心算子":
+// unpack the two nibbles of each byte, multiply by the int8 activations,
+// accumulate in int32, then scale by the fp32 product of the two fp16 block
+// scales; the nibble offset of 8 comes from section 2's decode.
+//
+// The kernel is bound by streaming the Q4_0 weights from HBM once:
+//  * each lane owns whole pairs of consecutive blocks of a row (36 bytes,
+//    three loads) -- G lanes share a row, 64/G rows per wave per row slot,
+//    and a lane carries up to kRmax rows at a time so that several pairs are
+//    in flight and each activation read serves several rows;
+//  * a nibble word splits into low/high nibbles with one AND and one
+//    shift+AND and meets the activations (stored in the matching order by the
+//    quantizer) in v_dot4_i32_i8, seeded with -8 * sum(q) so the offset costs
+//    nothing per element;
+//  * per block one convert and one FMA fold the int32 dot into fp32;
+//  * lanes of a row combine with a butterfly over G lanes.
+// Activations come from the quantizer's buffer, staged in LDS when they fit.
+#include "q4bq_device.h"
+#include "q4bq_internal.h"
+
+namespace q4bq {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kRmax = 4;          // rows per lane per task
+constexpr int kU = 2;             // pair slots per load batch
+constexpr size_t kMaxActLds = 64 * 1024;
+
+template <int NT, bool ACT_LDS, bool DOTS>
+__global__ void __launch_bounds__(kThreads)
+k_gemv(const uint8_t* __restrict__ Wq, int64_t rows, int nb,
+       const uint32_t* __restrict__ act_q_g, const ActScale* __restrict__ act_s_g,
+       float* __restrict__ Y, int32_t* __restrict__ D, int log2G, int rpi) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    const uint32_t* act_q = act_q_g;
+    const ActScale* act_s = act_s_g;
+    if constexpr (ACT_LDS) {
+        uint32_t* sq = reinterpret_cast<uint32_t*>(smem);
+        ActScale* ss = reinterpret_cast<ActScale*>(smem + static_cast<size_t>(NT) * nb * kActQBytes);
+        const int nq = NT * nb * 2;  // 16-byte chunks of activation values
+        for (int c = threadIdx.x; c < nq; c += kThreads)
+            reinterpret_cast<u32x4*>(sq)[c] = reinterpret_cast<const u32x4*>(act_q_g)[c];
+        for (int c = threadIdx.x; c < NT * nb; c += kThreads) ss[c] = act_s_g[c];
+        __syncthreads();
+        act_q = sq;
+        act_s = ss;
+    }
+
+    const int G = 1 << log2G;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int grp = lane >> log2G;
+    const int pos = lane & (G - 1);
+    const int RW = 64 >> log2G;                 // rows per wave per row slot
+    const int P = nb >> 1;                      // whole pairs per row
+    const int PPL = (P + G - 1) >> log2G;       // pair slots per lane
+    const int64_t rows_per_task = static_cast<int64_t>(RW) * rpi;
+    const int64_t ntasks = (rows + rows_per_task - 1) / rows_per_task;
+
+    for (int64_t task = static_cast<int64_t>(blockIdx.x) * kWaves + wave; task < ntasks;
+         task += static_cast<int64_t>(gridDim.x) * kWaves) {
+        int64_t r[kRmax];
+        bool rv[kRmax];
+#pragma unroll
+        for (int j = 0; j < kRmax; ++j) {
+            r[j] = task * rows_per_task + static_cast<int64_t>(j) * RW + grp;
+            rv[j] = (j < rpi) && (r[j] < rows);
+        }
+        float acc[kRmax][NT];
+#pragma unroll
+        for (int j = 0; j < kRmax; ++j)
+#pragma unroll
+            for (int n = 0; n < NT; ++n) acc[j][n] = 0.0f;
+
+        for (int i0 = 0; i0 < PPL; i0 += kU) {
+            Pair36 raw[kRmax][kU];
+            bool pv[kU];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) pv[u] = (pos + ((i0 + u) << log2G)) < P;
+            // issue every load of the batch before using any
+#pragma unroll
+            for (int j = 0; j < kRmax; ++j)
+#pragma unroll
+                for (int u = 0; u < kU; ++u) {
+                    const int p = pos + ((i0 + u) << log2G);
+                    if (rv[j] && pv[u])
+                        raw[j][u] = load_pair(Wq + (r[j] * nb + 2 * p) * kQ4Bytes);
+                }
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                if (!pv[u]) continue;
+                const int p = pos + ((i0 + u) << log2G);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int b = 2 * p + h;
+#pragma unroll
+                    for (int n = 0; n < NT; ++n) {
+                        const int64_t ab = static_cast<int64_t>(n) * nb + b;
+                        const u32x4 a0 = reinterpret_cast<const u32x4*>(act_q + ab * 8)[0];
+                        const u32x4 a1 = reinterpret_cast<const u32x4*>(act_q + ab * 8)[1];
+                        const ActScale sc = act_s[ab];
+                        const uint32_t a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+                        for (int j = 0; j < kRmax; ++j) {
+                            if (!rv[j]) continue;
+                            const Block4 blk = h ? pair_second(raw[j][u]) : pair_first(raw[j][u]);
+                            const int32_t s = block_dot(blk, a, sc.bias);
+                            if constexpr (DOTS) {
+                                D[(static_cast<int64_t>(n) * rows + r[j]) * nb + b] = s;
+                            } else {
+                                acc[j][n] = fmaf(static_cast<float>(s), half_bits_to_float(blk.dbits) * sc.d,
+                                                 acc[j][n]);
+                            }
+                        }
+                    }
+                }
+            }
+        }
+        if ((nb & 1) && pos == 0) {  // a row with an odd block count ends in one lone block
+            const int b = nb - 1;
+#pragma unroll
+            for (int j = 0; j < kRmax; ++j) {
+                if (!rv[j]) continue;
+                const Block4 blk = load_block(Wq + (r[j] * nb + b) * kQ4Bytes);
+#pragma unroll
+                for (int n = 0; n < NT; ++n) {
+                    const int64_t ab = static_cast<int64_t>(n) * nb + b;
+                    const u32x4 a0 = reinterpret_cast<const u32x4*>(act_q + ab * 8)[0];
+                    const u32x4 a1 = reinterpret_cast<const u32x4*>(act_q + ab * 8)[1];
+                    const ActScale sc = act_s[ab];
+                    const uint32_t a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+                    const int32_t s = block_dot(blk, a, sc.bias);
+                    if constexpr (DOTS) {
+                        D[(static_cast<int64_t>(n) * rows + r[j]) * nb + b] = s;
+                    } else {
+                        acc[j][n] = fmaf(static_cast<float>(s), half_bits_to_float(blk.dbits) * sc.d, acc[j][n]);
+                    }
+                }
+            }
+        }
+        if constexpr (!DOTS) {
+            for (int m = G >> 1; m >= 1; m >>= 1) {
+#pragma unroll
+                for (int j = 0; j < kRmax; ++j)
+#pragma unroll
+                    for (int n = 0; n < NT; ++n) acc[j][n] += __shfl_xor(acc[j][n], m, 64);
+            }
+            if (pos == 0) {
+#pragma unroll
+                for (int j = 0; j < kRmax; ++j) {
+                    if (!rv[j]) continue;
+#pragma unroll
+                    for (int n = 0; n < NT; ++n) Y[static_cast<int64_t>(n) * rows + r[j]] = acc[j][n];
+                }
+            }
+        }
+    }
+}
+
+// Lanes per row: the power of two in [4, 64] that leaves the fewest idle
+// pair slots, the widest among equals (wider = more contiguous bytes per row).
+int pick_log2g(int64_t P) {
+    int best = 6;
+    double best_util = -1.0;
+    for (int lg = 6; lg >= 2; --lg) {
+        const int64_t G = int64_t(1) << lg;
+        const int64_t slots = ((P + G - 1) / G) * G;
+        const double util = slots > 0 ? static_cast<double>(P) / static_cast<double>(slots) : 1.0;
+        if (util > best_util + 1e-9) {
+            best_util = util;
+            best = lg;
+        }
+    }
+    return best;
+}
+
+template <int NT, bool ACT_LDS, bool DOTS>
+hipError_t launch_nt(const DeviceInfo* dev, const uint8_t* Wq, int64_t rows, int64_t nb, const void* act,
+                     float* Y, int32_t* D, hipStream_t s) {
+    const int log2G = pick_log2g(nb >> 1);
+    const int RW = 64 >> log2G;
+    // rows per lane: as many as keep >= 16 waves' worth of tasks per CU
+    const int64_t want_tasks = static_cast<int64_t>(dev->num_cu) * 16;
+    int rpi = 1;
+    for (int c = kRmax; c >= 1; c >>= 1) {
+        if ((rows + int64_t(RW) * c - 1) / (int64_t(RW) * c) >= want_tasks) {
+            rpi = c;
+            break;
+        }
+    }
+    const int64_t ntasks = (rows + int64_t(RW) * rpi - 1) / (int64_t(RW) * rpi);
+    int64_t wgs = (ntasks + kWaves - 1) / kWaves;
+    const int64_t cap = static_cast<int64_t>(dev->num_cu) * 8;
+    if (wgs > cap) wgs = cap;
+    const uint32_t* aq = static_cast<const uint32_t*>(act);
+    const ActScale* as = reinterpret_cast<const ActScale*>(static_cast<const uint8_t*>(act) + NT * nb * kActQBytes);
+    const size_t lds = ACT_LDS ? static_cast<size_t>(NT) * nb * (kActQBytes + kActSBytes) : 0;
+    hipLaunchKernelGGL((k_gemv<NT, ACT_LDS, DOTS>), dim3(static_cast<uint32_t>(wgs)), dim3(kThreads), lds, s, Wq,
+                       rows, static_cast<int>(nb), aq, as, Y, D, log2G, rpi);
+    return hipGetLastError();
+}
+
+template <int NT>
+hipError_t launch_n(const DeviceInfo* dev, const uint8_t* Wq, int64_t rows, int64_t nb, const void* act, float* Y,
+                    int32_t* D, hipStream_t s) {
+    const bool lds = static_cast<size_t>(NT) * nb * (kActQBytes + kActSBytes) <= kMaxActLds;
+    if (D) {
+        return lds ? launch_nt<NT, true, true>(dev, Wq, rows, nb, act, Y, D, s)
+                   : launch_nt<NT, false, true>(dev, Wq, rows, nb, act, Y, D, s);
+    }
+    return lds ? launch_nt<NT, true, false>(dev, Wq, rows, nb, act, Y, D, s)
+               : launch_nt<NT, false, false>(dev, Wq, rows, nb, act, Y, D, s);
+}
+
+}  // namespace
+
+hipError_t launch_gemv(const DeviceInfo* dev, const uint8_t* Wq, int64_t rows, int64_t nb, const void* act,
+                       int64_t N, float* Y, int32_t* D, hipStream_t s) {
+    switch (N) {
+        case 1: return launch_n<1>(dev, Wq, rows, nb, act, Y, D, s);
+        case 2: return launch_n<2>(dev, Wq, rows, nb, act, Y, D, s);
+        case 3: return launch_n<3>(dev, Wq, rows, nb, act, Y, D, s);
+        case 4: return launch_n<4>(dev, Wq, rows, nb, act, Y, D, s);
+        case 5: return launch_n<5>(dev, Wq, rows, nb, act, Y, D, s);
+        case 6: return launch_n<6>(dev, Wq, rows, nb, act, Y, D, s);
+        case 7: return launch_n<7>(dev, Wq, rows, nb, act, Y, D, s);
+        case 8: return launch_n<8>(dev, Wq, rows, nb, act, Y, D, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace q4bq

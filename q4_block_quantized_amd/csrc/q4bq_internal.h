@@ -1,0 +1,49 @@
+// Host-side launchers shared between the C-ABI layer and the kernel files.
+// Arguments are validated by the caller (q4bq_api.cpp); launchers only
+// enqueue work on `stream` and return hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace q4bq {
+
+constexpr int kQK = 32;         // values per block
+constexpr int kQ4Bytes = 18;    // Q4_0 block: binary16 d + 16 nibble bytes
+constexpr int kQ8Bytes = 34;    // Q8_0 block: binary16 d + 32 int8
+constexpr int kActQBytes = 32;  // internal activation block (int8, dot order)
+constexpr int kActSBytes = 8;   // internal scale record {float d; int32 bias}
+
+struct DeviceInfo {
+    int id;
+    int num_cu;
+    int num_xcd;
+};
+
+// Launch parameters of the device current on this thread (cached).
+const DeviceInfo* current_device(hipError_t* err);
+
+// Internal activation buffer: N*nb blocks of 32 bytes (dot order), then
+// N*nb scale records of 8 bytes; both [n][b] with b fastest.
+size_t act_bytes(int64_t N, int64_t nb);
+
+hipError_t launch_q4_0_quantize(const float* W, int64_t nblocks, uint8_t* Wq, hipStream_t s);
+hipError_t launch_q8_0_quantize(const float* X, int64_t nblocks, uint8_t* Xq, hipStream_t s);
+
+// fp32 X (N x K) -> internal activations, or Q8_0 blocks -> internal.
+hipError_t launch_act_from_f32(const float* X, int64_t N, int64_t nb, void* act, hipStream_t s);
+hipError_t launch_act_from_q8(const uint8_t* Xq, int64_t N, int64_t nb, void* act, hipStream_t s);
+
+// Streaming decode kernel, N in 1..8.  D != nullptr selects the block-dot
+// export (D written, Y untouched).
+hipError_t launch_gemv(const DeviceInfo* dev, const uint8_t* Wq, int64_t rows, int64_t nb,
+                       const void* act, int64_t N, float* Y, int32_t* D, hipStream_t s);
+
+// Matrix-core kernel, any N.  D as above.
+hipError_t launch_gemm(const DeviceInfo* dev, const uint8_t* Wq, int64_t rows, int64_t nb,
+                       const void* act, int64_t N, float* Y, int32_t* D, hipStream_t s);
+
+constexpr int64_t kGemvMaxN = 8;
+
+}  // namespace q4bq

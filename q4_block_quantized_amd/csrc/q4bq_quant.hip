@@ -1,0 +1,183 @@
+// Block quantizers.
+//
+// Q4_0 encode follows "llama.cpp 深度解读" (luoboask.github.io) section 2
+// "量化数据结构 — Q4_0 格式详解": per 32 weights take the largest magnitude, the
+// scale is that over 8, each weight becomes round(w / scale) + 8 and two 4-bit
+// values share a byte (even element low).  The scale is stored as binary16 and
+// the division uses the stored value; round() is half away from zero; values
+// are clamped to the nibble range [0, 15]; an all-zero block stores d = 0 and
+// nibble 8.  The Q8_0 activation rule is the same with 127 levels and a
+// symmetric clamp to [-127, 127].
+//
+// One half-wave (32 lanes) owns one block: lane e holds element e, the
+// largest magnitude is a 5-step butterfly, and lanes OR their small fields
+// together before a few 16/32-bit stores.
+#include "q4bq_device.h"
+#include "q4bq_internal.h"
+
+namespace q4bq {
+
+namespace {
+
+constexpr int kThreads = 256;  // 4 waves = 8 blocks per workgroup iteration
+
+__device__ __forceinline__ int quant4(float w, float d) {
+    if (d == 0.0f) return 8;
+    int q = static_cast<int>(__builtin_roundf(w / d)) + 8;
+    return min(max(q, 0), 15);
+}
+
+__device__ __forceinline__ int quant8(float x, float d) {
+    if (d == 0.0f) return 0;
+    int q = static_cast<int>(__builtin_roundf(x / d));
+    return min(max(q, -127), 127);
+}
+
+__global__ void __launch_bounds__(kThreads)
+k_q4_0_quantize(const float* __restrict__ W, int64_t nblocks, uint8_t* __restrict__ Wq) {
+    const int e = threadIdx.x & 31;
+    const int64_t first = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) >> 5;
+    const int64_t step = static_cast<int64_t>(gridDim.x) * (kThreads / 32);
+    // The trip count is uniform over the wave: both halves iterate together.
+    const int64_t wave_first = first & ~static_cast<int64_t>(1);
+    for (int64_t g0 = wave_first; g0 < nblocks; g0 += step) {
+        const int64_t g = g0 + (first & 1);
+        const bool valid = g < nblocks;
+        const float w = valid ? W[g * kQK + e] : 0.0f;
+        const float amax = max32(fabsf(w));
+        const uint32_t dbits = float_to_half_bits(amax / 8.0f);
+        const float d = half_bits_to_float(dbits);
+        const uint32_t q = static_cast<uint32_t>(quant4(w, d));
+        // 16-bit word j of the nibble bytes holds elements 4j..4j+3.
+        uint32_t v = q << (4 * (e & 3));
+        v = or_lanes(v, 1);
+        v = or_lanes(v, 2);
+        if (valid) {
+            uint16_t* out = reinterpret_cast<uint16_t*>(Wq + g * kQ4Bytes);
+            if ((e & 3) == 0) out[1 + (e >> 2)] = static_cast<uint16_t>(v);
+            if (e == 0) out[0] = static_cast<uint16_t>(dbits);
+        }
+    }
+}
+
+__global__ void __launch_bounds__(kThreads)
+k_q8_0_quantize(const float* __restrict__ X, int64_t nblocks, uint8_t* __restrict__ Xq) {
+    const int e = threadIdx.x & 31;
+    const int64_t first = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) >> 5;
+    const int64_t step = static_cast<int64_t>(gridDim.x) * (kThreads / 32);
+    const int64_t wave_first = first & ~static_cast<int64_t>(1);
+    for (int64_t g0 = wave_first; g0 < nblocks; g0 += step) {
+        const int64_t g = g0 + (first & 1);
+        const bool valid = g < nblocks;
+        const float x = valid ? X[g * kQK + e] : 0.0f;
+        const float amax = max32(fabsf(x));
+        const uint32_t dbits = float_to_half_bits(amax / 127.0f);
+        const float d = half_bits_to_float(dbits);
+        const uint32_t q = static_cast<uint32_t>(quant8(x, d)) & 0xFFu;
+        uint32_t v = q << (8 * (e & 1));
+        v = or_lanes(v, 1);
+        if (valid) {
+            uint16_t* out = reinterpret_cast<uint16_t*>(Xq + g * kQ8Bytes);
+            if ((e & 1) == 0) out[1 + (e >> 1)] = static_cast<uint16_t>(v);
+            if (e == 0) out[0] = static_cast<uint16_t>(dbits);
+        }
+    }
+}
+
+// Pack one block's int8 values (lane e holds q_e) into the internal dot order
+// and store it with its scale record.
+__device__ __forceinline__ void store_act(int e, int q, float d, bool valid, int64_t g,
+                                          uint32_t* __restrict__ act_q, ActScale* __restrict__ act_s) {
+    // element e -> dword 2*(e/8) + (e%2), byte (e/2)%4
+    uint32_t v = (static_cast<uint32_t>(q) & 0xFFu) << (8 * ((e >> 1) & 3));
+    v = or_lanes(v, 2);
+    v = or_lanes(v, 4);
+    const int bias = -8 * sum32(q);
+    if (valid) {
+        if ((e & 6) == 0) act_q[g * 8 + 2 * (e >> 3) + (e & 1)] = v;
+        if (e == 0) act_s[g] = ActScale{d, bias};
+    }
+}
+
+__global__ void __launch_bounds__(kThreads)
+k_act_from_f32(const float* __restrict__ X, int64_t nblocks, uint32_t* __restrict__ act_q,
+               ActScale* __restrict__ act_s) {
+    const int e = threadIdx.x & 31;
+    const int64_t first = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) >> 5;
+    const int64_t step = static_cast<int64_t>(gridDim.x) * (kThreads / 32);
+    const int64_t wave_first = first & ~static_cast<int64_t>(1);
+    for (int64_t g0 = wave_first; g0 < nblocks; g0 += step) {
+        const int64_t g = g0 + (first & 1);
+        const bool valid = g < nblocks;
+        const float x = valid ? X[g * kQK + e] : 0.0f;
+        const float amax = max32(fabsf(x));
+        const uint32_t dbits = float_to_half_bits(amax / 127.0f);
+        const float d = half_bits_to_float(dbits);
+        store_act(e, quant8(x, d), d, valid, g, act_q, act_s);
+    }
+}
+
+__global__ void __launch_bounds__(kThreads)
+k_act_from_q8(const uint8_t* __restrict__ Xq, int64_t nblocks, uint32_t* __restrict__ act_q,
+              ActScale* __restrict__ act_s) {
+    const int e = threadIdx.x & 31;
+    const int64_t first = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) >> 5;
+    const int64_t step = static_cast<int64_t>(gridDim.x) * (kThreads / 32);
+    const int64_t wave_first = first & ~static_cast<int64_t>(1);
+    for (int64_t g0 = wave_first; g0 < nblocks; g0 += step) {
+        const int64_t g = g0 + (first & 1);
+        const bool valid = g < nblocks;
+        int q = 0;
+        uint32_t dbits = 0;
+        if (valid) {
+            const uint8_t* blk = Xq + g * kQ8Bytes;
+            q = static_cast<int>(static_cast<int8_t>(blk[2 + e]));
+            uint16_t h;
+            __builtin_memcpy(&h, blk, 2);
+            dbits = h;
+        }
+        store_act(e, q, half_bits_to_float(dbits), valid, g, act_q, act_s);
+    }
+}
+
+int quant_grid(int64_t nblocks) {
+    int64_t wgs = (nblocks + (kThreads / 32) - 1) / (kThreads / 32);
+    const int64_t cap = 8192;
+    if (wgs > cap) wgs = cap;
+    if (wgs < 1) wgs = 1;
+    return static_cast<int>(wgs);
+}
+
+}  // namespace
+
+size_t act_bytes(int64_t N, int64_t nb) {
+    return static_cast<size_t>(N * nb) * (kActQBytes + kActSBytes);
+}
+
+hipError_t launch_q4_0_quantize(const float* W, int64_t nblocks, uint8_t* Wq, hipStream_t s) {
+    hipLaunchKernelGGL(k_q4_0_quantize, dim3(quant_grid(nblocks)), dim3(kThreads), 0, s, W, nblocks, Wq);
+    return hipGetLastError();
+}
+
+hipError_t launch_q8_0_quantize(const float* X, int64_t nblocks, uint8_t* Xq, hipStream_t s) {
+    hipLaunchKernelGGL(k_q8_0_quantize, dim3(quant_grid(nblocks)), dim3(kThreads), 0, s, X, nblocks, Xq);
+    return hipGetLastError();
+}
+
+hipError_t launch_act_from_f32(const float* X, int64_t N, int64_t nb, void* act, hipStream_t s) {
+    const int64_t nblocks = N * nb;
+    uint32_t* q = static_cast<uint32_t*>(act);
+    ActScale* sc = reinterpret_cast<ActScale*>(static_cast<uint8_t*>(act) + nblocks * kActQBytes);
+    hipLaunchKernelGGL(k_act_from_f32, dim3(quant_grid(nblocks)), dim3(kThreads), 0, s, X, nblocks, q, sc);
+    return hipGetLastError();
+}
+
+hipError_t launch_act_from_q8(const uint8_t* Xq, int64_t N, int64_t nb, void* act, hipStream_t s) {
+    const int64_t nblocks = N * nb;
+    uint32_t* q = static_cast<uint32_t*>(act);
+    ActScale* sc = reinterpret_cast<ActScale*>(static_cast<uint8_t*>(act) + nblocks * kActQBytes);
+    hipLaunchKernelGGL(k_act_from_q8, dim3(quant_grid(nblocks)), dim3(kThreads), 0, s, Xq, nblocks, q, sc);
+    return hipGetLastError();
+}
+
+}  // namespace q4bq

@@ -1,0 +1,124 @@
+"""The C ABI on the CPU: the library loads, exports every declared entry point,
+and rejects bad arguments before anything reaches the GPU.  No compute call
+is made here (there is no device in this test's environment)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "q4bq.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?(?:int|size_t|char)\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+
+
+@pytest.fixture(scope="module")
+def L():
+    import torch  # noqa: F401  (one HIP runtime per process: torch's)
+    from q4_block_quantized_amd import binding
+    return binding.lib()
+
+
+def test_header_declares_the_boundary():
+    names = set(_declared())
+    assert {"q4_0_quantize", "q8_0_quantize", "mul_mat_q4_0_q8_0", "q4bq_workspace_size",
+            "mul_mat_q4_0_q8_0_ex", "mul_mat_q4_0_q8_0_pq", "q4_0_q8_0_block_dots",
+            "q4bq_status_string", "q4bq_version"} <= names
+
+
+def test_every_declared_symbol_is_exported(L):
+    from q4_block_quantized_amd import binding
+    for name in _declared():
+        assert hasattr(L, name), name
+        assert name in binding.EXPORTS, name
+
+
+def test_status_strings(L):
+    for rc in (0, -1, -2, -3, 7):
+        assert isinstance(L.q4bq_status_string(rc), bytes)
+    assert L.q4bq_status_string(0) == b"ok"
+    assert L.q4bq_version() >= 100
+
+
+def test_workspace_size(L):
+    assert L.q4bq_workspace_size(4096, 4096, 1) == 128 * 40 + (256 - (128 * 40) % 256) % 256
+    assert L.q4bq_workspace_size(14336, 4096, 512) == 512 * 128 * 40
+    assert L.q4bq_workspace_size(1, 31, 1) == 0
+    assert L.q4bq_workspace_size(0, 32, 1) == 0
+    assert L.q4bq_workspace_size(1, 32, 0) == 0
+
+
+A = 0x100000          # fake, well-aligned device addresses: never dereferenced,
+B = 0x200000          # every call below must fail validation first
+C = 0x300000
+WS = 0x400000
+EINVAL, ENOMEM = -1, -3
+
+
+def _bad_product_calls(L):
+    f = L.mul_mat_q4_0_q8_0
+    yield f(None, 4, 64, B, 1, C, None)            # null weights
+    yield f(A, 4, 64, None, 1, C, None)            # null activations
+    yield f(A, 4, 64, B, 1, None, None)            # null output
+    yield f(A, 0, 64, B, 1, C, None)               # rows < 1
+    yield f(A, 4, 64, B, 0, C, None)               # N < 1
+    yield f(A, 4, -32, B, 1, C, None)              # K < 0
+    yield f(A, 4, 0, B, 1, C, None)                # K = 0
+    yield f(A, 4, 16, B, 1, C, None)               # K < 32
+    yield f(A, 4, 48, B, 1, C, None)               # K % 32 != 0
+    yield f(A + 1, 4, 64, B, 1, C, None)           # Q4_0 data on an odd address
+    yield f(A, 4, 64, B + 2, 1, C, None)           # fp32 X not 4-byte aligned
+    yield f(A, 4, 64, B, 1, C + 2, None)           # Y not 4-byte aligned
+    yield f(A, 4, 64, B, 1, A + 8, None)           # Y overlaps the weights
+    yield f(A, 4, 64, B, 2, B + 16, None)          # Y overlaps X
+    yield f(A, 1 << 41, 64, B, 1, C, None)         # absurd row count
+    g = L.mul_mat_q4_0_q8_0_pq
+    yield g(A, 4, 64, B + 1, 1, C, None)           # Q8_0 data on an odd address
+    yield g(A, 4, 80, B, 1, C, None)               # K % 32 != 0
+    d = L.q4_0_q8_0_block_dots
+    yield d(A, 4, 64, B, 1, C + 1, None)           # D misaligned
+    yield d(A, 4, 64, B, 1, None, None)
+    e = L.mul_mat_q4_0_q8_0_ex
+    yield e(A, 4, 64, B, 1, C, None, 1 << 20, None)         # null workspace
+    yield e(A, 4, 64, B, 1, C, WS + 8, 1 << 20, None)       # workspace not 16-byte aligned
+    yield e(A, 4, 64, B, 1, C, A, 1 << 20, None)            # workspace overlaps the weights
+    q4 = L.q4_0_quantize
+    yield q4(None, 4, 64, B, None)
+    yield q4(A, 4, 48, B, None)
+    yield q4(A + 2, 4, 64, B, None)
+    yield q4(A, 4, 64, B + 1, None)
+    yield q4(A, 4, 64, A + 4, None)                # output inside the input
+    q8 = L.q8_0_quantize
+    yield q8(A, 0, 64, B, None)
+    yield q8(A, 4, 33, B, None)
+    yield q8(A, 4, 64, B + 1, None)
+
+
+def test_bad_arguments_return_einval(L):
+    for i, rc in enumerate(_bad_product_calls(L)):
+        assert rc == EINVAL, "case %d returned %d" % (i, rc)
+
+
+def test_workspace_too_small_is_enomem(L):
+    need = L.q4bq_workspace_size(4, 64, 1)
+    assert L.mul_mat_q4_0_q8_0_ex(A, 4, 64, B, 1, C, WS, need - 1, None) == ENOMEM
+
+
+def _has_gpu():
+    import torch
+    return torch.cuda.device_count() > 0
+
+
+@pytest.mark.skipif(_has_gpu(), reason="checks the no-device path; a device is present")
+def test_no_device_is_ehip_not_abort(L):
+    # valid arguments, no device: the library must report a HIP failure
+    assert L.mul_mat_q4_0_q8_0(A, 4, 64, B, 1, C, None) == -2
+    assert L.mul_mat_q4_0_q8_0_ex(A, 4, 64, B, 1, C, WS, 1 << 20, None) == -2
+    assert L.q4_0_quantize(A, 4, 64, B, None) == -2
+    assert L.q4_0_q8_0_block_dots(A, 4, 64, B, 1, C, None) == -2

@@ -1,0 +1,250 @@
+"""Parity of the HIP path with the CPU oracle, through the C ABI.
+
+Bars (fixed before any kernel existed):
+  * Q4_0 / Q8_0 bytes and per-block int32 dots: bit-exact;
+  * fp32 outputs: |Y - Y_ref| <= 1e-4 * |Y_ref| + 1e-5 element-wise, Y_ref the
+    oracle's fp64 accumulation of exact per-block terms.
+
+Every input is seeded and synthetic (q4_block_quantized_amd.inputs); the oracle
+quantizes its own copy of each fp32 input, nothing it sees comes from the GPU.
+"""
+import numpy as np
+import pytest
+import torch
+
+from conftest import hexbytes, read_golden
+from q4_block_quantized_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+RTOL, ATOL = 1e-4, 1e-5
+
+
+@pytest.fixture(scope="module")
+def hip():
+    if not torch.cuda.is_available():
+        pytest.fail("no HIP device: the parity tests need an MI355X")
+    from q4_block_quantized_amd import binding
+    binding.lib()
+    return binding
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def assert_close(Y, Yref, what):
+    Y = Y.astype(np.float64)
+    err = np.abs(Y - Yref)
+    lim = RTOL * np.abs(Yref) + ATOL
+    bad = err > lim
+    if bad.any():
+        i = np.argwhere(bad)[0]
+        raise AssertionError("%s: %d of %d outside tolerance; first at %s: got %r want %r"
+                             % (what, int(bad.sum()), Y.size, tuple(i), Y[tuple(i)], Yref[tuple(i)]))
+
+
+def edge_blocks():
+    rng = np.random.default_rng(5)
+    parts = [inputs.random_matrix(51, 64, 32, 0.02), inputs.random_matrix(52, 64, 32, 1.0),
+             inputs.random_matrix(53, 16, 32, 1e-6), inputs.random_matrix(54, 16, 32, 1e-9),
+             inputs.random_matrix(55, 16, 32, 3000.0), np.zeros((2, 32), np.float32)]
+    spiky = inputs.random_matrix(56, 32, 32, 0.02)
+    spiky[np.arange(32), rng.integers(0, 32, 32)] *= 10.0
+    parts.append(spiky)
+    ties = np.zeros((2, 32), np.float32)
+    ties[0, :6] = [-1.0, 0.0625, -0.0625, 0.1875, 0.3125, 1.0]
+    ties[1, :5] = [0.9921875, 2.0 ** -8, -1.5 * 2.0 ** -7, 2.5 * 2.0 ** -7, -0.5 * 2.0 ** -7]
+    parts.append(ties)
+    ramp = np.array([((k % 16) - 8) / 8 for k in range(32)], np.float32)[None]
+    parts += [ramp, np.ones((1, 32), np.float32), -np.zeros((1, 32), np.float32)]
+    return np.concatenate(parts, axis=0)
+
+
+# ---------------------------------------------------------------------------
+# quantizers
+# ---------------------------------------------------------------------------
+
+def test_quantizers_golden_blocks(hip, orc):
+    ramp = np.array([((k % 16) - 8) / 8 for k in range(32)], np.float32)[None]
+    got = host(hip.q4_0_quantize(dev(ramp)))[0]
+    assert np.array_equal(got, hexbytes(read_golden("q4_0_ramp_block.txt")["bytes"][0]))
+    w = np.zeros((1, 32), np.float32)
+    w[0, :6] = [-1.0, 0.0625, -0.0625, 0.1875, 0.3125, 1.0]
+    assert np.array_equal(host(hip.q4_0_quantize(dev(w)))[0],
+                          hexbytes(read_golden("q4_0_tie_clip_block.txt")["bytes"][0]))
+    assert np.array_equal(host(hip.q8_0_quantize(dev(np.ones((1, 32), np.float32))))[0],
+                          hexbytes(read_golden("q8_0_ones_block.txt")["bytes"][0]))
+    z = np.zeros((1, 32), np.float32)
+    g = read_golden("zero_blocks.txt")
+    assert np.array_equal(host(hip.q4_0_quantize(dev(z)))[0], hexbytes(g["q4_0_bytes"][0]))
+    assert np.array_equal(host(hip.q8_0_quantize(dev(z)))[0], hexbytes(g["q8_0_bytes"][0]))
+
+
+def test_quantizers_edge_blocks(hip, orc):
+    E = edge_blocks()
+    assert np.array_equal(host(hip.q4_0_quantize(dev(E))), orc.q4_0_quantize(E))
+    assert np.array_equal(host(hip.q8_0_quantize(dev(E))), orc.q8_0_quantize(E))
+
+
+@pytest.mark.parametrize("rows,K", [(1, 32), (3, 96), (37, 160), (1000, 768), (257, 4096)])
+def test_quantizers_random(hip, orc, rows, K):
+    W = inputs.random_matrix(1000 + rows + K, rows, K, 0.02)
+    W[inputs.random_matrix(2000 + rows + K, rows, K) > 2.33] *= 10.0
+    assert np.array_equal(host(hip.q4_0_quantize(dev(W))), orc.q4_0_quantize(W))
+    X = inputs.random_matrix(3000 + rows + K, rows, K)
+    assert np.array_equal(host(hip.q8_0_quantize(dev(X))), orc.q8_0_quantize(X))
+
+
+def test_quantizers_fp16_scale_sweep(hip, orc):
+    """Blocks whose largest magnitude sweeps many binade positions, so the
+    binary16 rounding of amax/8 and amax/127 meets ties and subnormals."""
+    rng = np.random.default_rng(77)
+    amax = np.float32(2.0) ** rng.uniform(-27, 15, 4096).astype(np.float32)
+    amax = np.concatenate([amax, (np.arange(1, 2049, dtype=np.float32) * np.float32(2.0 ** -24)) * 8,
+                           (np.arange(1, 2049, dtype=np.float32) * np.float32(2.0 ** -24)) * 127])
+    B = rng.uniform(-1, 1, (amax.size, 32)).astype(np.float32) * amax[:, None]
+    B[np.arange(amax.size), rng.integers(0, 32, amax.size)] = amax * np.where(rng.random(amax.size) < 0.5, -1, 1)
+    B = B.astype(np.float32)
+    assert np.array_equal(host(hip.q4_0_quantize(dev(B))), orc.q4_0_quantize(B))
+    assert np.array_equal(host(hip.q8_0_quantize(dev(B))), orc.q8_0_quantize(B))
+
+
+# ---------------------------------------------------------------------------
+# block dots and the product on a shape sweep (tiles, ragged tails, odd K/32)
+# ---------------------------------------------------------------------------
+
+SWEEP_K = [32, 64, 96, 160, 768, 4096]
+SWEEP_ROWS = [1, 31, 64, 129, 1000]
+SWEEP_N = [1, 2, 3, 4, 5, 7, 8, 9, 16, 63, 64, 65, 130]
+
+
+def _case(rows, K, N, seed):
+    W = inputs.random_matrix(seed, rows, K, 0.02)
+    W[inputs.random_matrix(seed + 1, rows, K) > 2.33] *= 10.0
+    X = inputs.random_matrix(seed + 2, N, K)
+    return W, X
+
+
+@pytest.mark.parametrize("K", SWEEP_K)
+@pytest.mark.parametrize("rows", SWEEP_ROWS)
+def test_product_sweep(hip, orc, rows, K):
+    for N in SWEEP_N:
+        if rows * K * N > 40_000_000:
+            continue
+        print("sweep rows=%d K=%d N=%d" % (rows, K, N), flush=True)
+        W, X = _case(rows, K, N, 10 * rows + K + 100000 * N)
+        Wq_o, Xq_o = orc.q4_0_quantize(W), orc.q8_0_quantize(X)
+        Wq = hip.q4_0_quantize(dev(W))
+        Xt = dev(X)
+        D = host(hip.q4_0_q8_0_block_dots(Wq, hip.q8_0_quantize(Xt), K))
+        assert np.array_equal(D, orc.block_dots(Wq_o, Xq_o, K)), (rows, K, N)
+        Y = host(hip.mul_mat_q4_0_q8_0(Wq, Xt))
+        assert Y.shape == (N, rows)
+        assert_close(Y, orc.mul_mat_ref(Wq_o, Xq_o, K), "rows=%d K=%d N=%d" % (rows, K, N))
+
+
+def test_paths_agree_bitwise(hip, orc):
+    """Fused quantization, pre-quantized input, caller workspace and the
+    stream-ordered scratch give the same bits; so do repeated calls and a
+    non-default stream."""
+    for rows, K, N in [(777, 4096, 1), (300, 768, 8), (129, 160, 5), (1000, 4096, 70)]:
+        W, X = _case(rows, K, N, 555 + rows)
+        Wq = hip.q4_0_quantize(dev(W))
+        Xt = dev(X)
+        Y1 = hip.mul_mat_q4_0_q8_0(Wq, Xt)
+        Y2 = hip.mul_mat_q4_0_q8_0_pq(Wq, hip.q8_0_quantize(Xt), K)
+        Y3 = hip.mul_mat_q4_0_q8_0_ex(Wq, Xt, hip.workspace(rows, K, N))
+        Y4 = hip.mul_mat_q4_0_q8_0(Wq, Xt)
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            Y5 = hip.mul_mat_q4_0_q8_0(Wq, Xt)
+        s.synchronize()
+        ws = hip.workspace(rows, K, N)
+        Y6 = hip.mul_mat_q4_0_q8_0_prepared(Wq, hip.q4bq_quantize_activations(Xt, ws), N, K)
+        ref = host(Y1)
+        for other in (Y2, Y3, Y4, Y5, Y6):
+            assert np.array_equal(host(other), ref), (rows, K, N)
+
+
+def test_unaligned_but_valid_pointers(hip, orc):
+    """Q4_0 data may start on any 2-byte boundary, fp32 data on any 4-byte one."""
+    rows, K, N = 65, 4096, 3
+    W, X = _case(rows, K, N, 4242)
+    Wq_o, Xq_o = orc.q4_0_quantize(W), orc.q8_0_quantize(X)
+    nbytes = Wq_o.size
+    buf = torch.zeros(nbytes + 64, dtype=torch.uint8, device="cuda")
+    Wq_off = buf[2:2 + nbytes]                       # 2 mod 4 address
+    hip.q4_0_quantize(dev(W), Wq_off)
+    xbuf = torch.zeros(N * K + 4, dtype=torch.float32, device="cuda")
+    X_off = xbuf[1:1 + N * K].view(N, K)             # 4 mod 16 address
+    X_off.copy_(dev(X))
+    assert np.array_equal(host(Wq_off).reshape(rows, -1), Wq_o)
+    Yref = orc.mul_mat_ref(Wq_o, Xq_o, K)
+    assert_close(host(hip.mul_mat_q4_0_q8_0(Wq_off, X_off)), Yref, "unaligned gemv")
+    Xn = inputs.random_matrix(4343, 40, K)
+    xbuf2 = torch.zeros(40 * K + 4, dtype=torch.float32, device="cuda")
+    Xn_off = xbuf2[1:1 + 40 * K].view(40, K)
+    Xn_off.copy_(dev(Xn))
+    assert_close(host(hip.mul_mat_q4_0_q8_0(Wq_off, Xn_off)),
+                 orc.mul_mat_ref(Wq_o, orc.q8_0_quantize(Xn), K), "unaligned gemm")
+
+
+def test_empty_inputs_are_rejected(hip):
+    Wq = torch.zeros((4, 36), dtype=torch.uint8, device="cuda")
+    with pytest.raises(hip.Q4BQError) as e:
+        hip.mul_mat_q4_0_q8_0(Wq, torch.zeros((0, 64), dtype=torch.float32, device="cuda"))
+    assert e.value.status == hip.Q4BQ_EINVAL
+
+
+# ---------------------------------------------------------------------------
+# the five workloads at full size, in the benchmark's launch configuration
+# ---------------------------------------------------------------------------
+
+def _sample_rows(rows, n, seed):
+    rng = np.random.default_rng(seed)
+    pick = np.concatenate([np.arange(min(rows, 256)), np.arange(max(0, rows - 256), rows),
+                           rng.integers(0, rows, n)])
+    return np.unique(pick)
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+def test_workload_full_size(hip, orc, cid):
+    wl = inputs.WORKLOADS[cid]
+    nmax = max(wl.ns)
+    for m, (rows, K) in enumerate(wl.mats):
+        print("workload %s matrix %d (%d x %d)" % (wl.name, m, rows, K), flush=True)
+        W = inputs.weights(cid, m, rows, K, outliers=wl.outliers)
+        X = inputs.activations(cid, m, nmax, K)
+        Wt = dev(W)
+        Wq = hip.q4_0_quantize(Wt)
+        del Wt
+        sample = _sample_rows(rows, 2048, 9000 + cid * 10 + m) if rows * K > 20_000_000 else np.arange(rows)
+        Wq_o = orc.q4_0_quantize(W[sample])
+        del W
+        Wq_h = host(Wq)
+        assert np.array_equal(Wq_h[sample], Wq_o), "Q4_0 bytes differ"
+        for N in wl.ns:
+            Xt = dev(X[:N])
+            Xq = hip.q8_0_quantize(Xt)
+            Xq_o = orc.q8_0_quantize(X[:N])
+            assert np.array_equal(host(Xq), Xq_o), "Q8_0 bytes differ"
+            ws = hip.workspace(rows, K, N)
+            Y = host(hip.mul_mat_q4_0_q8_0_ex(Wq, Xt, ws))
+            assert_close(Y[:, sample], orc.mul_mat_ref(Wq_o, Xq_o, K), "%s N=%d" % (wl.name, N))
+            # block dots on a sample of outputs
+            tok = np.arange(N) if N <= 8 else np.unique(np.r_[0, N - 1, np.arange(1, N, 37)])
+            Dg = hip.q4_0_q8_0_block_dots(Wq, Xq, K)
+            idx_r = torch.from_numpy(sample).cuda()
+            idx_t = torch.from_numpy(tok).cuda()
+            Ds = host(Dg.index_select(0, idx_t).index_select(1, idx_r))
+            del Dg
+            assert np.array_equal(Ds, orc.block_dots(Wq_o, Xq_o[tok], K)), "block dots differ"
+        del Wq
+        torch.cuda.empty_cache()
