@@ -47,6 +47,7 @@ int run_product(const uint8_t* Wq, int64_t rows, int64_t K, const float* X, cons
     const DeviceInfo* dev = current_device(&err);
     if (!dev) return Q4BQ_EHIP;
     const int64_t nb = K / kQK;
+    if (X && !D && gemv_fuses(N, nb)) return status_of(launch_gemv_fused(dev, Wq, rows, nb, X, N, Y, s));
     err = X ? launch_act_from_f32(X, N, nb, ws, s) : launch_act_from_q8(Xq, N, nb, ws, s);
     if (err != hipSuccess) return Q4BQ_EHIP;
     if (N <= kGemvMaxN)
@@ -61,6 +62,7 @@ int run_with_scratch(const uint8_t* Wq, int64_t rows, int64_t K, const float* X,
                      float* Y, int32_t* D, hipStream_t s) {
     hipError_t err = hipSuccess;
     if (!current_device(&err)) return Q4BQ_EHIP;
+    if (X && !D && gemv_fuses(N, K / kQK)) return run_product(Wq, rows, K, X, Xq, N, Y, D, nullptr, s);
     const size_t bytes = q4bq_workspace_size(rows, K, N);
     void* ws = nullptr;
     if (hipMallocAsync(&ws, bytes, s) != hipSuccess || ws == nullptr) {

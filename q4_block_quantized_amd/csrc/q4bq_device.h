@@ -53,6 +53,40 @@ __device__ __forceinline__ uint32_t or_lanes(uint32_t v, int m) {
     return v | static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), m, 32));
 }
 
+// Q8_0 activation rule on four consecutive values of a block: lane m of an
+// aligned group of 8 lanes holds elements 4m..4m+3 of the same block.
+//   d = binary16(amax / 127) (widened back to fp32), q = round(x / d) half
+//   away from zero, clamped to [-127, 127]; q = 0 when d == 0.
+// Returns the block's scale record and writes this lane's dword of the block
+// in dot order: the lane pair (2k, 2k+1) covers elements 8k..8k+7; lane 2k
+// keeps the even ones (8k, 8k+2, 8k+4, 8k+6) and lane 2k+1 the odd ones, so
+// lane m owns dword m.
+__device__ __forceinline__ int8_t q8_rule(float x, float d) {
+    if (d == 0.0f) return 0;
+    const int q = static_cast<int>(__builtin_roundf(x / d));
+    return static_cast<int8_t>(min(max(q, -127), 127));
+}
+
+__device__ __forceinline__ ActScale quant_act_quad(float x0, float x1, float x2, float x3, int m, uint32_t& word) {
+    float a = fmaxf(fmaxf(fabsf(x0), fabsf(x1)), fmaxf(fabsf(x2), fabsf(x3)));
+    a = fmaxf(a, __shfl_xor(a, 1, 8));
+    a = fmaxf(a, __shfl_xor(a, 2, 8));
+    a = fmaxf(a, __shfl_xor(a, 4, 8));
+    const uint32_t dbits = float_to_half_bits(a / 127.0f);
+    const float d = half_bits_to_float(dbits);
+    const int8_t q0 = q8_rule(x0, d), q1 = q8_rule(x1, d), q2 = q8_rule(x2, d), q3 = q8_rule(x3, d);
+    const uint32_t ev = static_cast<uint8_t>(q0) | (static_cast<uint32_t>(static_cast<uint8_t>(q2)) << 8);
+    const uint32_t od = static_cast<uint8_t>(q1) | (static_cast<uint32_t>(static_cast<uint8_t>(q3)) << 8);
+    const uint32_t mine = ev | (od << 16);
+    const uint32_t other = static_cast<uint32_t>(__shfl_xor(static_cast<int>(mine), 1, 8));
+    word = (m & 1) ? ((other >> 16) | (od << 16)) : (ev | (other << 16));
+    int sum = static_cast<int>(q0) + q1 + q2 + q3;
+    sum += __shfl_xor(sum, 1, 8);
+    sum += __shfl_xor(sum, 2, 8);
+    sum += __shfl_xor(sum, 4, 8);
+    return ActScale{d, -8 * sum};
+}
+
 // One 32-bit word of Q4_0 nibbles (bytes 4k..4k+3 of qs, elements 8k..8k+7)
 // split into the even elements (low nibbles) and odd elements (high nibbles),
 // each as four unsigned bytes 0..15.

@@ -17,7 +17,10 @@
 //    nothing per element;
 //  * per block one convert and one FMA fold the int32 dot into fp32;
 //  * lanes of a row combine with a butterfly over G lanes.
-// Activations come from the quantizer's buffer, staged in LDS when they fit.
+// Activations come from the quantizer's buffer (read in place, or copied to
+// LDS when they fit) or, for one or two tokens, are quantized from fp32 by the
+// kernel itself into LDS before it streams the weights; the Q8_0 arithmetic is
+// the same device function either way, so both give the same bits.
 #include "q4bq_device.h"
 #include "q4bq_internal.h"
 
@@ -25,27 +28,51 @@ namespace q4bq {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
 constexpr int kRmax = 4;          // rows per lane per task
 constexpr int kU = 2;             // pair slots per load batch
 constexpr size_t kMaxActLds = 64 * 1024;
 
-template <int NT, bool ACT_LDS, bool DOTS>
-__global__ void __launch_bounds__(kThreads)
-k_gemv(const uint8_t* __restrict__ Wq, int64_t rows, int nb,
-       const uint32_t* __restrict__ act_q_g, const ActScale* __restrict__ act_s_g,
+enum Src { kActGlobal = 0, kActLds = 1, kXF32 = 2 };
+
+template <int NT, int THREADS, int SRC, bool DOTS>
+__global__ void __launch_bounds__(THREADS)
+k_gemv(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __restrict__ src,
        float* __restrict__ Y, int32_t* __restrict__ D, int log2G, int rpi) {
+    constexpr int kWaves = THREADS / 64;
     extern __shared__ __align__(16) uint8_t smem[];
-    const uint32_t* act_q = act_q_g;
-    const ActScale* act_s = act_s_g;
-    if constexpr (ACT_LDS) {
+    const uint32_t* act_q;
+    const ActScale* act_s;
+    if constexpr (SRC == kActGlobal) {
+        act_q = static_cast<const uint32_t*>(src);
+        act_s = reinterpret_cast<const ActScale*>(static_cast<const uint8_t*>(src) +
+                                                  static_cast<size_t>(NT) * nb * kActQBytes);
+    } else {
         uint32_t* sq = reinterpret_cast<uint32_t*>(smem);
         ActScale* ss = reinterpret_cast<ActScale*>(smem + static_cast<size_t>(NT) * nb * kActQBytes);
-        const int nq = NT * nb * 2;  // 16-byte chunks of activation values
-        for (int c = threadIdx.x; c < nq; c += kThreads)
-            reinterpret_cast<u32x4*>(sq)[c] = reinterpret_cast<const u32x4*>(act_q_g)[c];
-        for (int c = threadIdx.x; c < NT * nb; c += kThreads) ss[c] = act_s_g[c];
+        if constexpr (SRC == kActLds) {
+            const u32x4* gq = static_cast<const u32x4*>(src);
+            const ActScale* gs = reinterpret_cast<const ActScale*>(static_cast<const uint8_t*>(src) +
+                                                                   static_cast<size_t>(NT) * nb * kActQBytes);
+            for (int c = threadIdx.x; c < NT * nb * 2; c += THREADS) reinterpret_cast<u32x4*>(sq)[c] = gq[c];
+            for (int c = threadIdx.x; c < NT * nb; c += THREADS) ss[c] = gs[c];
+        } else {
+            // quantize X (NT x K fp32) here: 8 lanes per block, 4 values per lane
+            const float* X = static_cast<const float*>(src);
+            const int m = threadIdx.x & 7;
+            const int nblk = NT * nb;
+            for (int g0 = (threadIdx.x >> 3) & ~7; g0 < nblk; g0 += THREADS / 8) {
+                const int g = g0 + ((threadIdx.x >> 3) & 7);
+                const bool valid = g < nblk;
+                float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (valid) __builtin_memcpy(&x, X + static_cast<int64_t>(g) * kQK + 4 * m, 16);
+                uint32_t word;
+                const ActScale sc = quant_act_quad(x.x, x.y, x.z, x.w, m, word);
+                if (valid) {
+                    sq[g * 8 + m] = word;
+                    if (m == 0) ss[g] = sc;
+                }
+            }
+        }
         __syncthreads();
         act_q = sq;
         act_s = ss;
@@ -179,29 +206,40 @@ int pick_log2g(int64_t P) {
     return best;
 }
 
-template <int NT, bool ACT_LDS, bool DOTS>
-hipError_t launch_nt(const DeviceInfo* dev, const uint8_t* Wq, int64_t rows, int64_t nb, const void* act,
-                     float* Y, int32_t* D, hipStream_t s) {
-    const int log2G = pick_log2g(nb >> 1);
-    const int RW = 64 >> log2G;
-    // rows per lane: as many as keep >= 16 waves' worth of tasks per CU
-    const int64_t want_tasks = static_cast<int64_t>(dev->num_cu) * 16;
-    int rpi = 1;
+struct Shape {
+    int log2G, rpi;
+    uint32_t wgs;
+};
+
+// Launch shape: rows per lane = as many (up to 4) as still leave `want_waves`
+// tasks; workgroups capped at `wg_per_cu` per CU (the grid strides over tasks).
+Shape pick_shape(const DeviceInfo* dev, int64_t rows, int64_t nb, int threads, int wg_per_cu, int want_waves_per_cu) {
+    Shape sh;
+    sh.log2G = pick_log2g(nb >> 1);
+    const int RW = 64 >> sh.log2G;
+    const int64_t want_tasks = static_cast<int64_t>(dev->num_cu) * want_waves_per_cu;
+    sh.rpi = 1;
     for (int c = kRmax; c >= 1; c >>= 1) {
         if ((rows + int64_t(RW) * c - 1) / (int64_t(RW) * c) >= want_tasks) {
-            rpi = c;
+            sh.rpi = c;
             break;
         }
     }
-    const int64_t ntasks = (rows + int64_t(RW) * rpi - 1) / (int64_t(RW) * rpi);
-    int64_t wgs = (ntasks + kWaves - 1) / kWaves;
-    const int64_t cap = static_cast<int64_t>(dev->num_cu) * 8;
+    const int waves = threads / 64;
+    const int64_t ntasks = (rows + int64_t(RW) * sh.rpi - 1) / (int64_t(RW) * sh.rpi);
+    int64_t wgs = (ntasks + waves - 1) / waves;
+    const int64_t cap = static_cast<int64_t>(dev->num_cu) * wg_per_cu;
     if (wgs > cap) wgs = cap;
-    const uint32_t* aq = static_cast<const uint32_t*>(act);
-    const ActScale* as = reinterpret_cast<const ActScale*>(static_cast<const uint8_t*>(act) + NT * nb * kActQBytes);
-    const size_t lds = ACT_LDS ? static_cast<size_t>(NT) * nb * (kActQBytes + kActSBytes) : 0;
-    hipLaunchKernelGGL((k_gemv<NT, ACT_LDS, DOTS>), dim3(static_cast<uint32_t>(wgs)), dim3(kThreads), lds, s, Wq,
-                       rows, static_cast<int>(nb), aq, as, Y, D, log2G, rpi);
+    sh.wgs = static_cast<uint32_t>(wgs < 1 ? 1 : wgs);
+    return sh;
+}
+
+template <int NT, int THREADS, int SRC, bool DOTS>
+hipError_t launch_v(const Shape& sh, const uint8_t* Wq, int64_t rows, int64_t nb, const void* src, float* Y,
+                    int32_t* D, hipStream_t s) {
+    const size_t lds = SRC == kActGlobal ? 0 : static_cast<size_t>(NT) * nb * (kActQBytes + kActSBytes);
+    hipLaunchKernelGGL((k_gemv<NT, THREADS, SRC, DOTS>), dim3(sh.wgs), dim3(THREADS), lds, s, Wq, rows,
+                       static_cast<int>(nb), src, Y, D, sh.log2G, sh.rpi);
     return hipGetLastError();
 }
 
@@ -209,15 +247,29 @@ template <int NT>
 hipError_t launch_n(const DeviceInfo* dev, const uint8_t* Wq, int64_t rows, int64_t nb, const void* act, float* Y,
                     int32_t* D, hipStream_t s) {
     const bool lds = static_cast<size_t>(NT) * nb * (kActQBytes + kActSBytes) <= kMaxActLds;
+    const Shape sh = pick_shape(dev, rows, nb, 256, 4, 16);
     if (D) {
-        return lds ? launch_nt<NT, true, true>(dev, Wq, rows, nb, act, Y, D, s)
-                   : launch_nt<NT, false, true>(dev, Wq, rows, nb, act, Y, D, s);
+        return lds ? launch_v<NT, 256, kActLds, true>(sh, Wq, rows, nb, act, Y, D, s)
+                   : launch_v<NT, 256, kActGlobal, true>(sh, Wq, rows, nb, act, Y, D, s);
     }
-    return lds ? launch_nt<NT, true, false>(dev, Wq, rows, nb, act, Y, D, s)
-               : launch_nt<NT, false, false>(dev, Wq, rows, nb, act, Y, D, s);
+    return lds ? launch_v<NT, 256, kActLds, false>(sh, Wq, rows, nb, act, Y, D, s)
+               : launch_v<NT, 256, kActGlobal, false>(sh, Wq, rows, nb, act, Y, D, s);
 }
 
 }  // namespace
+
+bool gemv_fuses(int64_t N, int64_t nb) {
+    return N <= kGemvFusedMaxN && static_cast<size_t>(N) * nb * (kActQBytes + kActSBytes) <= kMaxActLds;
+}
+
+hipError_t launch_gemv_fused(const DeviceInfo* dev, const uint8_t* Wq, int64_t rows, int64_t nb, const float* X,
+                             int64_t N, float* Y, hipStream_t s) {
+    const Shape sh = pick_shape(dev, rows, nb, 1024, 1, 16);
+    switch (N) {
+        case 1: return launch_v<1, 1024, kXF32, false>(sh, Wq, rows, nb, X, Y, nullptr, s);
+        default: return hipErrorInvalidValue;
+    }
+}
 
 hipError_t launch_gemv(const DeviceInfo* dev, const uint8_t* Wq, int64_t rows, int64_t nb, const void* act,
                        int64_t N, float* Y, int32_t* D, hipStream_t s) {

@@ -40,6 +40,14 @@ hipError_t launch_act_from_q8(const uint8_t* Xq, int64_t N, int64_t nb, void* ac
 hipError_t launch_gemv(const DeviceInfo* dev, const uint8_t* Wq, int64_t rows, int64_t nb,
                        const void* act, int64_t N, float* Y, int32_t* D, hipStream_t s);
 
+// Decode kernel that quantizes fp32 X itself (no scratch, one launch), for
+// N <= kGemvFusedMaxN when the quantized activations fit in LDS.  Same bits
+// as launch_act_from_f32 followed by launch_gemv.
+constexpr int64_t kGemvFusedMaxN = 1;
+bool gemv_fuses(int64_t N, int64_t nb);
+hipError_t launch_gemv_fused(const DeviceInfo* dev, const uint8_t* Wq, int64_t rows, int64_t nb, const float* X,
+                             int64_t N, float* Y, hipStream_t s);
+
 // Matrix-core kernel, any N.  D as above.
 hipError_t launch_gemm(const DeviceInfo* dev, const uint8_t* Wq, int64_t rows, int64_t nb,
                        const void* act, int64_t N, float* Y, int32_t* D, hipStream_t s);

@@ -84,8 +84,32 @@ k_q8_0_quantize(const float* __restrict__ X, int64_t nblocks, uint8_t* __restric
     }
 }
 
-// Pack one block's int8 values (lane e holds q_e) into the internal dot order
-// and store it with its scale record.
+// fp32 activations -> internal dot-order blocks: 8 lanes per block, four
+// consecutive values per lane (one 16-byte load).
+__global__ void __launch_bounds__(kThreads)
+k_act_from_f32(const float* __restrict__ X, int64_t nblocks, uint32_t* __restrict__ act_q,
+               ActScale* __restrict__ act_s) {
+    const int m = threadIdx.x & 7;
+    const int64_t first = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) >> 3;
+    const int64_t step = static_cast<int64_t>(gridDim.x) * (kThreads / 8);
+    // uniform trip count over the wave (8 blocks per wave)
+    const int64_t wave_first = first & ~static_cast<int64_t>(7);
+    for (int64_t g0 = wave_first; g0 < nblocks; g0 += step) {
+        const int64_t g = g0 + (first & 7);
+        const bool valid = g < nblocks;
+        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (valid) __builtin_memcpy(&x, X + g * kQK + 4 * m, 16);
+        uint32_t word;
+        const ActScale sc = quant_act_quad(x.x, x.y, x.z, x.w, m, word);
+        if (valid) {
+            act_q[g * 8 + m] = word;
+            if (m == 0) act_s[g] = sc;
+        }
+    }
+}
+
+// Pack one block's int8 values (lane e of a half-wave holds q_e) into the
+// internal dot order and store it with its scale record.
 __device__ __forceinline__ void store_act(int e, int q, float d, bool valid, int64_t g,
                                           uint32_t* __restrict__ act_q, ActScale* __restrict__ act_s) {
     // element e -> dword 2*(e/8) + (e%2), byte (e/2)%4
@@ -96,24 +120,6 @@ __device__ __forceinline__ void store_act(int e, int q, float d, bool valid, int
     if (valid) {
         if ((e & 6) == 0) act_q[g * 8 + 2 * (e >> 3) + (e & 1)] = v;
         if (e == 0) act_s[g] = ActScale{d, bias};
-    }
-}
-
-__global__ void __launch_bounds__(kThreads)
-k_act_from_f32(const float* __restrict__ X, int64_t nblocks, uint32_t* __restrict__ act_q,
-               ActScale* __restrict__ act_s) {
-    const int e = threadIdx.x & 31;
-    const int64_t first = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) >> 5;
-    const int64_t step = static_cast<int64_t>(gridDim.x) * (kThreads / 32);
-    const int64_t wave_first = first & ~static_cast<int64_t>(1);
-    for (int64_t g0 = wave_first; g0 < nblocks; g0 += step) {
-        const int64_t g = g0 + (first & 1);
-        const bool valid = g < nblocks;
-        const float x = valid ? X[g * kQK + e] : 0.0f;
-        const float amax = max32(fabsf(x));
-        const uint32_t dbits = float_to_half_bits(amax / 127.0f);
-        const float d = half_bits_to_float(dbits);
-        store_act(e, quant8(x, d), d, valid, g, act_q, act_s);
     }
 }
 
@@ -168,7 +174,9 @@ hipError_t launch_act_from_f32(const float* X, int64_t N, int64_t nb, void* act,
     const int64_t nblocks = N * nb;
     uint32_t* q = static_cast<uint32_t*>(act);
     ActScale* sc = reinterpret_cast<ActScale*>(static_cast<uint8_t*>(act) + nblocks * kActQBytes);
-    hipLaunchKernelGGL(k_act_from_f32, dim3(quant_grid(nblocks)), dim3(kThreads), 0, s, X, nblocks, q, sc);
+    int64_t wgs = (nblocks + (kThreads / 8) - 1) / (kThreads / 8);
+    if (wgs > 8192) wgs = 8192;
+    hipLaunchKernelGGL(k_act_from_f32, dim3(static_cast<uint32_t>(wgs)), dim3(kThreads), 0, s, X, nblocks, q, sc);
     return hipGetLastError();
 }
 
