@@ -29,6 +29,8 @@ CFLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",
     "--offload-arch=" + ARCH,
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core results straight into VGPRs (no accumulator-register copies)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I", INCLUDE, "-I", CSRC,
 ]
 

@@ -67,24 +67,38 @@ __device__ __forceinline__ int8_t q8_rule(float x, float d) {
     return static_cast<int8_t>(min(max(q, -127), 127));
 }
 
-__device__ __forceinline__ ActScale quant_act_quad(float x0, float x1, float x2, float x3, int m, uint32_t& word) {
-    float a = fmaxf(fmaxf(fabsf(x0), fabsf(x1)), fmaxf(fabsf(x2), fabsf(x3)));
-    a = fmaxf(a, __shfl_xor(a, 1, 8));
-    a = fmaxf(a, __shfl_xor(a, 2, 8));
-    a = fmaxf(a, __shfl_xor(a, 4, 8));
-    const uint32_t dbits = float_to_half_bits(a / 127.0f);
-    const float d = half_bits_to_float(dbits);
-    const int8_t q0 = q8_rule(x0, d), q1 = q8_rule(x1, d), q2 = q8_rule(x2, d), q3 = q8_rule(x3, d);
+// Four int8 values of lane m (elements 4m..4m+3) -> this lane's dot-order
+// dword, and the block's -8 * sum(q) (both over the 8-lane group).
+__device__ __forceinline__ uint32_t dot_order_word(int8_t q0, int8_t q1, int8_t q2, int8_t q3, int m, int& bias) {
     const uint32_t ev = static_cast<uint8_t>(q0) | (static_cast<uint32_t>(static_cast<uint8_t>(q2)) << 8);
     const uint32_t od = static_cast<uint8_t>(q1) | (static_cast<uint32_t>(static_cast<uint8_t>(q3)) << 8);
     const uint32_t mine = ev | (od << 16);
     const uint32_t other = static_cast<uint32_t>(__shfl_xor(static_cast<int>(mine), 1, 8));
-    word = (m & 1) ? ((other >> 16) | (od << 16)) : (ev | (other << 16));
     int sum = static_cast<int>(q0) + q1 + q2 + q3;
     sum += __shfl_xor(sum, 1, 8);
     sum += __shfl_xor(sum, 2, 8);
     sum += __shfl_xor(sum, 4, 8);
-    return ActScale{d, -8 * sum};
+    bias = -8 * sum;
+    return (m & 1) ? ((other >> 16) | (od << 16)) : (ev | (other << 16));
+}
+
+__device__ __forceinline__ ActScale quant_act_quad(float x0, float x1, float x2, float x3, int m, uint32_t& word,
+                                                   uint32_t& dbits) {
+    float a = fmaxf(fmaxf(fabsf(x0), fabsf(x1)), fmaxf(fabsf(x2), fabsf(x3)));
+    a = fmaxf(a, __shfl_xor(a, 1, 8));
+    a = fmaxf(a, __shfl_xor(a, 2, 8));
+    a = fmaxf(a, __shfl_xor(a, 4, 8));
+    dbits = float_to_half_bits(a / 127.0f);
+    const float d = half_bits_to_float(dbits);
+    const int8_t q0 = q8_rule(x0, d), q1 = q8_rule(x1, d), q2 = q8_rule(x2, d), q3 = q8_rule(x3, d);
+    int bias;
+    word = dot_order_word(q0, q1, q2, q3, m, bias);
+    return ActScale{d, bias};
+}
+
+__device__ __forceinline__ ActScale quant_act_quad(float x0, float x1, float x2, float x3, int m, uint32_t& word) {
+    uint32_t dbits;
+    return quant_act_quad(x0, x1, x2, x3, m, word, dbits);
 }
 
 // One 32-bit word of Q4_0 nibbles (bytes 4k..4k+3 of qs, elements 8k..8k+7)
@@ -93,11 +107,92 @@ __device__ __forceinline__ ActScale quant_act_quad(float x0, float x1, float x2,
 __device__ __forceinline__ uint32_t nib_lo(uint32_t w) { return w & 0x0F0F0F0Fu; }
 __device__ __forceinline__ uint32_t nib_hi(uint32_t w) { return (w >> 4) & 0x0F0F0F0Fu; }
 
-// Four unsigned nibble bytes (0..15) -> four signed bytes (nibble - 8).
-// Adding 0x78 to a byte <= 0x0F cannot carry into the next byte; flipping the
-// top bit then maps 0x78..0x87 to -8..7.
-__device__ __forceinline__ uint32_t nib_to_s8(uint32_t v) {
-    return (v + 0x78787878u) ^ 0x80808080u;
+// ---------------------------------------------------------------------------
+// fp6 (e2m3) operand codes for the prefill kernel.
+//
+// The block dot s = sum_j (nibble_j - 8) * q_j is evaluated exactly on the
+// fp6 matrix cores: with y = 16h + l (h = y >> 4 in [-8, 7], l = y & 15),
+//   s = sum_j [(nibble_j - 8)/2 * 2] * ([h_j/2 * 32] + [l_j/2 * 2]),
+// where (nibble - 8)/2, h/2 and l/2 are all exact e2m3 values and the powers
+// of two are the operands' E8M0 block scales.  Every product and partial sum
+// is an integer below 2^24, so the fp32 result equals the int32 dot.
+//
+// e2m3: sign bit, 2 exponent bits (bias 1), 3 mantissa bits.  Codes of k/2:
+//   k = 0..8  -> 00 04 08 0C 10 12 14 16 18,  k = 9..15 -> 19 1A 1B 1C 1D 1E 1F.
+// ---------------------------------------------------------------------------
+
+// Four bytes n (0..15) -> e2m3 codes of (n - 8) / 2, one per byte.
+__device__ __forceinline__ uint32_t e2m3_half_offset(uint32_t n) {
+    const uint32_t idx = n & 0x07070707u;
+    // n = 0..7: -8/2 .. -1/2 (sign bit set); n = 8..15: 0 .. 7/2
+    const uint32_t neg = __builtin_amdgcn_perm(0x24282C30u, 0x32343638u, idx);
+    const uint32_t pos = __builtin_amdgcn_perm(0x16141210u, 0x0C080400u, idx);
+    const uint32_t m = ((n >> 3) & 0x01010101u) * 0xFFu;
+    return (pos & m) | (neg & ~m);
+}
+
+// Four bytes l (0..15) -> e2m3 codes of l / 2.
+__device__ __forceinline__ uint32_t e2m3_half(uint32_t l) {
+    const uint32_t idx = l & 0x07070707u;
+    const uint32_t lo = __builtin_amdgcn_perm(0x16141210u, 0x0C080400u, idx);
+    const uint32_t hi = __builtin_amdgcn_perm(0x1F1E1D1Cu, 0x1B1A1918u, idx);
+    const uint32_t m = ((l >> 3) & 0x01010101u) * 0xFFu;
+    return (hi & m) | (lo & ~m);
+}
+
+// Four 6-bit codes (one per byte) -> 24 bits, code i at bits 6i..6i+5.
+__device__ __forceinline__ uint32_t pack4x6(uint32_t c) {
+    const uint32_t t = (c & 0x003F003Fu) | ((c >> 2) & 0x0FC00FC0u);
+    return (t & 0xFFFu) | ((t >> 4) & 0xFFF000u);
+}
+
+// Eight 24-bit chunks -> the six dwords of a 32-value fp6 operand.
+__device__ __forceinline__ void assemble6(const uint32_t P[8], uint32_t d[6]) {
+    d[0] = P[0] | (P[1] << 24);
+    d[1] = (P[1] >> 8) | (P[2] << 16);
+    d[2] = (P[2] >> 16) | (P[3] << 8);
+    d[3] = P[4] | (P[5] << 24);
+    d[4] = (P[5] >> 8) | (P[6] << 16);
+    d[5] = (P[6] >> 16) | (P[7] << 8);
+}
+
+// A Q4_0 block's nibbles -> fp6 operand in dot order: chunk 2k holds the even
+// elements of nibble word k, chunk 2k+1 the odd ones (the same element order
+// as the activation records).
+__device__ __forceinline__ void weight_fp6(const uint32_t qs[4], uint32_t d[6]) {
+    uint32_t P[8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        P[2 * k] = pack4x6(e2m3_half_offset(nib_lo(qs[k])));
+        P[2 * k + 1] = pack4x6(e2m3_half_offset(nib_hi(qs[k])));
+    }
+    assemble6(P, d);
+}
+
+// Prefill activation record of one block, written by its 8-lane group (lane m
+// holds dot-order dword m, i.e. chunk m, of int8 values): 64 bytes per
+// (token, block) -- the fp6 operand of h/2 in dwords 0..5, of l/2 in dwords
+// 8..13 -- and the block's binary16 scale bits in a separate array.
+constexpr int kAct6Bytes = 64;
+
+__device__ __forceinline__ void store_act6(int m, uint32_t word, uint32_t dbits, bool valid, int64_t g,
+                                           uint32_t* __restrict__ rec, uint16_t* __restrict__ dxb) {
+    const uint32_t ph = pack4x6(e2m3_half_offset(((word >> 4) & 0x0F0F0F0Fu) ^ 0x08080808u));  // h + 8
+    const uint32_t pl = pack4x6(e2m3_half(word & 0x0F0F0F0Fu));                                 // l
+    // output dword d (lanes 0..5) = chunk c1 shifted down | chunk c1+1 shifted up
+    const int d = m < 6 ? m : 0;
+    const int c1 = d + d / 3;
+    const int s1 = 32 * d - 24 * c1;
+    const int s2 = 24 * (c1 + 1) - 32 * d;
+    const uint32_t h1 = static_cast<uint32_t>(__shfl(static_cast<int>(ph), c1, 8));
+    const uint32_t h2 = static_cast<uint32_t>(__shfl(static_cast<int>(ph), c1 + 1, 8));
+    const uint32_t l1 = static_cast<uint32_t>(__shfl(static_cast<int>(pl), c1, 8));
+    const uint32_t l2 = static_cast<uint32_t>(__shfl(static_cast<int>(pl), c1 + 1, 8));
+    if (valid && m < 6) {
+        rec[g * 16 + d] = (h1 >> s1) | (h2 << s2);
+        rec[g * 16 + 8 + d] = (l1 >> s1) | (l2 << s2);
+    }
+    if (valid && m == 0) dxb[g] = static_cast<uint16_t>(dbits);
 }
 
 // 36 bytes starting at p (two consecutive Q4_0 blocks), any 2-byte alignment:

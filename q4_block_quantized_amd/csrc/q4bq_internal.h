@@ -24,8 +24,11 @@ struct DeviceInfo {
 // Launch parameters of the device current on this thread (cached).
 const DeviceInfo* current_device(hipError_t* err);
 
-// Internal activation buffer: N*nb blocks of 32 bytes (dot order), then
-// N*nb scale records of 8 bytes; both [n][b] with b fastest.
+// Internal activation buffer ([n][b], b fastest):
+//  N <= kGemvMaxN (decode kernel): N*nb blocks of 32 int8 bytes in dot order,
+//    then N*nb scale records of 8 bytes {float d; int32 -8*sum(q)};
+//  larger N (prefill kernel): N*nb records of 64 bytes (fp6 operands of the
+//    high and low parts of q), then N*nb binary16 scale bits.
 size_t act_bytes(int64_t N, int64_t nb);
 
 hipError_t launch_q4_0_quantize(const float* W, int64_t nblocks, uint8_t* Wq, hipStream_t s);

@@ -108,6 +108,49 @@ k_act_from_f32(const float* __restrict__ X, int64_t nblocks, uint32_t* __restric
     }
 }
 
+// fp32 activations -> prefill records (fp6 operands + binary16 scale bits).
+__global__ void __launch_bounds__(kThreads)
+k_act6_from_f32(const float* __restrict__ X, int64_t nblocks, uint32_t* __restrict__ rec,
+                uint16_t* __restrict__ dxb) {
+    const int m = threadIdx.x & 7;
+    const int64_t first = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) >> 3;
+    const int64_t step = static_cast<int64_t>(gridDim.x) * (kThreads / 8);
+    const int64_t wave_first = first & ~static_cast<int64_t>(7);
+    for (int64_t g0 = wave_first; g0 < nblocks; g0 += step) {
+        const int64_t g = g0 + (first & 7);
+        const bool valid = g < nblocks;
+        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (valid) __builtin_memcpy(&x, X + g * kQK + 4 * m, 16);
+        uint32_t word, dbits;
+        quant_act_quad(x.x, x.y, x.z, x.w, m, word, dbits);
+        store_act6(m, word, dbits, valid, g, rec, dxb);
+    }
+}
+
+// Q8_0 blocks -> prefill records.
+__global__ void __launch_bounds__(kThreads)
+k_act6_from_q8(const uint8_t* __restrict__ Xq, int64_t nblocks, uint32_t* __restrict__ rec,
+               uint16_t* __restrict__ dxb) {
+    const int m = threadIdx.x & 7;
+    const int64_t first = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) >> 3;
+    const int64_t step = static_cast<int64_t>(gridDim.x) * (kThreads / 8);
+    const int64_t wave_first = first & ~static_cast<int64_t>(7);
+    for (int64_t g0 = wave_first; g0 < nblocks; g0 += step) {
+        const int64_t g = g0 + (first & 7);
+        const bool valid = g < nblocks;
+        int8_t q[4] = {0, 0, 0, 0};
+        uint16_t h = 0;
+        if (valid) {
+            const uint8_t* blk = Xq + g * kQ8Bytes;
+            __builtin_memcpy(q, blk + 2 + 4 * m, 4);
+            __builtin_memcpy(&h, blk, 2);
+        }
+        int bias;
+        const uint32_t word = dot_order_word(q[0], q[1], q[2], q[3], m, bias);
+        store_act6(m, word, h, valid, g, rec, dxb);
+    }
+}
+
 // Pack one block's int8 values (lane e of a half-wave holds q_e) into the
 // internal dot order and store it with its scale record.
 __device__ __forceinline__ void store_act(int e, int q, float d, bool valid, int64_t g,
@@ -157,7 +200,8 @@ int quant_grid(int64_t nblocks) {
 }  // namespace
 
 size_t act_bytes(int64_t N, int64_t nb) {
-    return static_cast<size_t>(N * nb) * (kActQBytes + kActSBytes);
+    if (N <= kGemvMaxN) return static_cast<size_t>(N * nb) * (kActQBytes + kActSBytes);
+    return static_cast<size_t>(N * nb) * (kAct6Bytes + 2);
 }
 
 hipError_t launch_q4_0_quantize(const float* W, int64_t nblocks, uint8_t* Wq, hipStream_t s) {
@@ -170,8 +214,22 @@ hipError_t launch_q8_0_quantize(const float* X, int64_t nblocks, uint8_t* Xq, hi
     return hipGetLastError();
 }
 
+namespace {
+int act_grid(int64_t nblocks) {
+    int64_t wgs = (nblocks + (kThreads / 8) - 1) / (kThreads / 8);
+    if (wgs > 8192) wgs = 8192;
+    return static_cast<int>(wgs < 1 ? 1 : wgs);
+}
+}  // namespace
+
 hipError_t launch_act_from_f32(const float* X, int64_t N, int64_t nb, void* act, hipStream_t s) {
     const int64_t nblocks = N * nb;
+    if (N > kGemvMaxN) {
+        uint32_t* rec = static_cast<uint32_t*>(act);
+        uint16_t* dxb = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(act) + nblocks * kAct6Bytes);
+        hipLaunchKernelGGL(k_act6_from_f32, dim3(act_grid(nblocks)), dim3(kThreads), 0, s, X, nblocks, rec, dxb);
+        return hipGetLastError();
+    }
     uint32_t* q = static_cast<uint32_t*>(act);
     ActScale* sc = reinterpret_cast<ActScale*>(static_cast<uint8_t*>(act) + nblocks * kActQBytes);
     int64_t wgs = (nblocks + (kThreads / 8) - 1) / (kThreads / 8);
@@ -182,6 +240,12 @@ hipError_t launch_act_from_f32(const float* X, int64_t N, int64_t nb, void* act,
 
 hipError_t launch_act_from_q8(const uint8_t* Xq, int64_t N, int64_t nb, void* act, hipStream_t s) {
     const int64_t nblocks = N * nb;
+    if (N > kGemvMaxN) {
+        uint32_t* rec = static_cast<uint32_t*>(act);
+        uint16_t* dxb = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(act) + nblocks * kAct6Bytes);
+        hipLaunchKernelGGL(k_act6_from_q8, dim3(act_grid(nblocks)), dim3(kThreads), 0, s, Xq, nblocks, rec, dxb);
+        return hipGetLastError();
+    }
     uint32_t* q = static_cast<uint32_t*>(act);
     ActScale* sc = reinterpret_cast<ActScale*>(static_cast<uint8_t*>(act) + nblocks * kActQBytes);
     hipLaunchKernelGGL(k_act_from_q8, dim3(quant_grid(nblocks)), dim3(kThreads), 0, s, Xq, nblocks, q, sc);
