@@ -144,6 +144,7 @@ int check_product(const void* Wq, int64_t rows, int64_t K, const void* Xany, Act
     const int64_t nb = K / kQK;
     if (too_big(rows, K, 1) || too_big(N, K, 4) || too_big(N, rows, 4)) return Q4BQ_EINVAL;
     if (dots && too_big(N * rows, nb, 4)) return Q4BQ_EINVAL;
+    if (N > kGemvMaxN && ((rows + 127) / 128) * ((N + 255) / 256) >= (int64_t(1) << 31)) return Q4BQ_EINVAL;
     const uintptr_t x_align = kind == kF32 ? 4 : kind == kQ8 ? 2 : 16;
     if (!aligned(Wq, 2) || !aligned(Xany, x_align) || !aligned(out, 4)) return Q4BQ_EINVAL;
     const size_t w_bytes = static_cast<size_t>(rows * nb) * kQ4Bytes;

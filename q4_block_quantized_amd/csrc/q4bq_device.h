@@ -172,7 +172,8 @@ __device__ __forceinline__ void weight_fp6(const uint32_t qs[4], uint32_t d[6]) 
 // Prefill activation record of one block, written by its 8-lane group (lane m
 // holds dot-order dword m, i.e. chunk m, of int8 values): 64 bytes per
 // (token, block) -- the fp6 operand of h/2 in dwords 0..5, of l/2 in dwords
-// 8..13 -- and the block's binary16 scale bits in a separate array.
+// 8..13, dwords 6, 7, 14, 15 zero -- and the block's binary16 scale bits in a
+// separate array.
 constexpr int kAct6Bytes = 64;
 
 __device__ __forceinline__ void store_act6(int m, uint32_t word, uint32_t dbits, bool valid, int64_t g,
@@ -188,9 +189,10 @@ __device__ __forceinline__ void store_act6(int m, uint32_t word, uint32_t dbits,
     const uint32_t h2 = static_cast<uint32_t>(__shfl(static_cast<int>(ph), c1 + 1, 8));
     const uint32_t l1 = static_cast<uint32_t>(__shfl(static_cast<int>(pl), c1, 8));
     const uint32_t l2 = static_cast<uint32_t>(__shfl(static_cast<int>(pl), c1 + 1, 8));
-    if (valid && m < 6) {
-        rec[g * 16 + d] = (h1 >> s1) | (h2 << s2);
-        rec[g * 16 + 8 + d] = (l1 >> s1) | (l2 << s2);
+    if (valid) {
+        // dwords 6 and 7 of each half are zero: an operand is then two 16-byte reads
+        rec[g * 16 + m] = m < 6 ? (h1 >> s1) | (h2 << s2) : 0u;
+        rec[g * 16 + 8 + m] = m < 6 ? (l1 >> s1) | (l2 << s2) : 0u;
     }
     if (valid && m == 0) dxb[g] = static_cast<uint16_t>(dbits);
 }
