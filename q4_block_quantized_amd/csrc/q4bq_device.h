@@ -171,13 +171,13 @@ __device__ __forceinline__ void weight_fp6(const uint32_t qs[4], uint32_t d[6]) 
 
 // Prefill activation record of one block, written by its 8-lane group (lane m
 // holds dot-order dword m, i.e. chunk m, of int8 values): 64 bytes per
-// (token, block) -- the fp6 operand of h/2 in dwords 0..5, of l/2 in dwords
-// 8..13, dwords 6, 7, 14, 15 zero -- and the block's binary16 scale bits in a
-// separate array.
+// (token, block), stored block-major at record index o = block * N + token.
+// Dwords 0..5: fp6 operand of h/2; dword 6: the block's binary16 scale bits;
+// dword 7: zero; dwords 8..15: the same for l/2.
 constexpr int kAct6Bytes = 64;
 
-__device__ __forceinline__ void store_act6(int m, uint32_t word, uint32_t dbits, bool valid, int64_t g,
-                                           uint32_t* __restrict__ rec, uint16_t* __restrict__ dxb) {
+__device__ __forceinline__ void store_act6(int m, uint32_t word, uint32_t dbits, bool valid, int64_t o,
+                                           uint32_t* __restrict__ rec) {
     const uint32_t ph = pack4x6(e2m3_half_offset(((word >> 4) & 0x0F0F0F0Fu) ^ 0x08080808u));  // h + 8
     const uint32_t pl = pack4x6(e2m3_half(word & 0x0F0F0F0Fu));                                 // l
     // output dword d (lanes 0..5) = chunk c1 shifted down | chunk c1+1 shifted up
@@ -190,11 +190,10 @@ __device__ __forceinline__ void store_act6(int m, uint32_t word, uint32_t dbits,
     const uint32_t l1 = static_cast<uint32_t>(__shfl(static_cast<int>(pl), c1, 8));
     const uint32_t l2 = static_cast<uint32_t>(__shfl(static_cast<int>(pl), c1 + 1, 8));
     if (valid) {
-        // dwords 6 and 7 of each half are zero: an operand is then two 16-byte reads
-        rec[g * 16 + m] = m < 6 ? (h1 >> s1) | (h2 << s2) : 0u;
-        rec[g * 16 + 8 + m] = m < 6 ? (l1 >> s1) | (l2 << s2) : 0u;
+        const uint32_t tail = m == 6 ? (dbits & 0xFFFFu) : 0u;
+        rec[o * 16 + m] = m < 6 ? (h1 >> s1) | (h2 << s2) : tail;
+        rec[o * 16 + 8 + m] = m < 6 ? (l1 >> s1) | (l2 << s2) : tail;
     }
-    if (valid && m == 0) dxb[g] = static_cast<uint16_t>(dbits);
 }
 
 // 36 bytes starting at p (two consecutive Q4_0 blocks), any 2-byte alignment:

@@ -27,8 +27,9 @@ const DeviceInfo* current_device(hipError_t* err);
 // Internal activation buffer ([n][b], b fastest):
 //  N <= kGemvMaxN (decode kernel): N*nb blocks of 32 int8 bytes in dot order,
 //    then N*nb scale records of 8 bytes {float d; int32 -8*sum(q)};
-//  larger N (prefill kernel): N*nb records of 64 bytes (fp6 operands of the
-//    high and low parts of q), then N*nb binary16 scale bits.
+//  larger N (prefill kernel): N*nb records of 64 bytes, block-major
+//    ([b][n]): fp6 operands of the high and low parts of q, each followed by
+//    the block's binary16 scale bits and a zero dword.
 size_t act_bytes(int64_t N, int64_t nb);
 
 hipError_t launch_q4_0_quantize(const float* W, int64_t nblocks, uint8_t* Wq, hipStream_t s);

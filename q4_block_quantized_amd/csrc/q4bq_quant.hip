@@ -108,46 +108,53 @@ k_act_from_f32(const float* __restrict__ X, int64_t nblocks, uint32_t* __restric
     }
 }
 
+// Prefill records are written block-major: the 8-lane group that handles
+// record o = block * N + token reads block `block` of token `token`.
+__device__ __forceinline__ int64_t act6_source(int64_t o, int64_t N, int64_t nb) {
+    const int64_t b = o / N;
+    return (o - b * N) * nb + b;
+}
+
 // fp32 activations -> prefill records (fp6 operands + binary16 scale bits).
 __global__ void __launch_bounds__(kThreads)
-k_act6_from_f32(const float* __restrict__ X, int64_t nblocks, uint32_t* __restrict__ rec,
-                uint16_t* __restrict__ dxb) {
+k_act6_from_f32(const float* __restrict__ X, int64_t N, int64_t nb, uint32_t* __restrict__ rec) {
+    const int64_t nblocks = N * nb;
     const int m = threadIdx.x & 7;
     const int64_t first = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) >> 3;
     const int64_t step = static_cast<int64_t>(gridDim.x) * (kThreads / 8);
     const int64_t wave_first = first & ~static_cast<int64_t>(7);
-    for (int64_t g0 = wave_first; g0 < nblocks; g0 += step) {
-        const int64_t g = g0 + (first & 7);
-        const bool valid = g < nblocks;
+    for (int64_t o0 = wave_first; o0 < nblocks; o0 += step) {
+        const int64_t o = o0 + (first & 7);
+        const bool valid = o < nblocks;
         float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (valid) __builtin_memcpy(&x, X + g * kQK + 4 * m, 16);
+        if (valid) __builtin_memcpy(&x, X + act6_source(o, N, nb) * kQK + 4 * m, 16);
         uint32_t word, dbits;
         quant_act_quad(x.x, x.y, x.z, x.w, m, word, dbits);
-        store_act6(m, word, dbits, valid, g, rec, dxb);
+        store_act6(m, word, dbits, valid, o, rec);
     }
 }
 
 // Q8_0 blocks -> prefill records.
 __global__ void __launch_bounds__(kThreads)
-k_act6_from_q8(const uint8_t* __restrict__ Xq, int64_t nblocks, uint32_t* __restrict__ rec,
-               uint16_t* __restrict__ dxb) {
+k_act6_from_q8(const uint8_t* __restrict__ Xq, int64_t N, int64_t nb, uint32_t* __restrict__ rec) {
+    const int64_t nblocks = N * nb;
     const int m = threadIdx.x & 7;
     const int64_t first = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) >> 3;
     const int64_t step = static_cast<int64_t>(gridDim.x) * (kThreads / 8);
     const int64_t wave_first = first & ~static_cast<int64_t>(7);
-    for (int64_t g0 = wave_first; g0 < nblocks; g0 += step) {
-        const int64_t g = g0 + (first & 7);
-        const bool valid = g < nblocks;
+    for (int64_t o0 = wave_first; o0 < nblocks; o0 += step) {
+        const int64_t o = o0 + (first & 7);
+        const bool valid = o < nblocks;
         int8_t q[4] = {0, 0, 0, 0};
         uint16_t h = 0;
         if (valid) {
-            const uint8_t* blk = Xq + g * kQ8Bytes;
+            const uint8_t* blk = Xq + act6_source(o, N, nb) * kQ8Bytes;
             __builtin_memcpy(q, blk + 2 + 4 * m, 4);
             __builtin_memcpy(&h, blk, 2);
         }
         int bias;
         const uint32_t word = dot_order_word(q[0], q[1], q[2], q[3], m, bias);
-        store_act6(m, word, h, valid, g, rec, dxb);
+        store_act6(m, word, h, valid, o, rec);
     }
 }
 
@@ -201,7 +208,7 @@ int quant_grid(int64_t nblocks) {
 
 size_t act_bytes(int64_t N, int64_t nb) {
     if (N <= kGemvMaxN) return static_cast<size_t>(N * nb) * (kActQBytes + kActSBytes);
-    return static_cast<size_t>(N * nb) * (kAct6Bytes + 2);
+    return static_cast<size_t>(N * nb) * kAct6Bytes;
 }
 
 hipError_t launch_q4_0_quantize(const float* W, int64_t nblocks, uint8_t* Wq, hipStream_t s) {
@@ -226,8 +233,7 @@ hipError_t launch_act_from_f32(const float* X, int64_t N, int64_t nb, void* act,
     const int64_t nblocks = N * nb;
     if (N > kGemvMaxN) {
         uint32_t* rec = static_cast<uint32_t*>(act);
-        uint16_t* dxb = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(act) + nblocks * kAct6Bytes);
-        hipLaunchKernelGGL(k_act6_from_f32, dim3(act_grid(nblocks)), dim3(kThreads), 0, s, X, nblocks, rec, dxb);
+        hipLaunchKernelGGL(k_act6_from_f32, dim3(act_grid(nblocks)), dim3(kThreads), 0, s, X, N, nb, rec);
         return hipGetLastError();
     }
     uint32_t* q = static_cast<uint32_t*>(act);
@@ -242,8 +248,7 @@ hipError_t launch_act_from_q8(const uint8_t* Xq, int64_t N, int64_t nb, void* ac
     const int64_t nblocks = N * nb;
     if (N > kGemvMaxN) {
         uint32_t* rec = static_cast<uint32_t*>(act);
-        uint16_t* dxb = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(act) + nblocks * kAct6Bytes);
-        hipLaunchKernelGGL(k_act6_from_q8, dim3(act_grid(nblocks)), dim3(kThreads), 0, s, Xq, nblocks, rec, dxb);
+        hipLaunchKernelGGL(k_act6_from_q8, dim3(act_grid(nblocks)), dim3(kThreads), 0, s, Xq, N, nb, rec);
         return hipGetLastError();
     }
     uint32_t* q = static_cast<uint32_t*>(act);

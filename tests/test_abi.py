@@ -48,7 +48,7 @@ def test_status_strings(L):
 
 def test_workspace_size(L):
     assert L.q4bq_workspace_size(4096, 4096, 1) == 128 * 40 + (256 - (128 * 40) % 256) % 256
-    assert L.q4bq_workspace_size(14336, 4096, 512) == 512 * 128 * 66
+    assert L.q4bq_workspace_size(14336, 4096, 512) == 512 * 128 * 64
     assert L.q4bq_workspace_size(1, 31, 1) == 0
     assert L.q4bq_workspace_size(0, 32, 1) == 0
     assert L.q4bq_workspace_size(1, 32, 0) == 0
