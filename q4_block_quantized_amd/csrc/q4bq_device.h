@@ -112,13 +112,16 @@ __device__ __forceinline__ uint32_t nib_hi(uint32_t w) { return (w >> 4) & 0x0F0
 //
 // The block dot s = sum_j (nibble_j - 8) * q_j is evaluated exactly on the
 // fp6 matrix cores: with y = 16h + l (h = y >> 4 in [-8, 7], l = y & 15),
-//   s = sum_j [(nibble_j - 8)/2 * 2] * ([h_j/2 * 32] + [l_j/2 * 2]),
-// where (nibble - 8)/2, h/2 and l/2 are all exact e2m3 values and the powers
+//   s = sum_j [(nibble_j - 8)/8 * 8] * ([h_j/2 * 32] + [l_j/2 * 2]),
+// where (nibble - 8)/8, h/2 and l/2 are all exact e2m3 values and the powers
 // of two are the operands' E8M0 block scales.  Every product and partial sum
 // is an integer below 2^24, so the fp32 result equals the int32 dot.
 //
 // e2m3: sign bit, 2 exponent bits (bias 1), 3 mantissa bits.  Codes of k/2:
 //   k = 0..8  -> 00 04 08 0C 10 12 14 16 18,  k = 9..15 -> 19 1A 1B 1C 1D 1E 1F.
+// The byte-wise selects below pick, per byte, table entry `idx` from one of
+// two 8-entry tables according to bit 3 of the source nibble (v_perm_b32
+// with selector i or i + 4).
 // ---------------------------------------------------------------------------
 
 // Four bytes n (0..15) -> e2m3 codes of (n - 8) / 2, one per byte.
@@ -127,8 +130,7 @@ __device__ __forceinline__ uint32_t e2m3_half_offset(uint32_t n) {
     // n = 0..7: -8/2 .. -1/2 (sign bit set); n = 8..15: 0 .. 7/2
     const uint32_t neg = __builtin_amdgcn_perm(0x24282C30u, 0x32343638u, idx);
     const uint32_t pos = __builtin_amdgcn_perm(0x16141210u, 0x0C080400u, idx);
-    const uint32_t m = ((n >> 3) & 0x01010101u) * 0xFFu;
-    return (pos & m) | (neg & ~m);
+    return __builtin_amdgcn_perm(pos, neg, ((n >> 1) & 0x04040404u) | 0x03020100u);
 }
 
 // Four bytes l (0..15) -> e2m3 codes of l / 2.
@@ -136,14 +138,13 @@ __device__ __forceinline__ uint32_t e2m3_half(uint32_t l) {
     const uint32_t idx = l & 0x07070707u;
     const uint32_t lo = __builtin_amdgcn_perm(0x16141210u, 0x0C080400u, idx);
     const uint32_t hi = __builtin_amdgcn_perm(0x1F1E1D1Cu, 0x1B1A1918u, idx);
-    const uint32_t m = ((l >> 3) & 0x01010101u) * 0xFFu;
-    return (hi & m) | (lo & ~m);
+    return __builtin_amdgcn_perm(hi, lo, ((l >> 1) & 0x04040404u) | 0x03020100u);
 }
 
 // Four 6-bit codes (one per byte) -> 24 bits, code i at bits 6i..6i+5.
 __device__ __forceinline__ uint32_t pack4x6(uint32_t c) {
     const uint32_t t = (c & 0x003F003Fu) | ((c >> 2) & 0x0FC00FC0u);
-    return (t & 0xFFFu) | ((t >> 4) & 0xFFF000u);
+    return (t & 0xFFFu) | ((t >> 4) & ~0xFFFu);  // t bits 28..31 are zero
 }
 
 // Eight 24-bit chunks -> the six dwords of a 32-value fp6 operand.
@@ -156,15 +157,26 @@ __device__ __forceinline__ void assemble6(const uint32_t P[8], uint32_t d[6]) {
     d[5] = (P[6] >> 16) | (P[7] << 8);
 }
 
-// A Q4_0 block's nibbles -> fp6 operand in dot order: chunk 2k holds the even
-// elements of nibble word k, chunk 2k+1 the odd ones (the same element order
-// as the activation records).
+// Four nibble bytes n -> e2m3 codes of (n - 8) / 8, given idx = n & 7 in each
+// byte and sel4 = 4 in the bytes where n >= 8.  Below 1.0 the e2m3 codes are
+// linear (value code/8), and 1.0 = code 8, so k/8 for |k| <= 8 has the code
+// |k| plus the sign bit 0x20: n >= 8 gives k = idx, n < 8 gives
+// 0x20 | (8 - n) = 0x28 - idx (an 8-entry byte table).
+__device__ __forceinline__ uint32_t e2m3_eighth_offset(uint32_t idx, uint32_t sel4) {
+    const uint32_t neg = __builtin_amdgcn_perm(0x21222324u, 0x25262728u, idx);
+    return __builtin_amdgcn_perm(idx, neg, sel4 | 0x03020100u);
+}
+
+// A Q4_0 block's nibbles -> fp6 operand of (nibble - 8)/8 in dot order: chunk
+// 2k holds the even elements of nibble word k, chunk 2k+1 the odd ones (the
+// same element order as the activation records).
 __device__ __forceinline__ void weight_fp6(const uint32_t qs[4], uint32_t d[6]) {
     uint32_t P[8];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        P[2 * k] = pack4x6(e2m3_half_offset(nib_lo(qs[k])));
-        P[2 * k + 1] = pack4x6(e2m3_half_offset(nib_hi(qs[k])));
+        const uint32_t q = qs[k];
+        P[2 * k] = pack4x6(e2m3_eighth_offset(q & 0x07070707u, (q >> 1) & 0x04040404u));
+        P[2 * k + 1] = pack4x6(e2m3_eighth_offset((q >> 4) & 0x07070707u, (q >> 5) & 0x04040404u));
     }
     assemble6(P, d);
 }

@@ -5,8 +5,8 @@
 // (nibble - 8) with the int8 activations, then the fp32 scale d_w * d_x, the
 // scaled block terms summed in fp32), organised as a tiled GEMM:
 //  * the block dot runs on the fp6 matrix cores, exactly: the weights enter as
-//    e2m3 codes of (nibble - 8)/2, the activations as e2m3 codes of h/2 and l/2
-//    (y = 16h + l), with E8M0 block scales x2, x32 and x2; one
+//    e2m3 codes of (nibble - 8)/8, the activations as e2m3 codes of h/2 and l/2
+//    (y = 16h + l), with E8M0 block scales x8, x32 and x2; one
 //    v_mfma_scale_f32_32x32x64_f8f6f4 yields s for a 32-token x 32-row tile
 //    as an exact fp32 integer, with no int->float conversion;
 //  * the 1024 scale products d_x * d_w of a tile come from one
@@ -56,7 +56,7 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // E8M0 block scales: 127 is x1.
-constexpr int kScaleW = 128;       // weights hold (nibble - 8) / 2
+constexpr int kScaleW = 130;       // weights hold (nibble - 8) / 8
 constexpr int kScaleHi = 127 + 5;  // activation high part holds h / 2, weight 16 h
 constexpr int kScaleLo = 128;      // activation low part holds l / 2
 // Both K halves of the scale-product MFMA hold d in their first slot, so it
@@ -64,14 +64,41 @@ constexpr int kScaleLo = 128;      // activation low part holds l / 2
 // (exact: a power of two on an integer well inside the fp32 range).
 constexpr int kScaleDown = 1;
 
-__device__ __forceinline__ i32x8 join(const u32x4& x0, const u32x4& x1) {
-    return i32x8{static_cast<int>(x0.x), static_cast<int>(x0.y), static_cast<int>(x0.z), static_cast<int>(x0.w),
-                 static_cast<int>(x1.x), static_cast<int>(x1.y), static_cast<int>(x1.z), static_cast<int>(x1.w)};
+// One operand record in registers: fp6 codes in dwords 0..5, {scale bits, 0}
+// in dwords 6..7, read as two 16-byte halves that are only joined at use.
+struct Operand {
+    u32x4 lo;
+    u32x4 hi;
+};
+
+__device__ __forceinline__ Operand lds_operand(const uint8_t* p0, const uint8_t* p1) {
+    Operand o;
+    o.lo = *reinterpret_cast<const u32x4*>(p0);
+    o.hi = *reinterpret_cast<const u32x4*>(p1);
+    return o;
 }
 
-// Dwords 6 and 7 of an operand record: {scale bits, 0} as four binary16 lanes.
-__device__ __forceinline__ f16x4 scale_operand(const i32x8& v) {
-    return __builtin_bit_cast(f16x4, u32x2{static_cast<uint32_t>(v[6]), static_cast<uint32_t>(v[7])});
+__device__ __forceinline__ i32x8 fp6_operand(const Operand& o) {
+    return i32x8{static_cast<int>(o.lo.x), static_cast<int>(o.lo.y), static_cast<int>(o.lo.z),
+                 static_cast<int>(o.lo.w), static_cast<int>(o.hi.x), static_cast<int>(o.hi.y),
+                 static_cast<int>(o.hi.z), static_cast<int>(o.hi.w)};
+}
+
+__device__ __forceinline__ f16x4 scale_operand(const Operand& o) {
+    return __builtin_bit_cast(f16x4, u32x2{o.hi.z, o.hi.w});
+}
+
+// global_load_lds_dwordx4: 16 bytes per lane from src into LDS at dst + 16 *
+// lane (dst wave-uniform, through M0).  Written as inline assembly so that
+// the compiler does not track it: it would otherwise wait for these loads
+// before unrelated LDS reads.  The caller waits for them explicitly
+// (s_waitcnt vmcnt) before the data is read; loads complete in order, and
+// every load the compiler does track that is issued later is waited for with
+// a count that then also covers these.
+__device__ __forceinline__ void dma16(const uint8_t* src, const uint8_t* dst) {
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(
+        static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint8_t*)dst)));
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(lds), "v"(src) : "memory", "m0");
 }
 
 template <bool DOTS>
@@ -100,11 +127,12 @@ k_gemm(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const uint8_t* __re
 
     // --- activation staging -------------------------------------------------
     // Records are [block][token][64 bytes]; in LDS, 16-byte quarter q of
-    // token t sits at position q ^ ((t >> 1) & 3) of its record, so that the
-    // operand reads of 8 consecutive tokens hit 8 disjoint bank groups.
+    // token t sits at position q ^ ((t >> 2) & 3) of its record: a 16-byte
+    // LDS read serves 16 lanes per cycle from 64 banks, and with this swizzle
+    // the 16 tokens of such a group hit 16 disjoint 4-bank groups.
     // Instruction e of a block plane covers tokens wave*32 + 16e + lane/4;
-    // lane position lane%4 holds quarter (lane%4) ^ ((lane/8)%4).
-    const int dq = (lane & 3) ^ ((lane >> 3) & 3);
+    // lane position lane%4 holds quarter (lane%4) ^ ((lane/16)%4).
+    const int dq = (lane & 3) ^ ((lane >> 4) & 3);
     int64_t dma_off[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
@@ -119,33 +147,44 @@ k_gemm(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const uint8_t* __re
             int b = b0 + blk;
             if (b > nb - 1) b = nb - 1;  // past the end: neutralised by zero weight scales
             const uint8_t* src = act + static_cast<int64_t>(b) * N * kAct6Bytes + dma_off[e];
-            uint8_t* dst = sA + blk * kPlaneA + (wave * 32 + e * 16) * kAct6Bytes;
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                             (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+            const uint8_t* dst = sA + blk * kPlaneA + (wave * 32 + e * 16) * kAct6Bytes;
+            dma16(src, dst);
         }
     };
 
     // --- weight staging: one block per thread, row w_row, block w_blk ---------
     // LDS record (32 bytes): 6 dwords of fp6 codes, binary16 d bits, zero; the
-    // two 16-byte halves swap places in rows with bit 2 set (bank spread).
-    const int w_row = t >> 2;
-    const int w_blk = t & 3;
+    // two 16-byte halves swap places in rows with bit 3 set, so that 16
+    // consecutive rows (one LDS cycle of reads or writes) hit 16 disjoint
+    // 4-bank groups.  A wave stages 16 rows x 4 blocks; each 16-lane group
+    // holds one block of the 16 rows.
+    const int w_row = (t & 15) | ((t >> 6) << 4);
+    const int w_blk = (t >> 4) & 3;
     const bool w_row_ok = r0 + w_row < rows;
     const uint8_t* w_src = Wq + ((r0 + (w_row_ok ? w_row : 0)) * nb + w_blk) * kQ4Bytes;
-    const int w_swap = (w_row >> 2) & 1;
+    const int w_swap = (w_row >> 3) & 1;
     const int w_dst = w_blk * kPlaneB + w_row * kRecB;
-    Block4 rw;
-    bool rw_ok = false;
-    auto load_w = [&](int b0) __attribute__((always_inline)) {
-        rw_ok = w_row_ok && (b0 + w_blk < nb);
-        if (rw_ok) rw = load_block(w_src + static_cast<int64_t>(b0) * kQ4Bytes);
+    // Raw blocks are loaded two stages ahead into one of two register sets:
+    // set t % 2 holds stage t (the global loads hide behind two stages of
+    // matrix work).
+    Block4 rw[2];
+    bool rw_ok[2] = {false, false};
+    // The loads are issued unconditionally (from a valid block when the wanted
+    // one is past the end) so that the code around them stays branch-free and
+    // the compiler can count outstanding loads exactly.
+    auto load_w = [&](int st, auto set) __attribute__((always_inline)) {
+        constexpr int S = decltype(set)::value;
+        const int b0 = st * kKB;
+        rw_ok[S] = w_row_ok && st < nst && (b0 + w_blk < nb);
+        rw[S] = load_block(w_src + (rw_ok[S] ? static_cast<int64_t>(b0) * kQ4Bytes : 0));
     };
-    auto store_w = [&](uint8_t* sB) __attribute__((always_inline)) {
+    auto store_w = [&](uint8_t* sB, auto set) __attribute__((always_inline)) {
+        constexpr int S = decltype(set)::value;
         uint32_t d6[6] = {0u, 0u, 0u, 0u, 0u, 0u};
         uint32_t dbits = 0u;  // zero scale: the block contributes nothing
-        if (rw_ok) {
-            weight_fp6(rw.qs, d6);
-            dbits = rw.dbits;
+        if (rw_ok[S]) {
+            weight_fp6(rw[S].qs, d6);
+            dbits = rw[S].dbits;
         }
         uint8_t* p = sB + w_dst;
         *reinterpret_cast<u32x4*>(p + 16 * w_swap) = u32x4{d6[0], d6[1], d6[2], d6[3]};
@@ -153,11 +192,11 @@ k_gemm(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const uint8_t* __re
     };
 
     // --- operand reads --------------------------------------------------------
-    const int a_sw = (l32 >> 1) & 3;
+    const int a_sw = (l32 >> 2) & 3;
     const int a_row = (wm * 64 + l32) * kAct6Bytes;
     const int a_p0 = a_row + 16 * ((2 * half) ^ a_sw);
     const int a_p1 = a_row + 16 * ((2 * half + 1) ^ a_sw);
-    const int b_sw = (l32 >> 2) & 1;
+    const int b_sw = (l32 >> 3) & 1;
     const int b_row = (wn * 64 + l32) * kRecB;
     const int b_p0 = b_row + 16 * b_sw;
     const int b_p1 = b_row + 16 * (b_sw ^ 1);
@@ -177,34 +216,22 @@ k_gemm(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const uint8_t* __re
     // Operands of block plane `blk` (wrapping, so that a read past the last
     // plane is a harmless re-read of plane 0).  The two 16-byte halves are
     // kept apart until use, so that no register copy forces an early wait.
-    auto read_ops = [&](const uint8_t* sA, const uint8_t* sB, int blk, u32x4 (*a)[2], u32x4 (*w)[2])
+    auto read_ops = [&](const uint8_t* sA, const uint8_t* sB, int blk, Operand* a, Operand* w)
                         __attribute__((always_inline)) {
         const uint8_t* pa = sA + (blk & (kKB - 1)) * kPlaneA;
         const uint8_t* pb = sB + (blk & (kKB - 1)) * kPlaneB;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            a[i][0] = *reinterpret_cast<const u32x4*>(pa + a_p0 + i * 32 * kAct6Bytes);
-            a[i][1] = *reinterpret_cast<const u32x4*>(pa + a_p1 + i * 32 * kAct6Bytes);
-        }
+        for (int i = 0; i < 2; ++i) a[i] = lds_operand(pa + a_p0 + i * 32 * kAct6Bytes, pa + a_p1 + i * 32 * kAct6Bytes);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            w[j][0] = *reinterpret_cast<const u32x4*>(pb + b_p0 + j * 32 * kRecB);
-            w[j][1] = *reinterpret_cast<const u32x4*>(pb + b_p1 + j * 32 * kRecB);
-        }
+        for (int j = 0; j < 2; ++j) w[j] = lds_operand(pb + b_p0 + j * 32 * kRecB, pb + b_p1 + j * 32 * kRecB);
     };
     // The four 32 x 32 tiles of one block.
-    auto tiles = [&](const u32x4 (*ra)[2], const u32x4 (*rw)[2], int b) __attribute__((always_inline)) {
-        i32x8 a[2], w[2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            a[i] = join(ra[i][0], ra[i][1]);
-            w[i] = join(rw[i][0], rw[i][1]);
-        }
+    auto tiles = [&](const Operand* a, const Operand* w, int b) __attribute__((always_inline)) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int i = k >> 1, j = k & 1;
             const f32x16 sk = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                a[i], w[j], zero, 2, 2, 0, scale_a, 0, kScaleW);
+                fp6_operand(a[i]), fp6_operand(w[j]), zero, 2, 2, 0, scale_a, 0, kScaleW);
             if constexpr (DOTS) {
                 const int64_t r = r0 + wn * 64 + j * 32 + l32;
                 if (b < nb && r < rows) {
@@ -227,7 +254,7 @@ k_gemm(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const uint8_t* __re
     // One stage of kKB blocks; the next block's operands are read while the
     // current block computes (two register sets, ping-pong).
     auto compute = [&](const uint8_t* sA, const uint8_t* sB, int b0) __attribute__((always_inline)) {
-        u32x4 a0[2][2], w0[2][2], a1[2][2], w1[2][2];
+        Operand a0[2], w0[2], a1[2], w1[2];
         read_ops(sA, sB, 0, a0, w0);
 #pragma unroll 1
         for (int blk = 0; blk < kKB; blk += 2) {
@@ -238,26 +265,43 @@ k_gemm(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const uint8_t* __re
         }
     };
 
+    // Weight conversion is split between the two waves that share a SIMD
+    // (waves w and w + 4): waves 4-7 convert the next stage's weights when a
+    // stage starts, waves 0-3 when it ends.  One wave of each pair then keeps
+    // the matrix core busy while the other spends its vector ALU on the
+    // conversion.
+    const bool late = (wave >> 2) == 0;
+
     // One stage: prefetch stage s + 1 into the other buffers, compute stage s.
     auto stage = [&](auto bufsel, int s) __attribute__((always_inline)) {
         constexpr int X = decltype(bufsel)::value;
+        constexpr std::integral_constant<int, X> cur{};
+        constexpr std::integral_constant<int, X ^ 1> nxt{};
         uint8_t* sA = X ? sA1 : sA0;
         uint8_t* sB = X ? sB1 : sB0;
         uint8_t* sA_next = X ? sA0 : sA1;
         uint8_t* sB_next = X ? sB0 : sB1;
         const bool more = s + 1 < nst;
-        if (more) {
-            load_w((s + 1) * kKB);
-            issue_dma((s + 1) * kKB, sA_next);
-        }
+        if (!late && more) store_w(sB_next, nxt);  // stage s + 1
+        issue_dma((s + 1) * kKB, sA_next);        // past the end: harmless, never read
+        // The raw weights of stage s + 2 go out after the activation loads
+        // (loads complete in order): the barrier below then waits for the
+        // activations only and leaves these two loads in flight.
+        __builtin_amdgcn_sched_barrier(0);
+        load_w(s + 2, cur);  // set X held stage s, already converted
+        __builtin_amdgcn_sched_barrier(0);
         compute(sA, sB, s * kKB);
-        if (more) store_w(sB_next);
-        __syncthreads();
+        if (late && more) store_w(sB_next, nxt);
+        // vmcnt <= 2 (activation DMA landed in LDS), lgkmcnt = 0 (weight
+        // records written), expcnt unconstrained
+        __builtin_amdgcn_s_waitcnt(0x0072);
+        __builtin_amdgcn_s_barrier();
     };
 
-    load_w(0);
+    load_w(0, std::integral_constant<int, 0>{});
+    load_w(1, std::integral_constant<int, 1>{});
     issue_dma(0, sA0);
-    store_w(sB0);
+    store_w(sB0, std::integral_constant<int, 0>{});
     __syncthreads();
     for (int s = 0; s < nst; s += 2) {
         stage(std::integral_constant<int, 0>{}, s);
