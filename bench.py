@@ -68,7 +68,7 @@ def kernel_bytes(rows, K, N):
 class Mats:
     """Device copies of one workload's weights (rotated) and activations."""
 
-    def __init__(self, hip, torch, cid, N):
+    def __init__(self, hip, torch, cid, N, repack=False):
         from q4_block_quantized_amd import inputs
         wl = inputs.WORKLOADS[cid]
         self.wl, self.N = wl, N
@@ -77,6 +77,8 @@ class Mats:
             W = torch.from_numpy(inputs.weights(cid, m, rows, K, outliers=wl.outliers)).cuda()
             Wq = hip.q4_0_quantize(W)
             del W
+            if repack:  # the optional one-time repack (nibble stream + scale stream)
+                Wq = hip.q4_0_repack(Wq, K)
             X = torch.from_numpy(inputs.activations(cid, m, max(wl.ns), K)[:N].copy()).cuda()
             Y = torch.empty((N, rows), dtype=torch.float32, device="cuda")
             ws = hip.workspace(rows, K, N)
@@ -86,11 +88,13 @@ class Mats:
         for it in self.items:
             it[2] += [it[2][0].clone() for _ in range(copies - 1)]
         self.copies = copies
+        self.repack = repack
         torch.cuda.synchronize()
 
     def step(self, hip, i):
+        f = hip.mul_mat_q4_0r_q8_0_ex if self.repack else hip.mul_mat_q4_0_q8_0_ex
         for rows, K, Wqs, X, Y, ws in self.items:
-            hip.mul_mat_q4_0_q8_0_ex(Wqs[i % self.copies], X, ws, Y)
+            f(Wqs[i % self.copies], X, ws, Y)
 
     def kernel_only(self, hip, i):
         for rows, K, Wqs, X, Y, ws in self.items:
@@ -199,6 +203,14 @@ def main():
                 "bytes": mats.bytes_kernel() // n_launch}
     del mats
     torch.cuda.empty_cache()
+    # the same step on repacked weights (q4_0_repack, done once, outside the timed region)
+    rmats = Mats(hip, torch, cid, N, repack=True)
+    ms_rstep = timed(torch, lambda i: rmats.step(hip, i), args.steps, args.warmup)
+    rgbs = rmats.bytes_step() / (ms_rstep * 1e-3) / 1e9
+    log("repacked weights: step %.2f us -> %.1f GB/s" % (ms_rstep * 1e3, rgbs))
+    repacked = {"decode": {"ms_per_step": round(ms_rstep, 5), "GB/s": round(rgbs, 1)}}
+    del rmats
+    torch.cuda.empty_cache()
 
     prefill = None
     if not args.no_prefill:
@@ -215,6 +227,13 @@ def main():
                    "roofline": {"bound": "mfma", "achieved": round(ktops, 2), "peak": INT8_PEAK_TOPS,
                                 "unit": "TOPS", "frac": round(ktops / INT8_PEAK_TOPS, 4), "traffic": None}}
         del pm
+        torch.cuda.empty_cache()
+        rpm = Mats(hip, torch, 5, 512, repack=True)
+        ms_rp = timed(torch, lambda i: rpm.step(hip, i), max(10, args.steps // 4), max(3, args.warmup // 4))
+        rtops = rpm.ops() / (ms_rp * 1e-3) / 1e12
+        log("repacked weights: prefill step %.2f us -> %.1f TOPS" % (ms_rp * 1e3, rtops))
+        repacked["prefill"] = {"ms_per_step": round(ms_rp, 5), "TOPS": round(rtops, 2)}
+        del rpm
         torch.cuda.empty_cache()
 
     cpu = None if args.no_cpu else cpu_baseline(cid, N)
@@ -233,6 +252,7 @@ def main():
         "two_phase_product_kernel": {"us_per_launch": round(ms_kernel * 1e3 / n_launch, 3),
                                      "GB/s": round(kern_gbs, 1)},
         "prefill": prefill,
+        "repacked_weights": repacked,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

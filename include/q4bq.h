@@ -123,6 +123,33 @@ int mul_mat_q4_0_q8_0_prepared(const void *Wq, int64_t rows, int64_t K,
                                const void *workspace, int64_t N, float *Y, void *stream);
 
 /*
+ * Optional one-time weight repack for the product below.  The Q4_0 blocks of
+ * "llama.cpp 深度解读" section 2 ("量化数据结构 — Q4_0 格式详解") are split into
+ * two streams with the same total size, rows*(K/32)*18 bytes:
+ *   bytes [0, 16*nblk)            nibble stream: the 16 nibble bytes of block
+ *                                 (r, b) at (r * K/32 + b) * 16, unchanged;
+ *   bytes [16*nblk, 18*nblk)      scale stream: the binary16 scale of block
+ *                                 (r, b) at 16*nblk + (r * K/32 + b) * 2,
+ * with nblk = rows * K/32.  Every 16-byte nibble block is then aligned, so the
+ * kernels read it with single 16-byte loads.  No value changes.
+ *   Wq  rows x (K/32) Q4_0 blocks, 2-byte aligned.
+ *   Wr  rows*(K/32)*18 bytes, 16-byte aligned, must not overlap Wq.
+ * Requires rows >= 1, K >= 32, K % 32 == 0.
+ */
+int q4_0_repack(const void *Wq, int64_t rows, int64_t K, void *Wr, void *stream);
+
+/*
+ * mul_mat_q4_0_q8_0 and mul_mat_q4_0_q8_0_ex on repacked weights (Wr from
+ * q4_0_repack, 16-byte aligned); every other argument and the result are as
+ * for the forms on Q4_0 blocks, bit for bit.
+ */
+int mul_mat_q4_0r_q8_0(const void *Wr, int64_t rows, int64_t K, const float *X,
+                       int64_t N, float *Y, void *stream);
+int mul_mat_q4_0r_q8_0_ex(const void *Wr, int64_t rows, int64_t K, const float *X,
+                          int64_t N, float *Y, void *workspace, size_t ws_bytes,
+                          void *stream);
+
+/*
  * The operator with pre-quantized activations: Xq holds N x (K/32) Q8_0 blocks
  * (2-byte aligned), otherwise as mul_mat_q4_0_q8_0.  Feeding it the output of
  * q8_0_quantize(X) gives exactly the Y of mul_mat_q4_0_q8_0(X).

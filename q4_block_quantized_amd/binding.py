@@ -29,6 +29,7 @@ EXPORTS = (
     "q4_0_quantize", "q8_0_quantize", "mul_mat_q4_0_q8_0", "q4bq_workspace_size",
     "mul_mat_q4_0_q8_0_ex", "mul_mat_q4_0_q8_0_pq", "q4_0_q8_0_block_dots",
     "q4bq_status_string", "q4bq_version", "q4bq_quantize_activations", "mul_mat_q4_0_q8_0_prepared",
+    "q4_0_repack", "mul_mat_q4_0r_q8_0", "mul_mat_q4_0r_q8_0_ex",
 )
 
 
@@ -57,6 +58,9 @@ def lib() -> ctypes.CDLL:
         "q4bq_workspace_size": (ctypes.c_size_t, [I64, I64, I64]),
         "mul_mat_q4_0_q8_0_ex": (I, [P, I64, I64, P, I64, P, P, ctypes.c_size_t, P]),
         "mul_mat_q4_0_q8_0_pq": (I, [P, I64, I64, P, I64, P, P]),
+        "q4_0_repack": (I, [P, I64, I64, P, P]),
+        "mul_mat_q4_0r_q8_0": (I, [P, I64, I64, P, I64, P, P]),
+        "mul_mat_q4_0r_q8_0_ex": (I, [P, I64, I64, P, I64, P, P, ctypes.c_size_t, P]),
         "q4_0_q8_0_block_dots": (I, [P, I64, I64, P, I64, P, P]),
         "q4bq_quantize_activations": (I, [P, I64, I64, P, ctypes.c_size_t, P]),
         "mul_mat_q4_0_q8_0_prepared": (I, [P, I64, I64, P, I64, P, P]),
@@ -164,6 +168,40 @@ def mul_mat_q4_0_q8_0_ex(Wq: torch.Tensor, X: torch.Tensor, ws: torch.Tensor, Y:
     _check(lib().mul_mat_q4_0_q8_0_ex(_dev(Wq, torch.uint8, "Wq"), rows, K, _dev(X, torch.float32, "X"), N,
                                       _dev(Y, torch.float32, "Y"), _dev(ws, torch.uint8, "workspace"),
                                       ws.numel(), _stream(stream)), "mul_mat_q4_0_q8_0_ex")
+    return Y
+
+
+def q4_0_repack(Wq: torch.Tensor, K: int, Wr: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Q4_0 blocks -> repacked weights (nibble stream, then scale stream; same byte count)."""
+    rows = _rows(Wq, K)
+    if Wr is None:
+        Wr = torch.empty(Wq.numel(), dtype=torch.uint8, device=Wq.device)  # the allocator aligns to 256 bytes
+    _check(lib().q4_0_repack(_dev(Wq, torch.uint8, "Wq"), rows, K, _dev(Wr, torch.uint8, "Wr"), _stream(stream)),
+           "q4_0_repack")
+    return Wr
+
+
+def mul_mat_q4_0r_q8_0(Wr: torch.Tensor, X: torch.Tensor, Y: torch.Tensor | None = None,
+                       stream=None) -> torch.Tensor:
+    """mul_mat_q4_0_q8_0 on repacked weights."""
+    N, K = X.shape
+    rows = _rows(Wr, K)
+    if Y is None:
+        Y = torch.empty((N, rows), dtype=torch.float32, device=X.device)
+    _check(lib().mul_mat_q4_0r_q8_0(_dev(Wr, torch.uint8, "Wr"), rows, K, _dev(X, torch.float32, "X"), N,
+                                    _dev(Y, torch.float32, "Y"), _stream(stream)), "mul_mat_q4_0r_q8_0")
+    return Y
+
+
+def mul_mat_q4_0r_q8_0_ex(Wr: torch.Tensor, X: torch.Tensor, ws: torch.Tensor, Y: torch.Tensor | None = None,
+                          stream=None) -> torch.Tensor:
+    N, K = X.shape
+    rows = _rows(Wr, K)
+    if Y is None:
+        Y = torch.empty((N, rows), dtype=torch.float32, device=X.device)
+    _check(lib().mul_mat_q4_0r_q8_0_ex(_dev(Wr, torch.uint8, "Wr"), rows, K, _dev(X, torch.float32, "X"), N,
+                                       _dev(Y, torch.float32, "Y"), _dev(ws, torch.uint8, "workspace"),
+                                       ws.numel(), _stream(stream)), "mul_mat_q4_0r_q8_0_ex")
     return Y
 
 

@@ -41,35 +41,35 @@ bool too_big(int64_t a, int64_t b, int64_t bytes_per) {
     return v >= 4.0e18;
 }
 
-int run_product(const uint8_t* Wq, int64_t rows, int64_t K, const float* X, const uint8_t* Xq, int64_t N,
-                float* Y, int32_t* D, void* ws, hipStream_t s) {
+int run_product(WLayout lay, const uint8_t* Wq, int64_t rows, int64_t K, const float* X, const uint8_t* Xq,
+                int64_t N, float* Y, int32_t* D, void* ws, hipStream_t s) {
     hipError_t err = hipSuccess;
     const DeviceInfo* dev = current_device(&err);
     if (!dev) return Q4BQ_EHIP;
     const int64_t nb = K / kQK;
-    if (X && !D && gemv_fuses(N, nb)) return status_of(launch_gemv_fused(dev, Wq, rows, nb, X, N, Y, s));
+    if (X && !D && gemv_fuses(N, nb)) return status_of(launch_gemv_fused(dev, lay, Wq, rows, nb, X, N, Y, s));
     err = X ? launch_act_from_f32(X, N, nb, ws, s) : launch_act_from_q8(Xq, N, nb, ws, s);
     if (err != hipSuccess) return Q4BQ_EHIP;
     if (N <= kGemvMaxN)
-        err = launch_gemv(dev, Wq, rows, nb, ws, N, Y, D, s);
+        err = launch_gemv(dev, lay, Wq, rows, nb, ws, N, Y, D, s);
     else
-        err = launch_gemm(dev, Wq, rows, nb, ws, N, Y, D, s);
+        err = launch_gemm(dev, lay, Wq, rows, nb, ws, N, Y, D, s);
     return status_of(err);
 }
 
 // Runs the product with stream-ordered scratch taken from the device pool.
-int run_with_scratch(const uint8_t* Wq, int64_t rows, int64_t K, const float* X, const uint8_t* Xq, int64_t N,
-                     float* Y, int32_t* D, hipStream_t s) {
+int run_with_scratch(WLayout lay, const uint8_t* Wq, int64_t rows, int64_t K, const float* X, const uint8_t* Xq,
+                     int64_t N, float* Y, int32_t* D, hipStream_t s) {
     hipError_t err = hipSuccess;
     if (!current_device(&err)) return Q4BQ_EHIP;
-    if (X && !D && gemv_fuses(N, K / kQK)) return run_product(Wq, rows, K, X, Xq, N, Y, D, nullptr, s);
+    if (X && !D && gemv_fuses(N, K / kQK)) return run_product(lay, Wq, rows, K, X, Xq, N, Y, D, nullptr, s);
     const size_t bytes = q4bq_workspace_size(rows, K, N);
     void* ws = nullptr;
     if (hipMallocAsync(&ws, bytes, s) != hipSuccess || ws == nullptr) {
         (void)hipGetLastError();
         return Q4BQ_ENOMEM;
     }
-    const int rc = run_product(Wq, rows, K, X, Xq, N, Y, D, ws, s);
+    const int rc = run_product(lay, Wq, rows, K, X, Xq, N, Y, D, ws, s);
     if (hipFreeAsync(ws, s) != hipSuccess) return Q4BQ_EHIP;
     return rc;
 }
@@ -122,6 +122,18 @@ int q8_0_quantize(const float* X, int64_t N, int64_t K, void* Xq, void* stream) 
     return status_of(launch_q8_0_quantize(X, nblocks, static_cast<uint8_t*>(Xq), static_cast<hipStream_t>(stream)));
 }
 
+int q4_0_repack(const void* Wq, int64_t rows, int64_t K, void* Wr, void* stream) {
+    if (!Wq || !Wr || bad_dim(rows) || bad_k(K) || too_big(rows, K, 1)) return Q4BQ_EINVAL;
+    if (!aligned(Wq, 2) || !aligned(Wr, 16)) return Q4BQ_EINVAL;
+    const int64_t nblocks = rows * (K / kQK);
+    const size_t bytes = static_cast<size_t>(nblocks) * kQ4Bytes;
+    if (overlap(Wq, bytes, Wr, bytes)) return Q4BQ_EINVAL;
+    hipError_t err = hipSuccess;
+    if (!current_device(&err)) return Q4BQ_EHIP;
+    return status_of(launch_q4_0_repack(static_cast<const uint8_t*>(Wq), nblocks, static_cast<uint8_t*>(Wr),
+                                        static_cast<hipStream_t>(stream)));
+}
+
 size_t q4bq_workspace_size(int64_t rows, int64_t K, int64_t N) {
     if (bad_dim(rows) || bad_dim(N) || bad_k(K) || too_big(N, K, 4)) return 0;
     const size_t b = act_bytes(N, K / kQK);
@@ -139,14 +151,14 @@ namespace {
 enum ActKind { kF32, kQ8, kPrepared };
 
 int check_product(const void* Wq, int64_t rows, int64_t K, const void* Xany, ActKind kind, int64_t N,
-                  const void* out, bool dots) {
+                  const void* out, bool dots, WLayout lay = kAoS) {
     if (!Wq || !Xany || !out || bad_dim(rows) || bad_dim(N) || bad_k(K)) return Q4BQ_EINVAL;
     const int64_t nb = K / kQK;
     if (too_big(rows, K, 1) || too_big(N, K, 4) || too_big(N, rows, 4)) return Q4BQ_EINVAL;
     if (dots && too_big(N * rows, nb, 4)) return Q4BQ_EINVAL;
     if (N > kGemvMaxN && ((rows + 127) / 128) * ((N + 255) / 256) >= (int64_t(1) << 31)) return Q4BQ_EINVAL;
     const uintptr_t x_align = kind == kF32 ? 4 : kind == kQ8 ? 2 : 16;
-    if (!aligned(Wq, 2) || !aligned(Xany, x_align) || !aligned(out, 4)) return Q4BQ_EINVAL;
+    if (!aligned(Wq, lay == kRepacked ? 16 : 2) || !aligned(Xany, x_align) || !aligned(out, 4)) return Q4BQ_EINVAL;
     const size_t w_bytes = static_cast<size_t>(rows * nb) * kQ4Bytes;
     const size_t x_bytes = kind == kF32 ? static_cast<size_t>(N * K) * 4
                            : kind == kQ8 ? static_cast<size_t>(N * nb) * kQ8Bytes
@@ -163,7 +175,7 @@ extern "C" {
 int mul_mat_q4_0_q8_0(const void* Wq, int64_t rows, int64_t K, const float* X, int64_t N, float* Y, void* stream) {
     const int rc = check_product(Wq, rows, K, X, kF32, N, Y, false);
     if (rc != Q4BQ_OK) return rc;
-    return run_with_scratch(static_cast<const uint8_t*>(Wq), rows, K, X, nullptr, N, Y, nullptr,
+    return run_with_scratch(kAoS, static_cast<const uint8_t*>(Wq), rows, K, X, nullptr, N, Y, nullptr,
                             static_cast<hipStream_t>(stream));
 }
 
@@ -179,7 +191,30 @@ int mul_mat_q4_0_q8_0_ex(const void* Wq, int64_t rows, int64_t K, const float* X
         overlap(workspace, need, X, static_cast<size_t>(N * K) * 4) ||
         overlap(workspace, need, Wq, static_cast<size_t>(rows * nb) * kQ4Bytes))
         return Q4BQ_EINVAL;
-    return run_product(static_cast<const uint8_t*>(Wq), rows, K, X, nullptr, N, Y, nullptr, workspace,
+    return run_product(kAoS, static_cast<const uint8_t*>(Wq), rows, K, X, nullptr, N, Y, nullptr, workspace,
+                       static_cast<hipStream_t>(stream));
+}
+
+int mul_mat_q4_0r_q8_0(const void* Wr, int64_t rows, int64_t K, const float* X, int64_t N, float* Y, void* stream) {
+    const int rc = check_product(Wr, rows, K, X, kF32, N, Y, false, kRepacked);
+    if (rc != Q4BQ_OK) return rc;
+    return run_with_scratch(kRepacked, static_cast<const uint8_t*>(Wr), rows, K, X, nullptr, N, Y, nullptr,
+                            static_cast<hipStream_t>(stream));
+}
+
+int mul_mat_q4_0r_q8_0_ex(const void* Wr, int64_t rows, int64_t K, const float* X, int64_t N, float* Y,
+                          void* workspace, size_t ws_bytes, void* stream) {
+    const int rc = check_product(Wr, rows, K, X, kF32, N, Y, false, kRepacked);
+    if (rc != Q4BQ_OK) return rc;
+    if (!workspace || !aligned(workspace, 16)) return Q4BQ_EINVAL;
+    const size_t need = q4bq_workspace_size(rows, K, N);
+    if (ws_bytes < need) return Q4BQ_ENOMEM;
+    const int64_t nb = K / kQK;
+    if (overlap(workspace, need, Y, static_cast<size_t>(N * rows) * 4) ||
+        overlap(workspace, need, X, static_cast<size_t>(N * K) * 4) ||
+        overlap(workspace, need, Wr, static_cast<size_t>(rows * nb) * kQ4Bytes))
+        return Q4BQ_EINVAL;
+    return run_product(kRepacked, static_cast<const uint8_t*>(Wr), rows, K, X, nullptr, N, Y, nullptr, workspace,
                        static_cast<hipStream_t>(stream));
 }
 
@@ -187,16 +222,16 @@ int mul_mat_q4_0_q8_0_pq(const void* Wq, int64_t rows, int64_t K, const void* Xq
                          void* stream) {
     const int rc = check_product(Wq, rows, K, Xq, kQ8, N, Y, false);
     if (rc != Q4BQ_OK) return rc;
-    return run_with_scratch(static_cast<const uint8_t*>(Wq), rows, K, nullptr, static_cast<const uint8_t*>(Xq), N,
-                            Y, nullptr, static_cast<hipStream_t>(stream));
+    return run_with_scratch(kAoS, static_cast<const uint8_t*>(Wq), rows, K, nullptr, static_cast<const uint8_t*>(Xq),
+                            N, Y, nullptr, static_cast<hipStream_t>(stream));
 }
 
 int q4_0_q8_0_block_dots(const void* Wq, int64_t rows, int64_t K, const void* Xq, int64_t N, int32_t* D,
                          void* stream) {
     const int rc = check_product(Wq, rows, K, Xq, kQ8, N, D, true);
     if (rc != Q4BQ_OK) return rc;
-    return run_with_scratch(static_cast<const uint8_t*>(Wq), rows, K, nullptr, static_cast<const uint8_t*>(Xq), N,
-                            nullptr, D, static_cast<hipStream_t>(stream));
+    return run_with_scratch(kAoS, static_cast<const uint8_t*>(Wq), rows, K, nullptr, static_cast<const uint8_t*>(Xq),
+                            N, nullptr, D, static_cast<hipStream_t>(stream));
 }
 
 int q4bq_quantize_activations(const float* X, int64_t N, int64_t K, void* workspace, size_t ws_bytes,
@@ -220,8 +255,9 @@ int mul_mat_q4_0_q8_0_prepared(const void* Wq, int64_t rows, int64_t K, const vo
     if (!dev) return Q4BQ_EHIP;
     const int64_t nb = K / kQK;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    err = N <= kGemvMaxN ? launch_gemv(dev, static_cast<const uint8_t*>(Wq), rows, nb, workspace, N, Y, nullptr, s)
-                         : launch_gemm(dev, static_cast<const uint8_t*>(Wq), rows, nb, workspace, N, Y, nullptr, s);
+    const uint8_t* w = static_cast<const uint8_t*>(Wq);
+    err = N <= kGemvMaxN ? launch_gemv(dev, kAoS, w, rows, nb, workspace, N, Y, nullptr, s)
+                         : launch_gemm(dev, kAoS, w, rows, nb, workspace, N, Y, nullptr, s);
     return status_of(err);
 }
 

@@ -263,6 +263,51 @@ __device__ __forceinline__ Block4 load_block(const uint8_t* p) {
     return b;
 }
 
+// Repacked weights (q4_0_repack): a nibble stream of 16 bytes per block, then a
+// stream of the binary16 scales, both in (row, block) order.  Two consecutive
+// blocks: 32 aligned nibble bytes and 4 scale bytes, kept in the same nine
+// dwords as a raw pair (nibbles of the first block in w[0..3], of the second
+// in w[4..7], both scales in w[8]).
+__device__ __forceinline__ Pair36 load_pair_rp(const uint8_t* nib, const uint8_t* sc) {
+    Pair36 r;
+    u32x4 a, b;
+    uint32_t c;
+    __builtin_memcpy(&a, nib, 16);
+    __builtin_memcpy(&b, nib + 16, 16);
+    __builtin_memcpy(&c, sc, 4);
+    r.w[0] = a.x; r.w[1] = a.y; r.w[2] = a.z; r.w[3] = a.w;
+    r.w[4] = b.x; r.w[5] = b.y; r.w[6] = b.z; r.w[7] = b.w;
+    r.w[8] = c;
+    return r;
+}
+
+__device__ __forceinline__ Block4 pair_first_rp(const Pair36& p) {
+    Block4 b;
+    b.dbits = p.w[8] & 0xFFFFu;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) b.qs[k] = p.w[k];
+    return b;
+}
+
+__device__ __forceinline__ Block4 pair_second_rp(const Pair36& p) {
+    Block4 b;
+    b.dbits = p.w[8] >> 16;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) b.qs[k] = p.w[4 + k];
+    return b;
+}
+
+__device__ __forceinline__ Block4 load_block_rp(const uint8_t* nib, const uint8_t* sc) {
+    Block4 b;
+    uint16_t d;
+    u32x4 q;
+    __builtin_memcpy(&d, sc, 2);
+    __builtin_memcpy(&q, nib, 16);
+    b.dbits = d;
+    b.qs[0] = q.x; b.qs[1] = q.y; b.qs[2] = q.z; b.qs[3] = q.w;
+    return b;
+}
+
 // The block's integer dot with one activation block in dot order:
 //   s = sum_j (nibble_j - 8) * q_j = sum_j nibble_j * q_j + bias,
 // bias = -8 * sum_j q_j.  Nibbles 0..15 are valid positive int8, so the signed

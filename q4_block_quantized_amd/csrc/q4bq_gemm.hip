@@ -17,7 +17,8 @@
 //    zero, so the same two reads also deliver the scale-product operand;
 //  * the activation records go from global memory straight into LDS
 //    (global_load_lds, no registers); the weights are read as raw 18-byte
-//    blocks and turned into fp6 codes while they are staged into LDS;
+//    blocks (or, after q4_0_repack, as aligned nibble blocks plus a scale
+//    stream) and turned into fp6 codes while they are staged into LDS;
 //  * LDS is double-buffered: while one stage (4 blocks of K) is computed, the
 //    next stage's activations stream in and its weights are converted, with
 //    one barrier per stage.
@@ -101,7 +102,7 @@ __device__ __forceinline__ void dma16(const uint8_t* src, const uint8_t* dst) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(lds), "v"(src) : "memory", "m0");
 }
 
-template <bool DOTS>
+template <bool DOTS, bool RP>
 __global__ void __launch_bounds__(kThreads)
 k_gemm(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const uint8_t* __restrict__ act, int64_t N,
        float* __restrict__ Y, int32_t* __restrict__ D) {
@@ -161,7 +162,10 @@ k_gemm(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const uint8_t* __re
     const int w_row = (t & 15) | ((t >> 6) << 4);
     const int w_blk = (t >> 4) & 3;
     const bool w_row_ok = r0 + w_row < rows;
-    const uint8_t* w_src = Wq + ((r0 + (w_row_ok ? w_row : 0)) * nb + w_blk) * kQ4Bytes;
+    // RP: Wq holds the repacked streams (16 nibble bytes per block, then the scales)
+    const int64_t w_row_first = (r0 + (w_row_ok ? w_row : 0)) * nb;  // block index of the row's first block
+    const uint8_t* w_src = Wq + w_row_first * (RP ? 16 : kQ4Bytes);
+    const uint8_t* w_sc = Wq + (RP ? rows * nb * 16 + w_row_first * 2 : 0);
     const int w_swap = (w_row >> 3) & 1;
     const int w_dst = w_blk * kPlaneB + w_row * kRecB;
     // Raw blocks are loaded two stages ahead into one of two register sets:
@@ -176,7 +180,8 @@ k_gemm(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const uint8_t* __re
         constexpr int S = decltype(set)::value;
         const int b0 = st * kKB;
         rw_ok[S] = w_row_ok && st < nst && (b0 + w_blk < nb);
-        rw[S] = load_block(w_src + (rw_ok[S] ? static_cast<int64_t>(b0) * kQ4Bytes : 0));
+        const int64_t bo = rw_ok[S] ? b0 + w_blk : 0;  // else block 0 of a valid row
+        rw[S] = RP ? load_block_rp(w_src + bo * 16, w_sc + bo * 2) : load_block(w_src + bo * kQ4Bytes);
     };
     auto store_w = [&](uint8_t* sB, auto set) __attribute__((always_inline)) {
         constexpr int S = decltype(set)::value;
@@ -327,15 +332,18 @@ k_gemm(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const uint8_t* __re
 
 }  // namespace
 
-hipError_t launch_gemm(const DeviceInfo* dev, const uint8_t* Wq, int64_t rows, int64_t nb, const void* act,
-                       int64_t N, float* Y, int32_t* D, hipStream_t s) {
+hipError_t launch_gemm(const DeviceInfo* dev, WLayout lay, const uint8_t* Wq, int64_t rows, int64_t nb,
+                       const void* act, int64_t N, float* Y, int32_t* D, hipStream_t s) {
     (void)dev;
     const uint8_t* rec = static_cast<const uint8_t*>(act);
     const dim3 grid(static_cast<uint32_t>(((rows + kBR - 1) / kBR) * ((N + kBT - 1) / kBT)));
+    const int nbi = static_cast<int>(nb);
     if (D)
-        hipLaunchKernelGGL(k_gemm<true>, grid, dim3(kThreads), 0, s, Wq, rows, static_cast<int>(nb), rec, N, Y, D);
+        hipLaunchKernelGGL((k_gemm<true, false>), grid, dim3(kThreads), 0, s, Wq, rows, nbi, rec, N, Y, D);
+    else if (lay == kRepacked)
+        hipLaunchKernelGGL((k_gemm<false, true>), grid, dim3(kThreads), 0, s, Wq, rows, nbi, rec, N, Y, D);
     else
-        hipLaunchKernelGGL(k_gemm<false>, grid, dim3(kThreads), 0, s, Wq, rows, static_cast<int>(nb), rec, N, Y, D);
+        hipLaunchKernelGGL((k_gemm<false, false>), grid, dim3(kThreads), 0, s, Wq, rows, nbi, rec, N, Y, D);
     return hipGetLastError();
 }
 

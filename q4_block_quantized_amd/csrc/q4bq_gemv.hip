@@ -17,6 +17,9 @@
 //    nothing per element;
 //  * per block one convert and one FMA fold the int32 dot into fp32;
 //  * lanes of a row combine with a butterfly over G lanes.
+// The weights are read either as the pages' 18-byte blocks or, after
+// q4_0_repack, as 16-byte-aligned nibble blocks plus a separate scale stream
+// (same bytes, same arithmetic, same bits).
 // Activations come from the quantizer's buffer (read in place, or copied to
 // LDS when they fit) or, for one or two tokens, are quantized from fp32 by the
 // kernel itself into LDS before it streams the weights; the Q8_0 arithmetic is
@@ -34,11 +37,13 @@ constexpr size_t kMaxActLds = 64 * 1024;
 
 enum Src { kActGlobal = 0, kActLds = 1, kXF32 = 2 };
 
-template <int NT, int THREADS, int SRC, bool DOTS>
+template <int NT, int THREADS, int SRC, bool DOTS, bool RP>
 __global__ void __launch_bounds__(THREADS)
 k_gemv(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __restrict__ src,
        float* __restrict__ Y, int32_t* __restrict__ D, int log2G, int rpi) {
     constexpr int kWaves = THREADS / 64;
+    // RP: Wq holds the repacked streams (nibbles, then scales)
+    const uint8_t* __restrict__ Wsc = Wq + (RP ? rows * nb * 16 : 0);
     extern __shared__ __align__(16) uint8_t smem[];
     const uint32_t* act_q;
     const ActScale* act_s;
@@ -115,8 +120,10 @@ k_gemv(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __restr
 #pragma unroll
                 for (int u = 0; u < kU; ++u) {
                     const int p = pos + ((i0 + u) << log2G);
-                    if (rv[j] && pv[u])
-                        raw[j][u] = load_pair(Wq + (r[j] * nb + 2 * p) * kQ4Bytes);
+                    if (rv[j] && pv[u]) {
+                        const int64_t blk0 = r[j] * nb + 2 * p;
+                        raw[j][u] = RP ? load_pair_rp(Wq + blk0 * 16, Wsc + blk0 * 2) : load_pair(Wq + blk0 * kQ4Bytes);
+                    }
                 }
 #pragma unroll
             for (int u = 0; u < kU; ++u) {
@@ -135,7 +142,8 @@ k_gemv(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __restr
 #pragma unroll
                         for (int j = 0; j < kRmax; ++j) {
                             if (!rv[j]) continue;
-                            const Block4 blk = h ? pair_second(raw[j][u]) : pair_first(raw[j][u]);
+                            const Block4 blk = RP ? (h ? pair_second_rp(raw[j][u]) : pair_first_rp(raw[j][u]))
+                                                  : (h ? pair_second(raw[j][u]) : pair_first(raw[j][u]));
                             const int32_t s = block_dot(blk, a, sc.bias);
                             if constexpr (DOTS) {
                                 D[(static_cast<int64_t>(n) * rows + r[j]) * nb + b] = s;
@@ -153,7 +161,8 @@ k_gemv(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __restr
 #pragma unroll
             for (int j = 0; j < kRmax; ++j) {
                 if (!rv[j]) continue;
-                const Block4 blk = load_block(Wq + (r[j] * nb + b) * kQ4Bytes);
+                const int64_t bi = r[j] * nb + b;
+                const Block4 blk = RP ? load_block_rp(Wq + bi * 16, Wsc + bi * 2) : load_block(Wq + bi * kQ4Bytes);
 #pragma unroll
                 for (int n = 0; n < NT; ++n) {
                     const int64_t ab = static_cast<int64_t>(n) * nb + b;
@@ -235,25 +244,29 @@ Shape pick_shape(const DeviceInfo* dev, int64_t rows, int64_t nb, int threads, i
 }
 
 template <int NT, int THREADS, int SRC, bool DOTS>
-hipError_t launch_v(const Shape& sh, const uint8_t* Wq, int64_t rows, int64_t nb, const void* src, float* Y,
-                    int32_t* D, hipStream_t s) {
+hipError_t launch_v(const Shape& sh, WLayout lay, const uint8_t* Wq, int64_t rows, int64_t nb, const void* src,
+                    float* Y, int32_t* D, hipStream_t s) {
     const size_t lds = SRC == kActGlobal ? 0 : static_cast<size_t>(NT) * nb * (kActQBytes + kActSBytes);
-    hipLaunchKernelGGL((k_gemv<NT, THREADS, SRC, DOTS>), dim3(sh.wgs), dim3(THREADS), lds, s, Wq, rows,
-                       static_cast<int>(nb), src, Y, D, sh.log2G, sh.rpi);
+    if (lay == kRepacked)
+        hipLaunchKernelGGL((k_gemv<NT, THREADS, SRC, DOTS, true>), dim3(sh.wgs), dim3(THREADS), lds, s, Wq, rows,
+                           static_cast<int>(nb), src, Y, D, sh.log2G, sh.rpi);
+    else
+        hipLaunchKernelGGL((k_gemv<NT, THREADS, SRC, DOTS, false>), dim3(sh.wgs), dim3(THREADS), lds, s, Wq, rows,
+                           static_cast<int>(nb), src, Y, D, sh.log2G, sh.rpi);
     return hipGetLastError();
 }
 
 template <int NT>
-hipError_t launch_n(const DeviceInfo* dev, const uint8_t* Wq, int64_t rows, int64_t nb, const void* act, float* Y,
-                    int32_t* D, hipStream_t s) {
+hipError_t launch_n(const DeviceInfo* dev, WLayout lay, const uint8_t* Wq, int64_t rows, int64_t nb, const void* act,
+                    float* Y, int32_t* D, hipStream_t s) {
     const bool lds = static_cast<size_t>(NT) * nb * (kActQBytes + kActSBytes) <= kMaxActLds;
     const Shape sh = pick_shape(dev, rows, nb, 256, 4, 16);
     if (D) {
-        return lds ? launch_v<NT, 256, kActLds, true>(sh, Wq, rows, nb, act, Y, D, s)
-                   : launch_v<NT, 256, kActGlobal, true>(sh, Wq, rows, nb, act, Y, D, s);
+        return lds ? launch_v<NT, 256, kActLds, true>(sh, lay, Wq, rows, nb, act, Y, D, s)
+                   : launch_v<NT, 256, kActGlobal, true>(sh, lay, Wq, rows, nb, act, Y, D, s);
     }
-    return lds ? launch_v<NT, 256, kActLds, false>(sh, Wq, rows, nb, act, Y, D, s)
-               : launch_v<NT, 256, kActGlobal, false>(sh, Wq, rows, nb, act, Y, D, s);
+    return lds ? launch_v<NT, 256, kActLds, false>(sh, lay, Wq, rows, nb, act, Y, D, s)
+               : launch_v<NT, 256, kActGlobal, false>(sh, lay, Wq, rows, nb, act, Y, D, s);
 }
 
 }  // namespace
@@ -262,26 +275,26 @@ bool gemv_fuses(int64_t N, int64_t nb) {
     return N <= kGemvFusedMaxN && static_cast<size_t>(N) * nb * (kActQBytes + kActSBytes) <= kMaxActLds;
 }
 
-hipError_t launch_gemv_fused(const DeviceInfo* dev, const uint8_t* Wq, int64_t rows, int64_t nb, const float* X,
-                             int64_t N, float* Y, hipStream_t s) {
+hipError_t launch_gemv_fused(const DeviceInfo* dev, WLayout lay, const uint8_t* Wq, int64_t rows, int64_t nb,
+                             const float* X, int64_t N, float* Y, hipStream_t s) {
     const Shape sh = pick_shape(dev, rows, nb, 1024, 1, 16);
     switch (N) {
-        case 1: return launch_v<1, 1024, kXF32, false>(sh, Wq, rows, nb, X, Y, nullptr, s);
+        case 1: return launch_v<1, 1024, kXF32, false>(sh, lay, Wq, rows, nb, X, Y, nullptr, s);
         default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_gemv(const DeviceInfo* dev, const uint8_t* Wq, int64_t rows, int64_t nb, const void* act,
-                       int64_t N, float* Y, int32_t* D, hipStream_t s) {
+hipError_t launch_gemv(const DeviceInfo* dev, WLayout lay, const uint8_t* Wq, int64_t rows, int64_t nb,
+                       const void* act, int64_t N, float* Y, int32_t* D, hipStream_t s) {
     switch (N) {
-        case 1: return launch_n<1>(dev, Wq, rows, nb, act, Y, D, s);
-        case 2: return launch_n<2>(dev, Wq, rows, nb, act, Y, D, s);
-        case 3: return launch_n<3>(dev, Wq, rows, nb, act, Y, D, s);
-        case 4: return launch_n<4>(dev, Wq, rows, nb, act, Y, D, s);
-        case 5: return launch_n<5>(dev, Wq, rows, nb, act, Y, D, s);
-        case 6: return launch_n<6>(dev, Wq, rows, nb, act, Y, D, s);
-        case 7: return launch_n<7>(dev, Wq, rows, nb, act, Y, D, s);
-        case 8: return launch_n<8>(dev, Wq, rows, nb, act, Y, D, s);
+        case 1: return launch_n<1>(dev, lay, Wq, rows, nb, act, Y, D, s);
+        case 2: return launch_n<2>(dev, lay, Wq, rows, nb, act, Y, D, s);
+        case 3: return launch_n<3>(dev, lay, Wq, rows, nb, act, Y, D, s);
+        case 4: return launch_n<4>(dev, lay, Wq, rows, nb, act, Y, D, s);
+        case 5: return launch_n<5>(dev, lay, Wq, rows, nb, act, Y, D, s);
+        case 6: return launch_n<6>(dev, lay, Wq, rows, nb, act, Y, D, s);
+        case 7: return launch_n<7>(dev, lay, Wq, rows, nb, act, Y, D, s);
+        case 8: return launch_n<8>(dev, lay, Wq, rows, nb, act, Y, D, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -15,6 +15,10 @@ constexpr int kQ8Bytes = 34;    // Q8_0 block: binary16 d + 32 int8
 constexpr int kActQBytes = 32;  // internal activation block (int8, dot order)
 constexpr int kActSBytes = 8;   // internal scale record {float d; int32 bias}
 
+// Weight layouts: the pages' 18-byte blocks, or the repacked streams of
+// q4_0_repack (16 nibble bytes per block, then one binary16 scale per block).
+enum WLayout { kAoS = 0, kRepacked = 1 };
+
 struct DeviceInfo {
     int id;
     int num_cu;
@@ -34,6 +38,7 @@ size_t act_bytes(int64_t N, int64_t nb);
 
 hipError_t launch_q4_0_quantize(const float* W, int64_t nblocks, uint8_t* Wq, hipStream_t s);
 hipError_t launch_q8_0_quantize(const float* X, int64_t nblocks, uint8_t* Xq, hipStream_t s);
+hipError_t launch_q4_0_repack(const uint8_t* Wq, int64_t nblocks, uint8_t* Wr, hipStream_t s);
 
 // fp32 X (N x K) -> internal activations, or Q8_0 blocks -> internal.
 hipError_t launch_act_from_f32(const float* X, int64_t N, int64_t nb, void* act, hipStream_t s);
@@ -41,7 +46,7 @@ hipError_t launch_act_from_q8(const uint8_t* Xq, int64_t N, int64_t nb, void* ac
 
 // Streaming decode kernel, N in 1..8.  D != nullptr selects the block-dot
 // export (D written, Y untouched).
-hipError_t launch_gemv(const DeviceInfo* dev, const uint8_t* Wq, int64_t rows, int64_t nb,
+hipError_t launch_gemv(const DeviceInfo* dev, WLayout lay, const uint8_t* Wq, int64_t rows, int64_t nb,
                        const void* act, int64_t N, float* Y, int32_t* D, hipStream_t s);
 
 // Decode kernel that quantizes fp32 X itself (no scratch, one launch), for
@@ -49,11 +54,11 @@ hipError_t launch_gemv(const DeviceInfo* dev, const uint8_t* Wq, int64_t rows, i
 // as launch_act_from_f32 followed by launch_gemv.
 constexpr int64_t kGemvFusedMaxN = 1;
 bool gemv_fuses(int64_t N, int64_t nb);
-hipError_t launch_gemv_fused(const DeviceInfo* dev, const uint8_t* Wq, int64_t rows, int64_t nb, const float* X,
-                             int64_t N, float* Y, hipStream_t s);
+hipError_t launch_gemv_fused(const DeviceInfo* dev, WLayout lay, const uint8_t* Wq, int64_t rows, int64_t nb,
+                             const float* X, int64_t N, float* Y, hipStream_t s);
 
 // Matrix-core kernel, any N.  D as above.
-hipError_t launch_gemm(const DeviceInfo* dev, const uint8_t* Wq, int64_t rows, int64_t nb,
+hipError_t launch_gemm(const DeviceInfo* dev, WLayout lay, const uint8_t* Wq, int64_t rows, int64_t nb,
                        const void* act, int64_t N, float* Y, int32_t* D, hipStream_t s);
 
 constexpr int64_t kGemvMaxN = 8;

@@ -108,6 +108,21 @@ k_act_from_f32(const float* __restrict__ X, int64_t nblocks, uint32_t* __restric
     }
 }
 
+// The optional one-time repack: the 18-byte blocks split into a stream of
+// 16-byte nibble blocks (aligned, for plain 16-byte loads) followed by a
+// stream of the binary16 scales, both in (row, block) order.  Same bytes in
+// total; no value changes.
+__global__ void __launch_bounds__(kThreads)
+k_q4_0_repack(const uint8_t* __restrict__ Wq, int64_t nblocks, uint8_t* __restrict__ Wr) {
+    uint16_t* sc = reinterpret_cast<uint16_t*>(Wr + nblocks * 16);
+    for (int64_t g = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; g < nblocks;
+         g += static_cast<int64_t>(gridDim.x) * kThreads) {
+        const Block4 b = load_block(Wq + g * kQ4Bytes);
+        *reinterpret_cast<u32x4*>(Wr + g * 16) = u32x4{b.qs[0], b.qs[1], b.qs[2], b.qs[3]};
+        sc[g] = static_cast<uint16_t>(b.dbits);
+    }
+}
+
 // Prefill records are written block-major: the 8-lane group that handles
 // record o = block * N + token reads block `block` of token `token`.
 __device__ __forceinline__ int64_t act6_source(int64_t o, int64_t N, int64_t nb) {
@@ -213,6 +228,11 @@ size_t act_bytes(int64_t N, int64_t nb) {
 
 hipError_t launch_q4_0_quantize(const float* W, int64_t nblocks, uint8_t* Wq, hipStream_t s) {
     hipLaunchKernelGGL(k_q4_0_quantize, dim3(quant_grid(nblocks)), dim3(kThreads), 0, s, W, nblocks, Wq);
+    return hipGetLastError();
+}
+
+hipError_t launch_q4_0_repack(const uint8_t* Wq, int64_t nblocks, uint8_t* Wr, hipStream_t s) {
+    hipLaunchKernelGGL(k_q4_0_repack, dim3(quant_grid(nblocks)), dim3(kThreads), 0, s, Wq, nblocks, Wr);
     return hipGetLastError();
 }
 

@@ -94,6 +94,20 @@ def _bad_product_calls(L):
     yield q4(A + 2, 4, 64, B, None)
     yield q4(A, 4, 64, B + 1, None)
     yield q4(A, 4, 64, A + 4, None)                # output inside the input
+    rp = L.q4_0_repack
+    yield rp(None, 4, 64, B, None)
+    yield rp(A, 4, 64, None, None)
+    yield rp(A, 4, 48, B, None)                    # K % 32 != 0
+    yield rp(A + 1, 4, 64, B, None)                # Q4_0 data on an odd address
+    yield rp(A, 4, 64, B + 8, None)                # repacked output not 16-byte aligned
+    yield rp(A, 4, 64, A + 16, None)               # output overlaps the input
+    r = L.mul_mat_q4_0r_q8_0
+    yield r(A + 2, 4, 64, B, 1, C, None)           # repacked weights must be 16-byte aligned
+    yield r(A, 4, 64, B, 1, A + 8, None)           # Y overlaps the weights
+    yield r(A, 4, 48, B, 1, C, None)
+    rx = L.mul_mat_q4_0r_q8_0_ex
+    yield rx(A + 8, 4, 64, B, 1, C, WS, 1 << 20, None)
+    yield rx(A, 4, 64, B, 1, C, WS + 8, 1 << 20, None)
     q8 = L.q8_0_quantize
     yield q8(A, 0, 64, B, None)
     yield q8(A, 4, 33, B, None)
@@ -122,3 +136,5 @@ def test_no_device_is_ehip_not_abort(L):
     assert L.mul_mat_q4_0_q8_0_ex(A, 4, 64, B, 1, C, WS, 1 << 20, None) == -2
     assert L.q4_0_quantize(A, 4, 64, B, None) == -2
     assert L.q4_0_q8_0_block_dots(A, 4, 64, B, 1, C, None) == -2
+    assert L.q4_0_repack(A, 4, 64, B, None) == -2
+    assert L.mul_mat_q4_0r_q8_0(A, 4, 64, B, 1, C, None) == -2

@@ -196,6 +196,41 @@ def test_unaligned_but_valid_pointers(hip, orc):
                  orc.mul_mat_ref(Wq_o, orc.q8_0_quantize(Xn), K), "unaligned gemm")
 
 
+def _repack_expected(Wq_h):
+    """The repacked byte layout, written out from its definition: every block's
+    16 nibble bytes in block order, then every block's 2 scale bytes."""
+    blocks = Wq_h.reshape(-1, 18)
+    return np.concatenate([blocks[:, 2:].reshape(-1), blocks[:, :2].reshape(-1)])
+
+
+@pytest.mark.parametrize("rows,K", [(1, 32), (5, 96), (129, 160), (300, 768), (1000, 4096)])
+def test_repacked_weights(hip, orc, rows, K):
+    """q4_0_repack moves bytes only, and the product on the repacked weights
+    gives exactly the bits of the product on the blocks, decode and prefill."""
+    W, X = _case(rows, K, 130, 777 + rows + K)
+    Wq = hip.q4_0_quantize(dev(W))
+    Wr = hip.q4_0_repack(Wq, K)
+    assert np.array_equal(host(Wr), _repack_expected(host(Wq))), (rows, K)
+    Wq_o = orc.q4_0_quantize(W)
+    for N in (1, 2, 3, 8, 9, 64, 130):
+        print("repacked rows=%d K=%d N=%d" % (rows, K, N), flush=True)
+        Xt = dev(X[:N])
+        Y = host(hip.mul_mat_q4_0_q8_0(Wq, Xt))
+        Yr = host(hip.mul_mat_q4_0r_q8_0(Wr, Xt))
+        Yx = host(hip.mul_mat_q4_0r_q8_0_ex(Wr, Xt, hip.workspace(rows, K, N)))
+        assert np.array_equal(Yr, Y), (rows, K, N)
+        assert np.array_equal(Yx, Y), (rows, K, N)
+        assert_close(Yr, orc.mul_mat_ref(Wq_o, orc.q8_0_quantize(X[:N]), K), "repacked N=%d" % N)
+
+
+def test_repack_rejects_misaligned_output(hip):
+    Wq = torch.zeros((4, 36), dtype=torch.uint8, device="cuda")
+    buf = torch.zeros(4 * 36 + 32, dtype=torch.uint8, device="cuda")
+    with pytest.raises(hip.Q4BQError) as e:
+        hip.q4_0_repack(Wq, 64, buf[8:8 + 4 * 36])
+    assert e.value.status == hip.Q4BQ_EINVAL
+
+
 def test_empty_inputs_are_rejected(hip):
     Wq = torch.zeros((4, 36), dtype=torch.uint8, device="cuda")
     with pytest.raises(hip.Q4BQError) as e:
@@ -238,6 +273,10 @@ def test_workload_full_size(hip, orc, cid):
             ws = hip.workspace(rows, K, N)
             Y = host(hip.mul_mat_q4_0_q8_0_ex(Wq, Xt, ws))
             assert_close(Y[:, sample], orc.mul_mat_ref(Wq_o, Xq_o, K), "%s N=%d" % (wl.name, N))
+            # the repacked weights give the same bits
+            Wr = hip.q4_0_repack(Wq, K)
+            assert np.array_equal(host(hip.mul_mat_q4_0r_q8_0_ex(Wr, Xt, ws)), Y), "%s N=%d repacked" % (wl.name, N)
+            del Wr
             # block dots on a sample of outputs
             tok = np.arange(N) if N <= 8 else np.unique(np.r_[0, N - 1, np.arange(1, N, 37)])
             Dg = hip.q4_0_q8_0_block_dots(Wq, Xq, K)
