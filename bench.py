@@ -31,6 +31,16 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 matrix peak (5.0 POP/s)
 ROTATE_BYTES = 1 << 30
 
+# HBM bytes per launch of the dominant kernels, from two rocprofv3 --pmc runs
+# (FETCH_SIZE, then WRITE_SIZE, each scaled by what the counter reads for the
+# runtime's 512 MiB device copy in the same run); the summaries and commands
+# are in profiles/.  They describe the kernels as profiled; re-profile after a
+# kernel change.
+TRAFFIC_BYTES = {
+    ("llama3_8b_head", 1): 296277394,      # profiles/k_gemv_fused_vocab_head_128256x4096_N1.md
+    ("llama3_8b_prefill", 512): 116117089,  # profiles/k_gemm_prefill_14336x4096_N512.md
+}
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -225,7 +235,8 @@ def main():
         prefill = {"workload": "llama3_8b_prefill", "rows": 14336, "K": 4096, "N": 512,
                    "ms_per_step": round(ms_p, 5), "value": round(tops, 2), "unit": "TOPS (int8)",
                    "roofline": {"bound": "mfma", "achieved": round(ktops, 2), "peak": INT8_PEAK_TOPS,
-                                "unit": "TOPS", "frac": round(ktops / INT8_PEAK_TOPS, 4), "traffic": None}}
+                                "unit": "TOPS", "frac": round(ktops / INT8_PEAK_TOPS, 4),
+                                "traffic": TRAFFIC_BYTES.get(("llama3_8b_prefill", 512))}}
         del pm
         torch.cuda.empty_cache()
         rpm = Mats(hip, torch, 5, 512, repack=True)
@@ -246,7 +257,8 @@ def main():
         "config": {"workload": wl.name, "matrices": [list(m) for m in wl.mats], "N": N,
                    "weights_cold": "rotating copies >= 1 GiB"},
         "roofline": {"bound": "hbm", "achieved": round(roof["achieved"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(roof["achieved"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(roof["achieved"] / HBM_PEAK_GBS, 4),
+                     "traffic": TRAFFIC_BYTES.get((wl.name, N)) if fused_step(N) else None,
                      "kernel": roof["kernel"], "bytes_per_launch": roof["bytes"],
                      "us_per_launch": round(roof["ms"] * 1e3 / n_launch, 3)},
         "two_phase_product_kernel": {"us_per_launch": round(ms_kernel * 1e3 / n_launch, 3),
