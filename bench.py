@@ -142,6 +142,33 @@ def timed(torch, fn, steps, warmup):
     return start.elapsed_time(end) / steps  # ms
 
 
+def multi_matrix(hip, torch, args):
+    from q4_block_quantized_amd import inputs
+    wl = inputs.WORKLOADS[3]
+    mats = [(m, rk) for m, rk in enumerate(wl.mats) if rk[1] == 4096]
+    base = [hip.q4_0_quantize(torch.from_numpy(inputs.weights(3, m, r, k, outliers=wl.outliers)).cuda())
+            for m, (r, k) in mats]
+    total = sum(q4_bytes(r, k) for _, (r, k) in mats)
+    copies = max(1, -(-ROTATE_BYTES // total))
+    sets = [base] + [[w.clone() for w in base] for _ in range(copies - 1)]
+    X = torch.from_numpy(inputs.activations(3, 0, max(wl.ns), 4096)[:1].copy()).cuda()
+    Ys = [torch.empty((1, r), dtype=torch.float32, device="cuda") for _, (r, _k) in mats]
+    ws = hip.workspace(max(r for _, (r, _k) in mats), 4096, 1)
+    ms_one = timed(torch, lambda i: hip.mul_mat_q4_0_q8_0_multi(sets[i % copies], X, Ys), args.steps, args.warmup)
+    def sep(i):
+        for w, y in zip(sets[i % copies], Ys):
+            hip.mul_mat_q4_0_q8_0_ex(w, X, ws, y)
+    ms_sep = timed(torch, sep, args.steps, args.warmup)
+    nbytes = sum(step_bytes(r, k, 1) for _, (r, k) in mats)
+    log("multi-matrix decode (%s): one launch %.2f us, one call per matrix %.2f us"
+        % (" + ".join("%dx%d" % rk for _, rk in mats), ms_one * 1e3, ms_sep * 1e3))
+    del sets, base
+    torch.cuda.empty_cache()
+    return {"workload": "llama3_8b_decode matrices with K=4096: " + ", ".join("%dx%d" % rk for _, rk in mats),
+            "N": 1, "one_launch_us": round(ms_one * 1e3, 3), "per_matrix_calls_us": round(ms_sep * 1e3, 3),
+            "one_launch_GB/s": round(nbytes / (ms_one * 1e-3) / 1e9, 1)}
+
+
 def cpu_baseline(cid, N):
     """The oracle, as it stands, on a bounded row sample of the workload."""
     import oracle
@@ -170,7 +197,7 @@ def cpu_baseline(cid, N):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (got --gpus %d)" % args.gpus,
+        print("bench.py measures one GPU only: there is no multi-GPU path (got --gpus %d)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
     import torch
@@ -222,6 +249,10 @@ def main():
     del rmats
     torch.cuda.empty_cache()
 
+    # several matrices sharing one token (the Llama decode set's two K = 4096
+    # matrices): one launch against one call per matrix
+    multi = multi_matrix(hip, torch, args)
+
     prefill = None
     if not args.no_prefill:
         log("prefill: preparing")
@@ -265,6 +296,7 @@ def main():
                                      "GB/s": round(kern_gbs, 1)},
         "prefill": prefill,
         "repacked_weights": repacked,
+        "multi_matrix_decode": multi,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -150,6 +150,31 @@ int mul_mat_q4_0r_q8_0_ex(const void *Wr, int64_t rows, int64_t K, const float *
                           void *stream);
 
 /*
+ * Several products that read the same activations, in one launch for N <= 8:
+ * Y[i] = mul_mat(Wq[i], X) for i < count, all with the same K -- the
+ * projections of one token in "llama.cpp 深度解读" section 4 ("计算图构建 —
+ * 以 Llama 模型为例": step B's Q, K and V projections of the same normalised
+ * input; step I's up and gate projections).  X is quantized once.
+ *   count         1 <= count <= 8.
+ *   Wq, rows, Y   HOST arrays of count entries: device pointers to each
+ *                 matrix's Q4_0 blocks (rows[i] x K/32, 2-byte aligned) and to
+ *                 its output (fp32 N x rows[i], 4-byte aligned, overwritten);
+ *                 no output may overlap any input or another output.
+ *   X             fp32 N x K, 4-byte aligned.
+ *   workspace     NULL, or a device buffer of ws_bytes >=
+ *                 q4bq_workspace_size(1, K, N), 16-byte aligned; with NULL the
+ *                 scratch (not needed for N = 1) is taken with hipMallocAsync.
+ * For N <= 8 the decode kernel runs once over the concatenated rows; larger N
+ * runs the matrix-core kernel per matrix on the shared quantized X.  Each
+ * Y[i] equals mul_mat_q4_0_q8_0(Wq[i], X) within the operator's tolerance
+ * (the same block terms; the fp32 sum of a row may be split across lanes
+ * differently when the concatenated shape picks another launch shape).
+ */
+int mul_mat_q4_0_q8_0_multi(int count, const void *const *Wq, const int64_t *rows,
+                            int64_t K, const float *X, int64_t N, float *const *Y,
+                            void *workspace, size_t ws_bytes, void *stream);
+
+/*
  * The operator with pre-quantized activations: Xq holds N x (K/32) Q8_0 blocks
  * (2-byte aligned), otherwise as mul_mat_q4_0_q8_0.  Feeding it the output of
  * q8_0_quantize(X) gives exactly the Y of mul_mat_q4_0_q8_0(X).

@@ -29,7 +29,7 @@ EXPORTS = (
     "q4_0_quantize", "q8_0_quantize", "mul_mat_q4_0_q8_0", "q4bq_workspace_size",
     "mul_mat_q4_0_q8_0_ex", "mul_mat_q4_0_q8_0_pq", "q4_0_q8_0_block_dots",
     "q4bq_status_string", "q4bq_version", "q4bq_quantize_activations", "mul_mat_q4_0_q8_0_prepared",
-    "q4_0_repack", "mul_mat_q4_0r_q8_0", "mul_mat_q4_0r_q8_0_ex",
+    "q4_0_repack", "mul_mat_q4_0r_q8_0", "mul_mat_q4_0r_q8_0_ex", "mul_mat_q4_0_q8_0_multi",
 )
 
 
@@ -59,6 +59,7 @@ def lib() -> ctypes.CDLL:
         "mul_mat_q4_0_q8_0_ex": (I, [P, I64, I64, P, I64, P, P, ctypes.c_size_t, P]),
         "mul_mat_q4_0_q8_0_pq": (I, [P, I64, I64, P, I64, P, P]),
         "q4_0_repack": (I, [P, I64, I64, P, P]),
+        "mul_mat_q4_0_q8_0_multi": (I, [ctypes.c_int, P, P, I64, P, I64, P, P, ctypes.c_size_t, P]),
         "mul_mat_q4_0r_q8_0": (I, [P, I64, I64, P, I64, P, P]),
         "mul_mat_q4_0r_q8_0_ex": (I, [P, I64, I64, P, I64, P, P, ctypes.c_size_t, P]),
         "q4_0_q8_0_block_dots": (I, [P, I64, I64, P, I64, P, P]),
@@ -203,6 +204,24 @@ def mul_mat_q4_0r_q8_0_ex(Wr: torch.Tensor, X: torch.Tensor, ws: torch.Tensor, Y
                                        _dev(Y, torch.float32, "Y"), _dev(ws, torch.uint8, "workspace"),
                                        ws.numel(), _stream(stream)), "mul_mat_q4_0r_q8_0_ex")
     return Y
+
+
+def mul_mat_q4_0_q8_0_multi(Wqs, X: torch.Tensor, Ys=None, ws: torch.Tensor | None = None,
+                            stream=None) -> list:
+    """Y[i] = mul_mat_q4_0_q8_0(Wqs[i], X) for every i, one launch for N <= 8."""
+    N, K = X.shape
+    count = len(Wqs)
+    rows = [_rows(W, K) for W in Wqs]
+    if Ys is None:
+        Ys = [torch.empty((N, r), dtype=torch.float32, device=X.device) for r in rows]
+    wp = (ctypes.c_void_p * count)(*[_dev(W, torch.uint8, "Wq[%d]" % i) for i, W in enumerate(Wqs)])
+    yp = (ctypes.c_void_p * count)(*[_dev(Y, torch.float32, "Y[%d]" % i) for i, Y in enumerate(Ys)])
+    rp = (ctypes.c_int64 * count)(*rows)
+    wsp, wsn = (None, 0) if ws is None else (_dev(ws, torch.uint8, "workspace"), ws.numel())
+    _check(lib().mul_mat_q4_0_q8_0_multi(count, ctypes.cast(wp, ctypes.c_void_p), ctypes.cast(rp, ctypes.c_void_p), K,
+                                         _dev(X, torch.float32, "X"), N, ctypes.cast(yp, ctypes.c_void_p), wsp, wsn,
+                                         _stream(stream)), "mul_mat_q4_0_q8_0_multi")
+    return Ys
 
 
 def q4bq_quantize_activations(X: torch.Tensor, ws: torch.Tensor, stream=None) -> torch.Tensor:

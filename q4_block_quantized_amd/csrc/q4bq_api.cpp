@@ -218,6 +218,60 @@ int mul_mat_q4_0r_q8_0_ex(const void* Wr, int64_t rows, int64_t K, const float* 
                        static_cast<hipStream_t>(stream));
 }
 
+int mul_mat_q4_0_q8_0_multi(int count, const void* const* Wq, const int64_t* rows, int64_t K, const float* X,
+                            int64_t N, float* const* Y, void* workspace, size_t ws_bytes, void* stream) {
+    if (count < 1 || count > kMaxMulti || !Wq || !rows || !Y) return Q4BQ_EINVAL;
+    const int64_t nb = bad_k(K) ? 0 : K / kQK;
+    MultiDesc md{};
+    md.count = count;
+    md.first[0] = 0;
+    for (int i = 0; i < count; ++i) {
+        const int rc = check_product(Wq[i], rows[i], K, X, kF32, N, Y[i], false);
+        if (rc != Q4BQ_OK) return rc;
+        md.w[i] = static_cast<const uint8_t*>(Wq[i]);
+        md.y[i] = Y[i];
+        md.first[i + 1] = md.first[i] + rows[i];
+    }
+    if (bad_dim(md.first[count]) || too_big(md.first[count], K, 1)) return Q4BQ_EINVAL;
+    for (int i = 0; i < count; ++i)
+        for (int j = 0; j < count; ++j) {
+            const size_t yb = static_cast<size_t>(N * rows[i]) * 4;
+            if (overlap(Y[i], yb, Wq[j], static_cast<size_t>(rows[j] * nb) * kQ4Bytes)) return Q4BQ_EINVAL;
+            if (i != j && overlap(Y[i], yb, Y[j], static_cast<size_t>(N * rows[j]) * 4)) return Q4BQ_EINVAL;
+        }
+    const size_t need = q4bq_workspace_size(1, K, N);
+    if (workspace) {
+        if (!aligned(workspace, 16)) return Q4BQ_EINVAL;
+        if (ws_bytes < need) return Q4BQ_ENOMEM;
+        if (overlap(workspace, need, X, static_cast<size_t>(N * K) * 4)) return Q4BQ_EINVAL;
+        for (int i = 0; i < count; ++i)
+            if (overlap(workspace, need, Y[i], static_cast<size_t>(N * rows[i]) * 4) ||
+                overlap(workspace, need, Wq[i], static_cast<size_t>(rows[i] * nb) * kQ4Bytes))
+                return Q4BQ_EINVAL;
+    }
+    hipError_t err = hipSuccess;
+    const DeviceInfo* dev = current_device(&err);
+    if (!dev) return Q4BQ_EHIP;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (N <= kGemvMaxN && gemv_fuses(N, nb)) return status_of(launch_gemv_multi(dev, md, nb, X, nullptr, N, s));
+    void* ws = workspace;
+    if (!ws && (hipMallocAsync(&ws, need, s) != hipSuccess || ws == nullptr)) {
+        (void)hipGetLastError();
+        return Q4BQ_ENOMEM;
+    }
+    err = launch_act_from_f32(X, N, nb, ws, s);
+    if (err == hipSuccess) {
+        if (N <= kGemvMaxN) {
+            err = launch_gemv_multi(dev, md, nb, nullptr, ws, N, s);
+        } else {
+            for (int i = 0; i < count && err == hipSuccess; ++i)
+                err = launch_gemm(dev, kAoS, md.w[i], rows[i], nb, ws, N, md.y[i], nullptr, s);
+        }
+    }
+    if (!workspace && hipFreeAsync(ws, s) != hipSuccess) return Q4BQ_EHIP;
+    return status_of(err);
+}
+
 int mul_mat_q4_0_q8_0_pq(const void* Wq, int64_t rows, int64_t K, const void* Xq, int64_t N, float* Y,
                          void* stream) {
     const int rc = check_product(Wq, rows, K, Xq, kQ8, N, Y, false);

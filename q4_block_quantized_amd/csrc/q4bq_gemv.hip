@@ -37,51 +37,62 @@ constexpr size_t kMaxActLds = 64 * 1024;
 
 enum Src { kActGlobal = 0, kActLds = 1, kXF32 = 2 };
 
-template <int NT, int THREADS, int SRC, bool DOTS, bool RP>
-__global__ void __launch_bounds__(THREADS)
+enum Lay { kLayAoS = 0, kLayRepacked = 1, kLayMulti = 2 };
+
+template <int NT, int THREADS, int SRC, bool DOTS, int LAY>
+__global__ void __launch_bounds__(THREADS, NT == 1 ? 1024 / THREADS : 1)
 k_gemv(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __restrict__ src,
-       float* __restrict__ Y, int32_t* __restrict__ D, int log2G, int rpi) {
+       float* __restrict__ Y, int32_t* __restrict__ D, int log2G, int rpi, const MultiDesc md) {
     constexpr int kWaves = THREADS / 64;
+    constexpr bool RP = LAY == kLayRepacked;
+    constexpr bool MULTI = LAY == kLayMulti;  // rows of md's matrices, concatenated (rows = their total)
     // RP: Wq holds the repacked streams (nibbles, then scales)
     const uint8_t* __restrict__ Wsc = Wq + (RP ? rows * nb * 16 : 0);
     extern __shared__ __align__(16) uint8_t smem[];
-    const uint32_t* act_q;
-    const ActScale* act_s;
-    if constexpr (SRC == kActGlobal) {
-        act_q = static_cast<const uint32_t*>(src);
-        act_s = reinterpret_cast<const ActScale*>(static_cast<const uint8_t*>(src) +
-                                                  static_cast<size_t>(NT) * nb * kActQBytes);
-    } else {
-        uint32_t* sq = reinterpret_cast<uint32_t*>(smem);
-        ActScale* ss = reinterpret_cast<ActScale*>(smem + static_cast<size_t>(NT) * nb * kActQBytes);
-        if constexpr (SRC == kActLds) {
-            const u32x4* gq = static_cast<const u32x4*>(src);
-            const ActScale* gs = reinterpret_cast<const ActScale*>(static_cast<const uint8_t*>(src) +
-                                                                   static_cast<size_t>(NT) * nb * kActQBytes);
-            for (int c = threadIdx.x; c < NT * nb * 2; c += THREADS) reinterpret_cast<u32x4*>(sq)[c] = gq[c];
-            for (int c = threadIdx.x; c < NT * nb; c += THREADS) ss[c] = gs[c];
+    const uint32_t* act_q = nullptr;
+    const ActScale* act_s = nullptr;
+
+    // Activations: the quantizer's buffer read in place (kActGlobal), copied
+    // to LDS (kActLds), or quantized here from fp32 X into LDS (kXF32, the
+    // same Q8_0 device function as the quantizer).  Ends with a barrier when
+    // LDS is used, so every wave calls it exactly once.
+    auto setup_act = [&]() __attribute__((always_inline)) {
+        if constexpr (SRC == kActGlobal) {
+            act_q = static_cast<const uint32_t*>(src);
+            act_s = reinterpret_cast<const ActScale*>(static_cast<const uint8_t*>(src) +
+                                                      static_cast<size_t>(NT) * nb * kActQBytes);
         } else {
-            // quantize X (NT x K fp32) here: 8 lanes per block, 4 values per lane
-            const float* X = static_cast<const float*>(src);
-            const int m = threadIdx.x & 7;
-            const int nblk = NT * nb;
-            for (int g0 = (threadIdx.x >> 3) & ~7; g0 < nblk; g0 += THREADS / 8) {
-                const int g = g0 + ((threadIdx.x >> 3) & 7);
-                const bool valid = g < nblk;
-                float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (valid) __builtin_memcpy(&x, X + static_cast<int64_t>(g) * kQK + 4 * m, 16);
-                uint32_t word;
-                const ActScale sc = quant_act_quad(x.x, x.y, x.z, x.w, m, word);
-                if (valid) {
-                    sq[g * 8 + m] = word;
-                    if (m == 0) ss[g] = sc;
+            uint32_t* sq = reinterpret_cast<uint32_t*>(smem);
+            ActScale* ss = reinterpret_cast<ActScale*>(smem + static_cast<size_t>(NT) * nb * kActQBytes);
+            if constexpr (SRC == kActLds) {
+                const u32x4* gq = static_cast<const u32x4*>(src);
+                const ActScale* gs = reinterpret_cast<const ActScale*>(static_cast<const uint8_t*>(src) +
+                                                                       static_cast<size_t>(NT) * nb * kActQBytes);
+                for (int c = threadIdx.x; c < NT * nb * 2; c += THREADS) reinterpret_cast<u32x4*>(sq)[c] = gq[c];
+                for (int c = threadIdx.x; c < NT * nb; c += THREADS) ss[c] = gs[c];
+            } else {
+                // quantize X (NT x K fp32) here: 8 lanes per block, 4 values per lane
+                const float* X = static_cast<const float*>(src);
+                const int m = threadIdx.x & 7;
+                const int nblk = NT * nb;
+                for (int g0 = (threadIdx.x >> 3) & ~7; g0 < nblk; g0 += THREADS / 8) {
+                    const int g = g0 + ((threadIdx.x >> 3) & 7);
+                    const bool valid = g < nblk;
+                    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+                    if (valid) __builtin_memcpy(&x, X + static_cast<int64_t>(g) * kQK + 4 * m, 16);
+                    uint32_t word;
+                    const ActScale sc = quant_act_quad(x.x, x.y, x.z, x.w, m, word);
+                    if (valid) {
+                        sq[g * 8 + m] = word;
+                        if (m == 0) ss[g] = sc;
+                    }
                 }
             }
+            __syncthreads();
+            act_q = sq;
+            act_s = ss;
         }
-        __syncthreads();
-        act_q = sq;
-        act_s = ss;
-    }
+    };
 
     const int G = 1 << log2G;
     const int lane = threadIdx.x & 63;
@@ -94,14 +105,38 @@ k_gemv(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __restr
     const int64_t rows_per_task = static_cast<int64_t>(RW) * rpi;
     const int64_t ntasks = (rows + rows_per_task - 1) / rows_per_task;
 
-    for (int64_t task = static_cast<int64_t>(blockIdx.x) * kWaves + wave; task < ntasks;
-         task += static_cast<int64_t>(gridDim.x) * kWaves) {
+    // One task: rpi row slots of RW rows.  `first` marks the first task of a
+    // wave, whose first batch of weight loads is issued before the
+    // activations are set up, so that set-up runs while those bytes arrive.
+    auto do_task = [&](int64_t task, bool first) __attribute__((always_inline)) {
         int64_t r[kRmax];
         bool rv[kRmax];
 #pragma unroll
         for (int j = 0; j < kRmax; ++j) {
             r[j] = task * rows_per_task + static_cast<int64_t>(j) * RW + grp;
             rv[j] = (j < rpi) && (r[j] < rows);
+        }
+        // per row: its blocks and its output column (one matrix, or the matrix
+        // of md that owns the global row)
+        const uint8_t* wrow[kRmax];
+        float* yrow[kRmax];
+        int64_t ystride[kRmax];
+#pragma unroll
+        for (int j = 0; j < kRmax; ++j) {
+            if constexpr (MULTI) {
+                int m = 0;
+#pragma unroll
+                for (int k = 1; k < kMaxMulti; ++k)
+                    if (k < md.count && r[j] >= md.first[k]) m = k;
+                const int64_t loc = r[j] - md.first[m];
+                wrow[j] = md.w[m] + loc * nb * kQ4Bytes;
+                yrow[j] = md.y[m] + loc;
+                ystride[j] = md.first[m + 1] - md.first[m];
+            } else {
+                wrow[j] = Wq + r[j] * nb * kQ4Bytes;
+                yrow[j] = Y + r[j];
+                ystride[j] = rows;
+            }
         }
         float acc[kRmax][NT];
 #pragma unroll
@@ -122,9 +157,11 @@ k_gemv(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __restr
                     const int p = pos + ((i0 + u) << log2G);
                     if (rv[j] && pv[u]) {
                         const int64_t blk0 = r[j] * nb + 2 * p;
-                        raw[j][u] = RP ? load_pair_rp(Wq + blk0 * 16, Wsc + blk0 * 2) : load_pair(Wq + blk0 * kQ4Bytes);
+                        raw[j][u] = RP ? load_pair_rp(Wq + blk0 * 16, Wsc + blk0 * 2)
+                                       : load_pair(wrow[j] + 2 * p * kQ4Bytes);
                     }
                 }
+            if (first && i0 == 0) setup_act();
 #pragma unroll
             for (int u = 0; u < kU; ++u) {
                 if (!pv[u]) continue;
@@ -156,13 +193,14 @@ k_gemv(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __restr
                 }
             }
         }
+        if (first && PPL == 0) setup_act();  // rows of a single block: no batch above
         if ((nb & 1) && pos == 0) {  // a row with an odd block count ends in one lone block
             const int b = nb - 1;
 #pragma unroll
             for (int j = 0; j < kRmax; ++j) {
                 if (!rv[j]) continue;
                 const int64_t bi = r[j] * nb + b;
-                const Block4 blk = RP ? load_block_rp(Wq + bi * 16, Wsc + bi * 2) : load_block(Wq + bi * kQ4Bytes);
+                const Block4 blk = RP ? load_block_rp(Wq + bi * 16, Wsc + bi * 2) : load_block(wrow[j] + b * kQ4Bytes);
 #pragma unroll
                 for (int n = 0; n < NT; ++n) {
                     const int64_t ab = static_cast<int64_t>(n) * nb + b;
@@ -191,89 +229,142 @@ k_gemv(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __restr
                 for (int j = 0; j < kRmax; ++j) {
                     if (!rv[j]) continue;
 #pragma unroll
-                    for (int n = 0; n < NT; ++n) Y[static_cast<int64_t>(n) * rows + r[j]] = acc[j][n];
+                    for (int n = 0; n < NT; ++n) yrow[j][static_cast<int64_t>(n) * ystride[j]] = acc[j][n];
                 }
             }
         }
-    }
-}
+    };
 
-// Lanes per row: the power of two in [4, 64] that leaves the fewest idle
-// pair slots, the widest among equals (wider = more contiguous bytes per row).
-int pick_log2g(int64_t P) {
-    int best = 6;
-    double best_util = -1.0;
-    for (int lg = 6; lg >= 2; --lg) {
-        const int64_t G = int64_t(1) << lg;
-        const int64_t slots = ((P + G - 1) / G) * G;
-        const double util = slots > 0 ? static_cast<double>(P) / static_cast<double>(slots) : 1.0;
-        if (util > best_util + 1e-9) {
-            best_util = util;
-            best = lg;
-        }
-    }
-    return best;
+    const int64_t task0 = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
+    if (task0 < ntasks)
+        do_task(task0, true);
+    else
+        setup_act();  // the barrier, for waves without a task
+    for (int64_t task = task0 + static_cast<int64_t>(gridDim.x) * kWaves; task < ntasks;
+         task += static_cast<int64_t>(gridDim.x) * kWaves)
+        do_task(task, false);
 }
 
 struct Shape {
     int log2G, rpi;
     uint32_t wgs;
+    int64_t ntasks;
 };
 
-// Launch shape: rows per lane = as many (up to 4) as still leave `want_waves`
-// tasks; workgroups capped at `wg_per_cu` per CU (the grid strides over tasks).
-// Several tokens: with enough rows, 16 lanes per row (4 rows per wave and row
-// slot) beat 64 -- each lane then serves 4 x rpi rows per activation read and
-// the per-row butterfly is shorter (measured: 128256 x 4096 at N = 8, 126 us
-// against 165 us); with few rows the wider groups keep more waves busy.
-Shape pick_shape(const DeviceInfo* dev, int64_t rows, int64_t nb, int threads, int wg_per_cu, int want_waves_per_cu,
-                 int nt) {
-    Shape sh;
-    sh.log2G = pick_log2g(nb >> 1);
-    const int64_t want_tasks = static_cast<int64_t>(dev->num_cu) * want_waves_per_cu;
-    if (nt >= 2 && sh.log2G > 4 && (rows + 16 * kRmax - 1) / (16 * kRmax) >= want_tasks) sh.log2G = 4;
-    const int RW = 64 >> sh.log2G;
-    sh.rpi = 1;
-    for (int c = kRmax; c >= 1; c >>= 1) {
-        if ((rows + int64_t(RW) * c - 1) / (int64_t(RW) * c) >= want_tasks) {
-            sh.rpi = c;
-            break;
+// Launch shape.  A task is RW = 64 / G rows times rpi row slots of one wave;
+// waves stride over the tasks.  Each candidate (G lanes per row, rpi rows per
+// lane) is scored by
+//   util -- the share of a row's pair slots that hold a pair, and
+//   fill -- tasks / (rounds x waves), the share of the grid's wave slots that
+//           do work over the whole launch (rounds = ceil(tasks / waves)),
+// and the best wins; near-ties (within 2 %) go to wider G and more rows per
+// lane (more contiguous bytes per row, more loads in flight per lane).
+// Several tokens on tall matrices: 16 lanes per row with 4 rows per lane (16
+// rows per task) beat 64 when they fill the grid as well -- each lane then
+// serves 16 rows per activation read and the per-row butterfly is shorter
+// (measured: 128256 x 4096 at N = 8, 126 us against 165 us; on 14336 x 4096,
+// where only one row per lane fits, 64 lanes stay better).
+Shape pick_shape(const DeviceInfo* dev, int64_t rows, int64_t nb, int threads, int wg_per_cu, int nt) {
+    const int waves_per_wg = threads / 64;
+    const int64_t cap_wgs = static_cast<int64_t>(dev->num_cu) * wg_per_cu;
+    const int64_t max_waves = cap_wgs * waves_per_wg;
+    const int64_t P = nb >> 1;
+    Shape best{6, 1, 1, 1};
+    double best_score = -1.0, g16_score = -1.0;
+    Shape g16 = best;
+    for (int lg = 6; lg >= 2; --lg) {
+        const int64_t G = int64_t(1) << lg;
+        const double util = P > 0 ? static_cast<double>(P) / static_cast<double>(((P + G - 1) / G) * G) : 1.0;
+        const int64_t RW = 64 >> lg;
+        for (int rpi = kRmax; rpi >= 1; rpi >>= 1) {
+            const int64_t ntasks = (rows + RW * rpi - 1) / (RW * rpi);
+            const int64_t rounds = (ntasks + max_waves - 1) / max_waves;
+            const double fill = static_cast<double>(ntasks) / static_cast<double>(rounds * max_waves);
+            const double score = util * fill;
+            const Shape sh{lg, rpi, 0, ntasks};
+            if (score > best_score * 1.02) {
+                best_score = score;
+                best = sh;
+            }
+            if (lg == 4 && score > g16_score * 1.02) {
+                g16_score = score;
+                g16 = sh;
+            }
         }
     }
-    const int waves = threads / 64;
-    const int64_t ntasks = (rows + int64_t(RW) * sh.rpi - 1) / (int64_t(RW) * sh.rpi);
-    int64_t wgs = (ntasks + waves - 1) / waves;
-    const int64_t cap = static_cast<int64_t>(dev->num_cu) * wg_per_cu;
-    if (wgs > cap) wgs = cap;
-    sh.wgs = static_cast<uint32_t>(wgs < 1 ? 1 : wgs);
-    return sh;
+    if (nt >= 2 && best.log2G > 4 && g16.rpi == kRmax && g16_score >= 0.95 * best_score) best = g16;
+    int64_t wgs = (best.ntasks + waves_per_wg - 1) / waves_per_wg;
+    if (wgs > cap_wgs) wgs = cap_wgs;
+    best.wgs = static_cast<uint32_t>(wgs < 1 ? 1 : wgs);
+    return best;
 }
 
 template <int NT, int THREADS, int SRC, bool DOTS>
-hipError_t launch_v(const Shape& sh, WLayout lay, const uint8_t* Wq, int64_t rows, int64_t nb, const void* src,
-                    float* Y, int32_t* D, hipStream_t s) {
+hipError_t launch_v(const Shape& sh, int lay, const uint8_t* Wq, int64_t rows, int64_t nb, const void* src,
+                    float* Y, int32_t* D, const MultiDesc& md, hipStream_t s) {
     const size_t lds = SRC == kActGlobal ? 0 : static_cast<size_t>(NT) * nb * (kActQBytes + kActSBytes);
-    if (lay == kRepacked)
-        hipLaunchKernelGGL((k_gemv<NT, THREADS, SRC, DOTS, true>), dim3(sh.wgs), dim3(THREADS), lds, s, Wq, rows,
-                           static_cast<int>(nb), src, Y, D, sh.log2G, sh.rpi);
-    else
-        hipLaunchKernelGGL((k_gemv<NT, THREADS, SRC, DOTS, false>), dim3(sh.wgs), dim3(THREADS), lds, s, Wq, rows,
-                           static_cast<int>(nb), src, Y, D, sh.log2G, sh.rpi);
+    const int nbi = static_cast<int>(nb);
+    if (lay == kLayRepacked) {
+        hipLaunchKernelGGL((k_gemv<NT, THREADS, SRC, DOTS, kLayRepacked>), dim3(sh.wgs), dim3(THREADS), lds, s, Wq,
+                           rows, nbi, src, Y, D, sh.log2G, sh.rpi, md);
+    } else if (lay == kLayMulti) {
+        if constexpr (DOTS) {
+            return hipErrorInvalidValue;  // block dots are exported for one matrix only
+        } else {
+            hipLaunchKernelGGL((k_gemv<NT, THREADS, SRC, false, kLayMulti>), dim3(sh.wgs), dim3(THREADS), lds, s, Wq,
+                               rows, nbi, src, Y, D, sh.log2G, sh.rpi, md);
+        }
+    } else {
+        hipLaunchKernelGGL((k_gemv<NT, THREADS, SRC, DOTS, kLayAoS>), dim3(sh.wgs), dim3(THREADS), lds, s, Wq, rows,
+                           nbi, src, Y, D, sh.log2G, sh.rpi, md);
+    }
     return hipGetLastError();
 }
 
 template <int NT>
-hipError_t launch_n(const DeviceInfo* dev, WLayout lay, const uint8_t* Wq, int64_t rows, int64_t nb, const void* act,
-                    float* Y, int32_t* D, hipStream_t s) {
+hipError_t launch_n(const DeviceInfo* dev, int lay, const uint8_t* Wq, int64_t rows, int64_t nb, const void* act,
+                    float* Y, int32_t* D, const MultiDesc& md, hipStream_t s) {
     const bool lds = static_cast<size_t>(NT) * nb * (kActQBytes + kActSBytes) <= kMaxActLds;
-    const Shape sh = pick_shape(dev, rows, nb, 256, 4, 16, NT);
+    const Shape sh = pick_shape(dev, rows, nb, 256, 4, NT);
     if (D) {
-        return lds ? launch_v<NT, 256, kActLds, true>(sh, lay, Wq, rows, nb, act, Y, D, s)
-                   : launch_v<NT, 256, kActGlobal, true>(sh, lay, Wq, rows, nb, act, Y, D, s);
+        return lds ? launch_v<NT, 256, kActLds, true>(sh, lay, Wq, rows, nb, act, Y, D, md, s)
+                   : launch_v<NT, 256, kActGlobal, true>(sh, lay, Wq, rows, nb, act, Y, D, md, s);
     }
-    return lds ? launch_v<NT, 256, kActLds, false>(sh, lay, Wq, rows, nb, act, Y, D, s)
-               : launch_v<NT, 256, kActGlobal, false>(sh, lay, Wq, rows, nb, act, Y, D, s);
+    return lds ? launch_v<NT, 256, kActLds, false>(sh, lay, Wq, rows, nb, act, Y, D, md, s)
+               : launch_v<NT, 256, kActGlobal, false>(sh, lay, Wq, rows, nb, act, Y, D, md, s);
 }
+
+int lay_of(WLayout lay) { return lay == kRepacked ? kLayRepacked : kLayAoS; }
+
+// Fused decode (the kernel quantizes X itself): one 1024-thread workgroup per
+// CU, so the quantization is repeated once per CU; a matrix with fewer tasks
+// than 16 per CU runs in 256-thread workgroups instead, spread over more CUs.
+hipError_t fused_n(const DeviceInfo* dev, int lay, const uint8_t* Wq, int64_t rows, int64_t nb, const float* X,
+                   int64_t N, float* Y, const MultiDesc& md, hipStream_t s) {
+    if (N != 1) return hipErrorInvalidValue;
+    const Shape big = pick_shape(dev, rows, nb, 1024, 1, 1);
+    if (big.ntasks >= static_cast<int64_t>(dev->num_cu) * 16)
+        return launch_v<1, 1024, kXF32, false>(big, lay, Wq, rows, nb, X, Y, nullptr, md, s);
+    const Shape small = pick_shape(dev, rows, nb, 256, 4, 1);
+    return launch_v<1, 256, kXF32, false>(small, lay, Wq, rows, nb, X, Y, nullptr, md, s);
+}
+
+hipError_t gemv_n(const DeviceInfo* dev, int lay, const uint8_t* Wq, int64_t rows, int64_t nb, const void* act,
+                  int64_t N, float* Y, int32_t* D, const MultiDesc& md, hipStream_t s) {
+    switch (N) {
+        case 1: return launch_n<1>(dev, lay, Wq, rows, nb, act, Y, D, md, s);
+        case 2: return launch_n<2>(dev, lay, Wq, rows, nb, act, Y, D, md, s);
+        case 3: return launch_n<3>(dev, lay, Wq, rows, nb, act, Y, D, md, s);
+        case 4: return launch_n<4>(dev, lay, Wq, rows, nb, act, Y, D, md, s);
+        case 5: return launch_n<5>(dev, lay, Wq, rows, nb, act, Y, D, md, s);
+        case 6: return launch_n<6>(dev, lay, Wq, rows, nb, act, Y, D, md, s);
+        case 7: return launch_n<7>(dev, lay, Wq, rows, nb, act, Y, D, md, s);
+        case 8: return launch_n<8>(dev, lay, Wq, rows, nb, act, Y, D, md, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+const MultiDesc kNoMulti{};
 
 }  // namespace
 
@@ -283,26 +374,19 @@ bool gemv_fuses(int64_t N, int64_t nb) {
 
 hipError_t launch_gemv_fused(const DeviceInfo* dev, WLayout lay, const uint8_t* Wq, int64_t rows, int64_t nb,
                              const float* X, int64_t N, float* Y, hipStream_t s) {
-    const Shape sh = pick_shape(dev, rows, nb, 1024, 1, 16, static_cast<int>(N));
-    switch (N) {
-        case 1: return launch_v<1, 1024, kXF32, false>(sh, lay, Wq, rows, nb, X, Y, nullptr, s);
-        default: return hipErrorInvalidValue;
-    }
+    return fused_n(dev, lay_of(lay), Wq, rows, nb, X, N, Y, kNoMulti, s);
 }
 
 hipError_t launch_gemv(const DeviceInfo* dev, WLayout lay, const uint8_t* Wq, int64_t rows, int64_t nb,
                        const void* act, int64_t N, float* Y, int32_t* D, hipStream_t s) {
-    switch (N) {
-        case 1: return launch_n<1>(dev, lay, Wq, rows, nb, act, Y, D, s);
-        case 2: return launch_n<2>(dev, lay, Wq, rows, nb, act, Y, D, s);
-        case 3: return launch_n<3>(dev, lay, Wq, rows, nb, act, Y, D, s);
-        case 4: return launch_n<4>(dev, lay, Wq, rows, nb, act, Y, D, s);
-        case 5: return launch_n<5>(dev, lay, Wq, rows, nb, act, Y, D, s);
-        case 6: return launch_n<6>(dev, lay, Wq, rows, nb, act, Y, D, s);
-        case 7: return launch_n<7>(dev, lay, Wq, rows, nb, act, Y, D, s);
-        case 8: return launch_n<8>(dev, lay, Wq, rows, nb, act, Y, D, s);
-        default: return hipErrorInvalidValue;
-    }
+    return gemv_n(dev, lay_of(lay), Wq, rows, nb, act, N, Y, D, kNoMulti, s);
+}
+
+hipError_t launch_gemv_multi(const DeviceInfo* dev, const MultiDesc& md, int64_t nb, const float* X, const void* act,
+                             int64_t N, hipStream_t s) {
+    const int64_t rows = md.first[md.count];
+    if (X && gemv_fuses(N, nb)) return fused_n(dev, kLayMulti, nullptr, rows, nb, X, N, nullptr, md, s);
+    return gemv_n(dev, kLayMulti, nullptr, rows, nb, act, N, nullptr, nullptr, md, s);
 }
 
 }  // namespace q4bq

@@ -19,6 +19,17 @@ constexpr int kActSBytes = 8;   // internal scale record {float d; int32 bias}
 // q4_0_repack (16 nibble bytes per block, then one binary16 scale per block).
 enum WLayout { kAoS = 0, kRepacked = 1 };
 
+// Several matrices with the same K that read the same activations, handled as
+// one concatenation of their rows (decode kernel): matrix m owns global rows
+// [first[m], first[m + 1]), its blocks at w[m], its output (N x rows_m) at y[m].
+constexpr int kMaxMulti = 8;
+struct MultiDesc {
+    const uint8_t* w[kMaxMulti];
+    float* y[kMaxMulti];
+    int64_t first[kMaxMulti + 1];
+    int count;
+};
+
 struct DeviceInfo {
     int id;
     int num_cu;
@@ -56,6 +67,12 @@ constexpr int64_t kGemvFusedMaxN = 1;
 bool gemv_fuses(int64_t N, int64_t nb);
 hipError_t launch_gemv_fused(const DeviceInfo* dev, WLayout lay, const uint8_t* Wq, int64_t rows, int64_t nb,
                              const float* X, int64_t N, float* Y, hipStream_t s);
+
+// The decode kernel over the rows of several matrices (N <= kGemvMaxN; AoS
+// blocks).  X fp32 is quantized in the kernel when gemv_fuses(N, nb), else
+// `act` holds the quantizer's output.
+hipError_t launch_gemv_multi(const DeviceInfo* dev, const MultiDesc& md, int64_t nb, const float* X, const void* act,
+                             int64_t N, hipStream_t s);
 
 // Matrix-core kernel, any N.  D as above.
 hipError_t launch_gemm(const DeviceInfo* dev, WLayout lay, const uint8_t* Wq, int64_t rows, int64_t nb,

@@ -108,6 +108,17 @@ def _bad_product_calls(L):
     rx = L.mul_mat_q4_0r_q8_0_ex
     yield rx(A + 8, 4, 64, B, 1, C, WS, 1 << 20, None)
     yield rx(A, 4, 64, B, 1, C, WS + 8, 1 << 20, None)
+    mm = L.mul_mat_q4_0_q8_0_multi
+    ptrs = lambda *v: ctypes.cast((ctypes.c_void_p * len(v))(*v), ctypes.c_void_p)
+    i64s = lambda *v: ctypes.cast((ctypes.c_int64 * len(v))(*v), ctypes.c_void_p)
+    yield mm(0, ptrs(A), i64s(4), 64, B, 1, ptrs(C), None, 0, None)            # count < 1
+    yield mm(9, ptrs(*[A] * 9), i64s(*[4] * 9), 64, B, 1, ptrs(*[C + 256 * i for i in range(9)]), None, 0, None)
+    yield mm(2, None, i64s(4, 4), 64, B, 1, ptrs(C, C + 256), None, 0, None)   # null weight array
+    yield mm(2, ptrs(A, A + 4096), i64s(4, 4), 64, B, 1, ptrs(C, C + 8), None, 0, None)       # outputs overlap
+    yield mm(2, ptrs(A, A + 4096), i64s(4, 4), 64, B, 1, ptrs(C, A + 4100), None, 0, None)    # output inside a weight
+    yield mm(2, ptrs(A, A + 4096), i64s(4, 0), 64, B, 1, ptrs(C, C + 256), None, 0, None)     # a matrix with 0 rows
+    yield mm(2, ptrs(A, A + 4096), i64s(4, 4), 48, B, 1, ptrs(C, C + 256), None, 0, None)     # K % 32 != 0
+    yield mm(2, ptrs(A, A + 4096), i64s(4, 4), 64, B, 1, ptrs(C, C + 256), WS + 8, 1 << 20, None)  # workspace misaligned
     q8 = L.q8_0_quantize
     yield q8(A, 0, 64, B, None)
     yield q8(A, 4, 33, B, None)

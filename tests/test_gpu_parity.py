@@ -223,6 +223,51 @@ def test_repacked_weights(hip, orc, rows, K):
         assert_close(Yr, orc.mul_mat_ref(Wq_o, orc.q8_0_quantize(X[:N]), K), "repacked N=%d" % N)
 
 
+@pytest.mark.parametrize("K", [96, 768, 4096])
+def test_multi_matrix(hip, orc, K):
+    """Several matrices sharing one token matrix: every output matches the
+    oracle; above 8 tokens it is the single-matrix result bit for bit."""
+    shapes = [300, 77, 77, 1000]
+    Ws = [_case(r, K, 1, 3100 + 7 * r + K)[0] for r in shapes]
+    X = inputs.random_matrix(3200 + K, 70, K)
+    Wqs = [hip.q4_0_quantize(dev(W)) for W in Ws]
+    Wq_os = [orc.q4_0_quantize(W) for W in Ws]
+    for N in (1, 2, 5, 8, 9, 70):
+        print("multi K=%d N=%d" % (K, N), flush=True)
+        Xt = dev(X[:N])
+        Xq_o = orc.q8_0_quantize(X[:N])
+        Ys = hip.mul_mat_q4_0_q8_0_multi(Wqs, Xt)
+        Ys_ws = hip.mul_mat_q4_0_q8_0_multi(Wqs, Xt, ws=hip.workspace(1, K, N))
+        for i, r in enumerate(shapes):
+            Y = host(Ys[i])
+            assert Y.shape == (N, r)
+            assert np.array_equal(host(Ys_ws[i]), Y), (K, N, i)
+            assert_close(Y, orc.mul_mat_ref(Wq_os[i], Xq_o, K), "multi K=%d N=%d matrix %d" % (K, N, i))
+            if N > 8:
+                assert np.array_equal(Y, host(hip.mul_mat_q4_0_q8_0(Wqs[i], Xt))), (K, N, i)
+
+
+def test_multi_matrix_llama_decode_full_size(hip, orc):
+    """The two K = 4096 matrices of the Llama decode set in one launch, at full
+    size, N = 1 and 4, outputs sampled against the oracle."""
+    wl = inputs.WORKLOADS[3]
+    mats = [(m, rk) for m, rk in enumerate(wl.mats) if rk[1] == 4096]
+    Wqs, Wq_os, samples = [], [], []
+    for m, (rows, K) in mats:
+        W = inputs.weights(3, m, rows, K, outliers=wl.outliers)
+        Wqs.append(hip.q4_0_quantize(dev(W)))
+        samples.append(_sample_rows(rows, 1024, 9500 + m))
+        Wq_os.append(orc.q4_0_quantize(W[samples[-1]]))
+        del W
+    X = inputs.activations(3, 0, max(wl.ns), 4096)
+    for N in wl.ns:
+        print("multi llama decode N=%d" % N, flush=True)
+        Xq_o = orc.q8_0_quantize(X[:N])
+        Ys = hip.mul_mat_q4_0_q8_0_multi(Wqs, dev(X[:N]))
+        for i in range(len(mats)):
+            assert_close(host(Ys[i])[:, samples[i]], orc.mul_mat_ref(Wq_os[i], Xq_o, 4096), "multi N=%d" % N)
+
+
 def test_repack_rejects_misaligned_output(hip):
     Wq = torch.zeros((4, 36), dtype=torch.uint8, device="cuda")
     buf = torch.zeros(4 * 36 + 32, dtype=torch.uint8, device="cuda")
