@@ -12,7 +12,9 @@ roofline fraction of the dominant kernel (timed alone with HIP events on the
 stream it runs on) and the CPU oracle timed on a bounded sample.
 
 Weights rotate over enough copies (>= 1 GiB) that each step reads them from
-HBM, not from the 256 MB last-level cache.  Prints ONE JSON line on stdout.
+HBM, not from the 256 MB last-level cache.  Before the warm-up steps the step
+runs untimed for about a second so that the clocks have settled.  Prints ONE
+JSON line on stdout.
 """
 from __future__ import annotations
 
@@ -37,7 +39,7 @@ ROTATE_BYTES = 1 << 30
 # are in profiles/.  They describe the kernels as profiled; re-profile after a
 # kernel change.
 TRAFFIC_BYTES = {
-    ("llama3_8b_head", 1): 296277394,      # profiles/k_gemv_fused_vocab_head_128256x4096_N1.md
+    ("llama3_8b_head", 1): 296203473,      # profiles/k_gemv_rows_fused_vocab_head_128256x4096_N1.md
     ("llama3_8b_prefill", 512): 116117089,  # profiles/k_gemm_prefill_14336x4096_N512.md
 }
 
@@ -127,6 +129,31 @@ class Mats:
 def fused_step(N):
     """The operator runs as one kernel (activation quantizer fused) for one token."""
     return N == 1
+
+
+def decode_kernel(K, N):
+    """Name of the decode kernel the library picks: whole waves per row for one
+    token on long rows (an even block count whose pairs fill at least three
+    quarters of 64, 128 or 256 lanes), the task kernel otherwise."""
+    nb = K // 32
+    P = nb // 2
+    if N == 1 and nb % 2 == 0:
+        for ppl in (1, 2, 4):
+            if P <= 64 * ppl:
+                return "k_gemv_rows" if 4 * P >= 3 * 64 * ppl else "k_gemv"
+    return "k_gemv"
+
+
+def settle(torch, fn, seconds=1.0):
+    """Run the step, untimed, for about a second before any measurement: an
+    idle GPU ramps its clocks up over the first tenths of a second of work,
+    and a measurement taken during the ramp reads several percent slow."""
+    t0, i = time.perf_counter(), 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(50):
+            fn(i)
+            i += 1
+        torch.cuda.synchronize()
 
 
 def timed(torch, fn, steps, warmup):
@@ -223,6 +250,7 @@ def main():
     log("workload %s N=%d: preparing" % (wl.name, N))
     mats = Mats(hip, torch, cid, N)
     n_launch = len(mats.items)
+    settle(torch, lambda i: mats.step(hip, i))
     ms_step = timed(torch, lambda i: mats.step(hip, i), args.steps, args.warmup)
     gbs = mats.bytes_step() / (ms_step * 1e-3) / 1e9
     # two-phase form: activation quantizer once, then the product kernel alone
@@ -233,10 +261,12 @@ def main():
         % (ms_step * 1e3, gbs, ms_kernel * 1e3 / n_launch, kern_gbs))
     if fused_step(N):
         # one kernel per matrix: the step is the dominant kernel
-        roof = {"kernel": "k_gemv (fused activation quantizer)", "achieved": gbs, "ms": ms_step,
+        roof = {"kernel": decode_kernel(mats.items[0][1], N) + " (fused activation quantizer)", "achieved": gbs,
+                "ms": ms_step,
                 "bytes": mats.bytes_step() // n_launch}
     else:
-        roof = {"kernel": "k_gemv (product kernel alone)", "achieved": kern_gbs, "ms": ms_kernel,
+        roof = {"kernel": decode_kernel(mats.items[0][1], N) + " (product kernel alone)", "achieved": kern_gbs,
+                "ms": ms_kernel,
                 "bytes": mats.bytes_kernel() // n_launch}
     del mats
     torch.cuda.empty_cache()

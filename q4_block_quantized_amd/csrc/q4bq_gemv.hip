@@ -245,6 +245,225 @@ k_gemv(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __restr
         do_task(task, false);
 }
 
+// ---------------------------------------------------------------------------
+// One token, rows streamed by whole waves.
+//
+// The 64 lanes of a wave share one row: lane p owns pairs p, p + 64, ...
+// (PPL of them), so with one pair per lane its activation blocks never change
+// and stay in registers.  Wave w walks rows w, w + S, w + 2S, ... (S = waves
+// in the grid, so at any moment the grid reads one contiguous band of rows)
+// and keeps D rows' loads in flight: it waits only for the oldest row, folds
+// it, and issues the row D ahead.  The loads are unconditional -- past its
+// last row a wave re-reads that row, and a lane past the last pair re-reads
+// that pair -- so the compiler's in-order load counters wait for exactly one
+// row; the scheduling barriers keep the issue order fixed.  A row's lanes
+// combine with DPP adds inside rows of 16 lanes and two row broadcasts, and
+// lane 63 writes the result.
+//
+// Activations: fp32 X quantized by the workgroup into LDS (kXF32) or the
+// quantizer's buffer (kActGlobal).  Their loads are issued before the first
+// weight loads, so that waiting for them does not wait for the weights.
+// ---------------------------------------------------------------------------
+constexpr int kRowsMaxPPL = 4;
+
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, kRowMask, 0xF,
+                                                                 false));
+}
+
+// Sum over the 64 lanes; the total lands in lane 63.
+__device__ __forceinline__ float wave_sum_to_63(float v) {
+    v += dpp_f<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+    v += dpp_f<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+    v += dpp_f<0x141, 0xF>(v);  // row_half_mirror
+    v += dpp_f<0x140, 0xF>(v);  // row_mirror: every lane of a row holds the row's sum
+    v += dpp_f<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+    v += dpp_f<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+    return v;
+}
+
+// A 64-bit value the whole wave agrees on, in scalar registers.
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(static_cast<uint64_t>(v) >> 32));
+    return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+template <int THREADS, int PPL, int D, int SRC, bool RP>
+__global__ void __launch_bounds__(THREADS)
+k_gemv_rows(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __restrict__ src,
+            float* __restrict__ Y) {
+    static_assert(SRC == kXF32 || SRC == kActGlobal, "activation source");
+    constexpr bool kActReg = PPL == 1;            // activations in registers, else read from LDS per row
+    constexpr bool kUseLds = SRC == kXF32 || !kActReg;
+    constexpr int kWaves = THREADS / 64;
+    extern __shared__ __align__(16) uint8_t smem[];
+    uint32_t* sq = reinterpret_cast<uint32_t*>(smem);
+    ActScale* ss = reinterpret_cast<ActScale*>(smem + static_cast<size_t>(nb) * kActQBytes);
+    const uint8_t* __restrict__ Wsc = Wq + (RP ? rows * nb * 16 : 0);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar row arithmetic
+    const int P = nb >> 1;
+
+    // 1. activation loads (before any weight load)
+    //    kXF32: thread t quantizes quad (t & 7) of blocks t / 8 + (THREADS / 8) j
+    //    kActGlobal into LDS: thread t copies 16-byte piece t + THREADS j of
+    //    the int8 blocks and scale record t + THREADS j
+    constexpr int kJ = (1024 * PPL + THREADS - 1) / THREADS;  // nb <= 128 * PPL
+    float4 xv[SRC == kXF32 ? kJ : 1];
+    u32x4 gq[SRC == kActGlobal && kUseLds ? kJ : 1];
+    ActScale gs[SRC == kActGlobal && kUseLds ? kJ : 1];
+    if constexpr (SRC == kXF32) {
+        const float* X = static_cast<const float*>(src);
+#pragma unroll
+        for (int j = 0; j < kJ; ++j) {
+            const int g = min(static_cast<int>(threadIdx.x >> 3) + (THREADS / 8) * j, nb - 1);
+            __builtin_memcpy(&xv[j], X + static_cast<int64_t>(g) * kQK + 4 * (threadIdx.x & 7), 16);
+        }
+    } else if constexpr (kUseLds) {
+        const u32x4* q = static_cast<const u32x4*>(src);
+        const ActScale* sc = reinterpret_cast<const ActScale*>(static_cast<const uint8_t*>(src) +
+                                                               static_cast<size_t>(nb) * kActQBytes);
+#pragma unroll
+        for (int j = 0; j < kJ; ++j) {
+            gq[j] = q[min(static_cast<int>(threadIdx.x) + THREADS * j, 2 * nb - 1)];
+            gs[j] = sc[min(static_cast<int>(threadIdx.x) + THREADS * j, nb - 1)];
+        }
+    }
+    uint32_t areg[2][8];
+    ActScale sreg[2];
+    if constexpr (SRC == kActGlobal && kActReg) {
+        const int p = min(lane, P - 1);
+        const u32x4* q = static_cast<const u32x4*>(src) + 4 * p;
+        const ActScale* sc = reinterpret_cast<const ActScale*>(static_cast<const uint8_t*>(src) +
+                                                               static_cast<size_t>(nb) * kActQBytes) + 2 * p;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const u32x4 a0 = q[2 * h], a1 = q[2 * h + 1];
+            areg[h][0] = a0.x; areg[h][1] = a0.y; areg[h][2] = a0.z; areg[h][3] = a0.w;
+            areg[h][4] = a1.x; areg[h][5] = a1.y; areg[h][6] = a1.z; areg[h][7] = a1.w;
+            sreg[h] = sc[h];
+        }
+    }
+
+    // 2. the first D rows of this wave
+    const int64_t S = static_cast<int64_t>(gridDim.x) * kWaves;
+    const int64_t w0 = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
+    const int64_t nk = w0 < rows ? (rows - 1 - w0) / S + 1 : 0;
+    // a wave without rows (small matrices) still issues its loads, on the last
+    // row, so that no branch leaves the load counters uncertain
+    const int64_t rlast = nk > 0 ? w0 + (nk - 1) * S : rows - 1;
+    int pp[PPL];
+    bool pv[PPL];
+#pragma unroll
+    for (int i = 0; i < PPL; ++i) {
+        pv[i] = lane + 64 * i < P;
+        pp[i] = min(lane + 64 * i, P - 1);
+    }
+    // the row base is wave-uniform (scalar registers); lanes add a 32-bit offset
+    auto load_row = [&](Pair36 (&dst)[PPL], int64_t k) __attribute__((always_inline)) {
+        const int64_t rb = uniform64(min(w0 + k * S, rlast) * nb);
+        const uint8_t* wrow = Wq + rb * (RP ? 16 : kQ4Bytes);
+        const uint8_t* srow = Wsc + rb * 2;
+#pragma unroll
+        for (int i = 0; i < PPL; ++i) {
+            const uint32_t p = static_cast<uint32_t>(pp[i]);
+            dst[i] = RP ? load_pair_rp(wrow + 32 * p, srow + 4 * p) : load_pair(wrow + 36 * p);
+        }
+    };
+    Pair36 raw[D][PPL];
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        load_row(raw[d], d);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // 3. activations into LDS, then (one pair per lane) into registers
+    if constexpr (kUseLds) {
+        if constexpr (SRC == kXF32) {
+            const int m = threadIdx.x & 7;
+#pragma unroll
+            for (int j = 0; j < kJ; ++j) {
+                const int g = static_cast<int>(threadIdx.x >> 3) + (THREADS / 8) * j;
+                const bool valid = g < nb;
+                const float4 x = valid ? xv[j] : make_float4(0.f, 0.f, 0.f, 0.f);
+                uint32_t word;
+                const ActScale sc = quant_act_quad(x.x, x.y, x.z, x.w, m, word);
+                if (valid) {
+                    sq[g * 8 + m] = word;
+                    if (m == 0) ss[g] = sc;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < kJ; ++j) {
+                const int t = threadIdx.x + THREADS * j;
+                if (t < 2 * nb) reinterpret_cast<u32x4*>(sq)[t] = gq[j];
+                if (t < nb) ss[t] = gs[j];
+            }
+        }
+        // LDS writes done, then the workgroup barrier; no wait on the weight loads
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if constexpr (kActReg) {
+            const int p = min(lane, P - 1);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const u32x4 a0 = reinterpret_cast<const u32x4*>(sq)[(2 * p + h) * 2];
+                const u32x4 a1 = reinterpret_cast<const u32x4*>(sq)[(2 * p + h) * 2 + 1];
+                areg[h][0] = a0.x; areg[h][1] = a0.y; areg[h][2] = a0.z; areg[h][3] = a0.w;
+                areg[h][4] = a1.x; areg[h][5] = a1.y; areg[h][6] = a1.z; areg[h][7] = a1.w;
+                sreg[h] = ss[2 * p + h];
+            }
+        }
+    }
+    if (nk == 0) return;
+
+    // 4. the rolling loop
+    auto fold = [&](const Pair36 (&q)[PPL]) __attribute__((always_inline)) {
+        float part = 0.0f;
+#pragma unroll
+        for (int i = 0; i < PPL; ++i) {
+            float v[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const Block4 blk = RP ? (h ? pair_second_rp(q[i]) : pair_first_rp(q[i]))
+                                      : (h ? pair_second(q[i]) : pair_first(q[i]));
+                int32_t s;
+                float dx;
+                if constexpr (kActReg) {
+                    s = block_dot(blk, areg[h], sreg[h].bias);
+                    dx = sreg[h].d;
+                } else {
+                    const int b = 2 * pp[i] + h;
+                    const u32x4 a0 = reinterpret_cast<const u32x4*>(sq)[b * 2];
+                    const u32x4 a1 = reinterpret_cast<const u32x4*>(sq)[b * 2 + 1];
+                    const uint32_t a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+                    const ActScale sc = ss[b];
+                    s = block_dot(blk, a, sc.bias);
+                    dx = sc.d;
+                }
+                v[h] = static_cast<float>(s) * (half_bits_to_float(blk.dbits) * dx);
+            }
+            const float pair = v[0] + v[1];
+            part = i == 0 ? (pv[0] ? pair : 0.0f) : part + (pv[i] ? pair : 0.0f);
+        }
+        return part;
+    };
+    for (int64_t k = 0; k < nk; k += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const float t = wave_sum_to_63(fold(raw[d]));
+            if (k + d < nk && lane == 63) Y[w0 + (k + d) * S] = t;
+            load_row(raw[d], k + d + D);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
 struct Shape {
     int log2G, rpi;
     uint32_t wgs;
@@ -334,6 +553,49 @@ hipError_t launch_n(const DeviceInfo* dev, int lay, const uint8_t* Wq, int64_t r
                : launch_v<NT, 256, kActGlobal, false>(sh, lay, Wq, rows, nb, act, Y, D, md, s);
 }
 
+// Pairs per lane for the row-streaming kernel, or 0 where it does not apply:
+// one token, an even block count, and rows whose pairs fill at least three
+// quarters of the lanes (other shapes keep the task kernel above).
+int rows_ppl(int64_t nb) {
+    if (nb & 1) return 0;
+    const int64_t P = nb >> 1;
+    for (int ppl = 1; ppl <= kRowsMaxPPL; ppl *= 2)
+        if (P <= 64 * ppl) return 4 * P >= 3 * 64 * ppl ? ppl : 0;
+    return 0;
+}
+
+template <int SRC, bool RP>
+hipError_t launch_rows_t(const DeviceInfo* dev, const uint8_t* Wq, int64_t rows, int64_t nb, const void* src,
+                         float* Y, hipStream_t s) {
+    constexpr int kThreads = 1024;
+    const int ppl = rows_ppl(nb);
+    int64_t wgs = (rows + kThreads / 64 - 1) / (kThreads / 64);
+    if (wgs > dev->num_cu) wgs = dev->num_cu;
+    const size_t lds = (SRC == kXF32 || ppl > 1) ? static_cast<size_t>(nb) * (kActQBytes + kActSBytes) : 0;
+    const int nbi = static_cast<int>(nb);
+    const dim3 grid(static_cast<uint32_t>(wgs)), block(kThreads);
+    switch (ppl) {
+        case 1:
+            hipLaunchKernelGGL((k_gemv_rows<kThreads, 1, 1, SRC, RP>), grid, block, lds, s, Wq, rows, nbi, src, Y);
+            break;
+        case 2:
+            hipLaunchKernelGGL((k_gemv_rows<kThreads, 2, 1, SRC, RP>), grid, block, lds, s, Wq, rows, nbi, src, Y);
+            break;
+        case 4:
+            hipLaunchKernelGGL((k_gemv_rows<kThreads, 4, 1, SRC, RP>), grid, block, lds, s, Wq, rows, nbi, src, Y);
+            break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <int SRC>
+hipError_t launch_rows(const DeviceInfo* dev, int lay, const uint8_t* Wq, int64_t rows, int64_t nb, const void* src,
+                       float* Y, hipStream_t s) {
+    return lay == kLayRepacked ? launch_rows_t<SRC, true>(dev, Wq, rows, nb, src, Y, s)
+                               : launch_rows_t<SRC, false>(dev, Wq, rows, nb, src, Y, s);
+}
+
 int lay_of(WLayout lay) { return lay == kRepacked ? kLayRepacked : kLayAoS; }
 
 // Fused decode (the kernel quantizes X itself): one 1024-thread workgroup per
@@ -342,6 +604,7 @@ int lay_of(WLayout lay) { return lay == kRepacked ? kLayRepacked : kLayAoS; }
 hipError_t fused_n(const DeviceInfo* dev, int lay, const uint8_t* Wq, int64_t rows, int64_t nb, const float* X,
                    int64_t N, float* Y, const MultiDesc& md, hipStream_t s) {
     if (N != 1) return hipErrorInvalidValue;
+    if (lay != kLayMulti && rows_ppl(nb)) return launch_rows<kXF32>(dev, lay, Wq, rows, nb, X, Y, s);
     const Shape big = pick_shape(dev, rows, nb, 1024, 1, 1);
     if (big.ntasks >= static_cast<int64_t>(dev->num_cu) * 16)
         return launch_v<1, 1024, kXF32, false>(big, lay, Wq, rows, nb, X, Y, nullptr, md, s);
@@ -352,7 +615,9 @@ hipError_t fused_n(const DeviceInfo* dev, int lay, const uint8_t* Wq, int64_t ro
 hipError_t gemv_n(const DeviceInfo* dev, int lay, const uint8_t* Wq, int64_t rows, int64_t nb, const void* act,
                   int64_t N, float* Y, int32_t* D, const MultiDesc& md, hipStream_t s) {
     switch (N) {
-        case 1: return launch_n<1>(dev, lay, Wq, rows, nb, act, Y, D, md, s);
+        case 1:
+            if (!D && lay != kLayMulti && rows_ppl(nb)) return launch_rows<kActGlobal>(dev, lay, Wq, rows, nb, act, Y, s);
+            return launch_n<1>(dev, lay, Wq, rows, nb, act, Y, D, md, s);
         case 2: return launch_n<2>(dev, lay, Wq, rows, nb, act, Y, D, md, s);
         case 3: return launch_n<3>(dev, lay, Wq, rows, nb, act, Y, D, md, s);
         case 4: return launch_n<4>(dev, lay, Wq, rows, nb, act, Y, D, md, s);

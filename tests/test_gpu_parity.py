@@ -173,6 +173,24 @@ def test_paths_agree_bitwise(hip, orc):
             assert np.array_equal(host(other), ref), (rows, K, N)
 
 
+@pytest.mark.parametrize("K", [3008, 3072, 6144, 8192, 12288, 14336, 16384, 16416])
+def test_one_token_long_rows(hip, orc, K):
+    """One token on long rows, where a whole wave streams each row: the oracle
+    bar on ragged row counts, and the same bits from fused quantization, the
+    pre-quantized input and the repacked weights.  K = 3008 (47 pairs per
+    row) and 16416 (an odd block count) sit just outside that kernel's range."""
+    for rows in (1, 17, 300):
+        print("long rows rows=%d K=%d" % (rows, K), flush=True)
+        W, X = _case(rows, K, 1, 900 + rows + K)
+        Wq_o, Xq_o = orc.q4_0_quantize(W), orc.q8_0_quantize(X)
+        Wq = hip.q4_0_quantize(dev(W))
+        Xt = dev(X)
+        Y = host(hip.mul_mat_q4_0_q8_0(Wq, Xt))
+        assert_close(Y, orc.mul_mat_ref(Wq_o, Xq_o, K), "rows=%d K=%d" % (rows, K))
+        assert np.array_equal(host(hip.mul_mat_q4_0_q8_0_pq(Wq, hip.q8_0_quantize(Xt), K)), Y), (rows, K)
+        assert np.array_equal(host(hip.mul_mat_q4_0r_q8_0(hip.q4_0_repack(Wq, K), Xt)), Y), (rows, K)
+
+
 def test_unaligned_but_valid_pointers(hip, orc):
     """Q4_0 data may start on any 2-byte boundary, fp32 data on any 4-byte one."""
     rows, K, N = 65, 4096, 3
