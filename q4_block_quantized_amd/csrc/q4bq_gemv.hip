@@ -290,10 +290,12 @@ __device__ __forceinline__ int64_t uniform64(int64_t v) {
     return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
-template <int THREADS, int PPL, int D, int SRC, bool RP>
+template <int THREADS, int PPL, int D, int SRC, int LAY>
 __global__ void __launch_bounds__(THREADS)
 k_gemv_rows(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __restrict__ src,
-            float* __restrict__ Y) {
+            float* __restrict__ Y, const MultiDesc md) {
+    constexpr bool RP = LAY == kLayRepacked;
+    constexpr bool MULTI = LAY == kLayMulti;  // rows of md's matrices, concatenated (rows = their total)
     static_assert(SRC == kXF32 || SRC == kActGlobal, "activation source");
     constexpr bool kActReg = PPL == 1;            // activations in registers, else read from LDS per row
     constexpr bool kUseLds = SRC == kXF32 || !kActReg;
@@ -361,11 +363,42 @@ k_gemv_rows(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __
         pv[i] = lane + 64 * i < P;
         pp[i] = min(lane + 64 * i, P - 1);
     }
-    // the row base is wave-uniform (scalar registers); lanes add a 32-bit offset
+    // where a row's blocks and its output live; every value is wave-uniform
+    // (scalar registers) and lanes add a 32-bit offset
+    struct RowAt {
+        const uint8_t* w;
+        const uint8_t* sc;
+        float* y;
+    };
+    auto row_at = [&](int64_t r) __attribute__((always_inline)) {
+        RowAt a;
+        if constexpr (MULTI) {
+            const uint8_t* wb = md.w[0];
+            float* yb = md.y[0];
+            int64_t f = 0;
+#pragma unroll
+            for (int m = 1; m < kMaxMulti; ++m) {
+                if (m < md.count && r >= md.first[m]) {
+                    wb = md.w[m];
+                    yb = md.y[m];
+                    f = md.first[m];
+                }
+            }
+            a.w = wb + uniform64((r - f) * nb) * kQ4Bytes;
+            a.sc = nullptr;
+            a.y = yb + (r - f);
+        } else {
+            const int64_t rb = uniform64(r * nb);
+            a.w = Wq + rb * (RP ? 16 : kQ4Bytes);
+            a.sc = Wsc + rb * 2;
+            a.y = Y + r;
+        }
+        return a;
+    };
     auto load_row = [&](Pair36 (&dst)[PPL], int64_t k) __attribute__((always_inline)) {
-        const int64_t rb = uniform64(min(w0 + k * S, rlast) * nb);
-        const uint8_t* wrow = Wq + rb * (RP ? 16 : kQ4Bytes);
-        const uint8_t* srow = Wsc + rb * 2;
+        const RowAt a = row_at(min(w0 + k * S, rlast));
+        const uint8_t* wrow = a.w;
+        const uint8_t* srow = a.sc;
 #pragma unroll
         for (int i = 0; i < PPL; ++i) {
             const uint32_t p = static_cast<uint32_t>(pp[i]);
@@ -457,7 +490,7 @@ k_gemv_rows(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             const float t = wave_sum_to_63(fold(raw[d]));
-            if (k + d < nk && lane == 63) Y[w0 + (k + d) * S] = t;
+            if (k + d < nk && lane == 63) *row_at(w0 + (k + d) * S).y = t;
             load_row(raw[d], k + d + D);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -564,9 +597,9 @@ int rows_ppl(int64_t nb) {
     return 0;
 }
 
-template <int SRC, bool RP>
+template <int SRC, int LAY>
 hipError_t launch_rows_t(const DeviceInfo* dev, const uint8_t* Wq, int64_t rows, int64_t nb, const void* src,
-                         float* Y, hipStream_t s) {
+                         float* Y, const MultiDesc& md, hipStream_t s) {
     constexpr int kThreads = 1024;
     const int ppl = rows_ppl(nb);
     int64_t wgs = (rows + kThreads / 64 - 1) / (kThreads / 64);
@@ -576,13 +609,13 @@ hipError_t launch_rows_t(const DeviceInfo* dev, const uint8_t* Wq, int64_t rows,
     const dim3 grid(static_cast<uint32_t>(wgs)), block(kThreads);
     switch (ppl) {
         case 1:
-            hipLaunchKernelGGL((k_gemv_rows<kThreads, 1, 1, SRC, RP>), grid, block, lds, s, Wq, rows, nbi, src, Y);
+            hipLaunchKernelGGL((k_gemv_rows<kThreads, 1, 1, SRC, LAY>), grid, block, lds, s, Wq, rows, nbi, src, Y, md);
             break;
         case 2:
-            hipLaunchKernelGGL((k_gemv_rows<kThreads, 2, 1, SRC, RP>), grid, block, lds, s, Wq, rows, nbi, src, Y);
+            hipLaunchKernelGGL((k_gemv_rows<kThreads, 2, 1, SRC, LAY>), grid, block, lds, s, Wq, rows, nbi, src, Y, md);
             break;
         case 4:
-            hipLaunchKernelGGL((k_gemv_rows<kThreads, 4, 1, SRC, RP>), grid, block, lds, s, Wq, rows, nbi, src, Y);
+            hipLaunchKernelGGL((k_gemv_rows<kThreads, 4, 1, SRC, LAY>), grid, block, lds, s, Wq, rows, nbi, src, Y, md);
             break;
         default: return hipErrorInvalidValue;
     }
@@ -591,9 +624,12 @@ hipError_t launch_rows_t(const DeviceInfo* dev, const uint8_t* Wq, int64_t rows,
 
 template <int SRC>
 hipError_t launch_rows(const DeviceInfo* dev, int lay, const uint8_t* Wq, int64_t rows, int64_t nb, const void* src,
-                       float* Y, hipStream_t s) {
-    return lay == kLayRepacked ? launch_rows_t<SRC, true>(dev, Wq, rows, nb, src, Y, s)
-                               : launch_rows_t<SRC, false>(dev, Wq, rows, nb, src, Y, s);
+                       float* Y, const MultiDesc& md, hipStream_t s) {
+    switch (lay) {
+        case kLayRepacked: return launch_rows_t<SRC, kLayRepacked>(dev, Wq, rows, nb, src, Y, md, s);
+        case kLayMulti: return launch_rows_t<SRC, kLayMulti>(dev, Wq, rows, nb, src, Y, md, s);
+        default: return launch_rows_t<SRC, kLayAoS>(dev, Wq, rows, nb, src, Y, md, s);
+    }
 }
 
 int lay_of(WLayout lay) { return lay == kRepacked ? kLayRepacked : kLayAoS; }
@@ -604,7 +640,7 @@ int lay_of(WLayout lay) { return lay == kRepacked ? kLayRepacked : kLayAoS; }
 hipError_t fused_n(const DeviceInfo* dev, int lay, const uint8_t* Wq, int64_t rows, int64_t nb, const float* X,
                    int64_t N, float* Y, const MultiDesc& md, hipStream_t s) {
     if (N != 1) return hipErrorInvalidValue;
-    if (lay != kLayMulti && rows_ppl(nb)) return launch_rows<kXF32>(dev, lay, Wq, rows, nb, X, Y, s);
+    if (rows_ppl(nb)) return launch_rows<kXF32>(dev, lay, Wq, rows, nb, X, Y, md, s);
     const Shape big = pick_shape(dev, rows, nb, 1024, 1, 1);
     if (big.ntasks >= static_cast<int64_t>(dev->num_cu) * 16)
         return launch_v<1, 1024, kXF32, false>(big, lay, Wq, rows, nb, X, Y, nullptr, md, s);
@@ -616,7 +652,7 @@ hipError_t gemv_n(const DeviceInfo* dev, int lay, const uint8_t* Wq, int64_t row
                   int64_t N, float* Y, int32_t* D, const MultiDesc& md, hipStream_t s) {
     switch (N) {
         case 1:
-            if (!D && lay != kLayMulti && rows_ppl(nb)) return launch_rows<kActGlobal>(dev, lay, Wq, rows, nb, act, Y, s);
+            if (!D && rows_ppl(nb)) return launch_rows<kActGlobal>(dev, lay, Wq, rows, nb, act, Y, md, s);
             return launch_n<1>(dev, lay, Wq, rows, nb, act, Y, D, md, s);
         case 2: return launch_n<2>(dev, lay, Wq, rows, nb, act, Y, D, md, s);
         case 3: return launch_n<3>(dev, lay, Wq, rows, nb, act, Y, D, md, s);
