@@ -56,6 +56,7 @@ def parse():
     ap.add_argument("--workload", default="c4", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
+    ap.add_argument("--no-small", action="store_true", help="skip the other decode configurations (GPT-2, Llama layer, head at N=8)")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of this many MiB, 5 times (a known-size kernel for "
                          "scaling HBM byte counters)")
@@ -196,6 +197,65 @@ def multi_matrix(hip, torch, args):
             "one_launch_GB/s": round(nbytes / (ms_one * 1e-3) / 1e9, 1)}
 
 
+def graph_timed(torch, fn, n_steps, replays):
+    """Per-step time of n_steps consecutive steps captured in one HIP graph and
+    replayed: the device time of back-to-back operator calls, without the
+    host's per-call cost."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(3):
+            fn(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n_steps):
+            fn(i)
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(replays):
+        g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / (replays * n_steps), g
+
+
+def decode_configs(hip, torch):
+    """The other decode configurations (GPT-2 matrices, the Llama layer's three
+    matrices at one and four tokens, the vocabulary head at eight tokens),
+    whose steps run from a HIP graph so that the host's per-call cost of the
+    short ones is not counted.  Every replay's output is checked against an
+    eager call."""
+    from q4_block_quantized_amd import inputs
+    res = []
+    for cid, N in ((1, 1), (2, 1), (3, 1), (3, 4), (4, 8)):
+        wl = inputs.WORKLOADS[cid]
+        mats = Mats(hip, torch, cid, N)
+        mats.step(hip, 0)
+        torch.cuda.synchronize()
+        ref = [it[4].clone() for it in mats.items]
+        settle(torch, lambda i: mats.step(hip, i), 0.3)
+        n_steps = mats.copies
+        replays = max(3, int(0.05 / max(n_steps * len(mats.items) * 4e-6, 1e-9)))
+        ms, g = graph_timed(torch, lambda i: mats.step(hip, i), n_steps, replays)
+        same = all(torch.equal(it[4], r) for it, r in zip(mats.items, ref))
+        if not same:
+            raise RuntimeError("graph replay of %s N=%d differs from the eager call" % (wl.name, N))
+        gbs = mats.bytes_step() / (ms * 1e-3) / 1e9
+        log("%s N=%d: %.2f us per step (%d launches, HIP graph) -> %.1f GB/s"
+            % (wl.name, N, ms * 1e3, len(mats.items), gbs))
+        res.append({"workload": wl.name, "N": N, "matrices": [list(m) for m in wl.mats],
+                    "us_per_step": round(ms * 1e3, 3), "GB/s": round(gbs, 1),
+                    "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)})
+        del g, mats
+        torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(cid, N):
     """The oracle, as it stands, on a bounded row sample of the workload."""
     import oracle
@@ -283,6 +343,9 @@ def main():
     # matrices): one launch against one call per matrix
     multi = multi_matrix(hip, torch, args)
 
+    # the other decode configurations, device time from HIP graphs
+    small = None if args.no_small else decode_configs(hip, torch)
+
     prefill = None
     if not args.no_prefill:
         log("prefill: preparing")
@@ -327,6 +390,7 @@ def main():
         "prefill": prefill,
         "repacked_weights": repacked,
         "multi_matrix_decode": multi,
+        "decode_configs_graph": small,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

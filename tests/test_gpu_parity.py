@@ -153,7 +153,8 @@ def test_paths_agree_bitwise(hip, orc):
     """Fused quantization, pre-quantized input, caller workspace and the
     stream-ordered scratch give the same bits; so do repeated calls and a
     non-default stream."""
-    for rows, K, N in [(777, 4096, 1), (300, 768, 8), (129, 160, 5), (1000, 4096, 70)]:
+    for rows, K, N in [(777, 4096, 1), (300, 768, 8), (129, 160, 5), (1000, 4096, 70), (513, 4096, 5),
+                       (300, 8192, 3), (129, 14336, 2)]:
         W, X = _case(rows, K, N, 555 + rows)
         Wq = hip.q4_0_quantize(dev(W))
         Xt = dev(X)
@@ -174,21 +175,25 @@ def test_paths_agree_bitwise(hip, orc):
 
 
 @pytest.mark.parametrize("K", [3008, 3072, 6144, 8192, 12288, 14336, 16384, 16416])
-def test_one_token_long_rows(hip, orc, K):
-    """One token on long rows, where a whole wave streams each row: the oracle
-    bar on ragged row counts, and the same bits from fused quantization, the
-    pre-quantized input and the repacked weights.  K = 3008 (47 pairs per
-    row) and 16416 (an odd block count) sit just outside that kernel's range."""
+def test_long_rows_few_tokens(hip, orc, K):
+    """One to eight tokens on long rows, where whole waves stream each row: the
+    oracle bar on ragged row counts, and the same bits from fused quantization,
+    the pre-quantized input and the repacked weights.  K = 3008 (47 pairs per
+    row), K = 16416 (an odd block count) and the larger token counts on the
+    longest rows sit outside that kernel's range and check the other one."""
     for rows in (1, 17, 300):
-        print("long rows rows=%d K=%d" % (rows, K), flush=True)
-        W, X = _case(rows, K, 1, 900 + rows + K)
-        Wq_o, Xq_o = orc.q4_0_quantize(W), orc.q8_0_quantize(X)
-        Wq = hip.q4_0_quantize(dev(W))
-        Xt = dev(X)
-        Y = host(hip.mul_mat_q4_0_q8_0(Wq, Xt))
-        assert_close(Y, orc.mul_mat_ref(Wq_o, Xq_o, K), "rows=%d K=%d" % (rows, K))
-        assert np.array_equal(host(hip.mul_mat_q4_0_q8_0_pq(Wq, hip.q8_0_quantize(Xt), K)), Y), (rows, K)
-        assert np.array_equal(host(hip.mul_mat_q4_0r_q8_0(hip.q4_0_repack(Wq, K), Xt)), Y), (rows, K)
+        for N in (1, 2, 3, 4, 8):
+            if rows * K * N > 12_000_000:
+                continue
+            print("long rows rows=%d K=%d N=%d" % (rows, K, N), flush=True)
+            W, X = _case(rows, K, N, 900 + rows + K + 7 * N)
+            Wq_o, Xq_o = orc.q4_0_quantize(W), orc.q8_0_quantize(X)
+            Wq = hip.q4_0_quantize(dev(W))
+            Xt = dev(X)
+            Y = host(hip.mul_mat_q4_0_q8_0(Wq, Xt))
+            assert_close(Y, orc.mul_mat_ref(Wq_o, Xq_o, K), "rows=%d K=%d N=%d" % (rows, K, N))
+            assert np.array_equal(host(hip.mul_mat_q4_0_q8_0_pq(Wq, hip.q8_0_quantize(Xt), K)), Y), (rows, K, N)
+            assert np.array_equal(host(hip.mul_mat_q4_0r_q8_0(hip.q4_0_repack(Wq, K), Xt)), Y), (rows, K, N)
 
 
 def test_unaligned_but_valid_pointers(hip, orc):
