@@ -74,6 +74,20 @@ hipError_t launch_gemv_fused(const DeviceInfo* dev, WLayout lay, const uint8_t* 
 hipError_t launch_gemv_multi(const DeviceInfo* dev, const MultiDesc& md, int64_t nb, const float* X, const void* act,
                              int64_t N, hipStream_t s);
 
+// Decode kernels: activation sources and weight layouts (the rows of several
+// matrices, MultiDesc, count as one more layout).
+enum DecodeSrc { kActGlobal = 0, kActLds = 1, kXF32 = 2 };
+enum DecodeLayout { kLayAoS = 0, kLayRepacked = 1, kLayMulti = 2 };
+
+// Row-streaming decode (whole waves per row), for N tokens when
+// rows_apply(N, nb): from fp32 X quantized in the kernel, or from the
+// quantizer's buffer.  `lay` is a DecodeLayout; Wq/Y unused for kLayMulti.
+bool rows_apply(int64_t N, int64_t nb);
+hipError_t launch_rows_x(const DeviceInfo* dev, int lay, const uint8_t* Wq, int64_t rows, int64_t nb, const float* X,
+                         int64_t N, float* Y, const MultiDesc& md, hipStream_t s);
+hipError_t launch_rows_act(const DeviceInfo* dev, int lay, const uint8_t* Wq, int64_t rows, int64_t nb,
+                           const void* act, int64_t N, float* Y, const MultiDesc& md, hipStream_t s);
+
 // Matrix-core kernel, any N.  D as above.
 hipError_t launch_gemm(const DeviceInfo* dev, WLayout lay, const uint8_t* Wq, int64_t rows, int64_t nb,
                        const void* act, int64_t N, float* Y, int32_t* D, hipStream_t s);

@@ -1,0 +1,437 @@
+// Decode product on long rows, 1..8 tokens (`k_gemv_rows`): the kernel and
+// its launch templates.  Included by q4bq_rows_x.hip (fp32 X quantized in the
+// kernel) and q4bq_rows_act.hip (the quantizer's buffer), which instantiate it
+// for one activation source each.
+//
+// Arithmetic: the per-block integer dot of ggml_vec_dot_q4_0_q8_0 as described
+// in "llama.cpp 深度解读" (luoboask.github.io) section 3 "量化矩阵乘法 — 核心算子",
+// the nibble offset of 8 from section 2's decode; the same device functions as
+// the task kernel in q4bq_gemv.hip.
+#pragma once
+
+#include "q4bq_device.h"
+#include "q4bq_internal.h"
+
+namespace q4bq {
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// Long rows, 1..8 tokens: rows streamed by whole waves.
+//
+// The 64 lanes of a wave share one row: lane p owns pairs p, p + 64, ...
+// (PPL of them).  With one pair per lane its activation blocks never change,
+// so the NT tokens' blocks stay in registers; with longer rows they are read
+// from LDS.  Wave w walks rows w, w + S, w + 2S, ... (S = waves in the grid,
+// so at any moment the grid reads one contiguous band of rows) and keeps D
+// rows' loads in flight: it waits only for the oldest row, folds it, and
+// issues the row D ahead.  The loads are unconditional -- past its last row a
+// wave re-reads that row, and a lane past the last pair re-reads that pair --
+// so the compiler's in-order load counters wait for exactly one row; the
+// scheduling barriers keep the issue order fixed.  A row's nibbles are split
+// once and meet every token's activations.
+//
+// Row sums: with several tokens the lanes first trade halves of their
+// per-token partial sums (v_permlane32_swap, v_permlane16_swap, then a DPP
+// rotate), so each step halves both the lanes to combine and the values per
+// lane; the rest is DPP adds inside rows of 16 lanes.  One token: four DPP
+// adds and two row broadcasts, lane 63 holds the sum.
+//
+// Activations: fp32 X quantized by the workgroup into LDS (kXF32) or the
+// quantizer's buffer (kActGlobal).  Up to eight of X's 16-byte loads per
+// thread are issued before the first weight loads, so that waiting for them
+// does not wait for the weights.
+// ---------------------------------------------------------------------------
+constexpr int kRowsMaxPPL = 4;
+constexpr size_t kRowsMaxLds = 128 * 1024;  // quantized activations in LDS (one workgroup per CU)
+
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, kRowMask, 0xF,
+                                                                 false));
+}
+
+__device__ __forceinline__ void swap32(float& a, float& b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                                                    false, false);
+    a = __builtin_bit_cast(float, static_cast<uint32_t>(r[0]));
+    b = __builtin_bit_cast(float, static_cast<uint32_t>(r[1]));
+}
+
+__device__ __forceinline__ void swap16(float& a, float& b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                                                    false, false);
+    a = __builtin_bit_cast(float, static_cast<uint32_t>(r[0]));
+    b = __builtin_bit_cast(float, static_cast<uint32_t>(r[1]));
+}
+
+constexpr int pow2_at_least(int n) { return n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : 8; }
+
+// Sums each of the NT values over the 64 lanes.  Token t's total ends in lane
+// sum_lane<NT>(t) (and possibly others).
+template <int NT>
+__device__ __forceinline__ float wave_sums(const float (&part)[NT], int lane) {
+    constexpr int NTP = pow2_at_least(NT);
+    float v[NTP];
+#pragma unroll
+    for (int t = 0; t < NTP; ++t) v[t] = t < NT ? part[t] : 0.0f;
+    if constexpr (NTP >= 2) {
+        // lanes 0-31 keep token i, lanes 32-63 token i + NTP/2
+#pragma unroll
+        for (int i = 0; i < NTP / 2; ++i) {
+            swap32(v[i], v[i + NTP / 2]);
+            v[i] += v[i + NTP / 2];
+        }
+    }
+    if constexpr (NTP >= 4) {
+        // rows 0 and 2 keep token i, rows 1 and 3 token i + NTP/4
+#pragma unroll
+        for (int i = 0; i < NTP / 4; ++i) {
+            swap16(v[i], v[i + NTP / 4]);
+            v[i] += v[i + NTP / 4];
+        }
+    }
+    if constexpr (NTP >= 8) {
+        // lanes with bit 3 clear keep token i, set: token i + 1
+        const bool up = lane & 8;
+        const float mine = up ? v[1] : v[0];
+        const float other = up ? v[0] : v[1];
+        v[0] = mine + dpp_f<0x128, 0xF>(other);  // row_ror:8, the lane 8 apart in the row
+    }
+    float x = v[0];
+    x += dpp_f<0xB1, 0xF>(x);       // quad_perm [1,0,3,2]
+    x += dpp_f<0x4E, 0xF>(x);       // quad_perm [2,3,0,1]
+    x += dpp_f<0x141, 0xF>(x);      // row_half_mirror
+    if constexpr (NTP <= 4) x += dpp_f<0x140, 0xF>(x);   // row_mirror: each row holds its sum
+    if constexpr (NTP <= 2) x += dpp_f<0x142, 0xA>(x);   // row_bcast:15 into rows 1 and 3
+    if constexpr (NTP == 1) x += dpp_f<0x143, 0xC>(x);   // row_bcast:31 into rows 2 and 3
+    return x;
+}
+
+template <int NT>
+__device__ __forceinline__ int sum_lane(int t) {
+    constexpr int NTP = pow2_at_least(NT);
+    return NTP == 1 ? 63 : NTP == 2 ? 32 * t + 31 : NTP == 4 ? 16 * t : 8 * t;
+}
+template <int NT>
+__device__ __forceinline__ int lane_token(int lane) {
+    constexpr int NTP = pow2_at_least(NT);
+    return NTP == 1 ? (lane == 63 ? 0 : -1)
+         : NTP == 2 ? ((lane & 31) == 31 ? lane >> 5 : -1)
+         : NTP == 4 ? ((lane & 15) == 0 ? lane >> 4 : -1)
+                    : ((lane & 7) == 0 ? lane >> 3 : -1);
+}
+
+// A 64-bit value the whole wave agrees on, in scalar registers.
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(static_cast<uint64_t>(v) >> 32));
+    return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+template <int THREADS, int NT, int PPL, int D, int SRC, int LAY>
+__global__ void __launch_bounds__(THREADS)
+k_gemv_rows(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __restrict__ src,
+            float* __restrict__ Y, const MultiDesc md) {
+    static_assert(SRC == kXF32 || SRC == kActGlobal, "activation source");
+    constexpr bool RP = LAY == kLayRepacked;
+    constexpr bool MULTI = LAY == kLayMulti;  // rows of md's matrices, concatenated (rows = their total)
+    constexpr bool kActReg = PPL == 1;         // activations in registers, else read from LDS per row
+    constexpr bool kUseLds = SRC == kXF32 || !kActReg;
+    constexpr int kWaves = THREADS / 64;
+    extern __shared__ __align__(16) uint8_t smem[];
+    uint32_t* sq = reinterpret_cast<uint32_t*>(smem);
+    ActScale* ss = reinterpret_cast<ActScale*>(smem + static_cast<size_t>(NT) * nb * kActQBytes);
+    const uint8_t* __restrict__ Wsc = Wq + (RP ? rows * nb * 16 : 0);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar row arithmetic
+    const int P = nb >> 1;
+    const int nblk = NT * nb;  // activation blocks, token-major
+
+    // 1. activation loads (before any weight load)
+    //    kXF32: thread t quantizes quad (t & 7) of blocks t / 8 + (THREADS / 8) j
+    //    kActGlobal into LDS: thread t copies 16-byte piece t + THREADS j of
+    //    the int8 blocks and scale record t + THREADS j
+    constexpr int kJ = (1024 * NT * PPL + THREADS - 1) / THREADS;  // nb <= 128 * PPL
+    constexpr int kJpreMax = PPL == 1 ? 8 : 4;
+    constexpr int kJpre = kJ < kJpreMax ? kJ : kJpreMax;
+    float4 xv[SRC == kXF32 ? kJpre : 1];
+    if constexpr (SRC == kXF32) {
+        const float* X = static_cast<const float*>(src);
+#pragma unroll
+        for (int j = 0; j < kJpre; ++j) {
+            const int g = min(static_cast<int>(threadIdx.x >> 3) + (THREADS / 8) * j, nblk - 1);
+            __builtin_memcpy(&xv[j], X + static_cast<int64_t>(g) * kQK + 4 * (threadIdx.x & 7), 16);
+        }
+    }
+    uint32_t areg[kActReg ? NT : 1][2][8];
+    ActScale sreg[kActReg ? NT : 1][2];
+    if constexpr (SRC == kActGlobal && kActReg) {
+        const int p = min(lane, P - 1);
+        const u32x4* q = static_cast<const u32x4*>(src);
+        const ActScale* sc = reinterpret_cast<const ActScale*>(static_cast<const uint8_t*>(src) +
+                                                               static_cast<size_t>(nblk) * kActQBytes);
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int g = n * nb + 2 * p + h;
+                const u32x4 a0 = q[2 * g], a1 = q[2 * g + 1];
+                areg[n][h][0] = a0.x; areg[n][h][1] = a0.y; areg[n][h][2] = a0.z; areg[n][h][3] = a0.w;
+                areg[n][h][4] = a1.x; areg[n][h][5] = a1.y; areg[n][h][6] = a1.z; areg[n][h][7] = a1.w;
+                sreg[n][h] = sc[g];
+            }
+    }
+
+    // 2. the first D rows of this wave
+    const int64_t S = static_cast<int64_t>(gridDim.x) * kWaves;
+    const int64_t w0 = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
+    const int64_t nk = w0 < rows ? (rows - 1 - w0) / S + 1 : 0;
+    // a wave without rows (small matrices) still issues its loads, on the last
+    // row, so that no branch leaves the load counters uncertain
+    const int64_t rlast = nk > 0 ? w0 + (nk - 1) * S : rows - 1;
+    int pp[PPL];
+    bool pv[PPL];
+#pragma unroll
+    for (int i = 0; i < PPL; ++i) {
+        pv[i] = lane + 64 * i < P;
+        pp[i] = min(lane + 64 * i, P - 1);
+    }
+    // where a row's blocks and its output live; every value is wave-uniform
+    // (scalar registers) and lanes add a 32-bit offset
+    struct RowAt {
+        const uint8_t* w;
+        const uint8_t* sc;
+        float* y;
+        int64_t ystride;
+    };
+    auto row_at = [&](int64_t r) __attribute__((always_inline)) {
+        RowAt a;
+        if constexpr (MULTI) {
+            const uint8_t* wb = md.w[0];
+            float* yb = md.y[0];
+            int64_t f = 0, f1 = md.first[1];
+#pragma unroll
+            for (int m = 1; m < kMaxMulti; ++m) {
+                if (m < md.count && r >= md.first[m]) {
+                    wb = md.w[m];
+                    yb = md.y[m];
+                    f = md.first[m];
+                    f1 = md.first[m + 1];
+                }
+            }
+            a.w = wb + uniform64((r - f) * nb) * kQ4Bytes;
+            a.sc = nullptr;
+            a.y = yb + (r - f);
+            a.ystride = f1 - f;
+        } else {
+            const int64_t rb = uniform64(r * nb);
+            a.w = Wq + rb * (RP ? 16 : kQ4Bytes);
+            a.sc = Wsc + rb * 2;
+            a.y = Y + r;
+            a.ystride = rows;
+        }
+        return a;
+    };
+    auto load_row = [&](Pair36 (&dst)[PPL], int64_t k) __attribute__((always_inline)) {
+        const RowAt a = row_at(min(w0 + k * S, rlast));
+#pragma unroll
+        for (int i = 0; i < PPL; ++i) {
+            const uint32_t p = static_cast<uint32_t>(pp[i]);
+            dst[i] = RP ? load_pair_rp(a.w + 32 * p, a.sc + 4 * p) : load_pair(a.w + 36 * p);
+        }
+    };
+    Pair36 raw[D][PPL];
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        load_row(raw[d], d);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // 3. activations into LDS, then (one pair per lane) into registers
+    if constexpr (kUseLds) {
+        if constexpr (SRC == kXF32) {
+            const float* X = static_cast<const float*>(src);
+            const int m = threadIdx.x & 7;
+            auto quantize = [&](float4 x, int j) __attribute__((always_inline)) {
+                const int g = static_cast<int>(threadIdx.x >> 3) + (THREADS / 8) * j;
+                const bool valid = g < nblk;
+                if (!valid) x = make_float4(0.f, 0.f, 0.f, 0.f);
+                uint32_t word;
+                const ActScale sc = quant_act_quad(x.x, x.y, x.z, x.w, m, word);
+                if (valid) {
+                    sq[g * 8 + m] = word;
+                    if (m == 0) ss[g] = sc;
+                }
+            };
+#pragma unroll
+            for (int j = 0; j < kJpre; ++j) quantize(xv[j], j);
+            // the rest of a long X (loaded after the weights: these wait for them)
+#pragma unroll 2
+            for (int j = kJpre; j < kJ; ++j) {
+                const int g = min(static_cast<int>(threadIdx.x >> 3) + (THREADS / 8) * j, nblk - 1);
+                float4 x;
+                __builtin_memcpy(&x, X + static_cast<int64_t>(g) * kQK + 4 * m, 16);
+                quantize(x, j);
+            }
+        } else {
+            const u32x4* q = static_cast<const u32x4*>(src);
+            const ActScale* sc = reinterpret_cast<const ActScale*>(static_cast<const uint8_t*>(src) +
+                                                                   static_cast<size_t>(nblk) * kActQBytes);
+            for (int t = threadIdx.x; t < 2 * nblk; t += THREADS) reinterpret_cast<u32x4*>(sq)[t] = q[t];
+            for (int t = threadIdx.x; t < nblk; t += THREADS) ss[t] = sc[t];
+        }
+        // LDS writes done, then the workgroup barrier; no wait on the weight loads
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if constexpr (kActReg) {
+            const int p = min(lane, P - 1);
+#pragma unroll
+            for (int n = 0; n < NT; ++n)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int g = n * nb + 2 * p + h;
+                    const u32x4 a0 = reinterpret_cast<const u32x4*>(sq)[g * 2];
+                    const u32x4 a1 = reinterpret_cast<const u32x4*>(sq)[g * 2 + 1];
+                    areg[n][h][0] = a0.x; areg[n][h][1] = a0.y; areg[n][h][2] = a0.z; areg[n][h][3] = a0.w;
+                    areg[n][h][4] = a1.x; areg[n][h][5] = a1.y; areg[n][h][6] = a1.z; areg[n][h][7] = a1.w;
+                    sreg[n][h] = ss[g];
+                }
+        }
+    }
+    if (nk == 0) return;
+
+    // 4. the rolling loop
+    auto fold = [&](const Pair36 (&q)[PPL], float (&part)[NT]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int n = 0; n < NT; ++n) part[n] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < PPL; ++i) {
+            float v[NT][2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const Block4 blk = RP ? (h ? pair_second_rp(q[i]) : pair_first_rp(q[i]))
+                                      : (h ? pair_second(q[i]) : pair_first(q[i]));
+                const float dw = half_bits_to_float(blk.dbits);
+#pragma unroll
+                for (int n = 0; n < NT; ++n) {
+                    int32_t s;
+                    float dx;
+                    if constexpr (kActReg) {
+                        s = block_dot(blk, areg[n][h], sreg[n][h].bias);
+                        dx = sreg[n][h].d;
+                    } else {
+                        const int g = n * nb + 2 * pp[i] + h;
+                        const u32x4 a0 = reinterpret_cast<const u32x4*>(sq)[g * 2];
+                        const u32x4 a1 = reinterpret_cast<const u32x4*>(sq)[g * 2 + 1];
+                        const uint32_t a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+                        const ActScale sc = ss[g];
+                        s = block_dot(blk, a, sc.bias);
+                        dx = sc.d;
+                    }
+                    v[n][h] = static_cast<float>(s) * (dw * dx);
+                    // LDS operands: at most four tokens' reads in flight, so
+                    // the operands of a long row stay within the register budget
+                    if constexpr (!kActReg) {
+                        if ((n & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+            }
+#pragma unroll
+            for (int n = 0; n < NT; ++n) {
+                const float pair = v[n][0] + v[n][1];
+                part[n] = i == 0 ? (pv[0] ? pair : 0.0f) : part[n] + (pv[i] ? pair : 0.0f);
+            }
+        }
+    };
+    const int my_token = lane_token<NT>(lane);
+    for (int64_t k = 0; k < nk; k += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            float part[NT];
+            fold(raw[d], part);
+            const float t = wave_sums<NT>(part, lane);
+            if (k + d < nk && my_token >= 0 && my_token < NT) {
+                const RowAt a = row_at(w0 + (k + d) * S);
+                a.y[static_cast<int64_t>(my_token) * a.ystride] = t;
+            }
+            load_row(raw[d], k + d + D);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
+// Pairs per lane for the row-streaming kernel, or 0 where it does not apply:
+// an even block count, and rows whose pairs fill at least three quarters of
+// the lanes (other shapes keep the task kernel above).
+inline int rows_ppl(int64_t nb) {
+    if (nb & 1) return 0;
+    const int64_t P = nb >> 1;
+    for (int ppl = 1; ppl <= kRowsMaxPPL; ppl *= 2)
+        if (P <= 64 * ppl) return 4 * P >= 3 * 64 * ppl ? ppl : 0;
+    return 0;
+}
+
+// Workgroup size: 16 waves per CU (at most 128 registers per lane), or 8 where
+// more tokens need more registers (token activations with one pair per lane;
+// per-token partial sums and LDS operands on longer rows).  Depth: rows in
+// flight per wave.
+template <int NT, int PPL>
+constexpr int rows_threads() { return NT > (PPL == 1 ? 4 : PPL == 2 ? 6 : 4) ? 512 : 1024; }
+template <int NT, int PPL>
+constexpr int rows_depth() { return PPL == 1 && NT > 4 ? 2 : 1; }
+
+template <int SRC, int LAY, int NT, int PPL>
+hipError_t launch_rows_k(const DeviceInfo* dev, const uint8_t* Wq, int64_t rows, int64_t nb, const void* src,
+                         float* Y, const MultiDesc& md, hipStream_t s) {
+    constexpr int kThreads = rows_threads<NT, PPL>();
+    constexpr int kDepth = rows_depth<NT, PPL>();
+    const auto kernel = k_gemv_rows<kThreads, NT, PPL, kDepth, SRC, LAY>;
+    int64_t wgs = (rows + kThreads / 64 - 1) / (kThreads / 64);
+    const int64_t cap = static_cast<int64_t>(dev->num_cu) * (1024 / kThreads);
+    if (wgs > cap) wgs = cap;
+    const size_t lds = (SRC == kXF32 || PPL > 1) ? static_cast<size_t>(NT) * nb * (kActQBytes + kActSBytes) : 0;
+    if (lds > 64 * 1024) {
+        // beyond the default dynamic LDS limit: raise it once for this kernel
+        static const hipError_t raised = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                             static_cast<int>(kRowsMaxLds));
+        if (raised != hipSuccess) return raised;
+    }
+    hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(wgs)), dim3(kThreads), lds, s, Wq, rows,
+                       static_cast<int>(nb), src, Y, md);
+    return hipGetLastError();
+}
+
+template <int SRC, int LAY, int NT>
+hipError_t launch_rows_nt(const DeviceInfo* dev, const uint8_t* Wq, int64_t rows, int64_t nb, const void* src,
+                          float* Y, const MultiDesc& md, hipStream_t s) {
+    switch (rows_ppl(nb)) {
+        case 1: return launch_rows_k<SRC, LAY, NT, 1>(dev, Wq, rows, nb, src, Y, md, s);
+        case 2: return launch_rows_k<SRC, LAY, NT, 2>(dev, Wq, rows, nb, src, Y, md, s);
+        case 4: return launch_rows_k<SRC, LAY, NT, 4>(dev, Wq, rows, nb, src, Y, md, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int SRC, int LAY>
+hipError_t launch_rows_t(const DeviceInfo* dev, const uint8_t* Wq, int64_t rows, int64_t nb, const void* src,
+                         int64_t N, float* Y, const MultiDesc& md, hipStream_t s) {
+    switch (N) {
+        case 1: return launch_rows_nt<SRC, LAY, 1>(dev, Wq, rows, nb, src, Y, md, s);
+        case 2: return launch_rows_nt<SRC, LAY, 2>(dev, Wq, rows, nb, src, Y, md, s);
+        case 3: return launch_rows_nt<SRC, LAY, 3>(dev, Wq, rows, nb, src, Y, md, s);
+        case 4: return launch_rows_nt<SRC, LAY, 4>(dev, Wq, rows, nb, src, Y, md, s);
+        case 5: return launch_rows_nt<SRC, LAY, 5>(dev, Wq, rows, nb, src, Y, md, s);
+        case 6: return launch_rows_nt<SRC, LAY, 6>(dev, Wq, rows, nb, src, Y, md, s);
+        case 7: return launch_rows_nt<SRC, LAY, 7>(dev, Wq, rows, nb, src, Y, md, s);
+        case 8: return launch_rows_nt<SRC, LAY, 8>(dev, Wq, rows, nb, src, Y, md, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+}  // namespace q4bq
