@@ -126,6 +126,24 @@ def q4_0_dequantize(Wq: np.ndarray, K: int) -> np.ndarray:
     return out
 
 
+def q4_0_get_rows(Wq: np.ndarray, K: int, ids: np.ndarray) -> np.ndarray:
+    """Rows `ids` of a Q4_0 matrix, dequantized: out[i] = row ids[i] decoded
+    by section 2's rule, (nibble - 8) * d.  This is ggml_get_rows on a Q4_0
+    table, the token-embedding lookup of the Llama graph in section 4
+    ("inpL = ggml_get_rows(tok_embeddings, inp_tokens)"; "llama.cpp 深度解读")
+    and of GPT-2's wte/wpe in the ggml GPT-2 walkthrough (section 3.5).
+    Reading taken: an id outside [0, rows) yields a row of NaN (the pages do
+    not say; ggml asserts)."""
+    nb = _check_k(K)
+    table = q4_0_dequantize(Wq, K)
+    rows = table.shape[0]
+    ids = np.asarray(ids, dtype=np.int64).ravel()
+    out = np.full((ids.size, nb * QK), np.nan, dtype=np.float32)
+    ok = (ids >= 0) & (ids < rows)
+    out[ok] = table[ids[ok]]
+    return out
+
+
 def q8_0_quantize(X: np.ndarray) -> np.ndarray:
     """fp32 N x K -> uint8 N x (K/32*34), natural element order."""
     X = np.ascontiguousarray(X, dtype=np.float32)

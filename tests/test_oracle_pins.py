@@ -144,6 +144,39 @@ def test_p4_decode_table(orc):
 
 
 # ---------------------------------------------------------------------------
+# get_rows: the decode of selected rows (pinned to the hand-worked A1 block)
+# ---------------------------------------------------------------------------
+
+def test_get_rows_pinned_to_worked_block(orc):
+    # rows: [zero block, A1 block, A1 block negated]; the A1 block decodes to
+    # ((k mod 16) - 8) / 8 exactly (Appendix A1 / section 2's decode)
+    a1 = hexbytes(read_golden("q4_0_ramp_block.txt")["bytes"][0])
+    zero = hexbytes(read_golden("zero_blocks.txt")["q4_0_bytes"][0])
+    k = np.arange(32)
+    ramp = ((k % 16) - 8) / 8.0
+    neg = orc.q4_0_quantize(-ramp[None].astype(np.float32))[0]
+    Wq = np.stack([zero, a1, neg])
+    got = orc.q4_0_get_rows(Wq, 32, [1, 0, 1, 2, 3, -1])
+    assert np.array_equal(got[0], ramp.astype(np.float32))
+    assert np.array_equal(got[2], ramp.astype(np.float32))
+    assert np.all(got[1] == 0)
+    # -ramp: amax 1 from -1.0, d = 1/8; +7/8 ... -7/8 plus the +1.0 clamps to 7/8
+    want_neg = np.clip(np.round(-ramp * 8), -8, 7) / 8.0
+    assert np.array_equal(got[3], want_neg.astype(np.float32))
+    assert np.all(np.isnan(got[4])) and np.all(np.isnan(got[5]))
+
+
+def test_get_rows_is_an_index_into_the_decoded_table(orc):
+    W = inputs.random_matrix(61, 40, 96, 0.02)
+    Wq = orc.q4_0_quantize(W)
+    table = orc.q4_0_dequantize(Wq, 96)
+    ids = np.random.default_rng(3).integers(0, 40, 50)
+    assert np.array_equal(orc.q4_0_get_rows(Wq, 96, ids), table[ids])
+    assert np.array_equal(orc.q4_0_get_rows(Wq, 96, np.arange(40)), table)
+    assert orc.q4_0_get_rows(Wq, 96, []).shape == (0, 96)
+
+
+# ---------------------------------------------------------------------------
 # P5: round-trip invariants
 # ---------------------------------------------------------------------------
 
