@@ -256,6 +256,39 @@ def decode_configs(hip, torch):
     return res
 
 
+def get_rows_leg(hip, torch):
+    """Q4_0 get_rows (decoded embedding rows) on the Llama-3-8B-shaped token
+    table (128256 x 4096), for a 512-token batch and one token; device time
+    from HIP graphs, each replay's output checked against an eager call.
+    Algorithmic bytes: the selected Q4_0 rows, the int32 ids and the fp32
+    output (7x the rows read)."""
+    from q4_block_quantized_amd import inputs
+    rows, K = 128256, 4096
+    W = torch.from_numpy(inputs.weights(4, 0, rows, K)).cuda()
+    Wq = hip.q4_0_quantize(W)
+    del W
+    res = []
+    for n in (512, 1):
+        ids = torch.from_numpy(np.random.default_rng(11 + n).integers(0, rows, n).astype(np.int32)).cuda()
+        out = torch.empty((n, K), dtype=torch.float32, device="cuda")
+        fn = lambda i: hip.q4_0_get_rows(Wq, K, ids, out)
+        fn(0)
+        torch.cuda.synchronize()
+        ref = out.clone()
+        ms, g = graph_timed(torch, fn, 20, 50)
+        if not torch.equal(out, ref):
+            raise RuntimeError("graph replay of get_rows n=%d differs from the eager call" % n)
+        nbytes = n * (K // 32 * 18 + 4 + K * 4)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        log("get_rows 128256x4096 table, %d ids: %.2f us -> %.1f GB/s" % (n, ms * 1e3, gbs))
+        res.append({"table": [rows, K], "n": n, "us_per_call": round(ms * 1e3, 3), "GB/s": round(gbs, 1),
+                    "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)})
+        del g
+    del Wq
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(cid, N):
     """The oracle, as it stands, on a bounded row sample of the workload."""
     import oracle
@@ -345,6 +378,7 @@ def main():
 
     # the other decode configurations, device time from HIP graphs
     small = None if args.no_small else decode_configs(hip, torch)
+    rows_lookup = None if args.no_small else get_rows_leg(hip, torch)
 
     prefill = None
     if not args.no_prefill:
@@ -391,6 +425,7 @@ def main():
         "repacked_weights": repacked,
         "multi_matrix_decode": multi,
         "decode_configs_graph": small,
+        "get_rows_graph": rows_lookup,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -139,6 +139,23 @@ int mul_mat_q4_0_q8_0_prepared(const void *Wq, int64_t rows, int64_t K,
 int q4_0_repack(const void *Wq, int64_t rows, int64_t K, void *Wr, void *stream);
 
 /*
+ * Rows of a Q4_0 table, decoded: ggml_get_rows on Q4_0, the token-embedding
+ * lookup that starts the Llama graph in "llama.cpp 深度解读" section 4
+ * ("计算图构建 — 以 Llama 模型为例", inpL = ggml_get_rows(tok_embeddings,
+ * inp_tokens)) and GPT-2's wte/wpe lookups in the ggml GPT-2 walkthrough
+ * (section 3.5); the decode is section 2's: element j of a block is
+ * (nibble_j - 8) * d, exact in fp32.
+ *   Wq    device, rows x K/32 Q4_0 blocks (the pages' layout), 2-byte aligned.
+ *   ids   device, n int32 row indices, 4-byte aligned.
+ *   out   device, fp32 n x K (row i = row ids[i]), 16-byte aligned,
+ *         overwritten; may not overlap Wq or ids.
+ * An id outside [0, rows) gives a row of NaN (no out-of-range read; the
+ * pages do not define this case).  Errors as for q4_0_quantize; n >= 1.
+ */
+int q4_0_get_rows(const void *Wq, int64_t rows, int64_t K, const int32_t *ids,
+                  int64_t n, float *out, void *stream);
+
+/*
  * mul_mat_q4_0_q8_0 and mul_mat_q4_0_q8_0_ex on repacked weights (Wr from
  * q4_0_repack, 16-byte aligned); every other argument and the result are as
  * for the forms on Q4_0 blocks, bit for bit.

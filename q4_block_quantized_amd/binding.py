@@ -30,6 +30,7 @@ EXPORTS = (
     "mul_mat_q4_0_q8_0_ex", "mul_mat_q4_0_q8_0_pq", "q4_0_q8_0_block_dots",
     "q4bq_status_string", "q4bq_version", "q4bq_quantize_activations", "mul_mat_q4_0_q8_0_prepared",
     "q4_0_repack", "mul_mat_q4_0r_q8_0", "mul_mat_q4_0r_q8_0_ex", "mul_mat_q4_0_q8_0_multi",
+    "q4_0_get_rows",
 )
 
 
@@ -59,6 +60,7 @@ def lib() -> ctypes.CDLL:
         "mul_mat_q4_0_q8_0_ex": (I, [P, I64, I64, P, I64, P, P, ctypes.c_size_t, P]),
         "mul_mat_q4_0_q8_0_pq": (I, [P, I64, I64, P, I64, P, P]),
         "q4_0_repack": (I, [P, I64, I64, P, P]),
+        "q4_0_get_rows": (I, [P, I64, I64, P, I64, P, P]),
         "mul_mat_q4_0_q8_0_multi": (I, [ctypes.c_int, P, P, I64, P, I64, P, P, ctypes.c_size_t, P]),
         "mul_mat_q4_0r_q8_0": (I, [P, I64, I64, P, I64, P, P]),
         "mul_mat_q4_0r_q8_0_ex": (I, [P, I64, I64, P, I64, P, P, ctypes.c_size_t, P]),
@@ -170,6 +172,18 @@ def mul_mat_q4_0_q8_0_ex(Wq: torch.Tensor, X: torch.Tensor, ws: torch.Tensor, Y:
                                       _dev(Y, torch.float32, "Y"), _dev(ws, torch.uint8, "workspace"),
                                       ws.numel(), _stream(stream)), "mul_mat_q4_0_q8_0_ex")
     return Y
+
+
+def q4_0_get_rows(Wq: torch.Tensor, K: int, ids: torch.Tensor, out: torch.Tensor | None = None,
+                  stream=None) -> torch.Tensor:
+    """Rows `ids` (int32, device) of a Q4_0 table, decoded to fp32 (n x K)."""
+    rows = _rows(Wq, K)
+    n = ids.numel()
+    if out is None:
+        out = torch.empty((n, K), dtype=torch.float32, device=Wq.device)
+    _check(lib().q4_0_get_rows(_dev(Wq, torch.uint8, "Wq"), rows, K, _dev(ids, torch.int32, "ids"), n,
+                               _dev(out, torch.float32, "out"), _stream(stream)), "q4_0_get_rows")
+    return out
 
 
 def q4_0_repack(Wq: torch.Tensor, K: int, Wr: torch.Tensor | None = None, stream=None) -> torch.Tensor:

@@ -134,6 +134,21 @@ int q4_0_repack(const void* Wq, int64_t rows, int64_t K, void* Wr, void* stream)
                                         static_cast<hipStream_t>(stream)));
 }
 
+int q4_0_get_rows(const void* Wq, int64_t rows, int64_t K, const int32_t* ids, int64_t n, float* out, void* stream) {
+    if (!Wq || !ids || !out || bad_dim(rows) || bad_dim(n) || bad_k(K) || too_big(rows, K, 1) || too_big(n, K, 4))
+        return Q4BQ_EINVAL;
+    if (!aligned(Wq, 2) || !aligned(ids, 4) || !aligned(out, 16)) return Q4BQ_EINVAL;
+    const int64_t nb = K / kQK;
+    const size_t o_bytes = static_cast<size_t>(n * K) * 4;
+    if (overlap(out, o_bytes, Wq, static_cast<size_t>(rows * nb) * kQ4Bytes) ||
+        overlap(out, o_bytes, ids, static_cast<size_t>(n) * 4))
+        return Q4BQ_EINVAL;
+    hipError_t err = hipSuccess;
+    if (!current_device(&err)) return Q4BQ_EHIP;
+    return status_of(launch_q4_0_get_rows(static_cast<const uint8_t*>(Wq), rows, nb, ids, n, out,
+                                          static_cast<hipStream_t>(stream)));
+}
+
 size_t q4bq_workspace_size(int64_t rows, int64_t K, int64_t N) {
     if (bad_dim(rows) || bad_dim(N) || bad_k(K) || too_big(N, K, 4)) return 0;
     const size_t b = act_bytes(N, K / kQK);

@@ -50,6 +50,8 @@ size_t act_bytes(int64_t N, int64_t nb);
 hipError_t launch_q4_0_quantize(const float* W, int64_t nblocks, uint8_t* Wq, hipStream_t s);
 hipError_t launch_q8_0_quantize(const float* X, int64_t nblocks, uint8_t* Xq, hipStream_t s);
 hipError_t launch_q4_0_repack(const uint8_t* Wq, int64_t nblocks, uint8_t* Wr, hipStream_t s);
+hipError_t launch_q4_0_get_rows(const uint8_t* Wq, int64_t rows, int64_t nb, const int32_t* ids, int64_t n,
+                                float* out, hipStream_t s);
 
 // fp32 X (N x K) -> internal activations, or Q8_0 blocks -> internal.
 hipError_t launch_act_from_f32(const float* X, int64_t N, int64_t nb, void* act, hipStream_t s);

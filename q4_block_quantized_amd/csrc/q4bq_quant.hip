@@ -123,6 +123,41 @@ k_q4_0_repack(const uint8_t* __restrict__ Wq, int64_t nblocks, uint8_t* __restri
     }
 }
 
+// Rows `ids` of a Q4_0 table, decoded to fp32: ggml_get_rows on Q4_0, the
+// token-embedding lookup ("llama.cpp 深度解读" section 4, and the GPT-2
+// walkthrough's wte/wpe), each element (nibble - 8) * d by section 2's decode
+// (exact in fp32).  8 lanes per block, 4 consecutive values (16 bytes) per
+// lane, so a wave writes 8 blocks = 1 KB contiguously; the output stream is 7x
+// the input.  An id outside [0, rows) gives a row of NaN.
+__global__ void __launch_bounds__(kThreads)
+k_q4_0_get_rows(const uint8_t* __restrict__ Wq, int64_t rows, int64_t nb, const int32_t* __restrict__ ids,
+                int64_t n, float* __restrict__ out) {
+    const int64_t total = n * nb;
+    const int m = threadIdx.x & 7;
+    const int64_t step = static_cast<int64_t>(gridDim.x) * (kThreads / 8);
+    for (int64_t o = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) >> 3; o < total; o += step) {
+        const int64_t i = o / nb;
+        const int64_t b = o - i * nb;
+        const int64_t id = ids[i];
+        float4 v;
+        if (id >= 0 && id < rows) {
+            const uint8_t* blk = Wq + (id * nb + b) * kQ4Bytes;
+            uint16_t dbits, q2;
+            __builtin_memcpy(&dbits, blk, 2);
+            __builtin_memcpy(&q2, blk + 2 + 2 * m, 2);  // elements 4m .. 4m+3
+            const float d = half_bits_to_float(dbits);
+            v = make_float4(static_cast<float>(static_cast<int>(q2 & 15u) - 8) * d,
+                            static_cast<float>(static_cast<int>((q2 >> 4) & 15u) - 8) * d,
+                            static_cast<float>(static_cast<int>((q2 >> 8) & 15u) - 8) * d,
+                            static_cast<float>(static_cast<int>(q2 >> 12) - 8) * d);
+        } else {
+            const float nan = __builtin_nanf("");
+            v = make_float4(nan, nan, nan, nan);
+        }
+        *reinterpret_cast<float4*>(out + o * kQK + 4 * m) = v;
+    }
+}
+
 // Prefill records are written block-major: the 8-lane group that handles
 // record o = block * N + token reads block `block` of token `token`.
 __device__ __forceinline__ int64_t act6_source(int64_t o, int64_t N, int64_t nb) {
@@ -233,6 +268,15 @@ hipError_t launch_q4_0_quantize(const float* W, int64_t nblocks, uint8_t* Wq, hi
 
 hipError_t launch_q4_0_repack(const uint8_t* Wq, int64_t nblocks, uint8_t* Wr, hipStream_t s) {
     hipLaunchKernelGGL(k_q4_0_repack, dim3(quant_grid(nblocks)), dim3(kThreads), 0, s, Wq, nblocks, Wr);
+    return hipGetLastError();
+}
+
+hipError_t launch_q4_0_get_rows(const uint8_t* Wq, int64_t rows, int64_t nb, const int32_t* ids, int64_t n,
+                                float* out, hipStream_t s) {
+    int64_t wgs = (n * nb + (kThreads / 8) - 1) / (kThreads / 8);
+    if (wgs > 16384) wgs = 16384;
+    hipLaunchKernelGGL(k_q4_0_get_rows, dim3(static_cast<uint32_t>(wgs < 1 ? 1 : wgs)), dim3(kThreads), 0, s, Wq, rows,
+                       nb, ids, n, out);
     return hipGetLastError();
 }
 

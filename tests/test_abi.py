@@ -119,6 +119,17 @@ def _bad_product_calls(L):
     yield mm(2, ptrs(A, A + 4096), i64s(4, 0), 64, B, 1, ptrs(C, C + 256), None, 0, None)     # a matrix with 0 rows
     yield mm(2, ptrs(A, A + 4096), i64s(4, 4), 48, B, 1, ptrs(C, C + 256), None, 0, None)     # K % 32 != 0
     yield mm(2, ptrs(A, A + 4096), i64s(4, 4), 64, B, 1, ptrs(C, C + 256), WS + 8, 1 << 20, None)  # workspace misaligned
+    gr = L.q4_0_get_rows
+    yield gr(None, 4, 64, B, 3, C, None)           # null table
+    yield gr(A, 4, 64, None, 3, C, None)           # null ids
+    yield gr(A, 4, 64, B, 3, None, None)           # null output
+    yield gr(A, 4, 64, B, 0, C, None)              # n < 1
+    yield gr(A, 4, 48, B, 3, C, None)              # K % 32 != 0
+    yield gr(A + 1, 4, 64, B, 3, C, None)          # Q4_0 data on an odd address
+    yield gr(A, 4, 64, B + 2, 3, C, None)          # ids not 4-byte aligned
+    yield gr(A, 4, 64, B, 3, C + 4, None)          # output not 16-byte aligned
+    yield gr(A, 4, 64, B, 3, A + 16, None)         # output overlaps the table
+    yield gr(A, 4, 64, B, 3, B - 512, None)        # output overlaps ids
     q8 = L.q8_0_quantize
     yield q8(A, 0, 64, B, None)
     yield q8(A, 4, 33, B, None)
@@ -148,4 +159,5 @@ def test_no_device_is_ehip_not_abort(L):
     assert L.q4_0_quantize(A, 4, 64, B, None) == -2
     assert L.q4_0_q8_0_block_dots(A, 4, 64, B, 1, C, None) == -2
     assert L.q4_0_repack(A, 4, 64, B, None) == -2
+    assert L.q4_0_get_rows(A, 4, 64, B, 3, C, None) == -2
     assert L.mul_mat_q4_0r_q8_0(A, 4, 64, B, 1, C, None) == -2

@@ -196,6 +196,29 @@ def test_long_rows_few_tokens(hip, orc, K):
             assert np.array_equal(host(hip.mul_mat_q4_0r_q8_0(hip.q4_0_repack(Wq, K), Xt)), Y), (rows, K, N)
 
 
+@pytest.mark.parametrize("rows,K,n", [(1, 32, 1), (37, 96, 50), (1000, 768, 7), (300, 4096, 513),
+                                      (32768, 4096, 512)])
+def test_get_rows(hip, orc, rows, K, n):
+    """Decoded rows of a Q4_0 table, bit-exact against the oracle (every
+    element (nibble - 8) * d is exact in fp32), with repeated, unordered and
+    out-of-range ids (rows of NaN).  The last case is a 32768-row table drawn
+    like the Llama-3-8B-shaped embedding table, with a 512-token batch."""
+    if rows == 32768:
+        W = inputs.weights(4, 0, rows, K)
+    else:
+        W = inputs.random_matrix(7000 + rows + K, rows, K, 0.02)
+    rng = np.random.default_rng(rows + n)
+    ids = rng.integers(-2, rows + 2, n).astype(np.int32)
+    ids[: min(n, 3)] = [0, rows - 1, 0][: min(n, 3)]
+    print("get_rows rows=%d K=%d n=%d" % (rows, K, n), flush=True)
+    got = host(hip.q4_0_get_rows(hip.q4_0_quantize(dev(W)), K, dev(ids)))
+    want = orc.q4_0_get_rows(orc.q4_0_quantize(W), K, ids)
+    assert got.shape == (n, K)
+    assert np.array_equal(got, want, equal_nan=True)
+    bad = (ids < 0) | (ids >= rows)
+    assert np.all(np.isnan(got[bad])) and not np.any(np.isnan(got[~bad]))
+
+
 def test_unaligned_but_valid_pointers(hip, orc):
     """Q4_0 data may start on any 2-byte boundary, fp32 data on any 4-byte one."""
     rows, K, N = 65, 4096, 3
