@@ -53,7 +53,7 @@ int run_product(WLayout lay, const uint8_t* Wq, int64_t rows, int64_t K, const f
     if (N <= kGemvMaxN)
         err = launch_gemv(dev, lay, Wq, rows, nb, ws, N, Y, D, s);
     else
-        err = launch_gemm(dev, lay, Wq, rows, nb, ws, N, Y, D, s);
+        err = launch_prefill(dev, lay, Wq, rows, nb, ws, N, Y, D, s);
     return status_of(err);
 }
 
@@ -280,7 +280,7 @@ int mul_mat_q4_0_q8_0_multi(int count, const void* const* Wq, const int64_t* row
             err = launch_gemv_multi(dev, md, nb, nullptr, ws, N, s);
         } else {
             for (int i = 0; i < count && err == hipSuccess; ++i)
-                err = launch_gemm(dev, kAoS, md.w[i], rows[i], nb, ws, N, md.y[i], nullptr, s);
+                err = launch_prefill(dev, kAoS, md.w[i], rows[i], nb, ws, N, md.y[i], nullptr, s);
         }
     }
     if (!workspace && hipFreeAsync(ws, s) != hipSuccess) return Q4BQ_EHIP;
@@ -326,7 +326,7 @@ int mul_mat_q4_0_q8_0_prepared(const void* Wq, int64_t rows, int64_t K, const vo
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const uint8_t* w = static_cast<const uint8_t*>(Wq);
     err = N <= kGemvMaxN ? launch_gemv(dev, kAoS, w, rows, nb, workspace, N, Y, nullptr, s)
-                         : launch_gemm(dev, kAoS, w, rows, nb, workspace, N, Y, nullptr, s);
+                         : launch_prefill(dev, kAoS, w, rows, nb, workspace, N, Y, nullptr, s);
     return status_of(err);
 }
 

@@ -90,9 +90,10 @@ hipError_t launch_rows_x(const DeviceInfo* dev, int lay, const uint8_t* Wq, int6
 hipError_t launch_rows_act(const DeviceInfo* dev, int lay, const uint8_t* Wq, int64_t rows, int64_t nb,
                            const void* act, int64_t N, float* Y, const MultiDesc& md, hipStream_t s);
 
-// Matrix-core kernel, any N.  D as above.
-hipError_t launch_gemm(const DeviceInfo* dev, WLayout lay, const uint8_t* Wq, int64_t rows, int64_t nb,
-                       const void* act, int64_t N, float* Y, int32_t* D, hipStream_t s);
+// Matrix-core kernel (128-token x 224-row tiles), any N; the one the library
+// runs above kGemvMaxN.  D as above.
+hipError_t launch_prefill(const DeviceInfo* dev, WLayout lay, const uint8_t* Wq, int64_t rows, int64_t nb,
+                          const void* act, int64_t N, float* Y, int32_t* D, hipStream_t s);
 
 constexpr int64_t kGemvMaxN = 8;
 

@@ -1,0 +1,353 @@
+// Prefill product on the matrix cores, N > 8 tokens: compute waves and staging
+// waves.
+//
+// Same arithmetic as the decode kernels ("llama.cpp 深度解读", luoboask.github.io,
+// section 3 "量化矩阵乘法 — 核心算子": per 32-value block the integer dot of
+// (nibble - 8) with the int8 activations, then the fp32 scale d_w * d_x, the
+// scaled block terms summed in fp32), organised as a tiled GEMM:
+//  * the block dot runs on the fp6 matrix cores, exactly: the weights enter as
+//    e2m3 codes of (nibble - 8)/8, the activations as e2m3 codes of h/2 and l/2
+//    (y = 16h + l), with E8M0 block scales; one
+//    v_mfma_scale_f32_32x32x64_f8f6f4 yields s for a 32-token x 32-row tile as
+//    an exact fp32 integer;
+//  * the 1024 scale products d_x * d_w of a tile come from one
+//    v_mfma_f32_32x32x8_f16 outer product (binary16 x binary16 is exact in
+//    fp32), so each (token, row, block) costs one FMA on the vector ALU;
+//  * an fp6 operand occupies 6 of the 8 dwords that two 16-byte LDS reads
+//    fetch; the 7th carries the block's binary16 scale bits and the 8th is
+//    zero, so the same two reads also deliver the scale-product operand;
+//  * LDS layouts are swizzled so that a 16-byte read or write serves 16 lanes
+//    per cycle from 64 banks without conflicts: activation records
+//    ([block][token][64 bytes], from the quantizer) keep 16-byte quarter q of
+//    token t at position q ^ ((t >> 2) & 3); weight records (32 bytes per
+//    (row, block): 6 dwords of codes, d bits, zero) swap their two halves in
+//    rows with bit 3 set.
+//
+// Shape: a workgroup computes 128 tokens x 224 rows.  224 = 7 x 32 makes
+// 14336-row matrices split into 64 row tiles, so the 512-token prefill is 256
+// workgroups: every CU gets one.  Eight waves, two per SIMD:
+//  * waves 0-3 compute: wave w owns tokens 32w..32w+31 against all 7 row
+//    tiles, holds the 7 accumulator tiles (112 registers) and runs a software
+//    pipeline over its tile steps -- the two matrix instructions of step k are
+//    issued before the 16 FMAs that drain step k - 1, so the matrix core and
+//    the vector ALU work side by side;
+//  * waves 4-7 stage: activation records go from global memory straight into
+//    LDS (global_load_lds), Q4_0 blocks are loaded into registers and
+//    converted into fp6 weight records, ahead of the compute.
+// LDS: a ring of 4 stages x (16 KB activations + 14 KB weights) of 2 blocks;
+// one workgroup barrier per stage hands a stage from the staging waves to the
+// compute waves.
+#include "q4bq_device.h"
+#include "q4bq_internal.h"
+
+namespace q4bq {
+
+namespace {
+
+constexpr int kCW = 4;                     // compute waves (one per SIMD)
+constexpr int kT = 64 * 2 * kCW;           // threads: compute + staging waves
+constexpr int kTT = 32 * kCW;              // tokens per workgroup tile
+constexpr int kRT = 7;                     // 32-row tiles per workgroup tile
+constexpr int kTR = 32 * kRT;              // rows per workgroup tile
+constexpr int kKB = 2;                     // blocks per stage
+constexpr int kNS = 4;                     // stages in the LDS ring
+constexpr int kRecW = 32;                  // LDS bytes per (row, block)
+constexpr int kPlaneA = kTT * kAct6Bytes;  // one block of the token tile (8 KB)
+constexpr int kPlaneB = kTR * kRecW;       // one block of the row tile (7 KB)
+constexpr int kBufA = kKB * kPlaneA;
+constexpr int kBufB = kKB * kPlaneB;
+constexpr int kStage = kBufA + kBufB;
+constexpr int kST = kT / 2;  // staging threads
+// global_load_lds moves 16 bytes per lane: one instruction fills 16 tokens of
+// one block plane; staging wave sw moves tokens 32sw..32sw+31 of each plane.
+constexpr int kDma = kKB * 2;
+static_assert(kNS * kStage <= 160 * 1024, "LDS budget");
+static_assert(kDma * kCW * 16 == kKB * kTT, "activation staging covers the planes");
+static_assert(kTR <= kST, "one weight row per staging thread");
+
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// E8M0 block scales: 127 is x1.
+constexpr int kScaleW = 130;       // weights hold (nibble - 8) / 8
+constexpr int kScaleHi = 127 + 5;  // activation high part holds h / 2, weight 16 h
+constexpr int kScaleLo = 128;      // activation low part holds l / 2
+// Both K halves of the scale-product instruction hold d in their first slot,
+// so it returns 2 * d_x * d_w; the block dot is taken 2 times smaller to match.
+constexpr int kScaleDown = 1;
+
+struct Operand {
+    u32x4 lo;
+    u32x4 hi;
+};
+
+__device__ __forceinline__ Operand lds_operand(const uint8_t* p0, const uint8_t* p1) {
+    Operand o;
+    o.lo = *reinterpret_cast<const u32x4*>(p0);
+    o.hi = *reinterpret_cast<const u32x4*>(p1);
+    return o;
+}
+
+__device__ __forceinline__ i32x8 fp6_operand(const Operand& o) {
+    return i32x8{static_cast<int>(o.lo.x), static_cast<int>(o.lo.y), static_cast<int>(o.lo.z),
+                 static_cast<int>(o.lo.w), static_cast<int>(o.hi.x), static_cast<int>(o.hi.y),
+                 static_cast<int>(o.hi.z), static_cast<int>(o.hi.w)};
+}
+
+__device__ __forceinline__ f16x4 scale_operand(const Operand& o) {
+    return __builtin_bit_cast(f16x4, u32x2{o.hi.z, o.hi.w});
+}
+
+// global_load_lds_dwordx4: 16 bytes per lane from src into LDS at dst + 16 *
+// lane (dst wave-uniform, through M0).  Written as inline assembly so that
+// the compiler does not track it: it would otherwise wait for these loads
+// before unrelated LDS reads.  The caller waits for them explicitly
+// (s_waitcnt vmcnt) before the data is read; loads complete in order, and
+// every load the compiler does track that is issued later is waited for with
+// a count that then also covers these.
+__device__ __forceinline__ void dma16(const uint8_t* src, const uint8_t* dst) {
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(
+        static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint8_t*)dst)));
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(lds), "v"(src) : "memory", "m0");
+}
+
+// LDS writes done, at most `vm` global loads still in flight (vmcnt(vm),
+// lgkmcnt(0)), then the workgroup barrier.
+template <int vm>
+__device__ __forceinline__ void stage_barrier() {
+    static_assert(vm >= 0 && vm < 64, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt((vm & 0xF) | ((vm >> 4) << 14) | 0x0070);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <bool DOTS, bool RP>
+__global__ void __launch_bounds__(kT)
+k_prefill(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const uint8_t* __restrict__ act, int64_t N,
+          float* __restrict__ Y, int32_t* __restrict__ D) {
+    __shared__ __align__(16) uint8_t smem[kNS * kStage];
+
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int64_t ntt = (N + kTT - 1) / kTT;
+    const int64_t n0 = static_cast<int64_t>(blockIdx.x % ntt) * kTT;
+    const int64_t r0 = static_cast<int64_t>(blockIdx.x / ntt) * kTR;
+    const int nst = (nb + kKB - 1) / kKB;
+
+    if (wave >= kCW) {
+        // ====================== staging waves ====================================
+        const int sw = wave - kCW;
+        const int u = t - kST;  // staging thread 0..255
+        // activations; in LDS, 16-byte quarter q of token t sits at position
+        // q ^ ((t >> 2) & 3) of its record
+        const int dq = (lane & 3) ^ ((lane >> 4) & 3);
+        int64_t dma_off[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            int64_t tok = n0 + sw * 32 + e * 16 + (lane >> 2);
+            if (tok > N - 1) tok = N - 1;  // padding tokens: any valid record, never stored
+            dma_off[e] = tok * kAct6Bytes + dq * 16;
+        }
+        auto issue_dma = [&](int st) __attribute__((always_inline)) {
+            uint8_t* sA = smem + (st % kNS) * kStage;
+#pragma unroll
+            for (int i = 0; i < kDma; ++i) {
+                const int blk = i >> 1, e = i & 1;
+                int b = st * kKB + blk;
+                if (b > nb - 1) b = nb - 1;  // past the end: neutralised by zero weight scales
+                const uint8_t* src = act + static_cast<int64_t>(b) * N * kAct6Bytes + dma_off[e];
+                dma16(src, sA + blk * kPlaneA + (sw * 32 + e * 16) * kAct6Bytes);
+            }
+        };
+        // weights: staging thread u < 224 converts row u's blocks of a stage.
+        // LDS record: 6 dwords of fp6 codes, binary16 d bits, zero; the two
+        // 16-byte halves swap places in rows with bit 3 set.
+        const bool w_thread = u < kTR;
+        const int w_row = w_thread ? u : 0;
+        const bool w_row_ok = w_thread && r0 + w_row < rows;
+        const int64_t w_row_first = (r0 + (w_row_ok ? w_row : 0)) * nb;
+        const uint8_t* w_src = Wq + w_row_first * (RP ? 16 : kQ4Bytes);
+        const uint8_t* w_sc = Wq + (RP ? rows * nb * 16 + w_row_first * 2 : 0);
+        const int w_swap = (w_row >> 3) & 1;
+        Block4 rw[2][kKB];
+        bool rw_ok[2][kKB];
+        // loads are unconditional (block 0 of a valid row when the wanted block
+        // does not exist) so that the wait counts below stay exact
+        auto load_w = [&](int st, auto set) __attribute__((always_inline)) {
+            constexpr int S = decltype(set)::value;
+#pragma unroll
+            for (int k = 0; k < kKB; ++k) {
+                const int b = st * kKB + k;
+                rw_ok[S][k] = w_row_ok && b < nb;
+                const int64_t bo = rw_ok[S][k] ? b : 0;
+                rw[S][k] = RP ? load_block_rp(w_src + bo * 16, w_sc + bo * 2) : load_block(w_src + bo * kQ4Bytes);
+            }
+        };
+        auto store_w = [&](int st, auto set) __attribute__((always_inline)) {
+            constexpr int S = decltype(set)::value;
+            if (!w_thread) return;
+            uint8_t* sB = smem + (st % kNS) * kStage + kBufA;
+#pragma unroll
+            for (int k = 0; k < kKB; ++k) {
+                uint32_t d6[6] = {0u, 0u, 0u, 0u, 0u, 0u};
+                uint32_t dbits = 0u;  // zero scale: the block contributes nothing
+                if (rw_ok[S][k]) {
+                    weight_fp6(rw[S][k].qs, d6);
+                    dbits = rw[S][k].dbits;
+                }
+                uint8_t* p = sB + k * kPlaneB + w_row * kRecW;
+                *reinterpret_cast<u32x4*>(p + 16 * w_swap) = u32x4{d6[0], d6[1], d6[2], d6[3]};
+                *reinterpret_cast<u32x4*>(p + 16 * (w_swap ^ 1)) = u32x4{d6[4], d6[5], dbits, 0u};
+            }
+        };
+        // per stage a staging thread issues kDma activation loads and two loads
+        // per weight block
+        constexpr int kLoads = kDma + 2 * kKB;
+        static_assert(2 * kLoads < 64, "vmcnt range");
+
+        // stages 0 and 1 ready before the loop
+        load_w(0, std::integral_constant<int, 0>{});
+        load_w(1, std::integral_constant<int, 1>{});
+        issue_dma(0);
+        issue_dma(1);
+        store_w(0, std::integral_constant<int, 0>{});
+        stage_barrier<0>();
+        // iteration i (while stage i is computed): stage i + 2's raw weights
+        // and activations go out; stage i + 1's weights, loaded during
+        // iteration i - 1, are converted into its records
+        auto step = [&](int i, auto set) __attribute__((always_inline)) {
+            constexpr int S = decltype(set)::value;  // i % 2: held stage i, already converted
+            constexpr std::integral_constant<int, S ^ 1> other{};
+            load_w(i + 2, set);
+            store_w(i + 1, other);  // waits for stage i + 1's weight loads and all before them
+            issue_dma(i + 2);
+            // everything up to stage i + 1 has landed; only this iteration's
+            // loads may still be in flight
+            stage_barrier<kLoads>();
+        };
+        for (int i = 0; i < nst; i += 2) {
+            step(i, std::integral_constant<int, 0>{});
+            if (i + 1 < nst) step(i + 1, std::integral_constant<int, 1>{});
+        }
+        return;
+    }
+
+    // ======================== compute waves ======================================
+    const int l32 = lane & 31;
+    const int half = lane >> 5;
+    const int a_sw = (l32 >> 2) & 3;
+    const int a_row = (wave * 32 + l32) * kAct6Bytes;
+    const int a_p0 = a_row + 16 * ((2 * half) ^ a_sw);
+    const int a_p1 = a_row + 16 * ((2 * half + 1) ^ a_sw);
+    const int b_sw = (l32 >> 3) & 1;
+    const int b_row = l32 * kRecW;
+    const int b_p0 = b_row + 16 * b_sw;
+    const int b_p1 = b_row + 16 * (b_sw ^ 1);
+
+    f32x16 acc[kRT];
+#pragma unroll
+    for (int j = 0; j < kRT; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[j][v] = 0.0f;
+    const f32x16 zero = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    // two result sets: step k's matrix instructions fill set k & 1 while the
+    // FMAs of step k - 1 drain the other (a first drain of 0 * 0 is harmless)
+    f32x16 sr[2] = {zero, zero}, pr[2] = {zero, zero};
+    const int scale_a = (half ? kScaleLo : kScaleHi) - (DOTS ? 0 : kScaleDown);
+
+    // One stage: kKB blocks x 7 row tiles, unrolled.  Step k reads the next
+    // step's operands (one step ahead: a ring of two), issues its own two
+    // matrix instructions into result set k & 1, then the FMAs that drain set
+    // (k - 1) & 1, the previous step's tile.  The step count per stage is even,
+    // so the parity carries across stages.
+    auto compute = [&](int st) __attribute__((always_inline)) {
+        constexpr int kSteps = kKB * kRT;
+        static_assert(kSteps % 2 == 0, "result-set parity across stages");
+        const uint8_t* sA = smem + (st % kNS) * kStage;
+        const uint8_t* sB = sA + kBufA;
+        Operand a[2], w[2];
+        a[0] = lds_operand(sA + a_p0, sA + a_p1);
+        w[0] = lds_operand(sB + b_p0, sB + b_p1);
+#pragma unroll
+        for (int k = 0; k < kSteps; ++k) {
+            const int blk = k / kRT, j = k % kRT;
+            if (k + 1 < kSteps) {
+                const int nblk = (k + 1) / kRT, nj = (k + 1) % kRT;
+                const uint8_t* pb = sB + nblk * kPlaneB + nj * 32 * kRecW;
+                w[(k + 1) & 1] = lds_operand(pb + b_p0, pb + b_p1);
+                if (nj == 0) {
+                    const uint8_t* pa = sA + nblk * kPlaneA;
+                    a[nblk & 1] = lds_operand(pa + a_p0, pa + a_p1);
+                }
+            }
+            const Operand& ak = a[blk & 1];
+            const Operand& wk = w[k & 1];
+            const int cur = k & 1;
+            sr[cur] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fp6_operand(ak), fp6_operand(wk), zero, 2, 2,
+                                                                      0, scale_a, 0, kScaleW);
+            if constexpr (DOTS) {
+                const int b = st * kKB + blk;
+                const int64_t r = r0 + j * 32 + l32;
+                if (b < nb && r < rows) {
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int64_t n = n0 + wave * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+                        if (n < N) D[(n * rows + r) * nb + b] = static_cast<int32_t>(sr[cur][v]);
+                    }
+                }
+            } else {
+                pr[cur] = __builtin_amdgcn_mfma_f32_32x32x8f16(scale_operand(ak), scale_operand(wk), zero, 0, 0, 0);
+                const int pj = j == 0 ? kRT - 1 : j - 1;  // the previous step's row tile
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[pj][v] = fmaf(sr[cur ^ 1][v], pr[cur ^ 1][v], acc[pj][v]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    stage_barrier<0>();  // stages 0 and 1 staged
+    for (int i = 0; i < nst; ++i) {
+        compute(i);
+        stage_barrier<0>();
+    }
+
+    if constexpr (!DOTS) {
+        // drain the last step: row tile 6 of the last block, in set 1 (the
+        // step count is even)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[kRT - 1][v] = fmaf(sr[1][v], pr[1][v], acc[kRT - 1][v]);
+#pragma unroll
+        for (int j = 0; j < kRT; ++j) {
+            const int64_t r = r0 + j * 32 + l32;
+            if (r >= rows) continue;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int64_t n = n0 + wave * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+                if (n < N) Y[n * rows + r] = acc[j][v];
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const DeviceInfo* dev, WLayout lay, const uint8_t* Wq, int64_t rows, int64_t nb,
+                          const void* act, int64_t N, float* Y, int32_t* D, hipStream_t s) {
+    (void)dev;
+    const uint8_t* rec = static_cast<const uint8_t*>(act);
+    const dim3 grid(static_cast<uint32_t>(((rows + kTR - 1) / kTR) * ((N + kTT - 1) / kTT)));
+    const int nbi = static_cast<int>(nb);
+    if (D)
+        hipLaunchKernelGGL((k_prefill<true, false>), grid, dim3(kT), 0, s, Wq, rows, nbi, rec, N, Y, D);
+    else if (lay == kRepacked)
+        hipLaunchKernelGGL((k_prefill<false, true>), grid, dim3(kT), 0, s, Wq, rows, nbi, rec, N, Y, D);
+    else
+        hipLaunchKernelGGL((k_prefill<false, false>), grid, dim3(kT), 0, s, Wq, rows, nbi, rec, N, Y, D);
+    return hipGetLastError();
+}
+
+}  // namespace q4bq
