@@ -124,18 +124,35 @@ int mul_mat_q4_0_q8_0_prepared(const void *Wq, int64_t rows, int64_t K,
 
 /*
  * Optional one-time weight repack for the product below.  The Q4_0 blocks of
- * "llama.cpp 深度解读" section 2 ("量化数据结构 — Q4_0 格式详解") are split into
- * two streams with the same total size, rows*(K/32)*18 bytes:
+ * "llama.cpp 深度解读" section 2 ("量化数据结构 — Q4_0 格式详解") are laid out
+ * again as three streams (nblk = rows * K/32, nb = K/32):
  *   bytes [0, 16*nblk)            nibble stream: the 16 nibble bytes of block
- *                                 (r, b) at (r * K/32 + b) * 16, unchanged;
+ *                                 (r, b) at (r * nb + b) * 16, unchanged;
  *   bytes [16*nblk, 18*nblk)      scale stream: the binary16 scale of block
- *                                 (r, b) at 16*nblk + (r * K/32 + b) * 2,
- * with nblk = rows * K/32.  Every 16-byte nibble block is then aligned, so the
- * kernels read it with single 16-byte loads.  No value changes.
+ *                                 (r, b) at 16*nblk + (r * nb + b) * 2;
+ *   bytes [R, R + (nb+1)*rows*32) record stream, R = 18*nblk rounded up to a
+ *                                 multiple of 256: a 32-byte record for block
+ *                                 (r, b) at R + (b * rows + r) * 32 (block
+ *                                 major), then one plane (b = nb) of zero
+ *                                 records.  A record is 24 bytes of 6-bit
+ *                                 codes, code c at bits 6c..6c+5 (little
+ *                                 endian), then the 2 scale bytes, then 6 zero
+ *                                 bytes; code c = 4*m + i stands for element
+ *                                 8*(m/2) + 2*i + (m%2) of the block and is
+ *                                 the FP6 E2M3 encoding of (nibble - 8)/8
+ *                                 (exact: |nibble - 8| <= 8).  In rows with
+ *                                 bit 3 of r set the record's two 16-byte
+ *                                 halves are stored swapped.
+ * The bytes in [18*nblk, R) are zero.  q4bq_repack_size(rows, K) gives the
+ * total (0 for invalid sizes).  Every
+ * 16-byte nibble block is aligned, so the decode kernels read it with single
+ * 16-byte loads; the records are the matrix-core operands of the many-token
+ * kernel, converted once instead of at every use.  No value changes.
  *   Wq  rows x (K/32) Q4_0 blocks, 2-byte aligned.
- *   Wr  rows*(K/32)*18 bytes, 16-byte aligned, must not overlap Wq.
+ *   Wr  q4bq_repack_size(rows, K) bytes, 16-byte aligned, must not overlap Wq.
  * Requires rows >= 1, K >= 32, K % 32 == 0.
  */
+size_t q4bq_repack_size(int64_t rows, int64_t K);
 int q4_0_repack(const void *Wq, int64_t rows, int64_t K, void *Wr, void *stream);
 
 /*

@@ -30,7 +30,7 @@ EXPORTS = (
     "mul_mat_q4_0_q8_0_ex", "mul_mat_q4_0_q8_0_pq", "q4_0_q8_0_block_dots",
     "q4bq_status_string", "q4bq_version", "q4bq_quantize_activations", "mul_mat_q4_0_q8_0_prepared",
     "q4_0_repack", "mul_mat_q4_0r_q8_0", "mul_mat_q4_0r_q8_0_ex", "mul_mat_q4_0_q8_0_multi",
-    "q4_0_get_rows",
+    "q4_0_get_rows", "q4bq_repack_size",
 )
 
 
@@ -60,6 +60,7 @@ def lib() -> ctypes.CDLL:
         "mul_mat_q4_0_q8_0_ex": (I, [P, I64, I64, P, I64, P, P, ctypes.c_size_t, P]),
         "mul_mat_q4_0_q8_0_pq": (I, [P, I64, I64, P, I64, P, P]),
         "q4_0_repack": (I, [P, I64, I64, P, P]),
+        "q4bq_repack_size": (ctypes.c_size_t, [I64, I64]),
         "q4_0_get_rows": (I, [P, I64, I64, P, I64, P, P]),
         "mul_mat_q4_0_q8_0_multi": (I, [ctypes.c_int, P, P, I64, P, I64, P, P, ctypes.c_size_t, P]),
         "mul_mat_q4_0r_q8_0": (I, [P, I64, I64, P, I64, P, P]),
@@ -140,6 +141,22 @@ def _rows(Wq: torch.Tensor, K: int) -> int:
     return Wq.numel() // (nb * Q4_0_BYTES)
 
 
+def q4bq_repack_size(rows: int, K: int) -> int:
+    return int(lib().q4bq_repack_size(rows, K))
+
+
+def _repacked_rows(Wr: torch.Tensor, K: int) -> int:
+    """The row count whose repacked size is Wr's byte count."""
+    nb = _nb(K)
+    n = Wr.numel()
+    r = n // (nb * Q4_0_BYTES + (nb + 1) * 32)  # at most a few rows above the answer (alignment padding)
+    while r > 0 and q4bq_repack_size(r, K) > n:
+        r -= 1
+    if r < 1 or q4bq_repack_size(r, K) != n:
+        raise ValueError("Wr size %d is not a repacked matrix of K=%d" % (n, K))
+    return r
+
+
 def mul_mat_q4_0_q8_0(Wq: torch.Tensor, X: torch.Tensor, Y: torch.Tensor | None = None,
                       stream=None) -> torch.Tensor:
     """Y (N x rows, fp32) = Q4_0 weights Wq times fp32 activations X (N x K)."""
@@ -187,10 +204,14 @@ def q4_0_get_rows(Wq: torch.Tensor, K: int, ids: torch.Tensor, out: torch.Tensor
 
 
 def q4_0_repack(Wq: torch.Tensor, K: int, Wr: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """Q4_0 blocks -> repacked weights (nibble stream, then scale stream; same byte count)."""
+    """Q4_0 blocks -> repacked weights (nibble stream, scale stream, matrix-core
+    weight records; q4bq_repack_size bytes)."""
     rows = _rows(Wq, K)
     if Wr is None:
-        Wr = torch.empty(Wq.numel(), dtype=torch.uint8, device=Wq.device)  # the allocator aligns to 256 bytes
+        n = lib().q4bq_repack_size(rows, K)
+        if n == 0:
+            raise Q4BQError(Q4BQ_EINVAL, "q4bq_repack_size")
+        Wr = torch.empty(n, dtype=torch.uint8, device=Wq.device)  # the allocator aligns to 256 bytes
     _check(lib().q4_0_repack(_dev(Wq, torch.uint8, "Wq"), rows, K, _dev(Wr, torch.uint8, "Wr"), _stream(stream)),
            "q4_0_repack")
     return Wr
@@ -200,7 +221,7 @@ def mul_mat_q4_0r_q8_0(Wr: torch.Tensor, X: torch.Tensor, Y: torch.Tensor | None
                        stream=None) -> torch.Tensor:
     """mul_mat_q4_0_q8_0 on repacked weights."""
     N, K = X.shape
-    rows = _rows(Wr, K)
+    rows = _repacked_rows(Wr, K)
     if Y is None:
         Y = torch.empty((N, rows), dtype=torch.float32, device=X.device)
     _check(lib().mul_mat_q4_0r_q8_0(_dev(Wr, torch.uint8, "Wr"), rows, K, _dev(X, torch.float32, "X"), N,
@@ -211,7 +232,7 @@ def mul_mat_q4_0r_q8_0(Wr: torch.Tensor, X: torch.Tensor, Y: torch.Tensor | None
 def mul_mat_q4_0r_q8_0_ex(Wr: torch.Tensor, X: torch.Tensor, ws: torch.Tensor, Y: torch.Tensor | None = None,
                           stream=None) -> torch.Tensor:
     N, K = X.shape
-    rows = _rows(Wr, K)
+    rows = _repacked_rows(Wr, K)
     if Y is None:
         Y = torch.empty((N, rows), dtype=torch.float32, device=X.device)
     _check(lib().mul_mat_q4_0r_q8_0_ex(_dev(Wr, torch.uint8, "Wr"), rows, K, _dev(X, torch.float32, "X"), N,

@@ -122,15 +122,19 @@ int q8_0_quantize(const float* X, int64_t N, int64_t K, void* Xq, void* stream) 
     return status_of(launch_q8_0_quantize(X, nblocks, static_cast<uint8_t*>(Xq), static_cast<hipStream_t>(stream)));
 }
 
+size_t q4bq_repack_size(int64_t rows, int64_t K) {
+    if (bad_dim(rows) || bad_k(K) || too_big(rows, K + kQK, 2)) return 0;
+    return repack_bytes(rows, K / kQK);
+}
+
 int q4_0_repack(const void* Wq, int64_t rows, int64_t K, void* Wr, void* stream) {
-    if (!Wq || !Wr || bad_dim(rows) || bad_k(K) || too_big(rows, K, 1)) return Q4BQ_EINVAL;
+    if (!Wq || !Wr || bad_dim(rows) || bad_k(K) || too_big(rows, K + kQK, 2)) return Q4BQ_EINVAL;
     if (!aligned(Wq, 2) || !aligned(Wr, 16)) return Q4BQ_EINVAL;
-    const int64_t nblocks = rows * (K / kQK);
-    const size_t bytes = static_cast<size_t>(nblocks) * kQ4Bytes;
-    if (overlap(Wq, bytes, Wr, bytes)) return Q4BQ_EINVAL;
+    const int64_t nb = K / kQK;
+    if (overlap(Wq, static_cast<size_t>(rows * nb) * kQ4Bytes, Wr, repack_bytes(rows, nb))) return Q4BQ_EINVAL;
     hipError_t err = hipSuccess;
     if (!current_device(&err)) return Q4BQ_EHIP;
-    return status_of(launch_q4_0_repack(static_cast<const uint8_t*>(Wq), nblocks, static_cast<uint8_t*>(Wr),
+    return status_of(launch_q4_0_repack(static_cast<const uint8_t*>(Wq), rows, nb, static_cast<uint8_t*>(Wr),
                                         static_cast<hipStream_t>(stream)));
 }
 
@@ -174,7 +178,8 @@ int check_product(const void* Wq, int64_t rows, int64_t K, const void* Xany, Act
     if (N > kGemvMaxN && ((rows + 127) / 128) * ((N + 255) / 256) >= (int64_t(1) << 31)) return Q4BQ_EINVAL;
     const uintptr_t x_align = kind == kF32 ? 4 : kind == kQ8 ? 2 : 16;
     if (!aligned(Wq, lay == kRepacked ? 16 : 2) || !aligned(Xany, x_align) || !aligned(out, 4)) return Q4BQ_EINVAL;
-    const size_t w_bytes = static_cast<size_t>(rows * nb) * kQ4Bytes;
+    if (lay == kRepacked && too_big(rows, K + kQK, 2)) return Q4BQ_EINVAL;
+    const size_t w_bytes = lay == kRepacked ? repack_bytes(rows, nb) : static_cast<size_t>(rows * nb) * kQ4Bytes;
     const size_t x_bytes = kind == kF32 ? static_cast<size_t>(N * K) * 4
                            : kind == kQ8 ? static_cast<size_t>(N * nb) * kQ8Bytes
                                          : act_bytes(N, nb);
@@ -227,7 +232,7 @@ int mul_mat_q4_0r_q8_0_ex(const void* Wr, int64_t rows, int64_t K, const float* 
     const int64_t nb = K / kQK;
     if (overlap(workspace, need, Y, static_cast<size_t>(N * rows) * 4) ||
         overlap(workspace, need, X, static_cast<size_t>(N * K) * 4) ||
-        overlap(workspace, need, Wr, static_cast<size_t>(rows * nb) * kQ4Bytes))
+        overlap(workspace, need, Wr, repack_bytes(rows, nb)))
         return Q4BQ_EINVAL;
     return run_product(kRepacked, static_cast<const uint8_t*>(Wr), rows, K, X, nullptr, N, Y, nullptr, workspace,
                        static_cast<hipStream_t>(stream));

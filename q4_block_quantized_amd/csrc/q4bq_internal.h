@@ -49,7 +49,12 @@ size_t act_bytes(int64_t N, int64_t nb);
 
 hipError_t launch_q4_0_quantize(const float* W, int64_t nblocks, uint8_t* Wq, hipStream_t s);
 hipError_t launch_q8_0_quantize(const float* X, int64_t nblocks, uint8_t* Xq, hipStream_t s);
-hipError_t launch_q4_0_repack(const uint8_t* Wq, int64_t nblocks, uint8_t* Wr, hipStream_t s);
+// Repacked weights: nibble stream, scale stream, then (from
+// repack_records_offset) the prefill kernel's weight records, block-major,
+// with one trailing plane of zero records; repack_bytes in all.
+int64_t repack_records_offset(int64_t rows, int64_t nb);
+size_t repack_bytes(int64_t rows, int64_t nb);
+hipError_t launch_q4_0_repack(const uint8_t* Wq, int64_t rows, int64_t nb, uint8_t* Wr, hipStream_t s);
 hipError_t launch_q4_0_get_rows(const uint8_t* Wq, int64_t rows, int64_t nb, const int32_t* ids, int64_t n,
                                 float* out, hipStream_t s);
 

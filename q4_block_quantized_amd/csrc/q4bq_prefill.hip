@@ -26,11 +26,14 @@
 // Shape: a workgroup computes 128 tokens x 224 rows.  224 = 7 x 32 makes
 // 14336-row matrices split into 64 row tiles, so the 512-token prefill is 256
 // workgroups: every CU gets one.  Eight waves, two per SIMD:
-//  * waves 0-3 compute: wave w owns tokens 32w..32w+31 against all 7 row
-//    tiles, holds the 7 accumulator tiles (112 registers) and runs a software
-//    pipeline over its tile steps -- the two matrix instructions of step k are
-//    issued before the 16 FMAs that drain step k - 1, so the matrix core and
-//    the vector ALU work side by side;
+//  * waves 0-3 compute: each owns seven of the 28 tiles of 32 tokens x 32
+//    rows -- two token tiles against three row tiles, plus one more tile --
+//    so that every weight operand read from LDS (the binding resource: about
+//    128 bytes per clock per CU) serves two tiles; a wave holds its 7
+//    accumulator tiles (112 registers) and runs a software pipeline over its
+//    tile steps -- the two matrix instructions of step k are issued around the
+//    16 FMAs that drain step k - 1, so the matrix core and the vector ALU work
+//    side by side;
 //  * waves 4-7 stage: activation records go from global memory straight into
 //    LDS (global_load_lds), Q4_0 blocks are loaded into registers and
 //    converted into fp6 weight records, ahead of the compute.
@@ -110,7 +113,7 @@ __device__ __forceinline__ f16x4 scale_operand(const Operand& o) {
 __device__ __forceinline__ void dma16(const uint8_t* src, const uint8_t* dst) {
     const uint32_t lds = __builtin_amdgcn_readfirstlane(
         static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint8_t*)dst)));
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(lds), "v"(src) : "memory", "m0");
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(lds), "v"(src) : "memory", "m0");
 }
 
 // LDS writes done, at most `vm` global loads still in flight (vmcnt(vm),
@@ -124,18 +127,71 @@ __device__ __forceinline__ void stage_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// Workgroups are dealt to the 8 XCDs round-robin (workgroup x runs on XCD
+// x % 8), and each XCD has its own L2.  Tile order puts the token tiles of one
+// row tile next to each other; this map gives every XCD a contiguous range of
+// tiles, so the token tiles that read the same weights share one L2.
+__device__ __forceinline__ int64_t xcd_tile(uint32_t x, uint32_t grid) {
+    constexpr uint32_t kXcd = 8;
+    const uint32_t q = grid / kXcd, rem = grid % kXcd, j = x % kXcd;
+    return static_cast<int64_t>(j * q + (j < rem ? j : rem) + x / kXcd);
+}
+
+// One tile step of the product: the block dot and the scale products of the
+// current tile go into result set (sr_cur, pr_cur), and 16 FMAs fold the
+// previous tile's set, issued a whole step earlier, into its accumulator.
+// SPLIT places the scale products first and the FMAs around the block dot, so
+// the vector ALU works while the matrix core does: the better order when the
+// compute waves have their SIMDs to themselves (records staged by DMA).  With
+// the staging waves converting weights on the same SIMDs, the plain order
+// (both matrix instructions, then the FMAs) is the faster one.
+template <bool SPLIT>
+__device__ __forceinline__ void tile_step(const Operand& ak, const Operand& wk, int scale_a, f32x16& sr_cur,
+                                          f32x16& pr_cur, const f32x16& sr_prev, const f32x16& pr_prev,
+                                          f32x16& acc_prev) {
+    const f32x16 zero = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if constexpr (!SPLIT) {
+        sr_cur = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fp6_operand(ak), fp6_operand(wk), zero, 2, 2, 0,
+                                                                 scale_a, 0, kScaleW);
+        pr_cur = __builtin_amdgcn_mfma_f32_32x32x8f16(scale_operand(ak), scale_operand(wk), zero, 0, 0, 0);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc_prev[v] = fmaf(sr_prev[v], pr_prev[v], acc_prev[v]);
+        return;
+    }
+    pr_cur = __builtin_amdgcn_mfma_f32_32x32x8f16(scale_operand(ak), scale_operand(wk), zero, 0, 0, 0);
+#pragma unroll
+    for (int v = 0; v < 8; ++v) acc_prev[v] = fmaf(sr_prev[v], pr_prev[v], acc_prev[v]);
+    sr_cur = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fp6_operand(ak), fp6_operand(wk), zero, 2, 2, 0, scale_a,
+                                                             0, kScaleW);
+#pragma unroll
+    for (int v = 8; v < 16; ++v) acc_prev[v] = fmaf(sr_prev[v], pr_prev[v], acc_prev[v]);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // LDS reads ahead
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // scale-product MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // FMAs
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // block-dot MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);  // FMAs, operand moves
+}
+
+// Weight records of one stage: kKB planes of kPlaneB bytes, each a contiguous
+// run of the repacked record stream, moved by kRecDma wave instructions of 1 KB
+// dealt round-robin to the staging waves.
+constexpr int kRecDma = kBufB / 1024;
+static_assert(kBufB % 1024 == 0 && kPlaneB % 16 == 0, "record staging in 1 KB wave moves");
+static_assert(kTR % 16 == 0, "row tiles keep the record swizzle (bit 3 of the row)");
+
 template <bool DOTS, bool RP>
 __global__ void __launch_bounds__(kT)
-k_prefill(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const uint8_t* __restrict__ act, int64_t N,
-          float* __restrict__ Y, int32_t* __restrict__ D) {
+k_prefill(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Wrec, int64_t rows, int nb,
+          const uint8_t* __restrict__ act, int64_t N, float* __restrict__ Y, int32_t* __restrict__ D) {
     __shared__ __align__(16) uint8_t smem[kNS * kStage];
 
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int64_t ntt = (N + kTT - 1) / kTT;
-    const int64_t n0 = static_cast<int64_t>(blockIdx.x % ntt) * kTT;
-    const int64_t r0 = static_cast<int64_t>(blockIdx.x / ntt) * kTR;
+    const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
+    const int64_t n0 = (tile % ntt) * kTT;
+    const int64_t r0 = (tile / ntt) * kTR;
     const int nst = (nb + kKB - 1) / kKB;
 
     if (wave >= kCW) {
@@ -163,6 +219,63 @@ k_prefill(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const uint8_t* _
                 dma16(src, sA + blk * kPlaneA + (sw * 32 + e * 16) * kAct6Bytes);
             }
         };
+        if constexpr (RP) {
+            // Pre-converted records: the weights go straight into LDS as well,
+            // three stages ahead (the ring slot of stage i + 3 is the one
+            // stage i - 1 used).  Staging wave sw issues instructions g = sw,
+            // sw + 4, ... < kRecDma; lane l of instruction g moves 16-byte
+            // piece q = (g % 7) * 64 + l of plane g / 7: half q & 1 of row q / 2
+            // (rows past the end read the last row: their outputs are never
+            // stored).  Blocks past the end read the zero plane (block nb).
+            constexpr int kPer = (kRecDma + kCW - 1) / kCW;
+            const int nrec = (kRecDma - sw + kCW - 1) / kCW;  // 4 or 3
+            int64_t rec_off[kPer];
+            int rec_blk[kPer];
+#pragma unroll
+            for (int m = 0; m < kPer; ++m) {
+                const int g = sw + kCW * m < kRecDma ? sw + kCW * m : sw;
+                const int q = (g % (kPlaneB / 1024)) * 64 + lane;
+                int64_t r = r0 + (q >> 1);
+                if (r > rows - 1) r = rows - 1;
+                rec_off[m] = r * kRecW + (q & 1) * 16;
+                rec_blk[m] = g / (kPlaneB / 1024);
+            }
+            auto issue_rec = [&](int st) __attribute__((always_inline)) {
+                uint8_t* sB = smem + (st % kNS) * kStage + kBufA;
+#pragma unroll
+                for (int m = 0; m < kPer; ++m) {
+                    if (m < nrec) {  // wave-uniform
+                        int b = st * kKB + rec_blk[m];
+                        if (b > nb) b = nb;
+                        const int g = sw + kCW * m;
+                        dma16(Wrec + static_cast<int64_t>(b) * rows * kRecW + rec_off[m], sB + g * 1024);
+                    }
+                }
+            };
+            auto run = [&](auto per) __attribute__((always_inline)) {
+                constexpr int L = kDma + decltype(per)::value;  // loads per stage for this wave
+                issue_rec(0);
+                issue_dma(0);
+                issue_rec(1);
+                issue_dma(1);
+                issue_rec(2);
+                issue_dma(2);
+                stage_barrier<2 * L>();  // stage 0 landed
+                for (int i = 0; i < nst; ++i) {
+                    issue_rec(i + 3);
+                    issue_dma(i + 3);
+                    stage_barrier<2 * L>();  // stage i + 1 landed
+                }
+            };
+            static_assert(kNS >= 4, "three stages ahead need four ring slots");
+            static_assert(2 * (kDma + kPer) < 64, "vmcnt range");
+            if (nrec == kPer)
+                run(std::integral_constant<int, kPer>{});
+            else
+                run(std::integral_constant<int, kPer - 1>{});
+            __builtin_amdgcn_s_waitcnt(0);  // no LDS writes in flight when the wave ends
+            return;
+        }
         // weights: staging thread u < 224 converts row u's blocks of a stage.
         // LDS record: 6 dwords of fp6 codes, binary16 d bits, zero; the two
         // 16-byte halves swap places in rows with bit 3 set.
@@ -170,8 +283,7 @@ k_prefill(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const uint8_t* _
         const int w_row = w_thread ? u : 0;
         const bool w_row_ok = w_thread && r0 + w_row < rows;
         const int64_t w_row_first = (r0 + (w_row_ok ? w_row : 0)) * nb;
-        const uint8_t* w_src = Wq + w_row_first * (RP ? 16 : kQ4Bytes);
-        const uint8_t* w_sc = Wq + (RP ? rows * nb * 16 + w_row_first * 2 : 0);
+        const uint8_t* w_src = Wq + w_row_first * kQ4Bytes;
         const int w_swap = (w_row >> 3) & 1;
         Block4 rw[2][kKB];
         bool rw_ok[2][kKB];
@@ -184,7 +296,7 @@ k_prefill(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const uint8_t* _
                 const int b = st * kKB + k;
                 rw_ok[S][k] = w_row_ok && b < nb;
                 const int64_t bo = rw_ok[S][k] ? b : 0;
-                rw[S][k] = RP ? load_block_rp(w_src + bo * 16, w_sc + bo * 2) : load_block(w_src + bo * kQ4Bytes);
+                rw[S][k] = load_block(w_src + bo * kQ4Bytes);
             }
         };
         auto store_w = [&](int st, auto set) __attribute__((always_inline)) {
@@ -233,105 +345,138 @@ k_prefill(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const uint8_t* _
             step(i, std::integral_constant<int, 0>{});
             if (i + 1 < nst) step(i + 1, std::integral_constant<int, 1>{});
         }
+        __builtin_amdgcn_s_waitcnt(0);
         return;
     }
 
     // ======================== compute waves ======================================
+    // Wave w takes token tiles A = 2 (w >> 1) and B = A + 1 and, by rh = w & 1,
+    // row tiles 4 rh, 4 rh + 1, 4 rh + 2 for both of them plus row tile 3 for
+    // one of them (A when rh = 0, B when rh = 1): seven 32 x 32 tiles, visited
+    // as (A, R0) (B, R0) (A, R1) (B, R1) (A, R2) (B, R2) (X, 3), so that one
+    // weight operand read from LDS serves two tiles.
     const int l32 = lane & 31;
     const int half = lane >> 5;
+    const int tp = wave >> 1;
     const int a_sw = (l32 >> 2) & 3;
-    const int a_row = (wave * 32 + l32) * kAct6Bytes;
-    const int a_p0 = a_row + 16 * ((2 * half) ^ a_sw);
-    const int a_p1 = a_row + 16 * ((2 * half + 1) ^ a_sw);
+    int a_p0[2], a_p1[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int a_row = ((2 * tp + u) * 32 + l32) * kAct6Bytes;
+        a_p0[u] = a_row + 16 * ((2 * half) ^ a_sw);
+        a_p1[u] = a_row + 16 * ((2 * half + 1) ^ a_sw);
+    }
     const int b_sw = (l32 >> 3) & 1;
     const int b_row = l32 * kRecW;
     const int b_p0 = b_row + 16 * b_sw;
     const int b_p1 = b_row + 16 * (b_sw ^ 1);
-
-    f32x16 acc[kRT];
-#pragma unroll
-    for (int j = 0; j < kRT; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[j][v] = 0.0f;
     const f32x16 zero = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    // two result sets: step k's matrix instructions fill set k & 1 while the
-    // FMAs of step k - 1 drain the other (a first drain of 0 * 0 is harmless)
-    f32x16 sr[2] = {zero, zero}, pr[2] = {zero, zero};
     const int scale_a = (half ? kScaleLo : kScaleHi) - (DOTS ? 0 : kScaleDown);
 
-    // One stage: kKB blocks x 7 row tiles, unrolled.  Step k reads the next
-    // step's operands (one step ahead: a ring of two), issues its own two
-    // matrix instructions into result set k & 1, then the FMAs that drain set
-    // (k - 1) & 1, the previous step's tile.  The step count per stage is even,
-    // so the parity carries across stages.
-    auto compute = [&](int st) __attribute__((always_inline)) {
-        constexpr int kSteps = kKB * kRT;
-        static_assert(kSteps % 2 == 0, "result-set parity across stages");
-        const uint8_t* sA = smem + (st % kNS) * kStage;
-        const uint8_t* sB = sA + kBufA;
-        Operand a[2], w[2];
-        a[0] = lds_operand(sA + a_p0, sA + a_p1);
-        w[0] = lds_operand(sB + b_p0, sB + b_p1);
+    auto run = [&](auto rh_c) __attribute__((always_inline)) {
+        constexpr int RH = decltype(rh_c)::value;
+        constexpr int kPos = 7;                                                     // tiles per block
+        constexpr int kSeqT[kPos] = {0, 1, 0, 1, 0, 1, RH};                          // A = 0, B = 1
+        constexpr int kSeqR[kPos] = {4 * RH, 4 * RH, 4 * RH + 1, 4 * RH + 1, 4 * RH + 2, 4 * RH + 2, 3};
+        constexpr int kSeqW[kPos] = {0, 0, 1, 1, 2, 2, 3};                          // weight read of the block
+        static_assert(kPos == kRT, "seven tiles per wave");
+
+        f32x16 acc[kPos];
 #pragma unroll
-        for (int k = 0; k < kSteps; ++k) {
-            const int blk = k / kRT, j = k % kRT;
-            if (k + 1 < kSteps) {
-                const int nblk = (k + 1) / kRT, nj = (k + 1) % kRT;
-                const uint8_t* pb = sB + nblk * kPlaneB + nj * 32 * kRecW;
-                w[(k + 1) & 1] = lds_operand(pb + b_p0, pb + b_p1);
-                if (nj == 0) {
-                    const uint8_t* pa = sA + nblk * kPlaneA;
-                    a[nblk & 1] = lds_operand(pa + a_p0, pa + a_p1);
+        for (int j = 0; j < kPos; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[j][v] = 0.0f;
+        // two result sets: step k's matrix instructions fill set k & 1 while
+        // the FMAs of step k - 1 drain the other (a first drain of 0 * 0 is
+        // harmless)
+        f32x16 sr[2] = {zero, zero}, pr[2] = {zero, zero};
+
+        // One stage: kKB blocks x 7 tiles, unrolled.  Operands are read one
+        // step before their first use: the weights in a ring of two (four reads
+        // per block), the next block's token operands while the current block
+        // runs.  Step k issues its two matrix instructions into result set
+        // k & 1 and drains set (k - 1) & 1, the previous step's tile, with 16
+        // FMAs.  The step count per stage is even, so the parity carries over.
+        auto compute = [&](int st) __attribute__((always_inline)) {
+            constexpr int kSteps = kKB * kPos;
+            static_assert(kSteps % 2 == 0, "result-set parity across stages");
+            const uint8_t* sA = smem + (st % kNS) * kStage;
+            const uint8_t* sB = sA + kBufA;
+            auto w_at = [&](int blk, int p) __attribute__((always_inline)) {
+                const uint8_t* pb = sB + blk * kPlaneB + kSeqR[p] * 32 * kRecW;
+                return lds_operand(pb + b_p0, pb + b_p1);
+            };
+            auto a_at = [&](int blk, int u) __attribute__((always_inline)) {
+                const uint8_t* pa = sA + blk * kPlaneA;
+                return lds_operand(pa + a_p0[u], pa + a_p1[u]);
+            };
+            Operand a[2][2], w[2];
+            a[0][0] = a_at(0, 0);
+            a[0][1] = a_at(0, 1);
+            w[0] = w_at(0, 0);
+#pragma unroll
+            for (int k = 0; k < kSteps; ++k) {
+                const int blk = k / kPos, p = k % kPos;
+                const int g = blk * 4 + kSeqW[p];  // weight read index within the stage
+                // next step's weights, when it starts a new weight pair
+                if (k + 1 < kSteps) {
+                    const int nblk = (k + 1) / kPos, np = (k + 1) % kPos;
+                    if (np == 0 || kSeqW[np] != kSeqW[p]) w[(g + 1) & 1] = w_at(nblk, np);
                 }
-            }
-            const Operand& ak = a[blk & 1];
-            const Operand& wk = w[k & 1];
-            const int cur = k & 1;
-            sr[cur] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fp6_operand(ak), fp6_operand(wk), zero, 2, 2,
-                                                                      0, scale_a, 0, kScaleW);
-            if constexpr (DOTS) {
-                const int b = st * kKB + blk;
-                const int64_t r = r0 + j * 32 + l32;
-                if (b < nb && r < rows) {
+                // next block's token operands, early in this block
+                if (blk + 1 < kKB && (p == 2 || p == 3)) a[(blk + 1) & 1][p - 2] = a_at(blk + 1, p - 2);
+                const Operand& ak = a[blk & 1][kSeqT[p]];
+                const Operand& wk = w[g & 1];
+                const int cur = k & 1;
+                if constexpr (!DOTS) {
+                    const int pj = p == 0 ? kPos - 1 : p - 1;  // the previous step's tile
+                    tile_step<RP>(ak, wk, scale_a, sr[cur], pr[cur], sr[cur ^ 1], pr[cur ^ 1], acc[pj]);
+                } else {
+                    sr[cur] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fp6_operand(ak), fp6_operand(wk), zero,
+                                                                              2, 2, 0, scale_a, 0, kScaleW);
+                    const int b = st * kKB + blk;
+                    const int64_t r = r0 + kSeqR[p] * 32 + l32;
+                    if (b < nb && r < rows) {
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int64_t n = n0 + wave * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-                        if (n < N) D[(n * rows + r) * nb + b] = static_cast<int32_t>(sr[cur][v]);
+                        for (int v = 0; v < 16; ++v) {
+                            const int64_t n = n0 + (2 * tp + kSeqT[p]) * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+                            if (n < N) D[(n * rows + r) * nb + b] = static_cast<int32_t>(sr[cur][v]);
+                        }
                     }
                 }
-            } else {
-                pr[cur] = __builtin_amdgcn_mfma_f32_32x32x8f16(scale_operand(ak), scale_operand(wk), zero, 0, 0, 0);
-                const int pj = j == 0 ? kRT - 1 : j - 1;  // the previous step's row tile
-#pragma unroll
-                for (int v = 0; v < 16; ++v) acc[pj][v] = fmaf(sr[cur ^ 1][v], pr[cur ^ 1][v], acc[pj][v]);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_barrier(0);
+        };
+
+        stage_barrier<0>();  // the first stages staged
+        for (int i = 0; i < nst; ++i) {
+            compute(i);
+            stage_barrier<0>();
+        }
+
+        if constexpr (!DOTS) {
+            // drain the last step: tile 6 of the last block, in set 1 (the
+            // step count is even)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[kPos - 1][v] = fmaf(sr[1][v], pr[1][v], acc[kPos - 1][v]);
+#pragma unroll
+            for (int j = 0; j < kPos; ++j) {
+                const int64_t r = r0 + kSeqR[j] * 32 + l32;
+                if (r >= rows) continue;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int64_t n = n0 + (2 * tp + kSeqT[j]) * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+                    if (n < N) Y[n * rows + r] = acc[j][v];
+                }
+            }
         }
     };
-
-    stage_barrier<0>();  // stages 0 and 1 staged
-    for (int i = 0; i < nst; ++i) {
-        compute(i);
-        stage_barrier<0>();
-    }
-
-    if constexpr (!DOTS) {
-        // drain the last step: row tile 6 of the last block, in set 1 (the
-        // step count is even)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[kRT - 1][v] = fmaf(sr[1][v], pr[1][v], acc[kRT - 1][v]);
-#pragma unroll
-        for (int j = 0; j < kRT; ++j) {
-            const int64_t r = r0 + j * 32 + l32;
-            if (r >= rows) continue;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int64_t n = n0 + wave * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-                if (n < N) Y[n * rows + r] = acc[j][v];
-            }
-        }
-    }
+    if (wave & 1)
+        run(std::integral_constant<int, 1>{});
+    else
+        run(std::integral_constant<int, 0>{});
 }
+
 
 }  // namespace
 
@@ -342,11 +487,12 @@ hipError_t launch_prefill(const DeviceInfo* dev, WLayout lay, const uint8_t* Wq,
     const dim3 grid(static_cast<uint32_t>(((rows + kTR - 1) / kTR) * ((N + kTT - 1) / kTT)));
     const int nbi = static_cast<int>(nb);
     if (D)
-        hipLaunchKernelGGL((k_prefill<true, false>), grid, dim3(kT), 0, s, Wq, rows, nbi, rec, N, Y, D);
+        hipLaunchKernelGGL((k_prefill<true, false>), grid, dim3(kT), 0, s, Wq, nullptr, rows, nbi, rec, N, Y, D);
     else if (lay == kRepacked)
-        hipLaunchKernelGGL((k_prefill<false, true>), grid, dim3(kT), 0, s, Wq, rows, nbi, rec, N, Y, D);
+        hipLaunchKernelGGL((k_prefill<false, true>), grid, dim3(kT), 0, s, Wq, Wq + repack_records_offset(rows, nb),
+                           rows, nbi, rec, N, Y, D);
     else
-        hipLaunchKernelGGL((k_prefill<false, false>), grid, dim3(kT), 0, s, Wq, rows, nbi, rec, N, Y, D);
+        hipLaunchKernelGGL((k_prefill<false, false>), grid, dim3(kT), 0, s, Wq, nullptr, rows, nbi, rec, N, Y, D);
     return hipGetLastError();
 }
 

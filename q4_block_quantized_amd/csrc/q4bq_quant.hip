@@ -108,18 +108,48 @@ k_act_from_f32(const float* __restrict__ X, int64_t nblocks, uint32_t* __restric
     }
 }
 
-// The optional one-time repack: the 18-byte blocks split into a stream of
-// 16-byte nibble blocks (aligned, for plain 16-byte loads) followed by a
-// stream of the binary16 scales, both in (row, block) order.  Same bytes in
-// total; no value changes.
+// The optional one-time repack, three streams:
+//  * 16-byte nibble blocks in (row, block) order (aligned, for plain 16-byte
+//    loads in the decode kernels);
+//  * the binary16 scales in (row, block) order;
+//  * at rec_off, the matrix-core weight records of the prefill kernel, block
+//    major ([block][row], 32 bytes: 6 dwords of fp6 codes of (nibble - 8)/8,
+//    the scale bits, a zero dword; the two 16-byte halves swapped in rows with
+//    bit 3 set, the LDS order), followed by one plane of zero records that
+//    stands for blocks past the end.
+// The bytes between the scale stream and the records are zero.  No value
+// changes; the records are the kernel's own conversion, done once.
 __global__ void __launch_bounds__(kThreads)
-k_q4_0_repack(const uint8_t* __restrict__ Wq, int64_t nblocks, uint8_t* __restrict__ Wr) {
+k_q4_0_repack(const uint8_t* __restrict__ Wq, int64_t rows, int64_t nb, int64_t rec_off, uint8_t* __restrict__ Wr) {
+    const int64_t nblocks = rows * nb;
     uint16_t* sc = reinterpret_cast<uint16_t*>(Wr + nblocks * 16);
-    for (int64_t g = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; g < nblocks;
+    uint8_t* rec = Wr + rec_off;
+    const int64_t pad = rec_off - nblocks * kQ4Bytes;  // zero bytes before the records
+    for (int64_t g = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; g < nblocks + rows + pad;
          g += static_cast<int64_t>(gridDim.x) * kThreads) {
-        const Block4 b = load_block(Wq + g * kQ4Bytes);
-        *reinterpret_cast<u32x4*>(Wr + g * 16) = u32x4{b.qs[0], b.qs[1], b.qs[2], b.qs[3]};
-        sc[g] = static_cast<uint16_t>(b.dbits);
+        if (g >= nblocks + rows) {
+            Wr[nblocks * kQ4Bytes + (g - nblocks - rows)] = 0;
+            continue;
+        }
+        uint32_t d6[6] = {0u, 0u, 0u, 0u, 0u, 0u};
+        uint32_t dbits = 0u;
+        int64_t r, b;
+        if (g < nblocks) {
+            const Block4 blk = load_block(Wq + g * kQ4Bytes);
+            *reinterpret_cast<u32x4*>(Wr + g * 16) = u32x4{blk.qs[0], blk.qs[1], blk.qs[2], blk.qs[3]};
+            sc[g] = static_cast<uint16_t>(blk.dbits);
+            weight_fp6(blk.qs, d6);
+            dbits = blk.dbits;
+            r = g / nb;
+            b = g - r * nb;
+        } else {
+            r = g - nblocks;  // the zero plane
+            b = nb;
+        }
+        const int swap = static_cast<int>((r >> 3) & 1);
+        uint8_t* p = rec + (b * rows + r) * 32;
+        *reinterpret_cast<u32x4*>(p + 16 * swap) = u32x4{d6[0], d6[1], d6[2], d6[3]};
+        *reinterpret_cast<u32x4*>(p + 16 * (swap ^ 1)) = u32x4{d6[4], d6[5], dbits, 0u};
     }
 }
 
@@ -266,8 +296,15 @@ hipError_t launch_q4_0_quantize(const float* W, int64_t nblocks, uint8_t* Wq, hi
     return hipGetLastError();
 }
 
-hipError_t launch_q4_0_repack(const uint8_t* Wq, int64_t nblocks, uint8_t* Wr, hipStream_t s) {
-    hipLaunchKernelGGL(k_q4_0_repack, dim3(quant_grid(nblocks)), dim3(kThreads), 0, s, Wq, nblocks, Wr);
+int64_t repack_records_offset(int64_t rows, int64_t nb) { return (rows * nb * kQ4Bytes + 255) & ~int64_t(255); }
+
+size_t repack_bytes(int64_t rows, int64_t nb) {
+    return static_cast<size_t>(repack_records_offset(rows, nb) + (nb + 1) * rows * 32);
+}
+
+hipError_t launch_q4_0_repack(const uint8_t* Wq, int64_t rows, int64_t nb, uint8_t* Wr, hipStream_t s) {
+    hipLaunchKernelGGL(k_q4_0_repack, dim3(quant_grid(rows * nb + rows + 256)), dim3(kThreads), 0, s, Wq, rows, nb,
+                       repack_records_offset(rows, nb), Wr);
     return hipGetLastError();
 }
 

@@ -101,9 +101,11 @@ def _bad_product_calls(L):
     yield rp(A + 1, 4, 64, B, None)                # Q4_0 data on an odd address
     yield rp(A, 4, 64, B + 8, None)                # repacked output not 16-byte aligned
     yield rp(A, 4, 64, A + 16, None)               # output overlaps the input
+    yield rp(A + 256, 4, 64, A, None)              # the record stream would overlap the input
     r = L.mul_mat_q4_0r_q8_0
     yield r(A + 2, 4, 64, B, 1, C, None)           # repacked weights must be 16-byte aligned
     yield r(A, 4, 64, B, 1, A + 8, None)           # Y overlaps the weights
+    yield r(A, 4, 64, B, 1, A + 600, None)         # Y overlaps the repacked record stream
     yield r(A, 4, 48, B, 1, C, None)
     rx = L.mul_mat_q4_0r_q8_0_ex
     yield rx(A + 8, 4, 64, B, 1, C, WS, 1 << 20, None)
@@ -139,6 +141,15 @@ def _bad_product_calls(L):
 def test_bad_arguments_return_einval(L):
     for i, rc in enumerate(_bad_product_calls(L)):
         assert rc == EINVAL, "case %d returned %d" % (i, rc)
+
+
+def test_repack_size(L):
+    # nibble + scale streams (rounded up to 256 bytes), then (K/32 + 1) planes of 32-byte records
+    assert L.q4bq_repack_size(4, 64) == 256 + 3 * 4 * 32
+    assert L.q4bq_repack_size(128256, 4096) == 128256 * 128 * 18 + 129 * 128256 * 32
+    assert L.q4bq_repack_size(1, 32) == 256 + 2 * 32
+    assert L.q4bq_repack_size(0, 64) == 0
+    assert L.q4bq_repack_size(4, 48) == 0
 
 
 def test_workspace_too_small_is_enomem(L):

@@ -242,11 +242,45 @@ def test_unaligned_but_valid_pointers(hip, orc):
                  orc.mul_mat_ref(Wq_o, orc.q8_0_quantize(Xn), K), "unaligned gemm")
 
 
-def _repack_expected(Wq_h):
+def _e2m3_value(code):
+    """FP6 E2M3 (OCP MX formats): sign bit, 2 exponent bits (bias 1), 3 mantissa bits."""
+    s, e, m = code >> 5, (code >> 3) & 3, code & 7
+    v = m / 8.0 if e == 0 else (1 + m / 8.0) * 2.0 ** (e - 1)
+    return -v if s else v
+
+
+def _repack_expected(Wq_h, rows, K):
     """The repacked byte layout, written out from its definition: every block's
-    16 nibble bytes in block order, then every block's 2 scale bytes."""
-    blocks = Wq_h.reshape(-1, 18)
-    return np.concatenate([blocks[:, 2:].reshape(-1), blocks[:, :2].reshape(-1)])
+    16 nibble bytes in block order, every block's 2 scale bytes, zero padding to
+    a multiple of 256, then the block-major 32-byte records (24 bytes of E2M3
+    codes of (nibble - 8)/8, code c at bits 6c, code 4m + i for element
+    8(m//2) + 2i + m%2; the scale bytes; 6 zero bytes; 16-byte halves swapped
+    in rows with bit 3 set) and one plane of zero records."""
+    nb = K // 32
+    blocks = Wq_h.reshape(rows * nb, 18)
+    head = np.concatenate([blocks[:, 2:].reshape(-1), blocks[:, :2].reshape(-1)])
+    R = (head.size + 255) // 256 * 256
+    # element j of a block: nibble j % 2 of byte j // 2 (low first)
+    nib = np.empty((rows * nb, 32), dtype=np.int64)
+    nib[:, 0::2] = blocks[:, 2:] & 15
+    nib[:, 1::2] = blocks[:, 2:] >> 4
+    code_of = {}
+    for code in range(64):
+        code_of.setdefault(_e2m3_value(code), code)  # +0 before -0
+    lut = np.array([code_of[(n - 8) / 8.0] for n in range(16)], dtype=np.uint8)
+    c = np.arange(32)
+    elem = 8 * ((c // 4) // 2) + 2 * (c % 4) + (c // 4) % 2
+    codes = lut[nib[:, elem]]
+    bits = ((codes[:, :, None] >> np.arange(6)) & 1).astype(np.uint8).reshape(-1, 192)
+    rec = np.zeros((rows * nb, 32), dtype=np.uint8)
+    rec[:, :24] = np.packbits(bits, axis=1, bitorder="little")
+    rec[:, 24:26] = blocks[:, :2]
+    rec = rec.reshape(rows, nb, 32)
+    swap = (np.arange(rows) & 8) != 0
+    rec[swap] = np.concatenate([rec[swap][:, :, 16:], rec[swap][:, :, :16]], axis=2)
+    planes = np.zeros((nb + 1, rows, 32), dtype=np.uint8)
+    planes[:nb] = rec.transpose(1, 0, 2)
+    return np.concatenate([head, np.zeros(R - head.size, dtype=np.uint8), planes.reshape(-1)])
 
 
 @pytest.mark.parametrize("rows,K", [(1, 32), (5, 96), (129, 160), (300, 768), (1000, 4096)])
@@ -256,7 +290,7 @@ def test_repacked_weights(hip, orc, rows, K):
     W, X = _case(rows, K, 130, 777 + rows + K)
     Wq = hip.q4_0_quantize(dev(W))
     Wr = hip.q4_0_repack(Wq, K)
-    assert np.array_equal(host(Wr), _repack_expected(host(Wq))), (rows, K)
+    assert np.array_equal(host(Wr), _repack_expected(host(Wq), rows, K)), (rows, K)
     Wq_o = orc.q4_0_quantize(W)
     for N in (1, 2, 3, 8, 9, 64, 130):
         print("repacked rows=%d K=%d N=%d" % (rows, K, N), flush=True)
