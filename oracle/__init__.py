@@ -13,6 +13,7 @@ R1-R6 / G1 / G5 stated at the top of the C file.
 
 Layouts (all row-major, innermost dimension contiguous):
   W  : rows x K fp32            Wq : rows x (K/32) blocks of 18 bytes
+                                Wq8: rows x (K/32) Q8_0 weight blocks of 34 bytes
   X  : N x K fp32               Xq : N x (K/32) blocks of 34 bytes
   Y  : N x rows                 D  : N x rows x (K/32) int32
 """
@@ -67,6 +68,9 @@ def _load():
         "orc_mul_mat_ref": (None, [P, I64, I64, P, I64, P]),
         "orc_mul_mat_pages_f32": (None, [P, I64, I64, P, I64, P]),
         "orc_mul_mat": (ctypes.c_int, [P, I64, I64, P, I64, P, ctypes.c_int]),
+        "orc_block_dot_q8": (ctypes.c_int32, [P, P]),
+        "orc_block_dots_q8": (None, [P, I64, I64, P, I64, P]),
+        "orc_mul_mat_q8_ref": (None, [P, I64, I64, P, I64, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -184,6 +188,41 @@ def mul_mat_ref(Wq: np.ndarray, Xq: np.ndarray, K: int) -> np.ndarray:
     N = Xq.size // (nb * Q8_BYTES)
     Y = np.empty((N, rows), dtype=np.float64)
     _load().orc_mul_mat_ref(_ptr(Wq), rows, K, _ptr(Xq), N, _ptr(Y))
+    return Y
+
+
+def block_dot_q8(wblk: np.ndarray, xblk: np.ndarray) -> int:
+    """Integer dot of one Q8_0 weight block with one Q8_0 activation block
+    (34 bytes each): sum of int8 products, no offset."""
+    wblk = np.ascontiguousarray(wblk, dtype=np.uint8)
+    xblk = np.ascontiguousarray(xblk, dtype=np.uint8)
+    return int(_load().orc_block_dot_q8(_ptr(wblk), _ptr(xblk)))
+
+
+def block_dots_q8(Wq8: np.ndarray, Xq: np.ndarray, K: int) -> np.ndarray:
+    """int32 N x rows x (K/32): every per-block dot of Q8_0 weights with Q8_0
+    activations."""
+    Wq8 = np.ascontiguousarray(Wq8, dtype=np.uint8)
+    Xq = np.ascontiguousarray(Xq, dtype=np.uint8)
+    nb = _check_k(K)
+    rows = Wq8.size // (nb * Q8_BYTES)
+    N = Xq.size // (nb * Q8_BYTES)
+    D = np.empty((N, rows, nb), dtype=np.int32)
+    _load().orc_block_dots_q8(_ptr(Wq8), rows, K, _ptr(Xq), N, _ptr(D))
+    return D
+
+
+def mul_mat_q8_ref(Wq8: np.ndarray, Xq: np.ndarray, K: int) -> np.ndarray:
+    """fp64 N x rows for Q8_0 weights (section 1's type table lists Q8_0 as a
+    weight type; its block is the block_q8_0 of the activations): exact
+    per-block terms d_w * d_x * s summed in fp64."""
+    Wq8 = np.ascontiguousarray(Wq8, dtype=np.uint8)
+    Xq = np.ascontiguousarray(Xq, dtype=np.uint8)
+    nb = _check_k(K)
+    rows = Wq8.size // (nb * Q8_BYTES)
+    N = Xq.size // (nb * Q8_BYTES)
+    Y = np.empty((N, rows), dtype=np.float64)
+    _load().orc_mul_mat_q8_ref(_ptr(Wq8), rows, K, _ptr(Xq), N, _ptr(Y))
     return Y
 
 

@@ -18,6 +18,8 @@
  *           per block d = d_x * d_y (both fp16 widened to fp32), integer sum of
  *           nibble * int8 products, then sumf += d * sumi.  Activations are
  *           Q8_0-quantized so the dot runs in the integer domain.
+ *   [P3-1]  same page, section 1: the table of ggml quantization types, with
+ *           Q8_0 (8 bits per weight) beside Q4_0 as a weight format.
  *   [P2-mm] "解锁模型适配能力：Llama.cpp 框架下新架构开发全流程指南" (tahou.com),
  *           section "GGML 的特性与注意事项", item 2: ggml's mul_mat contracts the
  *           innermost dimension of both operands.
@@ -296,6 +298,56 @@ void orc_mul_mat_pages_f32(const uint8_t *Wq, int64_t rows, int64_t K,
                 sumf += d * (float)sumi;
             }
             Y[n * rows + r] = sumf;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Q8_0 weights ([P3-1]'s type table lists Q8_0 as a weight type next to     */
+/* Q4_0; its block is the block_q8_0 the product takes as activations: fp16  */
+/* d + 32 int8).  Weight element j is q_j * d, so the block dot is the plain */
+/* integer dot of the two int8 vectors, with no offset.                      */
+/* ------------------------------------------------------------------------ */
+
+int32_t orc_block_dot_q8(const uint8_t *wblk, const uint8_t *xblk)
+{
+    const int8_t *w = (const int8_t *)(wblk + 2);
+    const int8_t *y = (const int8_t *)(xblk + 2);
+    int32_t sumi = 0;
+    for (int j = 0; j < ORC_QK; ++j)
+        sumi += (int32_t)w[j] * (int32_t)y[j];
+    return sumi;
+}
+
+void orc_block_dots_q8(const uint8_t *Wq, int64_t rows, int64_t K,
+                       const uint8_t *Xq, int64_t N, int32_t *D)
+{
+    int64_t nb = K / ORC_QK;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t r = 0; r < rows; ++r)
+            for (int64_t b = 0; b < nb; ++b)
+                D[(n * rows + r) * nb + b] =
+                    orc_block_dot_q8(Wq + (r * nb + b) * ORC_Q8_BYTES,
+                                     Xq + (n * nb + b) * ORC_Q8_BYTES);
+}
+
+/* Y[n][r] = sum_b d_w * d_x * s over Q8_0 weight blocks, every term exact in
+ * fp64, summed in fp64 in increasing b (the same reference as for Q4_0). */
+void orc_mul_mat_q8_ref(const uint8_t *Wq, int64_t rows, int64_t K,
+                        const uint8_t *Xq, int64_t N, double *Y)
+{
+    int64_t nb = K / ORC_QK;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t r = 0; r < rows; ++r) {
+            double acc = 0.0;
+            for (int64_t b = 0; b < nb; ++b) {
+                const uint8_t *wb = Wq + (r * nb + b) * ORC_Q8_BYTES;
+                const uint8_t *xb = Xq + (n * nb + b) * ORC_Q8_BYTES;
+                double dw = (double)orc_block_d(wb);
+                double dx = (double)orc_block_d(xb);
+                acc += dw * dx * (double)orc_block_dot_q8(wb, xb);
+            }
+            Y[n * rows + r] = acc;
         }
     }
 }

@@ -424,3 +424,77 @@ def test_pages_f32_loop_within_tolerance(orc):
     Yr = orc.mul_mat_ref(Wq, Xq, 4096)
     Yf = orc.mul_mat_pages_f32(Wq, Xq, 4096).astype(np.float64)
     assert np.all(np.abs(Yf - Yr) <= 1e-4 * np.abs(Yr) + 1e-5)
+
+
+# ---------------------------------------------------------------------------
+# Q8_0 weights (section 1's type table: Q8_0 is a weight type next to Q4_0;
+# its block is the block_q8_0 the product takes as activations)
+# ---------------------------------------------------------------------------
+
+def _q8_block(d_bits, q):
+    """34 bytes: little-endian binary16 bits, then 32 int8."""
+    return np.concatenate([np.array([d_bits & 0xFF, d_bits >> 8], np.uint8),
+                           np.asarray(q, np.int64).astype(np.int8).view(np.uint8)])
+
+
+def test_q8w_block_dot_closed_form(orc):
+    """d = 1.0 (0x3C00) on both sides, w_j = j - 16 and x_j = j - 8:
+    s = sum_j (j-16)(j-8) = sum j^2 - 24 sum j + 32*128 = 10416 - 11904 + 4096
+    = 2608; with x reversed (x_j = 23 - j) the sum is -sum_j (j-16)(j-23)
+    = -(10416 - 39*496 + 32*368) = -(10416 - 19344 + 11776) = -2848.  A
+    dropped sign, a nibble decode or a reversed element order fails."""
+    j = np.arange(32)
+    w = _q8_block(0x3C00, j - 16)
+    assert orc.block_dot_q8(w, _q8_block(0x3C00, j - 8)) == 2608
+    assert orc.block_dot_q8(w, _q8_block(0x3C00, 23 - j)) == -2848
+    Y = orc.mul_mat_q8_ref(w[None], _q8_block(0x3C00, j - 8)[None], 32)
+    assert Y.shape == (1, 1) and Y[0, 0] == 2608.0
+
+
+def test_q8w_ones_block_squared(orc):
+    """The all-ones Q8_0 block of the worked examples (d = 0x2008 =
+    2^-7 * 1032/1024, every q = 127) as both weight and activation:
+    s = 32 * 127^2 = 516128 and Y = d^2 * s = (1032^2 * 516128) / 2^34 exactly
+    (an fp64 value: 20 + 20 bits of significand)."""
+    xq = hexbytes(read_golden("q8_0_ones_block.txt")["bytes"][0])
+    assert orc.block_dot_q8(xq, xq) == 32 * 127 * 127
+    Y = orc.mul_mat_q8_ref(xq[None], xq[None], 32)
+    assert Y[0, 0] == (1032 * 1032 * 516128) / 2.0 ** 34
+
+
+def test_q8w_zero_and_single_weight(orc):
+    X = inputs.random_matrix(77, 3, 64)
+    Xq = orc.q8_0_quantize(X)
+    Wq8 = orc.q8_0_quantize(np.zeros((4, 64), np.float32))
+    assert not orc.mul_mat_q8_ref(Wq8, Xq, 64).any()
+    W = np.zeros((4, 64), np.float32)
+    W[2, 37] = 0.5                      # block 1, element 5: q = 127, d = fp16(0.5/127)
+    Wq8 = orc.q8_0_quantize(W)
+    Y = orc.mul_mat_q8_ref(Wq8, Xq, 64)
+    d_w = float(Wq8.reshape(4, 2, 34)[2, 1, 0:2].copy().view(np.float16)[0])
+    xb = Xq.reshape(3, 2, 34)[:, 1]
+    d_x = xb[:, 0:2].copy().view(np.float16)[:, 0].astype(np.float64)
+    q_x = xb[:, 2 + 5].view(np.int8).astype(np.float64)
+    assert np.array_equal(Y[:, 2], d_w * d_x * 127.0 * q_x)
+    assert not Y[:, [0, 1, 3]].any()
+
+
+@pytest.mark.parametrize("rows,K,N", [(1, 32, 1), (3, 64, 2), (8, 96, 4), (5, 256, 3)])
+def test_q8w_brute_force_fp64(orc, rows, K, N):
+    """Dequantize both operands with NumPy (fp16 d via numpy.float16, int8
+    values) and multiply densely in fp64; per-block dots against the decoded
+    integer products."""
+    W = inputs.random_matrix(1800 + rows * K, rows, K, 0.02)
+    W[0, 0] *= 10.0
+    X = inputs.random_matrix(1900 + N * K, N, K)
+    Wq8 = orc.q8_0_quantize(W)
+    Xq = orc.q8_0_quantize(X)
+    Y = orc.mul_mat_q8_ref(Wq8, Xq, K)
+    assert Y.shape == (N, rows)
+    Yb = _np_dequant_q8(Xq, K) @ _np_dequant_q8(Wq8, K).T
+    assert np.allclose(Y, Yb, rtol=1e-12, atol=1e-15)
+    D = orc.block_dots_q8(Wq8, Xq, K)
+    nb = K // 32
+    Wi = Wq8.reshape(rows, nb, 34)[:, :, 2:].copy().view(np.int8).astype(np.int64)
+    Xi = Xq.reshape(N, nb, 34)[:, :, 2:].copy().view(np.int8).astype(np.int64)
+    assert np.array_equal(D.astype(np.int64), np.einsum("nbj,rbj->nrb", Xi, Wi))
