@@ -289,6 +289,41 @@ def get_rows_leg(hip, torch):
     return res
 
 
+def q8w_leg(hip, torch):
+    """Q8_0 weights (Q8_0 blocks of 34 bytes from the same Q8_0 rule as the
+    activations) at N = 1 and N = 8 on the vocabulary head (128256 x 4096) and
+    the Llama MLP matrix (14336 x 4096); weights rotate over >= 1 GiB of copies
+    so every step reads HBM; device time from HIP graphs, each replay checked
+    against an eager call.  Algorithmic bytes: Q8_0 weights + fp32 X + fp32 Y."""
+    from q4_block_quantized_amd import inputs
+    res = []
+    for cid, rows, K in ((4, 128256, 4096), (5, 14336, 4096)):
+        Wq8 = hip.q8_0_quantize(torch.from_numpy(inputs.weights(cid, 0, rows, K)).cuda())
+        wbytes = rows * (K // 32) * 34
+        copies = max(2, -(-ROTATE_BYTES // wbytes))
+        Ws = [Wq8] + [Wq8.clone() for _ in range(copies - 1)]
+        for N in (1, 8):
+            X = torch.from_numpy(inputs.activations(cid, 0, N, K).copy()).cuda()
+            Y = torch.empty((N, rows), dtype=torch.float32, device="cuda")
+            fn = lambda i: hip.mul_mat_q8_0_q8_0(Ws[i % copies], X, Y)
+            fn(0)
+            torch.cuda.synchronize()
+            ref = Y.clone()
+            settle(torch, fn, 0.3)
+            ms, g = graph_timed(torch, fn, copies, max(3, int(0.05 / (copies * wbytes / 6e12))))
+            if not torch.equal(Y, ref):
+                raise RuntimeError("graph replay of the Q8_0-weight product differs from the eager call")
+            nbytes = wbytes + N * K * 4 + N * rows * 4
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            log("Q8_0 weights %dx%d N=%d: %.2f us -> %.1f GB/s" % (rows, K, N, ms * 1e3, gbs))
+            res.append({"matrix": [rows, K], "N": N, "us_per_call": round(ms * 1e3, 3), "GB/s": round(gbs, 1),
+                        "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)})
+            del g
+        del Ws, Wq8
+        torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(cid, N):
     """The oracle, as it stands, on a bounded row sample of the workload."""
     import oracle
@@ -379,6 +414,7 @@ def main():
     # the other decode configurations, device time from HIP graphs
     small = None if args.no_small else decode_configs(hip, torch)
     rows_lookup = None if args.no_small else get_rows_leg(hip, torch)
+    q8_weights = None if args.no_small else q8w_leg(hip, torch)
 
     prefill = None
     if not args.no_prefill:
@@ -428,6 +464,7 @@ def main():
         "multi_matrix_decode": multi,
         "decode_configs_graph": small,
         "get_rows_graph": rows_lookup,
+        "q8_0_weights_graph": q8_weights,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -228,6 +228,32 @@ int mul_mat_q4_0_q8_0_pq(const void *Wq, int64_t rows, int64_t K, const void *Xq
 int q4_0_q8_0_block_dots(const void *Wq, int64_t rows, int64_t K, const void *Xq,
                          int64_t N, int32_t *D, void *stream);
 
+/*
+ * Q8_0 weights: Y = mul_mat with weight blocks in the Q8_0 format.  Section 1
+ * of "llama.cpp 深度解读" lists Q8_0 (8 bits per weight) beside Q4_0 in its
+ * table of quantization types; its block is the block_q8_0 of the
+ * activations (binary16 d, then 32 int8 q; element j = q_j * d), so the
+ * weights come from q8_0_quantize(W, rows, K, Wq8).  Per block the integer
+ * dot s = sum_j qw_j * qx_j (no offset) is scaled by d_w * d_x in fp32, as in
+ * section 3's product.
+ *   Wq8  device, rows x (K/32) blocks of 34 bytes, 2-byte aligned.
+ *   X, N, Y, stream  as for mul_mat_q4_0_q8_0 (X is quantized inside).
+ * Requires K/32 <= 1024 (K <= 32768); other errors as for mul_mat_q4_0_q8_0.
+ * Decode-shaped: one row-streaming launch per group of at most 8 tokens (fewer
+ * for K above 14336), each reading all of Wq8.  No scratch memory.
+ */
+int mul_mat_q8_0_q8_0(const void *Wq8, int64_t rows, int64_t K, const float *X,
+                      int64_t N, float *Y, void *stream);
+
+/*
+ * Test export for Q8_0 weights: D[(n * rows + r) * (K/32) + b] = the integer
+ * dot of weight block (r, b) with activation block (n, b) of Xq (pages' Q8_0
+ * layout), computed by the product kernel's dot function.  D: N*rows*(K/32)
+ * int32, 4-byte aligned, must not overlap the inputs.
+ */
+int q8_0_q8_0_block_dots(const void *Wq8, int64_t rows, int64_t K, const void *Xq,
+                         int64_t N, int32_t *D, void *stream);
+
 /* Static text for a status code. */
 const char *q4bq_status_string(int status);
 

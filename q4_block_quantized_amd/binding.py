@@ -30,7 +30,7 @@ EXPORTS = (
     "mul_mat_q4_0_q8_0_ex", "mul_mat_q4_0_q8_0_pq", "q4_0_q8_0_block_dots",
     "q4bq_status_string", "q4bq_version", "q4bq_quantize_activations", "mul_mat_q4_0_q8_0_prepared",
     "q4_0_repack", "mul_mat_q4_0r_q8_0", "mul_mat_q4_0r_q8_0_ex", "mul_mat_q4_0_q8_0_multi",
-    "q4_0_get_rows", "q4bq_repack_size",
+    "q4_0_get_rows", "q4bq_repack_size", "mul_mat_q8_0_q8_0", "q8_0_q8_0_block_dots",
 )
 
 
@@ -61,6 +61,8 @@ def lib() -> ctypes.CDLL:
         "mul_mat_q4_0_q8_0_pq": (I, [P, I64, I64, P, I64, P, P]),
         "q4_0_repack": (I, [P, I64, I64, P, P]),
         "q4bq_repack_size": (ctypes.c_size_t, [I64, I64]),
+        "mul_mat_q8_0_q8_0": (I, [P, I64, I64, P, I64, P, P]),
+        "q8_0_q8_0_block_dots": (I, [P, I64, I64, P, I64, P, P]),
         "q4_0_get_rows": (I, [P, I64, I64, P, I64, P, P]),
         "mul_mat_q4_0_q8_0_multi": (I, [ctypes.c_int, P, P, I64, P, I64, P, P, ctypes.c_size_t, P]),
         "mul_mat_q4_0r_q8_0": (I, [P, I64, I64, P, I64, P, P]),
@@ -189,6 +191,37 @@ def mul_mat_q4_0_q8_0_ex(Wq: torch.Tensor, X: torch.Tensor, ws: torch.Tensor, Y:
                                       _dev(Y, torch.float32, "Y"), _dev(ws, torch.uint8, "workspace"),
                                       ws.numel(), _stream(stream)), "mul_mat_q4_0_q8_0_ex")
     return Y
+
+
+def _rows_q8(Wq8: torch.Tensor, K: int) -> int:
+    nb = _nb(K)
+    if Wq8.numel() % (nb * Q8_0_BYTES):
+        raise ValueError("Wq8 size %d is not a whole number of Q8_0 rows of K=%d" % (Wq8.numel(), K))
+    return Wq8.numel() // (nb * Q8_0_BYTES)
+
+
+def mul_mat_q8_0_q8_0(Wq8: torch.Tensor, X: torch.Tensor, Y: torch.Tensor | None = None,
+                      stream=None) -> torch.Tensor:
+    """Y = X @ W^T with Q8_0 weights (from q8_0_quantize(W)); X fp32 N x K."""
+    N, K = X.shape
+    rows = _rows_q8(Wq8, K)
+    if Y is None:
+        Y = torch.empty((N, rows), dtype=torch.float32, device=X.device)
+    _check(lib().mul_mat_q8_0_q8_0(_dev(Wq8, torch.uint8, "Wq8"), rows, K, _dev(X, torch.float32, "X"), N,
+                                   _dev(Y, torch.float32, "Y"), _stream(stream)), "mul_mat_q8_0_q8_0")
+    return Y
+
+
+def q8_0_q8_0_block_dots(Wq8: torch.Tensor, Xq: torch.Tensor, K: int, D: torch.Tensor | None = None,
+                         stream=None) -> torch.Tensor:
+    """Every per-block int32 dot of Q8_0 weights with Q8_0 activations (N x rows x K/32)."""
+    rows = _rows_q8(Wq8, K)
+    N = _rows_q8(Xq, K)
+    if D is None:
+        D = torch.empty((N, rows, K // 32), dtype=torch.int32, device=Wq8.device)
+    _check(lib().q8_0_q8_0_block_dots(_dev(Wq8, torch.uint8, "Wq8"), rows, K, _dev(Xq, torch.uint8, "Xq"), N,
+                                      _dev(D, torch.int32, "D"), _stream(stream)), "q8_0_q8_0_block_dots")
+    return D
 
 
 def q4_0_get_rows(Wq: torch.Tensor, K: int, ids: torch.Tensor, out: torch.Tensor | None = None,

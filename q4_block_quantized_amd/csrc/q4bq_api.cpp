@@ -308,6 +308,38 @@ int q4_0_q8_0_block_dots(const void* Wq, int64_t rows, int64_t K, const void* Xq
                             N, nullptr, D, static_cast<hipStream_t>(stream));
 }
 
+int mul_mat_q8_0_q8_0(const void* Wq8, int64_t rows, int64_t K, const float* X, int64_t N, float* Y, void* stream) {
+    if (!Wq8 || !X || !Y || bad_dim(rows) || bad_dim(N) || bad_k(K)) return Q4BQ_EINVAL;
+    const int64_t nb = K / kQK;
+    if (!q8w_supported_k(nb) || too_big(rows, K, 2) || too_big(N, K, 4) || too_big(N, rows, 4)) return Q4BQ_EINVAL;
+    if (!aligned(Wq8, 2) || !aligned(X, 4) || !aligned(Y, 4)) return Q4BQ_EINVAL;
+    const size_t y_bytes = static_cast<size_t>(N * rows) * 4;
+    if (overlap(Y, y_bytes, Wq8, static_cast<size_t>(rows * nb) * kQ8Bytes) ||
+        overlap(Y, y_bytes, X, static_cast<size_t>(N * K) * 4))
+        return Q4BQ_EINVAL;
+    hipError_t err = hipSuccess;
+    const DeviceInfo* dev = current_device(&err);
+    if (!dev) return Q4BQ_EHIP;
+    return status_of(launch_q8w_product(dev, static_cast<const uint8_t*>(Wq8), rows, nb, X, N, Y,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int q8_0_q8_0_block_dots(const void* Wq8, int64_t rows, int64_t K, const void* Xq, int64_t N, int32_t* D,
+                         void* stream) {
+    if (!Wq8 || !Xq || !D || bad_dim(rows) || bad_dim(N) || bad_k(K)) return Q4BQ_EINVAL;
+    const int64_t nb = K / kQK;
+    if (too_big(rows, K, 2) || too_big(N, K, 2) || too_big(N * rows, nb, 4)) return Q4BQ_EINVAL;
+    if (!aligned(Wq8, 2) || !aligned(Xq, 2) || !aligned(D, 4)) return Q4BQ_EINVAL;
+    const size_t d_bytes = static_cast<size_t>(N * rows * nb) * 4;
+    if (overlap(D, d_bytes, Wq8, static_cast<size_t>(rows * nb) * kQ8Bytes) ||
+        overlap(D, d_bytes, Xq, static_cast<size_t>(N * nb) * kQ8Bytes))
+        return Q4BQ_EINVAL;
+    hipError_t err = hipSuccess;
+    if (!current_device(&err)) return Q4BQ_EHIP;
+    return status_of(launch_q8w_block_dots(static_cast<const uint8_t*>(Wq8), rows, nb,
+                                           static_cast<const uint8_t*>(Xq), N, D, static_cast<hipStream_t>(stream)));
+}
+
 int q4bq_quantize_activations(const float* X, int64_t N, int64_t K, void* workspace, size_t ws_bytes,
                               void* stream) {
     if (!X || !workspace || bad_dim(N) || bad_k(K) || too_big(N, K, 4)) return Q4BQ_EINVAL;

@@ -55,6 +55,15 @@ hipError_t launch_q8_0_quantize(const float* X, int64_t nblocks, uint8_t* Xq, hi
 int64_t repack_records_offset(int64_t rows, int64_t nb);
 size_t repack_bytes(int64_t rows, int64_t nb);
 hipError_t launch_q4_0_repack(const uint8_t* Wq, int64_t rows, int64_t nb, uint8_t* Wr, hipStream_t s);
+// Q8_0 weights (34-byte blocks) x Q8_0 activations: row-streaming decode in
+// groups of up to q8w_tokens_per_launch tokens (whose quantized blocks fit the
+// kernel's LDS); block dots with the same dot function.
+int64_t q8w_tokens_per_launch(int64_t nb);
+bool q8w_supported_k(int64_t nb);
+hipError_t launch_q8w_product(const DeviceInfo* dev, const uint8_t* W, int64_t rows, int64_t nb, const float* X,
+                              int64_t N, float* Y, hipStream_t s);
+hipError_t launch_q8w_block_dots(const uint8_t* W, int64_t rows, int64_t nb, const uint8_t* Xq, int64_t N, int32_t* D,
+                                 hipStream_t s);
 hipError_t launch_q4_0_get_rows(const uint8_t* Wq, int64_t rows, int64_t nb, const int32_t* ids, int64_t n,
                                 float* out, hipStream_t s);
 

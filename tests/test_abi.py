@@ -132,6 +132,19 @@ def _bad_product_calls(L):
     yield gr(A, 4, 64, B, 3, C + 4, None)          # output not 16-byte aligned
     yield gr(A, 4, 64, B, 3, A + 16, None)         # output overlaps the table
     yield gr(A, 4, 64, B, 3, B - 512, None)        # output overlaps ids
+    m8 = L.mul_mat_q8_0_q8_0
+    yield m8(None, 4, 64, B, 1, C, None)           # null weights
+    yield m8(A, 4, 48, B, 1, C, None)              # K % 32 != 0
+    yield m8(A, 4, 32800, B, 1, C, None)           # K / 32 above 1024
+    yield m8(A + 1, 4, 64, B, 1, C, None)          # Q8_0 weights on an odd address
+    yield m8(A, 4, 64, B + 2, 1, C, None)          # X not 4-byte aligned
+    yield m8(A, 4, 64, B, 1, A + 32, None)         # Y overlaps the weights
+    yield m8(A, 4, 64, B, 0, C, None)              # N < 1
+    d8 = L.q8_0_q8_0_block_dots
+    yield d8(A, 4, 64, None, 1, C, None)           # null activations
+    yield d8(A, 4, 64, B + 1, 1, C, None)          # activations on an odd address
+    yield d8(A, 4, 64, B, 1, C + 2, None)          # D not 4-byte aligned
+    yield d8(A, 4, 64, B, 1, B + 4, None)          # D overlaps the activations
     q8 = L.q8_0_quantize
     yield q8(A, 0, 64, B, None)
     yield q8(A, 4, 33, B, None)
@@ -171,4 +184,6 @@ def test_no_device_is_ehip_not_abort(L):
     assert L.q4_0_q8_0_block_dots(A, 4, 64, B, 1, C, None) == -2
     assert L.q4_0_repack(A, 4, 64, B, None) == -2
     assert L.q4_0_get_rows(A, 4, 64, B, 3, C, None) == -2
+    assert L.mul_mat_q8_0_q8_0(A, 4, 64, B, 1, C, None) == -2
+    assert L.q8_0_q8_0_block_dots(A, 4, 64, B, 1, C, None) == -2
     assert L.mul_mat_q4_0r_q8_0(A, 4, 64, B, 1, C, None) == -2

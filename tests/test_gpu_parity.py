@@ -348,6 +348,56 @@ def test_multi_matrix_llama_decode_full_size(hip, orc):
             assert_close(host(Ys[i])[:, samples[i]], orc.mul_mat_ref(Wq_os[i], Xq_o, 4096), "multi N=%d" % N)
 
 
+# ---------------------------------------------------------------------------
+# Q8_0 weights (Q8_0 weight blocks, from the same Q8_0 rule as the activations)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("rows,K,N", [(1, 32, 1), (37, 96, 3), (300, 768, 9), (129, 4096, 2), (5, 20480, 3)])
+def test_q8w_block_dots(hip, orc, rows, K, N):
+    """Q8_0 weight bytes and every per-block int32 dot, bit for bit."""
+    W, X = _case(rows, K, N, 4100 + rows + K)
+    print("q8w block dots rows=%d K=%d N=%d" % (rows, K, N), flush=True)
+    Wq8 = hip.q8_0_quantize(dev(W))
+    Wq8_o = orc.q8_0_quantize(W)
+    assert np.array_equal(host(Wq8).reshape(-1), Wq8_o.reshape(-1))
+    Xq_o = orc.q8_0_quantize(X)
+    D = host(hip.q8_0_q8_0_block_dots(Wq8, dev(Xq_o), K))
+    assert np.array_equal(D, orc.block_dots_q8(Wq8_o, Xq_o, K))
+
+
+Q8W_K = [32, 96, 768, 2048, 3072, 4096, 4128, 8192, 14336, 16384, 16416, 20480, 32768]
+
+
+@pytest.mark.parametrize("K", Q8W_K)
+def test_q8w_product(hip, orc, K):
+    """Every lane-block count (1 to 16 per lane, ragged), token groups of 1..8
+    and the grouping above 8 tokens (or above 2 on rows over 16384)."""
+    rows = 301 if K <= 4128 else 67
+    W, X = _case(rows, K, 17, 4200 + K)
+    Wq8 = hip.q8_0_quantize(dev(W))
+    Wq8_o = orc.q8_0_quantize(W)
+    for N in (1, 2, 3, 5, 8, 9, 17):
+        print("q8w product rows=%d K=%d N=%d" % (rows, K, N), flush=True)
+        Y = host(hip.mul_mat_q8_0_q8_0(Wq8, dev(X[:N])))
+        assert Y.shape == (N, rows)
+        assert_close(Y, orc.mul_mat_q8_ref(Wq8_o, orc.q8_0_quantize(X[:N]), K), "q8w K=%d N=%d" % (K, N))
+
+
+@pytest.mark.parametrize("rows,K", [(14336, 4096), (4096, 14336)])
+def test_q8w_full_size(hip, orc, rows, K):
+    """Llama-size Q8_0 matrices at N = 1 and 8, in the benchmark's launch
+    configuration; outputs sampled on the first, last and random rows."""
+    W, X = _case(rows, K, 8, 4300 + rows)
+    Wq8 = hip.q8_0_quantize(dev(W))
+    Wq8_o = orc.q8_0_quantize(W)
+    sample = np.unique(np.concatenate([[0, 1, rows - 1], np.random.default_rng(rows).integers(0, rows, 61)]))
+    Ws = Wq8_o.reshape(rows, -1)[sample]
+    for N in (1, 8):
+        print("q8w full size rows=%d K=%d N=%d" % (rows, K, N), flush=True)
+        Y = host(hip.mul_mat_q8_0_q8_0(Wq8, dev(X[:N])))
+        assert_close(Y[:, sample], orc.mul_mat_q8_ref(Ws, orc.q8_0_quantize(X[:N]), K), "q8w full N=%d" % N)
+
+
 def test_repack_rejects_misaligned_output(hip):
     Wq = torch.zeros((4, 36), dtype=torch.uint8, device="cuda")
     buf = torch.zeros(4 * 36 + 32, dtype=torch.uint8, device="cuda")
