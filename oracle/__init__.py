@@ -71,6 +71,10 @@ def _load():
         "orc_block_dot_q8": (ctypes.c_int32, [P, P]),
         "orc_block_dots_q8": (None, [P, I64, I64, P, I64, P]),
         "orc_mul_mat_q8_ref": (None, [P, I64, I64, P, I64, P]),
+        "orc_layernorm": (None, [P, I64, I64, P, P, ctypes.c_float, P]),
+        "orc_gelu": (ctypes.c_double, [ctypes.c_double]),
+        "orc_silu": (ctypes.c_double, [ctypes.c_double]),
+        "orc_epilogue": (None, [P, I64, I64, P, ctypes.c_int, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -223,6 +227,43 @@ def mul_mat_q8_ref(Wq8: np.ndarray, Xq: np.ndarray, K: int) -> np.ndarray:
     N = Xq.size // (nb * Q8_BYTES)
     Y = np.empty((N, rows), dtype=np.float64)
     _load().orc_mul_mat_q8_ref(_ptr(Wq8), rows, K, _ptr(Xq), N, _ptr(Y))
+    return Y
+
+
+ACT_NONE, ACT_GELU, ACT_SILU = 0, 1, 2
+
+
+def layernorm(X: np.ndarray, gamma: np.ndarray, beta: np.ndarray, eps: float) -> np.ndarray:
+    """LayerNorm of each row of X (the GPT-2 walkthrough, section 3.1:
+    gamma * (x - mu) / sqrt(sigma^2 + eps) + beta), statistics and arithmetic
+    in fp64, the result rounded to fp32."""
+    X = np.ascontiguousarray(X, dtype=np.float32)
+    N, K = X.shape
+    g = np.ascontiguousarray(gamma, dtype=np.float32).reshape(K)
+    b = np.ascontiguousarray(beta, dtype=np.float32).reshape(K)
+    out = np.empty((N, K), dtype=np.float32)
+    _load().orc_layernorm(_ptr(X), N, K, _ptr(g), _ptr(b), float(eps), _ptr(out))
+    return out
+
+
+def gelu(x: float) -> float:
+    """GELU in GPT-2's tanh form."""
+    return float(_load().orc_gelu(float(x)))
+
+
+def silu(x: float) -> float:
+    """SiLU(x) = x * sigmoid(x) ("llama.cpp 深度解读" section 4)."""
+    return float(_load().orc_silu(float(x)))
+
+
+def epilogue(Y: np.ndarray, bias=None, act: int = ACT_NONE, mul=None) -> np.ndarray:
+    """act(Y + bias) * mul in fp64 (bias per row, mul N x rows; either may be
+    None): the bias add and GELU after GPT-2's c_mlp_fc, and SiLU(gate) * up."""
+    Y = np.array(Y, dtype=np.float64, order="C", copy=True)
+    N, rows = Y.shape
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32).reshape(rows)
+    m = None if mul is None else np.ascontiguousarray(mul, dtype=np.float64).reshape(N, rows)
+    _load().orc_epilogue(_ptr(Y), N, rows, None if b is None else _ptr(b), int(act), None if m is None else _ptr(m))
     return Y
 
 

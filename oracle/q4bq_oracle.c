@@ -20,6 +20,11 @@
  *           Q8_0-quantized so the dot runs in the integer domain.
  *   [P3-1]  same page, section 1: the table of ggml quantization types, with
  *           Q8_0 (8 bits per weight) beside Q4_0 as a weight format.
+ *   [P4]    ggml GPT-2 walkthrough (aicoding.csdn.net): section 3.1 LayerNorm
+ *           (gamma * (x - mu) / sqrt(sigma^2 + eps) + beta, after ggml_norm),
+ *           section 3.5 (bias add then GELU after c_mlp_fc).
+ *   [P3-4]  "llama.cpp 深度解读" section 4: SiLU(x) = x * sigmoid(x) and the
+ *           SwiGLU feed-forward SiLU(gate) * up.
  *   [P2-mm] "解锁模型适配能力：Llama.cpp 框架下新架构开发全流程指南" (tahou.com),
  *           section "GGML 的特性与注意事项", item 2: ggml's mul_mat contracts the
  *           innermost dimension of both operands.
@@ -350,6 +355,72 @@ void orc_mul_mat_q8_ref(const uint8_t *Wq, int64_t rows, int64_t K,
             Y[n * rows + r] = acc;
         }
     }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Around the product: LayerNorm before it, bias / activation / gate after   */
+/* it ([P4] 3.1 and 3.5, [P3-4]).                                            */
+/* ------------------------------------------------------------------------ */
+
+/* LayerNorm of each token (row of X): mu = mean, sigma^2 = mean of (x - mu)^2
+ * (the population variance), both in fp64; out = gamma * (x - mu) /
+ * sqrt(sigma^2 + eps) + beta evaluated in fp64 and rounded once to fp32.
+ * (Reading: the pages give the formula, not its precision; the fp64 statistics
+ * make the fp32 result, which decides the Q8_0 codes, independent of the
+ * summation order.) */
+void orc_layernorm(const float *X, int64_t N, int64_t K, const float *gamma,
+                   const float *beta, float eps, float *out)
+{
+    for (int64_t n = 0; n < N; ++n) {
+        const float *x = X + n * K;
+        double mu = 0.0;
+        for (int64_t k = 0; k < K; ++k)
+            mu += (double)x[k];
+        mu /= (double)K;
+        double var = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double c = (double)x[k] - mu;
+            var += c * c;
+        }
+        var /= (double)K;
+        double rstd = 1.0 / sqrt(var + (double)eps);
+        for (int64_t k = 0; k < K; ++k)
+            out[n * K + k] = (float)((double)gamma[k] * (((double)x[k] - mu) * rstd) + (double)beta[k]);
+    }
+}
+
+/* GELU, the tanh form GPT-2 uses (reading: the pages name GELU without a
+ * formula): 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))). */
+double orc_gelu(double x)
+{
+    const double c = 0.79788456080286535588; /* sqrt(2 / pi) */
+    return 0.5 * x * (1.0 + tanh(c * (x + 0.044715 * x * x * x)));
+}
+
+/* SiLU(x) = x * sigmoid(x) = x / (1 + exp(-x)). */
+double orc_silu(double x)
+{
+    return x / (1.0 + exp(-x));
+}
+
+/* Y[n][r] = act(Y[n][r] + bias[r]) * mul[n][r], in place, fp64; bias and mul
+ * may be NULL; act 0 = none, 1 = GELU, 2 = SiLU. */
+void orc_epilogue(double *Y, int64_t N, int64_t rows, const float *bias, int act,
+                  const double *mul)
+{
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t r = 0; r < rows; ++r) {
+            double y = Y[n * rows + r];
+            if (bias)
+                y += (double)bias[r];
+            if (act == 1)
+                y = orc_gelu(y);
+            else if (act == 2)
+                y = orc_silu(y);
+            if (mul)
+                y *= mul[n * rows + r];
+            Y[n * rows + r] = y;
+        }
 }
 
 /* Whole operator with fp32 activations: quantize X to Q8_0, then the

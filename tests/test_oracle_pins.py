@@ -498,3 +498,76 @@ def test_q8w_brute_force_fp64(orc, rows, K, N):
     Wi = Wq8.reshape(rows, nb, 34)[:, :, 2:].copy().view(np.int8).astype(np.int64)
     Xi = Xq.reshape(N, nb, 34)[:, :, 2:].copy().view(np.int8).astype(np.int64)
     assert np.array_equal(D.astype(np.int64), np.einsum("nbj,rbj->nrb", Xi, Wi))
+
+
+# ---------------------------------------------------------------------------
+# Around the product: LayerNorm (ggml GPT-2 walkthrough, section 3.1), GELU
+# after the bias of c_mlp_fc (section 3.5), SiLU and SwiGLU ("llama.cpp 深度解读"
+# section 4)
+# ---------------------------------------------------------------------------
+
+def test_layernorm_closed_form(orc):
+    """x_j = j (j < 32): mu = 31/2 and sigma^2 = (32^2 - 1)/12 = 85.25 (the
+    variance of a discrete uniform ramp); with gamma = 1, beta = 0, eps = 0:
+    out_j = (j - 15.5)/sqrt(85.25).  With eps = 0.75: sqrt(86) instead."""
+    x = np.arange(32, dtype=np.float32)[None]
+    one, zero = np.ones(32, np.float32), np.zeros(32, np.float32)
+    out = orc.layernorm(x, one, zero, 0.0)
+    want = np.array([np.float32((j - 15.5) / np.sqrt(85.25)) for j in range(32)])
+    assert np.array_equal(out[0], want)
+    out = orc.layernorm(x, one, zero, 0.75)
+    assert np.array_equal(out[0], np.array([np.float32((j - 15.5) / np.sqrt(86.0)) for j in range(32)]))
+
+
+def test_layernorm_invariants(orc):
+    """Zero mean and unit population variance (gamma = 1, beta = 0, eps = 0);
+    invariance under x -> a x + b; gamma and beta act per element."""
+    X = inputs.random_matrix(901, 5, 768, 3.0) + 2.0
+    one, zero = np.ones(768, np.float32), np.zeros(768, np.float32)
+    out = orc.layernorm(X, one, zero, 0.0).astype(np.float64)
+    assert np.all(np.abs(out.mean(axis=1)) < 1e-6)
+    assert np.all(np.abs(out.var(axis=1) - 1.0) < 1e-6)
+    shifted = orc.layernorm((4.0 * X.astype(np.float64) - 3.0).astype(np.float32), one, zero, 0.0)
+    assert np.allclose(shifted, out, rtol=0, atol=2e-6)
+    g = inputs.random_matrix(902, 1, 768)[0]
+    b = inputs.random_matrix(903, 1, 768)[0]
+    out_gb = orc.layernorm(X, g, b, 0.0).astype(np.float64)
+    assert np.allclose(out_gb, g.astype(np.float64) * out + b, rtol=0, atol=1e-5)
+    eps = 0.5   # eps adds to the variance: unit variance becomes var / (var + eps)
+    var = X.astype(np.float64).var(axis=1)
+    out_e = orc.layernorm(X, one, zero, eps).astype(np.float64)
+    assert np.allclose(out_e.var(axis=1), var / (var + eps), rtol=1e-6)
+
+
+def test_gelu_against_the_normal_cdf(orc):
+    """The tanh form is odd up to the identity GELU(x) - GELU(-x) = x, is 0 at
+    0, and stays within 1e-3 of the exact x * Phi(x) (scipy.special.ndtr)."""
+    from scipy.special import ndtr
+    assert orc.gelu(0.0) == 0.0
+    for x in np.linspace(-8, 8, 321):
+        assert abs(orc.gelu(x) - orc.gelu(-x) - x) < 1e-12
+        assert abs(orc.gelu(x) - x * ndtr(x)) < 1e-3
+    assert orc.gelu(30.0) == 30.0 and orc.gelu(-30.0) == 0.0
+
+
+def test_silu_is_x_times_sigmoid(orc):
+    from scipy.special import expit
+    for x in np.linspace(-40, 40, 401):
+        assert abs(orc.silu(x) - x * expit(x)) <= 1e-15 * max(1.0, abs(x))
+        assert abs(orc.silu(x) - orc.silu(-x) - x) < 1e-12
+
+
+def test_epilogue_composition(orc):
+    """Bias per row, then the activation, then the element-wise factor."""
+    Y = inputs.random_matrix(904, 3, 7).astype(np.float64)
+    b = inputs.random_matrix(905, 1, 7)[0]
+    m = inputs.random_matrix(906, 3, 7).astype(np.float64)
+    assert np.array_equal(orc.epilogue(Y), Y)
+    assert np.array_equal(orc.epilogue(Y, bias=b), Y + b.astype(np.float64))
+    assert np.array_equal(orc.epilogue(Y, mul=m), Y * m)
+    g = orc.epilogue(Y, bias=b, act=orc.ACT_GELU)
+    s = orc.epilogue(Y, act=orc.ACT_SILU, mul=m)
+    for n in range(3):
+        for r in range(7):
+            assert g[n, r] == orc.gelu(Y[n, r] + np.float64(b[r]))
+            assert s[n, r] == orc.silu(Y[n, r]) * m[n, r]
