@@ -324,6 +324,88 @@ def q8w_leg(hip, torch):
     return res
 
 
+def fused_leg(hip, torch):
+    """The steps around the product, fused (HIP graphs, each replay checked
+    against an eager call; weights rotate over >= 1 GiB):
+      * Llama-3-8B feed-forward first half at one token: LayerNorm, the gate
+        and up products (14336 x 4096 each) and SiLU(gate) * up in
+        mul_mat_q4_0_q8_0_swiglu, against the two bare products;
+      * GPT-2's c_mlp_fc (3072 x 768) at one token with LayerNorm, bias and
+        GELU (mul_mat_q4_0_q8_0_fused), against the bare product.
+    Bytes: the Q4_0 weights + fp32 X + fp32 outputs of the fused call."""
+    from q4_block_quantized_amd import inputs
+    res = []
+    # Llama SwiGLU
+    rows, K = 14336, 4096
+    Wg = hip.q4_0_quantize(torch.from_numpy(inputs.weights(3, 1, rows, K, outliers=True)).cuda())
+    Wu = hip.q4_0_quantize(torch.from_numpy(inputs.weights(3, 4, rows, K, outliers=True)).cuda())
+    wbytes = 2 * q4_bytes(rows, K)
+    copies = max(1, -(-ROTATE_BYTES // wbytes))
+    sets = [(Wg, Wu)] + [(Wg.clone(), Wu.clone()) for _ in range(copies - 1)]
+    X = torch.from_numpy(inputs.activations(3, 0, 1, K).copy()).cuda()
+    g = torch.from_numpy(inputs.random_matrix(5500, 1, K, 0.5)[0] + 1.0).cuda()
+    b = torch.from_numpy(inputs.random_matrix(5501, 1, K, 0.1)[0]).cuda()
+    H = torch.empty((1, rows), dtype=torch.float32, device="cuda")
+    Y2 = torch.empty((2, 1, rows), dtype=torch.float32, device="cuda")
+    ws = hip.fused_workspace(rows, K, 1)
+    fused = lambda i: hip.mul_mat_q4_0_q8_0_swiglu(sets[i % copies][0], sets[i % copies][1], X, g, b, 1e-5, H, ws)
+    def bare(i):
+        hip.mul_mat_q4_0_q8_0(sets[i % copies][0], X, Y2[0])
+        hip.mul_mat_q4_0_q8_0(sets[i % copies][1], X, Y2[1])
+    for name, fn, out in (("swiglu", fused, H), ("bare", bare, Y2)):
+        fn(0)
+        torch.cuda.synchronize()
+        ref = out.clone()
+        settle(torch, fn, 0.3)
+        ms, gr = graph_timed(torch, fn, copies, 40)
+        if not torch.equal(out, ref):
+            raise RuntimeError("graph replay of the %s leg differs from the eager call" % name)
+        del gr
+        if name == "swiglu":
+            ms_fused = ms
+        else:
+            ms_bare = ms
+    nbytes = wbytes + K * 4 + rows * 4
+    log("Llama SwiGLU (LayerNorm + gate + up + SiLU*up), N=1: %.2f us (bare products %.2f us) -> %.1f GB/s"
+        % (ms_fused * 1e3, ms_bare * 1e3, nbytes / (ms_fused * 1e-3) / 1e9))
+    res.append({"workload": "llama3_8b ffn gate+up 2 x 14336x4096, LayerNorm, SiLU(gate)*up", "N": 1,
+                "fused_us": round(ms_fused * 1e3, 3), "bare_products_us": round(ms_bare * 1e3, 3),
+                "GB/s": round(nbytes / (ms_fused * 1e-3) / 1e9, 1)})
+    del sets, Wg, Wu
+    torch.cuda.empty_cache()
+    # GPT-2 c_mlp_fc with LayerNorm, bias, GELU
+    rows, K = 3072, 768
+    W = hip.q4_0_quantize(torch.from_numpy(inputs.weights(2, 2, rows, K)).cuda())
+    copies = max(1, -(-ROTATE_BYTES // q4_bytes(rows, K)))
+    Ws = [W] + [W.clone() for _ in range(copies - 1)]
+    X = torch.from_numpy(inputs.activations(2, 2, 1, K).copy()).cuda()
+    g = torch.from_numpy(inputs.random_matrix(5600, 1, K, 0.5)[0] + 1.0).cuda()
+    b = torch.from_numpy(inputs.random_matrix(5601, 1, K, 0.1)[0]).cuda()
+    bias = torch.from_numpy(inputs.random_matrix(5602, 1, rows, 0.1)[0]).cuda()
+    Y = torch.empty((1, rows), dtype=torch.float32, device="cuda")
+    ws = hip.fused_workspace(rows, K, 1)
+    fused = lambda i: hip.mul_mat_q4_0_q8_0_fused(Ws[i % copies], X, g, b, 1e-5, bias, hip.ACT_GELU, None, Y, ws)
+    bare = lambda i: hip.mul_mat_q4_0_q8_0(Ws[i % copies], X, Y)
+    out = {}
+    for name, fn in (("fused", fused), ("bare", bare)):
+        fn(0)
+        torch.cuda.synchronize()
+        ref = Y.clone()
+        settle(torch, fn, 0.3)
+        ms, gr = graph_timed(torch, fn, min(copies, 64), 40)
+        if not torch.equal(Y, ref):
+            raise RuntimeError("graph replay of the GPT-2 %s leg differs from the eager call" % name)
+        del gr
+        out[name] = ms
+    log("GPT-2 c_mlp_fc (LayerNorm + product + bias + GELU), N=1: %.2f us (bare product %.2f us)"
+        % (out["fused"] * 1e3, out["bare"] * 1e3))
+    res.append({"workload": "gpt2 c_mlp_fc 3072x768, LayerNorm, bias, GELU", "N": 1,
+                "fused_us": round(out["fused"] * 1e3, 3), "bare_product_us": round(out["bare"] * 1e3, 3)})
+    del Ws, W
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(cid, N):
     """The oracle, as it stands, on a bounded row sample of the workload."""
     import oracle
@@ -415,6 +497,7 @@ def main():
     small = None if args.no_small else decode_configs(hip, torch)
     rows_lookup = None if args.no_small else get_rows_leg(hip, torch)
     q8_weights = None if args.no_small else q8w_leg(hip, torch)
+    fusion = None if args.no_small else fused_leg(hip, torch)
 
     prefill = None
     if not args.no_prefill:
@@ -465,6 +548,7 @@ def main():
         "decode_configs_graph": small,
         "get_rows_graph": rows_lookup,
         "q8_0_weights_graph": q8_weights,
+        "fused_graph": fusion,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -229,6 +229,55 @@ int q4_0_q8_0_block_dots(const void *Wq, int64_t rows, int64_t K, const void *Xq
                          int64_t N, int32_t *D, void *stream);
 
 /*
+ * The product with the steps around it fused: LayerNorm of X before it (the
+ * ggml GPT-2 walkthrough, section 3.1: gamma * (x - mu) / sqrt(sigma^2 + eps)
+ * + beta over each token's K values), and after it the bias add and
+ * activation of section 3.5 (GELU after c_mlp_fc) or SiLU ("llama.cpp 深度解读"
+ * section 4), and an element-wise factor:
+ *   Y[n][r] = act(sum_k LN(X)[n][k] W[r][k] + bias[r]) * mul[n][r]
+ * with the Q4_0 x Q8_0 product of mul_mat_q4_0_q8_0 (LN(X) is what gets
+ * quantized).  LayerNorm: mean and population variance in fp64, the normalized
+ * value evaluated in fp64 and rounded to fp32.  GELU: GPT-2's tanh form
+ * 0.5 y (1 + tanh(sqrt(2/pi) (y + 0.044715 y^3))); SiLU: y / (1 + exp(-y)).
+ *   ln_gamma, ln_beta  device fp32[K] each, or both NULL (no LayerNorm);
+ *                      ln_eps >= 0.
+ *   bias               device fp32[rows] or NULL.
+ *   act                Q4BQ_ACT_NONE, Q4BQ_ACT_GELU or Q4BQ_ACT_SILU.
+ *   mul                device fp32 N x rows or NULL; may be Y itself (read
+ *                      before Y is written), otherwise must not overlap it.
+ *   workspace          NULL (the library takes stream-ordered scratch) or a
+ *                      16-byte aligned device buffer of ws_bytes >=
+ *                      q4bq_fused_workspace_size(rows, K, N), apart from every
+ *                      other buffer (the form for graph capture).
+ * Other arguments and errors as for mul_mat_q4_0_q8_0 (a short workspace:
+ * Q4BQ_ENOMEM); N < 2^31 with LayerNorm.  Launches: LayerNorm statistics (if
+ * any), one quantization pass, the product with the epilogue in its store.
+ */
+#define Q4BQ_ACT_NONE 0
+#define Q4BQ_ACT_GELU 1
+#define Q4BQ_ACT_SILU 2
+size_t q4bq_fused_workspace_size(int64_t rows, int64_t K, int64_t N);
+int mul_mat_q4_0_q8_0_fused(const void *Wq, int64_t rows, int64_t K, const float *X,
+                            int64_t N, const float *ln_gamma, const float *ln_beta,
+                            float ln_eps, const float *bias, int act, const float *mul,
+                            float *Y, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * The Llama feed-forward's first half ("llama.cpp 深度解读" section 4, step I:
+ * up and gate projections of the same normalized input, then
+ * SiLU(gate) * up):
+ *   H = SiLU(LN(X) Wgate^T) * (LN(X) Wup^T)
+ * X is normalized (optional, as above) and quantized once; the gate product
+ * writes SiLU(gate) into H and the up product multiplies it in its store.
+ *   Wgate, Wup  rows x (K/32) Q4_0 blocks each; H device fp32 N x rows.
+ * Workspace and errors as for mul_mat_q4_0_q8_0_fused.
+ */
+int mul_mat_q4_0_q8_0_swiglu(const void *Wgate, const void *Wup, int64_t rows, int64_t K,
+                             const float *X, int64_t N, const float *ln_gamma,
+                             const float *ln_beta, float ln_eps, float *H, void *workspace,
+                             size_t ws_bytes, void *stream);
+
+/*
  * Q8_0 weights: Y = mul_mat with weight blocks in the Q8_0 format.  Section 1
  * of "llama.cpp 深度解读" lists Q8_0 (8 bits per weight) beside Q4_0 in its
  * table of quantization types; its block is the block_q8_0 of the

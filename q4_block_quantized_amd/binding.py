@@ -31,7 +31,10 @@ EXPORTS = (
     "q4bq_status_string", "q4bq_version", "q4bq_quantize_activations", "mul_mat_q4_0_q8_0_prepared",
     "q4_0_repack", "mul_mat_q4_0r_q8_0", "mul_mat_q4_0r_q8_0_ex", "mul_mat_q4_0_q8_0_multi",
     "q4_0_get_rows", "q4bq_repack_size", "mul_mat_q8_0_q8_0", "q8_0_q8_0_block_dots",
+    "mul_mat_q4_0_q8_0_fused", "mul_mat_q4_0_q8_0_swiglu", "q4bq_fused_workspace_size",
 )
+
+ACT_NONE, ACT_GELU, ACT_SILU = 0, 1, 2
 
 
 class Q4BQError(RuntimeError):
@@ -62,6 +65,10 @@ def lib() -> ctypes.CDLL:
         "q4_0_repack": (I, [P, I64, I64, P, P]),
         "q4bq_repack_size": (ctypes.c_size_t, [I64, I64]),
         "mul_mat_q8_0_q8_0": (I, [P, I64, I64, P, I64, P, P]),
+        "mul_mat_q4_0_q8_0_fused": (I, [P, I64, I64, P, I64, P, P, ctypes.c_float, P, I, P, P, P, ctypes.c_size_t,
+                                        P]),
+        "mul_mat_q4_0_q8_0_swiglu": (I, [P, P, I64, I64, P, I64, P, P, ctypes.c_float, P, P, ctypes.c_size_t, P]),
+        "q4bq_fused_workspace_size": (ctypes.c_size_t, [I64, I64, I64]),
         "q8_0_q8_0_block_dots": (I, [P, I64, I64, P, I64, P, P]),
         "q4_0_get_rows": (I, [P, I64, I64, P, I64, P, P]),
         "mul_mat_q4_0_q8_0_multi": (I, [ctypes.c_int, P, P, I64, P, I64, P, P, ctypes.c_size_t, P]),
@@ -191,6 +198,56 @@ def mul_mat_q4_0_q8_0_ex(Wq: torch.Tensor, X: torch.Tensor, ws: torch.Tensor, Y:
                                       _dev(Y, torch.float32, "Y"), _dev(ws, torch.uint8, "workspace"),
                                       ws.numel(), _stream(stream)), "mul_mat_q4_0_q8_0_ex")
     return Y
+
+
+def _opt(t, dtype, what):
+    return None if t is None else _dev(t, dtype, what)
+
+
+def fused_workspace(rows: int, K: int, N: int, device=None) -> torch.Tensor:
+    """A device buffer for the fused forms at these sizes."""
+    return torch.empty(max(int(lib().q4bq_fused_workspace_size(rows, K, N)), 16), dtype=torch.uint8,
+                       device=device or "cuda")
+
+
+def _ws(ws):
+    return (None, 0) if ws is None else (_dev(ws, torch.uint8, "workspace"), ws.numel())
+
+
+def mul_mat_q4_0_q8_0_fused(Wq: torch.Tensor, X: torch.Tensor, ln_gamma=None, ln_beta=None, ln_eps: float = 1e-5,
+                            bias=None, act: int = ACT_NONE, mul=None, Y: torch.Tensor | None = None, ws=None,
+                            stream=None) -> torch.Tensor:
+    """Y = act(LN(X) @ W^T + bias) * mul, LayerNorm and epilogue optional;
+    ws: optional workspace (fused_workspace), else the library allocates."""
+    N, K = X.shape
+    rows = _rows(Wq, K)
+    if Y is None:
+        Y = torch.empty((N, rows), dtype=torch.float32, device=X.device)
+    _check(lib().mul_mat_q4_0_q8_0_fused(_dev(Wq, torch.uint8, "Wq"), rows, K, _dev(X, torch.float32, "X"), N,
+                                         _opt(ln_gamma, torch.float32, "ln_gamma"),
+                                         _opt(ln_beta, torch.float32, "ln_beta"), float(ln_eps),
+                                         _opt(bias, torch.float32, "bias"), int(act),
+                                         _opt(mul, torch.float32, "mul"), _dev(Y, torch.float32, "Y"), *_ws(ws),
+                                         _stream(stream)), "mul_mat_q4_0_q8_0_fused")
+    return Y
+
+
+def mul_mat_q4_0_q8_0_swiglu(Wgate: torch.Tensor, Wup: torch.Tensor, X: torch.Tensor, ln_gamma=None, ln_beta=None,
+                             ln_eps: float = 1e-5, H: torch.Tensor | None = None, ws=None,
+                             stream=None) -> torch.Tensor:
+    """H = SiLU(LN(X) @ Wgate^T) * (LN(X) @ Wup^T)."""
+    N, K = X.shape
+    rows = _rows(Wgate, K)
+    if _rows(Wup, K) != rows:
+        raise ValueError("gate and up matrices differ in rows")
+    if H is None:
+        H = torch.empty((N, rows), dtype=torch.float32, device=X.device)
+    _check(lib().mul_mat_q4_0_q8_0_swiglu(_dev(Wgate, torch.uint8, "Wgate"), _dev(Wup, torch.uint8, "Wup"), rows, K,
+                                          _dev(X, torch.float32, "X"), N, _opt(ln_gamma, torch.float32, "ln_gamma"),
+                                          _opt(ln_beta, torch.float32, "ln_beta"), float(ln_eps),
+                                          _dev(H, torch.float32, "H"), *_ws(ws), _stream(stream)),
+           "mul_mat_q4_0_q8_0_swiglu")
+    return H
 
 
 def _rows_q8(Wq8: torch.Tensor, K: int) -> int:

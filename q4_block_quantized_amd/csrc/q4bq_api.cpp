@@ -308,6 +308,122 @@ int q4_0_q8_0_block_dots(const void* Wq, int64_t rows, int64_t K, const void* Xq
                             N, nullptr, D, static_cast<hipStream_t>(stream));
 }
 
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the fused forms: the LayerNorm parameters (both or
+// neither), the epilogue's bias and factor, their alignment and overlaps.
+int check_fusion(int64_t K, int64_t rows, int64_t N, const float* ln_gamma, const float* ln_beta, float ln_eps,
+                 const float* bias, int act, const float* mul, const float* Y) {
+    if ((ln_gamma == nullptr) != (ln_beta == nullptr)) return Q4BQ_EINVAL;
+    if (ln_gamma && (!(ln_eps >= 0.0f) || ln_eps > 3.0e38f || N >= (int64_t(1) << 31))) return Q4BQ_EINVAL;
+    if (act != kEpiNone && act != kEpiGelu && act != kEpiSilu) return Q4BQ_EINVAL;
+    if (!aligned(ln_gamma, 4) || !aligned(ln_beta, 4) || !aligned(bias, 4) || !aligned(mul, 4)) return Q4BQ_EINVAL;
+    const size_t y_bytes = static_cast<size_t>(N * rows) * 4;
+    if ((ln_gamma && overlap(Y, y_bytes, ln_gamma, static_cast<size_t>(K) * 4)) ||
+        (ln_beta && overlap(Y, y_bytes, ln_beta, static_cast<size_t>(K) * 4)) ||
+        (bias && overlap(Y, y_bytes, bias, static_cast<size_t>(rows) * 4)))
+        return Q4BQ_EINVAL;
+    if (mul && mul != Y && overlap(Y, y_bytes, mul, y_bytes)) return Q4BQ_EINVAL;  // in place, or apart
+    return Q4BQ_OK;
+}
+
+// LayerNorm (optional) + Q8_0 of X into stream-ordered scratch, then the
+// products of `count` matrices on it, each with its epilogue.
+size_t fused_act_bytes(int64_t N, int64_t nb) { return (act_bytes(N, nb) + 255) & ~static_cast<size_t>(255); }
+
+int run_fused(int count, const uint8_t* const* Wq, int64_t rows, int64_t K, const float* X, int64_t N,
+              const float* ln_gamma, const float* ln_beta, float ln_eps, const Epilogue* epi, float* const* Y,
+              void* workspace, size_t ws_bytes, hipStream_t s) {
+    hipError_t err = hipSuccess;
+    const DeviceInfo* dev = current_device(&err);
+    if (!dev) return Q4BQ_EHIP;
+    const int64_t nb = K / kQK;
+    const size_t bytes = fused_act_bytes(N, nb);
+    void* ws = workspace;
+    if (ws) {
+        if (ws_bytes < bytes) return Q4BQ_ENOMEM;
+    } else if (hipMallocAsync(&ws, bytes, s) != hipSuccess || ws == nullptr) {
+        (void)hipGetLastError();
+        return Q4BQ_ENOMEM;
+    }
+    if (ln_gamma) {
+        err = launch_ln_act(X, N, nb, ln_gamma, ln_beta, ln_eps, ws, s);
+    } else {
+        err = launch_act_from_f32(X, N, nb, ws, s);
+    }
+    for (int i = 0; i < count && err == hipSuccess; ++i)
+        err = N <= kGemvMaxN ? launch_gemv(dev, kAoS, Wq[i], rows, nb, ws, N, Y[i], nullptr, s, epi[i])
+                             : launch_prefill(dev, kAoS, Wq[i], rows, nb, ws, N, Y[i], nullptr, s, epi[i]);
+    const hipError_t ferr = workspace ? hipSuccess : hipFreeAsync(ws, s);
+    if (err != hipSuccess) return Q4BQ_EHIP;
+    return ferr == hipSuccess ? Q4BQ_OK : Q4BQ_EHIP;
+}
+
+// A caller's workspace: 16-byte aligned, apart from every other buffer.
+int check_workspace(const void* ws, int64_t rows, int64_t K, int64_t N, const void* const* bufs, const size_t* sizes,
+                    int nbufs) {
+    if (!ws) return Q4BQ_OK;
+    if (!aligned(ws, 16)) return Q4BQ_EINVAL;
+    const size_t need = fused_act_bytes(N, K / kQK);
+    for (int i = 0; i < nbufs; ++i)
+        if (bufs[i] && overlap(ws, need, bufs[i], sizes[i])) return Q4BQ_EINVAL;
+    (void)rows;
+    return Q4BQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t q4bq_fused_workspace_size(int64_t rows, int64_t K, int64_t N) {
+    if (bad_dim(rows) || bad_dim(N) || bad_k(K) || too_big(N, K, 4)) return 0;
+    return fused_act_bytes(N, K / kQK);
+}
+
+int mul_mat_q4_0_q8_0_fused(const void* Wq, int64_t rows, int64_t K, const float* X, int64_t N,
+                            const float* ln_gamma, const float* ln_beta, float ln_eps, const float* bias, int act,
+                            const float* mul, float* Y, void* workspace, size_t ws_bytes, void* stream) {
+    int rc = check_product(Wq, rows, K, X, kF32, N, Y, false);
+    if (rc != Q4BQ_OK) return rc;
+    rc = check_fusion(K, rows, N, ln_gamma, ln_beta, ln_eps, bias, act, mul, Y);
+    if (rc != Q4BQ_OK) return rc;
+    const void* bufs[] = {Wq, X, Y, ln_gamma, ln_beta, bias, mul};
+    const size_t sizes[] = {static_cast<size_t>(rows * (K / kQK)) * kQ4Bytes, static_cast<size_t>(N * K) * 4,
+                            static_cast<size_t>(N * rows) * 4, static_cast<size_t>(K) * 4, static_cast<size_t>(K) * 4,
+                            static_cast<size_t>(rows) * 4, static_cast<size_t>(N * rows) * 4};
+    rc = check_workspace(workspace, rows, K, N, bufs, sizes, 7);
+    if (rc != Q4BQ_OK) return rc;
+    const uint8_t* w = static_cast<const uint8_t*>(Wq);
+    const Epilogue epi{bias, mul, act};
+    return run_fused(1, &w, rows, K, X, N, ln_gamma, ln_beta, ln_eps, &epi, &Y, workspace, ws_bytes,
+                     static_cast<hipStream_t>(stream));
+}
+
+int mul_mat_q4_0_q8_0_swiglu(const void* Wgate, const void* Wup, int64_t rows, int64_t K, const float* X, int64_t N,
+                             const float* ln_gamma, const float* ln_beta, float ln_eps, float* H, void* workspace,
+                             size_t ws_bytes, void* stream) {
+    int rc = check_product(Wgate, rows, K, X, kF32, N, H, false);
+    if (rc != Q4BQ_OK) return rc;
+    rc = check_product(Wup, rows, K, X, kF32, N, H, false);
+    if (rc != Q4BQ_OK) return rc;
+    rc = check_fusion(K, rows, N, ln_gamma, ln_beta, ln_eps, nullptr, kEpiNone, nullptr, H);
+    if (rc != Q4BQ_OK) return rc;
+    const size_t w_bytes = static_cast<size_t>(rows * (K / kQK)) * kQ4Bytes;
+    const void* bufs[] = {Wgate, Wup, X, H, ln_gamma, ln_beta};
+    const size_t sizes[] = {w_bytes, w_bytes, static_cast<size_t>(N * K) * 4, static_cast<size_t>(N * rows) * 4,
+                            static_cast<size_t>(K) * 4, static_cast<size_t>(K) * 4};
+    rc = check_workspace(workspace, rows, K, N, bufs, sizes, 6);
+    if (rc != Q4BQ_OK) return rc;
+    // H = SiLU(gate) first, then H = up * H in place
+    const uint8_t* w[2] = {static_cast<const uint8_t*>(Wgate), static_cast<const uint8_t*>(Wup)};
+    const Epilogue epi[2] = {Epilogue{nullptr, nullptr, kEpiSilu}, Epilogue{nullptr, H, kEpiNone}};
+    float* const y[2] = {H, H};
+    return run_fused(2, w, rows, K, X, N, ln_gamma, ln_beta, ln_eps, epi, y, workspace, ws_bytes,
+                     static_cast<hipStream_t>(stream));
+}
+
 int mul_mat_q8_0_q8_0(const void* Wq8, int64_t rows, int64_t K, const float* X, int64_t N, float* Y, void* stream) {
     if (!Wq8 || !X || !Y || bad_dim(rows) || bad_dim(N) || bad_k(K)) return Q4BQ_EINVAL;
     const int64_t nb = K / kQK;

@@ -322,4 +322,18 @@ __device__ __forceinline__ int32_t block_dot(const Block4& w, const uint32_t* a,
     return s;
 }
 
+// The epilogue of a product output y for token n, row r (rows per token:
+// rows): y + bias[r], then GELU (GPT-2's tanh form) or SiLU (x * sigmoid(x)),
+// then times mul[n][r].
+__device__ __forceinline__ float apply_epilogue(float y, int64_t n, int64_t r, int64_t rows, const Epilogue& e) {
+    if (e.bias) y += e.bias[r];
+    if (e.act == kEpiGelu) {
+        y = 0.5f * y * (1.0f + tanhf(0.7978845608028654f * (y + 0.044715f * y * y * y)));
+    } else if (e.act == kEpiSilu) {
+        y = y / (1.0f + expf(-y));
+    }
+    if (e.mul) y *= e.mul[n * rows + r];
+    return y;
+}
+
 }  // namespace q4bq

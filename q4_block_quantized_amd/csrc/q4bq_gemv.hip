@@ -36,7 +36,7 @@ constexpr int kU = 2;             // pair slots per load batch
 constexpr size_t kMaxActLds = 64 * 1024;
 
 
-template <int NT, int THREADS, int SRC, bool DOTS, int LAY>
+template <int NT, int THREADS, int SRC, bool DOTS, int LAY, bool EPI>
 __global__ void __launch_bounds__(THREADS)
 k_gemv(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __restrict__ src,
        float* __restrict__ Y, int32_t* __restrict__ D, int log2G, int rpi, const MultiDesc md) {
@@ -215,7 +215,9 @@ k_gemv(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __restr
                 for (int j = 0; j < kRmax; ++j) {
                     if (!rv[j]) continue;
 #pragma unroll
-                    for (int n = 0; n < NT; ++n) yrow[j][static_cast<int64_t>(n) * ystride[j]] = acc[j][n];
+                    for (int n = 0; n < NT; ++n)
+                        yrow[j][static_cast<int64_t>(n) * ystride[j]] =
+                            EPI ? apply_epilogue(acc[j][n], n, r[j], rows, md.epi) : acc[j][n];
                 }
             }
         }
@@ -281,19 +283,25 @@ hipError_t launch_v(const Shape& sh, int lay, const uint8_t* Wq, int64_t rows, i
                     float* Y, int32_t* D, const MultiDesc& md, hipStream_t s) {
     const size_t lds = SRC == kActGlobal ? 0 : static_cast<size_t>(NT) * nb * (kActQBytes + kActSBytes);
     const int nbi = static_cast<int>(nb);
+    const bool fused = md.epi.bias || md.epi.mul || md.epi.act != kEpiNone;
     if (lay == kLayRepacked) {
-        hipLaunchKernelGGL((k_gemv<NT, THREADS, SRC, DOTS, kLayRepacked>), dim3(sh.wgs), dim3(THREADS), lds, s, Wq,
-                           rows, nbi, src, Y, D, sh.log2G, sh.rpi, md);
+        if (fused) return hipErrorInvalidValue;  // the fused forms take the pages' blocks
+        hipLaunchKernelGGL((k_gemv<NT, THREADS, SRC, DOTS, kLayRepacked, false>), dim3(sh.wgs), dim3(THREADS), lds, s,
+                           Wq, rows, nbi, src, Y, D, sh.log2G, sh.rpi, md);
     } else if (lay == kLayMulti) {
         if constexpr (DOTS) {
             return hipErrorInvalidValue;  // block dots are exported for one matrix only
         } else {
-            hipLaunchKernelGGL((k_gemv<NT, THREADS, SRC, false, kLayMulti>), dim3(sh.wgs), dim3(THREADS), lds, s, Wq,
-                               rows, nbi, src, Y, D, sh.log2G, sh.rpi, md);
+            hipLaunchKernelGGL((k_gemv<NT, THREADS, SRC, false, kLayMulti, false>), dim3(sh.wgs), dim3(THREADS), lds,
+                               s, Wq, rows, nbi, src, Y, D, sh.log2G, sh.rpi, md);
         }
+    } else if (fused && SRC != kXF32 && !DOTS) {
+        hipLaunchKernelGGL((k_gemv<NT, THREADS, SRC, false, kLayAoS, true>), dim3(sh.wgs), dim3(THREADS), lds, s, Wq,
+                           rows, nbi, src, Y, D, sh.log2G, sh.rpi, md);
     } else {
-        hipLaunchKernelGGL((k_gemv<NT, THREADS, SRC, DOTS, kLayAoS>), dim3(sh.wgs), dim3(THREADS), lds, s, Wq, rows,
-                           nbi, src, Y, D, sh.log2G, sh.rpi, md);
+        if (fused) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((k_gemv<NT, THREADS, SRC, DOTS, kLayAoS, false>), dim3(sh.wgs), dim3(THREADS), lds, s, Wq,
+                           rows, nbi, src, Y, D, sh.log2G, sh.rpi, md);
     }
     return hipGetLastError();
 }
@@ -360,8 +368,10 @@ hipError_t launch_gemv_fused(const DeviceInfo* dev, WLayout lay, const uint8_t* 
 }
 
 hipError_t launch_gemv(const DeviceInfo* dev, WLayout lay, const uint8_t* Wq, int64_t rows, int64_t nb,
-                       const void* act, int64_t N, float* Y, int32_t* D, hipStream_t s) {
-    return gemv_n(dev, lay_of(lay), Wq, rows, nb, act, N, Y, D, kNoMulti, s);
+                       const void* act, int64_t N, float* Y, int32_t* D, hipStream_t s, const Epilogue& epi) {
+    MultiDesc md = kNoMulti;
+    md.epi = epi;
+    return gemv_n(dev, lay_of(lay), Wq, rows, nb, act, N, Y, D, md, s);
 }
 
 hipError_t launch_gemv_multi(const DeviceInfo* dev, const MultiDesc& md, int64_t nb, const float* X, const void* act,

@@ -23,11 +23,24 @@ enum WLayout { kAoS = 0, kRepacked = 1 };
 // one concatenation of their rows (decode kernel): matrix m owns global rows
 // [first[m], first[m + 1]), its blocks at w[m], its output (N x rows_m) at y[m].
 constexpr int kMaxMulti = 8;
+
+// What a product kernel applies to each output before it stores it: the bias
+// add and activation after GPT-2's c_mlp_fc, or the element-wise factor of
+// SiLU(gate) * up: y = act(y + bias[r]) * mul[n][r], every part optional
+// (null pointers, kEpiNone).  Single-matrix launches only.
+enum EpiAct { kEpiNone = 0, kEpiGelu = 1, kEpiSilu = 2 };
+struct Epilogue {
+    const float* bias;
+    const float* mul;
+    int act;
+};
+
 struct MultiDesc {
     const uint8_t* w[kMaxMulti];
     float* y[kMaxMulti];
     int64_t first[kMaxMulti + 1];
     int count;
+    Epilogue epi;  // decode kernels on one matrix
 };
 
 struct DeviceInfo {
@@ -69,12 +82,18 @@ hipError_t launch_q4_0_get_rows(const uint8_t* Wq, int64_t rows, int64_t nb, con
 
 // fp32 X (N x K) -> internal activations, or Q8_0 blocks -> internal.
 hipError_t launch_act_from_f32(const float* X, int64_t N, int64_t nb, void* act, hipStream_t s);
+// LayerNorm + the same quantization, one workgroup per token (N < 2^31): fp64
+// mean and population variance, then gamma * (x - mu) / sqrt(var + eps) +
+// beta evaluated in fp64, rounded to fp32 and quantized.
+hipError_t launch_ln_act(const float* X, int64_t N, int64_t nb, const float* gamma, const float* beta, float eps,
+                         void* act, hipStream_t s);
 hipError_t launch_act_from_q8(const uint8_t* Xq, int64_t N, int64_t nb, void* act, hipStream_t s);
 
 // Streaming decode kernel, N in 1..8.  D != nullptr selects the block-dot
 // export (D written, Y untouched).
 hipError_t launch_gemv(const DeviceInfo* dev, WLayout lay, const uint8_t* Wq, int64_t rows, int64_t nb,
-                       const void* act, int64_t N, float* Y, int32_t* D, hipStream_t s);
+                       const void* act, int64_t N, float* Y, int32_t* D, hipStream_t s,
+                       const Epilogue& epi = Epilogue{nullptr, nullptr, kEpiNone});
 
 // Decode kernel that quantizes fp32 X itself (no scratch, one launch), for
 // N <= kGemvFusedMaxN when the quantized activations fit in LDS.  Same bits
@@ -107,7 +126,8 @@ hipError_t launch_rows_act(const DeviceInfo* dev, int lay, const uint8_t* Wq, in
 // Matrix-core kernel (128-token x 224-row tiles), any N; the one the library
 // runs above kGemvMaxN.  D as above.
 hipError_t launch_prefill(const DeviceInfo* dev, WLayout lay, const uint8_t* Wq, int64_t rows, int64_t nb,
-                          const void* act, int64_t N, float* Y, int32_t* D, hipStream_t s);
+                          const void* act, int64_t N, float* Y, int32_t* D, hipStream_t s,
+                          const Epilogue& epi = Epilogue{nullptr, nullptr, kEpiNone});
 
 constexpr int64_t kGemvMaxN = 8;
 

@@ -179,10 +179,11 @@ constexpr int kRecDma = kBufB / 1024;
 static_assert(kBufB % 1024 == 0 && kPlaneB % 16 == 0, "record staging in 1 KB wave moves");
 static_assert(kTR % 16 == 0, "row tiles keep the record swizzle (bit 3 of the row)");
 
-template <bool DOTS, bool RP>
+template <bool DOTS, bool RP, bool EPI>
 __global__ void __launch_bounds__(kT)
 k_prefill(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Wrec, int64_t rows, int nb,
-          const uint8_t* __restrict__ act, int64_t N, float* __restrict__ Y, int32_t* __restrict__ D) {
+          const uint8_t* __restrict__ act, int64_t N, float* __restrict__ Y, int32_t* __restrict__ D,
+          const Epilogue epi) {
     __shared__ __align__(16) uint8_t smem[kNS * kStage];
 
     const int t = threadIdx.x;
@@ -466,7 +467,7 @@ k_prefill(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Wrec, int6
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int64_t n = n0 + (2 * tp + kSeqT[j]) * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-                    if (n < N) Y[n * rows + r] = acc[j][v];
+                    if (n < N) Y[n * rows + r] = EPI ? apply_epilogue(acc[j][v], n, r, rows, epi) : acc[j][v];
                 }
             }
         }
@@ -481,18 +482,26 @@ k_prefill(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Wrec, int6
 }  // namespace
 
 hipError_t launch_prefill(const DeviceInfo* dev, WLayout lay, const uint8_t* Wq, int64_t rows, int64_t nb,
-                          const void* act, int64_t N, float* Y, int32_t* D, hipStream_t s) {
+                          const void* act, int64_t N, float* Y, int32_t* D, hipStream_t s, const Epilogue& epi) {
     (void)dev;
     const uint8_t* rec = static_cast<const uint8_t*>(act);
     const dim3 grid(static_cast<uint32_t>(((rows + kTR - 1) / kTR) * ((N + kTT - 1) / kTT)));
     const int nbi = static_cast<int>(nb);
+    const bool fused = epi.bias || epi.mul || epi.act != kEpiNone;
     if (D)
-        hipLaunchKernelGGL((k_prefill<true, false>), grid, dim3(kT), 0, s, Wq, nullptr, rows, nbi, rec, N, Y, D);
+        hipLaunchKernelGGL((k_prefill<true, false, false>), grid, dim3(kT), 0, s, Wq, nullptr, rows, nbi, rec, N, Y, D,
+                           epi);
+    else if (fused && lay == kRepacked)
+        return hipErrorInvalidValue;  // the fused forms take the pages' blocks
+    else if (fused)
+        hipLaunchKernelGGL((k_prefill<false, false, true>), grid, dim3(kT), 0, s, Wq, nullptr, rows, nbi, rec, N, Y,
+                           D, epi);
     else if (lay == kRepacked)
-        hipLaunchKernelGGL((k_prefill<false, true>), grid, dim3(kT), 0, s, Wq, Wq + repack_records_offset(rows, nb),
-                           rows, nbi, rec, N, Y, D);
+        hipLaunchKernelGGL((k_prefill<false, true, false>), grid, dim3(kT), 0, s, Wq,
+                           Wq + repack_records_offset(rows, nb), rows, nbi, rec, N, Y, D, epi);
     else
-        hipLaunchKernelGGL((k_prefill<false, false>), grid, dim3(kT), 0, s, Wq, nullptr, rows, nbi, rec, N, Y, D);
+        hipLaunchKernelGGL((k_prefill<false, false, false>), grid, dim3(kT), 0, s, Wq, nullptr, rows, nbi, rec, N, Y,
+                           D, epi);
     return hipGetLastError();
 }
 

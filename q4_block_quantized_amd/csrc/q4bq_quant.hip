@@ -84,6 +84,123 @@ k_q8_0_quantize(const float* __restrict__ X, int64_t nblocks, uint8_t* __restric
     }
 }
 
+// ---------------------------------------------------------------------------
+// LayerNorm before the product (the ggml GPT-2 walkthrough, section 3.1:
+// gamma * (x - mu) / sqrt(sigma^2 + eps) + beta over each token's K values).
+// The statistics are taken in fp64, one workgroup per token, and the
+// quantizers below evaluate the normalized value in fp64 and round it once to
+// fp32: the fp32 value that decides the Q8_0 codes then does not depend on the
+// summation order.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float ln_value(float x, double mu, double rstd, float g, float b) {
+#pragma clang fp contract(off)
+    return static_cast<float>(static_cast<double>(g) * ((static_cast<double>(x) - mu) * rstd) +
+                              static_cast<double>(b));
+}
+
+// One workgroup per token: the statistics (fp64, two passes), then the token's
+// blocks normalized and quantized, into the decode layout (token-major blocks
+// g = n nb + b, PREFILL false) or the prefill records (o = b N + n).  Thread t
+// holds quads t, t + T, ... (QPT of them, four values each, loaded in one
+// round); T is a multiple of 8, so the 8 lanes of a block are neighbours, as
+// the quantizer wants.  QPT = 0: rows too long for registers, re-read per pass.
+constexpr int kLnActThreads = 1024;
+
+__device__ __forceinline__ double block_sum_big(double v, double* red) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    double t = 0.0;
+#pragma unroll
+    for (int i = 0; i < kLnActThreads / 64; ++i) t += red[i];
+    __syncthreads();
+    return t;
+}
+
+template <bool PREFILL, int QPT>
+__global__ void __launch_bounds__(kLnActThreads)
+k_ln_act(const float* __restrict__ X, int64_t N, int64_t nb, const float* __restrict__ gamma,
+         const float* __restrict__ beta, float eps, uint32_t* __restrict__ act_q, ActScale* __restrict__ act_s) {
+    __shared__ double red[kLnActThreads / 64];
+    const int64_t n = blockIdx.x;
+    const int64_t nq = nb * 8;  // quads of the token
+    const float* x = X + n * nb * kQK;
+    constexpr int kReg = QPT > 0 ? QPT : 1;
+    float4 xr[kReg];
+    double s = 0.0;
+    if constexpr (QPT > 0) {
+#pragma unroll
+        for (int i = 0; i < QPT; ++i) {
+            const int64_t q = threadIdx.x + static_cast<int64_t>(kLnActThreads) * i;
+            xr[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (q < nq) __builtin_memcpy(&xr[i], x + 4 * q, 16);
+        }
+#pragma unroll
+        for (int i = 0; i < QPT; ++i)
+            s += (static_cast<double>(xr[i].x) + static_cast<double>(xr[i].y)) +
+                 (static_cast<double>(xr[i].z) + static_cast<double>(xr[i].w));
+    } else {
+        for (int64_t q = threadIdx.x; q < nq; q += kLnActThreads) {
+            float4 v;
+            __builtin_memcpy(&v, x + 4 * q, 16);
+            s += (static_cast<double>(v.x) + static_cast<double>(v.y)) + (static_cast<double>(v.z) + static_cast<double>(v.w));
+        }
+    }
+    const double K = static_cast<double>(nb * kQK);
+    const double mu = block_sum_big(s, red) / K;
+    auto sq = [&](const float4& v) __attribute__((always_inline)) {
+        const double a = static_cast<double>(v.x) - mu, b = static_cast<double>(v.y) - mu;
+        const double c = static_cast<double>(v.z) - mu, d = static_cast<double>(v.w) - mu;
+        return (a * a + b * b) + (c * c + d * d);
+    };
+    double v2 = 0.0;
+    if constexpr (QPT > 0) {
+#pragma unroll
+        for (int i = 0; i < QPT; ++i)
+            if (threadIdx.x + static_cast<int64_t>(kLnActThreads) * i < nq) v2 += sq(xr[i]);
+    } else {
+        for (int64_t q = threadIdx.x; q < nq; q += kLnActThreads) {
+            float4 v;
+            __builtin_memcpy(&v, x + 4 * q, 16);
+            v2 += sq(v);
+        }
+    }
+    const double rstd = 1.0 / sqrt(block_sum_big(v2, red) / K + static_cast<double>(eps));
+    const int m = threadIdx.x & 7;
+    auto emit = [&](float4 v, int64_t q) __attribute__((always_inline)) {
+        const int64_t k = 4 * q;
+        v.x = ln_value(v.x, mu, rstd, gamma[k], beta[k]);
+        v.y = ln_value(v.y, mu, rstd, gamma[k + 1], beta[k + 1]);
+        v.z = ln_value(v.z, mu, rstd, gamma[k + 2], beta[k + 2]);
+        v.w = ln_value(v.w, mu, rstd, gamma[k + 3], beta[k + 3]);
+        uint32_t word, dbits;
+        const ActScale sc = quant_act_quad(v.x, v.y, v.z, v.w, m, word, dbits);
+        const int64_t b = q >> 3;
+        if constexpr (PREFILL) {
+            store_act6(m, word, dbits, true, b * N + n, act_q);
+        } else {
+            act_q[(n * nb + b) * 8 + m] = word;
+            if (m == 0) act_s[n * nb + b] = sc;
+        }
+    };
+    // a block's 8 quads sit in 8 neighbouring lanes, all valid or all past the end
+    if constexpr (QPT > 0) {
+#pragma unroll
+        for (int i = 0; i < QPT; ++i) {
+            const int64_t q = threadIdx.x + static_cast<int64_t>(kLnActThreads) * i;
+            if (q < nq) emit(xr[i], q);
+        }
+    } else {
+        for (int64_t q = threadIdx.x; q < nq; q += kLnActThreads) {
+            float4 v;
+            __builtin_memcpy(&v, x + 4 * q, 16);
+            emit(v, q);
+        }
+    }
+}
+
 // fp32 activations -> internal dot-order blocks: 8 lanes per block, four
 // consecutive values per lane (one 16-byte load).
 __global__ void __launch_bounds__(kThreads)
@@ -343,6 +460,37 @@ hipError_t launch_act_from_f32(const float* X, int64_t N, int64_t nb, void* act,
     if (wgs > 8192) wgs = 8192;
     hipLaunchKernelGGL(k_act_from_f32, dim3(static_cast<uint32_t>(wgs)), dim3(kThreads), 0, s, X, nblocks, q, sc);
     return hipGetLastError();
+}
+
+namespace {
+
+template <bool PREFILL, int QPT>
+hipError_t ln_act_k(const float* X, int64_t N, int64_t nb, const float* gamma, const float* beta, float eps,
+                    uint32_t* q, ActScale* sc, hipStream_t s) {
+    hipLaunchKernelGGL((k_ln_act<PREFILL, QPT>), dim3(static_cast<uint32_t>(N)), dim3(kLnActThreads), 0, s, X, N, nb,
+                       gamma, beta, eps, q, sc);
+    return hipGetLastError();
+}
+
+template <bool PREFILL>
+hipError_t ln_act_p(const float* X, int64_t N, int64_t nb, const float* gamma, const float* beta, float eps,
+                    uint32_t* q, ActScale* sc, hipStream_t s) {
+    const int64_t qpt = (nb * 8 + kLnActThreads - 1) / kLnActThreads;
+    if (qpt <= 1) return ln_act_k<PREFILL, 1>(X, N, nb, gamma, beta, eps, q, sc, s);
+    if (qpt <= 2) return ln_act_k<PREFILL, 2>(X, N, nb, gamma, beta, eps, q, sc, s);
+    if (qpt <= 4) return ln_act_k<PREFILL, 4>(X, N, nb, gamma, beta, eps, q, sc, s);
+    if (qpt <= 8) return ln_act_k<PREFILL, 8>(X, N, nb, gamma, beta, eps, q, sc, s);
+    return ln_act_k<PREFILL, 0>(X, N, nb, gamma, beta, eps, q, sc, s);
+}
+
+}  // namespace
+
+hipError_t launch_ln_act(const float* X, int64_t N, int64_t nb, const float* gamma, const float* beta, float eps,
+                         void* act, hipStream_t s) {
+    uint32_t* q = static_cast<uint32_t*>(act);
+    if (N > kGemvMaxN) return ln_act_p<true>(X, N, nb, gamma, beta, eps, q, nullptr, s);
+    ActScale* sc = reinterpret_cast<ActScale*>(static_cast<uint8_t*>(act) + N * nb * kActQBytes);
+    return ln_act_p<false>(X, N, nb, gamma, beta, eps, q, sc, s);
 }
 
 hipError_t launch_act_from_q8(const uint8_t* Xq, int64_t N, int64_t nb, void* act, hipStream_t s) {

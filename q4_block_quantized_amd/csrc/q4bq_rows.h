@@ -129,7 +129,7 @@ __device__ __forceinline__ int64_t uniform64(int64_t v) {
     return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
-template <int THREADS, int NT, int PPL, int D, int SRC, int LAY>
+template <int THREADS, int NT, int PPL, int D, int SRC, int LAY, bool EPI>
 __global__ void __launch_bounds__(THREADS)
 k_gemv_rows(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __restrict__ src,
             float* __restrict__ Y, const MultiDesc md) {
@@ -354,8 +354,10 @@ k_gemv_rows(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __
             fold(raw[d], part);
             const float t = wave_sums<NT>(part, lane);
             if (k + d < nk && my_token >= 0 && my_token < NT) {
-                const RowAt a = row_at(w0 + (k + d) * S);
-                a.y[static_cast<int64_t>(my_token) * a.ystride] = t;
+                const int64_t r = w0 + (k + d) * S;
+                const RowAt a = row_at(r);
+                a.y[static_cast<int64_t>(my_token) * a.ystride] =
+                    EPI ? apply_epilogue(t, my_token, r, rows, md.epi) : t;
             }
             load_row(raw[d], k + d + D);
             __builtin_amdgcn_sched_barrier(0);
@@ -383,12 +385,12 @@ constexpr int rows_threads() { return NT > (PPL == 1 ? 4 : PPL == 2 ? 6 : 4) ? 5
 template <int NT, int PPL>
 constexpr int rows_depth() { return PPL == 1 && NT > 4 ? 2 : 1; }
 
-template <int SRC, int LAY, int NT, int PPL>
+template <int SRC, int LAY, bool EPI, int NT, int PPL>
 hipError_t launch_rows_k(const DeviceInfo* dev, const uint8_t* Wq, int64_t rows, int64_t nb, const void* src,
                          float* Y, const MultiDesc& md, hipStream_t s) {
     constexpr int kThreads = rows_threads<NT, PPL>();
     constexpr int kDepth = rows_depth<NT, PPL>();
-    const auto kernel = k_gemv_rows<kThreads, NT, PPL, kDepth, SRC, LAY>;
+    const auto kernel = k_gemv_rows<kThreads, NT, PPL, kDepth, SRC, LAY, EPI>;
     int64_t wgs = (rows + kThreads / 64 - 1) / (kThreads / 64);
     const int64_t cap = static_cast<int64_t>(dev->num_cu) * (1024 / kThreads);
     if (wgs > cap) wgs = cap;
@@ -405,29 +407,29 @@ hipError_t launch_rows_k(const DeviceInfo* dev, const uint8_t* Wq, int64_t rows,
     return hipGetLastError();
 }
 
-template <int SRC, int LAY, int NT>
+template <int SRC, int LAY, bool EPI, int NT>
 hipError_t launch_rows_nt(const DeviceInfo* dev, const uint8_t* Wq, int64_t rows, int64_t nb, const void* src,
                           float* Y, const MultiDesc& md, hipStream_t s) {
     switch (rows_ppl(nb)) {
-        case 1: return launch_rows_k<SRC, LAY, NT, 1>(dev, Wq, rows, nb, src, Y, md, s);
-        case 2: return launch_rows_k<SRC, LAY, NT, 2>(dev, Wq, rows, nb, src, Y, md, s);
-        case 4: return launch_rows_k<SRC, LAY, NT, 4>(dev, Wq, rows, nb, src, Y, md, s);
+        case 1: return launch_rows_k<SRC, LAY, EPI, NT, 1>(dev, Wq, rows, nb, src, Y, md, s);
+        case 2: return launch_rows_k<SRC, LAY, EPI, NT, 2>(dev, Wq, rows, nb, src, Y, md, s);
+        case 4: return launch_rows_k<SRC, LAY, EPI, NT, 4>(dev, Wq, rows, nb, src, Y, md, s);
         default: return hipErrorInvalidValue;
     }
 }
 
-template <int SRC, int LAY>
+template <int SRC, int LAY, bool EPI = false>
 hipError_t launch_rows_t(const DeviceInfo* dev, const uint8_t* Wq, int64_t rows, int64_t nb, const void* src,
                          int64_t N, float* Y, const MultiDesc& md, hipStream_t s) {
     switch (N) {
-        case 1: return launch_rows_nt<SRC, LAY, 1>(dev, Wq, rows, nb, src, Y, md, s);
-        case 2: return launch_rows_nt<SRC, LAY, 2>(dev, Wq, rows, nb, src, Y, md, s);
-        case 3: return launch_rows_nt<SRC, LAY, 3>(dev, Wq, rows, nb, src, Y, md, s);
-        case 4: return launch_rows_nt<SRC, LAY, 4>(dev, Wq, rows, nb, src, Y, md, s);
-        case 5: return launch_rows_nt<SRC, LAY, 5>(dev, Wq, rows, nb, src, Y, md, s);
-        case 6: return launch_rows_nt<SRC, LAY, 6>(dev, Wq, rows, nb, src, Y, md, s);
-        case 7: return launch_rows_nt<SRC, LAY, 7>(dev, Wq, rows, nb, src, Y, md, s);
-        case 8: return launch_rows_nt<SRC, LAY, 8>(dev, Wq, rows, nb, src, Y, md, s);
+        case 1: return launch_rows_nt<SRC, LAY, EPI, 1>(dev, Wq, rows, nb, src, Y, md, s);
+        case 2: return launch_rows_nt<SRC, LAY, EPI, 2>(dev, Wq, rows, nb, src, Y, md, s);
+        case 3: return launch_rows_nt<SRC, LAY, EPI, 3>(dev, Wq, rows, nb, src, Y, md, s);
+        case 4: return launch_rows_nt<SRC, LAY, EPI, 4>(dev, Wq, rows, nb, src, Y, md, s);
+        case 5: return launch_rows_nt<SRC, LAY, EPI, 5>(dev, Wq, rows, nb, src, Y, md, s);
+        case 6: return launch_rows_nt<SRC, LAY, EPI, 6>(dev, Wq, rows, nb, src, Y, md, s);
+        case 7: return launch_rows_nt<SRC, LAY, EPI, 7>(dev, Wq, rows, nb, src, Y, md, s);
+        case 8: return launch_rows_nt<SRC, LAY, EPI, 8>(dev, Wq, rows, nb, src, Y, md, s);
         default: return hipErrorInvalidValue;
     }
 }

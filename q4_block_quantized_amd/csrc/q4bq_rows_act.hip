@@ -8,7 +8,10 @@ hipError_t launch_rows_act(const DeviceInfo* dev, int lay, const uint8_t* Wq, in
     switch (lay) {
         case kLayRepacked: return launch_rows_t<kActGlobal, kLayRepacked>(dev, Wq, rows, nb, src, N, Y, md, s);
         case kLayMulti: return launch_rows_t<kActGlobal, kLayMulti>(dev, Wq, rows, nb, src, N, Y, md, s);
-        default: return launch_rows_t<kActGlobal, kLayAoS>(dev, Wq, rows, nb, src, N, Y, md, s);
+        default:
+            if (md.epi.bias || md.epi.mul || md.epi.act != kEpiNone)
+                return launch_rows_t<kActGlobal, kLayAoS, true>(dev, Wq, rows, nb, src, N, Y, md, s);
+            return launch_rows_t<kActGlobal, kLayAoS>(dev, Wq, rows, nb, src, N, Y, md, s);
     }
 }
 

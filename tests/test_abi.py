@@ -132,6 +132,19 @@ def _bad_product_calls(L):
     yield gr(A, 4, 64, B, 3, C + 4, None)          # output not 16-byte aligned
     yield gr(A, 4, 64, B, 3, A + 16, None)         # output overlaps the table
     yield gr(A, 4, 64, B, 3, B - 512, None)        # output overlaps ids
+    fu = L.mul_mat_q4_0_q8_0_fused
+    yield fu(A, 4, 64, B, 1, WS, None, ctypes.c_float(1e-5), None, 0, None, C, None, 0, None)   # gamma without beta
+    yield fu(A, 4, 64, B, 1, WS, WS + 256, ctypes.c_float(-1.0), None, 0, None, C, None, 0, None)  # eps < 0
+    yield fu(A, 4, 64, B, 1, None, None, ctypes.c_float(0.0), None, 3, None, C, None, 0, None)    # unknown activation
+    yield fu(A, 4, 64, B, 1, None, None, ctypes.c_float(0.0), C + 4, 0, None, C, None, 0, None)   # bias overlaps Y
+    yield fu(A, 4, 64, B, 1, None, None, ctypes.c_float(0.0), None, 0, C + 4, C, None, 0, None)   # factor partly over Y
+    yield fu(A, 4, 64, B, 1, None, None, ctypes.c_float(0.0), WS + 2, 0, None, C, None, 0, None)  # bias misaligned
+    yield fu(A, 4, 64, B, 1, None, None, ctypes.c_float(0.0), None, 0, None, C, WS + 8, 1 << 20, None)  # ws misaligned
+    yield fu(A, 4, 64, B, 1, None, None, ctypes.c_float(0.0), None, 0, None, C, C, 1 << 20, None)       # ws over Y
+    sw = L.mul_mat_q4_0_q8_0_swiglu
+    yield sw(A, None, 4, 64, B, 1, None, None, ctypes.c_float(0.0), C, None, 0, None)   # null up matrix
+    yield sw(A, A + 4096, 4, 64, B, 1, WS, None, ctypes.c_float(0.0), C, None, 0, None)  # beta missing
+    yield sw(A, A + 4096, 4, 64, B, 1, None, None, ctypes.c_float(0.0), A + 4100, None, 0, None)  # H in a weight
     m8 = L.mul_mat_q8_0_q8_0
     yield m8(None, 4, 64, B, 1, C, None)           # null weights
     yield m8(A, 4, 48, B, 1, C, None)              # K % 32 != 0
@@ -165,6 +178,15 @@ def test_repack_size(L):
     assert L.q4bq_repack_size(4, 48) == 0
 
 
+def test_fused_workspace_size(L):
+    # the activation records (N <= 8: 40 bytes per block; above: 64), rounded up to 256 bytes
+    assert L.q4bq_fused_workspace_size(4096, 4096, 1) == 5120
+    assert L.q4bq_fused_workspace_size(14336, 4096, 3) == (3 * 128 * 40 + 255) // 256 * 256
+    assert L.q4bq_fused_workspace_size(14336, 4128, 3) == (3 * 129 * 40 + 255) // 256 * 256
+    assert L.q4bq_fused_workspace_size(14336, 4096, 512) == 512 * 128 * 64
+    assert L.q4bq_fused_workspace_size(4, 48, 1) == 0
+
+
 def test_workspace_too_small_is_enomem(L):
     need = L.q4bq_workspace_size(4, 64, 1)
     assert L.mul_mat_q4_0_q8_0_ex(A, 4, 64, B, 1, C, WS, need - 1, None) == ENOMEM
@@ -185,5 +207,7 @@ def test_no_device_is_ehip_not_abort(L):
     assert L.q4_0_repack(A, 4, 64, B, None) == -2
     assert L.q4_0_get_rows(A, 4, 64, B, 3, C, None) == -2
     assert L.mul_mat_q8_0_q8_0(A, 4, 64, B, 1, C, None) == -2
+    assert L.mul_mat_q4_0_q8_0_fused(A, 4, 64, B, 1, WS, WS + 256, ctypes.c_float(1e-5), None, 2, None, C,
+                                     None, 0, None) == -2
     assert L.q8_0_q8_0_block_dots(A, 4, 64, B, 1, C, None) == -2
     assert L.mul_mat_q4_0r_q8_0(A, 4, 64, B, 1, C, None) == -2

@@ -398,6 +398,103 @@ def test_q8w_full_size(hip, orc, rows, K):
         assert_close(Y[:, sample], orc.mul_mat_q8_ref(Ws, orc.q8_0_quantize(X[:N]), K), "q8w full N=%d" % N)
 
 
+# ---------------------------------------------------------------------------
+# the steps around the product: LayerNorm before it, bias / activation /
+# element-wise factor after it, SwiGLU
+# ---------------------------------------------------------------------------
+
+def _fusion_inputs(rows, K, N, seed):
+    W, X = _case(rows, K, N, seed)
+    X = X * 3.0 + 1.5                                   # a mean and scale for the LayerNorm to remove
+    gamma = inputs.random_matrix(seed + 10, 1, K, 0.5)[0] + 1.0
+    beta = inputs.random_matrix(seed + 11, 1, K, 0.1)[0]
+    bias = inputs.random_matrix(seed + 12, 1, rows, 0.1)[0]
+    mul = inputs.random_matrix(seed + 13, N, rows)
+    return W, X.astype(np.float32), gamma, beta, bias, mul
+
+
+# decode task kernel (K = 768), row kernel (K = 4096), prefill kernel (N > 8)
+@pytest.mark.parametrize("rows,K,N", [(3072, 768, 1), (3072, 768, 4), (300, 4096, 1), (300, 4096, 5),
+                                      (1000, 4096, 9), (777, 768, 130)])
+def test_fused_product(hip, orc, rows, K, N):
+    W, X, gamma, beta, bias, mul = _fusion_inputs(rows, K, N, 5100 + rows + K + N)
+    eps = 1e-5
+    Wq = hip.q4_0_quantize(dev(W))
+    Wq_o = orc.q4_0_quantize(W)
+    Xt, gt, bt, bit, mt = dev(X), dev(gamma), dev(beta), dev(bias), dev(mul)
+    Y_plain = orc.mul_mat_ref(Wq_o, orc.q8_0_quantize(X), K)
+    Y_ln = orc.mul_mat_ref(Wq_o, orc.q8_0_quantize(orc.layernorm(X, gamma, beta, eps)), K)
+    cases = [(False, None, hip.ACT_NONE, None), (True, None, hip.ACT_NONE, None),
+             (True, bias, hip.ACT_GELU, None), (False, bias, hip.ACT_SILU, None),
+             (True, None, hip.ACT_SILU, mul), (False, bias, hip.ACT_NONE, mul)]
+    for ln, b, act, m in cases:
+        print("fused rows=%d K=%d N=%d ln=%d bias=%d act=%d mul=%d"
+              % (rows, K, N, ln, b is not None, act, m is not None), flush=True)
+        Y = host(hip.mul_mat_q4_0_q8_0_fused(Wq, Xt, gt if ln else None, bt if ln else None, eps,
+                                             bit if b is not None else None, act, mt if m is not None else None))
+        ref = orc.epilogue(Y_ln if ln else Y_plain, bias=b, act=act, mul=m)
+        assert_close(Y, ref, "fused ln=%d act=%d" % (ln, act))
+    # nothing fused: the same bits as the operator
+    assert np.array_equal(host(hip.mul_mat_q4_0_q8_0_fused(Wq, Xt)), host(hip.mul_mat_q4_0_q8_0(Wq, Xt)))
+    # a caller's workspace gives the same bits
+    ws = hip.fused_workspace(rows, K, N)
+    assert np.array_equal(host(hip.mul_mat_q4_0_q8_0_fused(Wq, Xt, gt, bt, eps, bit, hip.ACT_GELU, mt, ws=ws)),
+                          host(hip.mul_mat_q4_0_q8_0_fused(Wq, Xt, gt, bt, eps, bit, hip.ACT_GELU, mt)))
+    # the factor read in place
+    Yo = host(hip.mul_mat_q4_0_q8_0_fused(Wq, Xt, gt, bt, eps, None, hip.ACT_SILU, mt))
+    Yi = mt.clone()
+    hip.mul_mat_q4_0_q8_0_fused(Wq, Xt, gt, bt, eps, None, hip.ACT_SILU, Yi, Y=Yi)
+    assert np.array_equal(host(Yi), Yo)
+
+
+@pytest.mark.parametrize("K", [32, 768, 4096, 8192, 14336, 32768, 40960])
+def test_fused_layernorm_k_sweep(hip, orc, K):
+    """The LayerNorm + quantization kernel at every register layout (1, 2, 4, 8
+    quads per thread, and re-reading above 32768 values), into both activation
+    layouts (N <= 8 and N > 8)."""
+    rows = 37
+    W, X, gamma, beta, _, _ = _fusion_inputs(rows, K, 11, 5700 + K)
+    Wq = hip.q4_0_quantize(dev(W))
+    Wq_o = orc.q4_0_quantize(W)
+    for N in (1, 11):
+        print("fused layernorm K=%d N=%d" % (K, N), flush=True)
+        Y = host(hip.mul_mat_q4_0_q8_0_fused(Wq, dev(X[:N]), dev(gamma), dev(beta), 1e-5))
+        ref = orc.mul_mat_ref(Wq_o, orc.q8_0_quantize(orc.layernorm(X[:N], gamma, beta, 1e-5)), K)
+        assert_close(Y, ref, "layernorm K=%d N=%d" % (K, N))
+
+
+@pytest.mark.parametrize("rows,K,N", [(1000, 4096, 1), (1000, 4096, 3), (600, 768, 2), (300, 4096, 40)])
+def test_swiglu(hip, orc, rows, K, N):
+    Wg, X, gamma, beta, _, _ = _fusion_inputs(rows, K, N, 5300 + rows + N)
+    Wu = _case(rows, K, 1, 5400 + rows)[0]
+    eps = 1e-6
+    print("swiglu rows=%d K=%d N=%d" % (rows, K, N), flush=True)
+    H = host(hip.mul_mat_q4_0_q8_0_swiglu(hip.q4_0_quantize(dev(Wg)), hip.q4_0_quantize(dev(Wu)), dev(X),
+                                          dev(gamma), dev(beta), eps))
+    Xq = orc.q8_0_quantize(orc.layernorm(X, gamma, beta, eps))
+    g = orc.epilogue(orc.mul_mat_ref(orc.q4_0_quantize(Wg), Xq, K), act=orc.ACT_SILU)
+    ref = orc.epilogue(orc.mul_mat_ref(orc.q4_0_quantize(Wu), Xq, K), mul=g)
+    assert_close(H, ref, "swiglu N=%d" % N)
+
+
+def test_swiglu_llama_full_size(hip, orc):
+    """The Llama-3-8B feed-forward's gate and up matrices (14336 x 4096) at one
+    token, sampled rows."""
+    rows, K = 14336, 4096
+    Wg = inputs.weights(3, 1, rows, K, outliers=True)   # the workload's 14336 x 4096 matrix as the gate
+    Wu = inputs.weights(3, 4, rows, K, outliers=True)   # an up matrix of the same shape, its own seed
+    X = inputs.activations(3, 0, 1, K)
+    gamma = inputs.random_matrix(5500, 1, K, 0.5)[0] + 1.0
+    beta = inputs.random_matrix(5501, 1, K, 0.1)[0]
+    H = host(hip.mul_mat_q4_0_q8_0_swiglu(hip.q4_0_quantize(dev(Wg)), hip.q4_0_quantize(dev(Wu)), dev(X),
+                                          dev(gamma), dev(beta), 1e-5))
+    sample = np.unique(np.concatenate([[0, rows - 1], np.random.default_rng(7).integers(0, rows, 62)]))
+    Xq = orc.q8_0_quantize(orc.layernorm(X, gamma, beta, 1e-5))
+    g = orc.epilogue(orc.mul_mat_ref(orc.q4_0_quantize(Wg[sample]), Xq, K), act=orc.ACT_SILU)
+    ref = orc.epilogue(orc.mul_mat_ref(orc.q4_0_quantize(Wu[sample]), Xq, K), mul=g)
+    assert_close(H[:, sample], ref, "swiglu llama")
+
+
 def test_repack_rejects_misaligned_output(hip):
     Wq = torch.zeros((4, 36), dtype=torch.uint8, device="cuda")
     buf = torch.zeros(4 * 36 + 32, dtype=torch.uint8, device="cuda")
