@@ -47,7 +47,10 @@ int run_product(WLayout lay, const uint8_t* Wq, int64_t rows, int64_t K, const f
     const DeviceInfo* dev = current_device(&err);
     if (!dev) return Q4BQ_EHIP;
     const int64_t nb = K / kQK;
-    if (X && !D && gemv_fuses(N, nb)) return status_of(launch_gemv_fused(dev, lay, Wq, rows, nb, X, N, Y, s));
+    // without a workspace the fused kernel runs whenever it fits (run_with_scratch
+    // passes none in exactly that case)
+    if (X && !D && (ws ? gemv_prefers_fused(N, nb) : gemv_fuses(N, nb)))
+        return status_of(launch_gemv_fused(dev, lay, Wq, rows, nb, X, N, Y, s));
     err = X ? launch_act_from_f32(X, N, nb, ws, s) : launch_act_from_q8(Xq, N, nb, ws, s);
     if (err != hipSuccess) return Q4BQ_EHIP;
     if (N <= kGemvMaxN)
@@ -273,7 +276,8 @@ int mul_mat_q4_0_q8_0_multi(int count, const void* const* Wq, const int64_t* row
     const DeviceInfo* dev = current_device(&err);
     if (!dev) return Q4BQ_EHIP;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    if (N <= kGemvMaxN && gemv_fuses(N, nb)) return status_of(launch_gemv_multi(dev, md, nb, X, nullptr, N, s));
+    if (N <= kGemvMaxN && (workspace ? gemv_prefers_fused(N, nb) : gemv_fuses(N, nb)))
+        return status_of(launch_gemv_multi(dev, md, nb, X, nullptr, N, s));
     void* ws = workspace;
     if (!ws && (hipMallocAsync(&ws, need, s) != hipSuccess || ws == nullptr)) {
         (void)hipGetLastError();

@@ -362,6 +362,18 @@ bool gemv_fuses(int64_t N, int64_t nb) {
            (N <= kGemvFusedMaxN && static_cast<size_t>(N) * nb * (kActQBytes + kActSBytes) <= kMaxActLds);
 }
 
+// With several tokens, every workgroup of the fused kernel quantizes all of X
+// itself, and past N * K = 16384 values that prologue costs more than one
+// separate quantizer launch into a caller's workspace (measured on 4096 x
+// 14336 at N = 2, 4, 8 and on 14336 x 4096 and 128256 x 4096 at N = 8; below
+// it, e.g. 4096- and 14336-row matrices with K = 4096 at N = 4, the fused
+// kernel is faster).
+constexpr int64_t kFusedMaxValues = 16384;
+
+bool gemv_prefers_fused(int64_t N, int64_t nb) {
+    return gemv_fuses(N, nb) && (N == 1 || N * nb * kQK <= kFusedMaxValues);
+}
+
 hipError_t launch_gemv_fused(const DeviceInfo* dev, WLayout lay, const uint8_t* Wq, int64_t rows, int64_t nb,
                              const float* X, int64_t N, float* Y, hipStream_t s) {
     return fused_n(dev, lay_of(lay), Wq, rows, nb, X, N, Y, kNoMulti, s);

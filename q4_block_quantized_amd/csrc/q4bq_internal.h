@@ -100,6 +100,9 @@ hipError_t launch_gemv(const DeviceInfo* dev, WLayout lay, const uint8_t* Wq, in
 // as launch_act_from_f32 followed by launch_gemv.
 constexpr int64_t kGemvFusedMaxN = 1;
 bool gemv_fuses(int64_t N, int64_t nb);
+// Whether the fused kernel is also the faster choice when the caller has a
+// workspace for a separate quantizer launch.
+bool gemv_prefers_fused(int64_t N, int64_t nb);
 hipError_t launch_gemv_fused(const DeviceInfo* dev, WLayout lay, const uint8_t* Wq, int64_t rows, int64_t nb,
                              const float* X, int64_t N, float* Y, hipStream_t s);
 
