@@ -28,8 +28,8 @@
 // workgroups: every CU gets one.  Eight waves, two per SIMD:
 //  * waves 0-3 compute: each owns seven of the 28 tiles of 32 tokens x 32
 //    rows -- two token tiles against three row tiles, plus one more tile --
-//    so that every weight operand read from LDS (the binding resource: about
-//    128 bytes per clock per CU) serves two tiles; a wave holds its 7
+//    so that every weight operand read from LDS serves two tiles (fewer
+//    reads to issue and to wait for); a wave holds its 7
 //    accumulator tiles (112 registers) and runs a software pipeline over its
 //    tile steps -- the two matrix instructions of step k are issued around the
 //    16 FMAs that drain step k - 1, so the matrix core and the vector ALU work
