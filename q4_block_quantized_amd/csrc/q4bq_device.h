@@ -53,6 +53,23 @@ __device__ __forceinline__ uint32_t or_lanes(uint32_t v, int m) {
     return v | static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), m, 32));
 }
 
+// Cross-lane steps inside aligned groups of 8 lanes on the vector ALU (DPP,
+// no LDS round trip): lane i reads lane i ^ 1 or i ^ 2 (quad permutations), or
+// lane 7 - i of its group (half-row mirror).  After the two quad steps every
+// quad holds its own reduction, so the mirror step completes a reduction over
+// the 8 lanes.  The whole group must be active.
+constexpr int kDppXor1 = 0xB1;     // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;     // quad_perm [2, 3, 0, 1]
+constexpr int kDppMirror8 = 0x141;  // row_half_mirror
+template <int kCtrl>
+__device__ __forceinline__ int dpp8_i(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, kCtrl, 0xF, 0xF, false);
+}
+template <int kCtrl>
+__device__ __forceinline__ float dpp8_f(float v) {
+    return __builtin_bit_cast(float, dpp8_i<kCtrl>(__builtin_bit_cast(int, v)));
+}
+
 // Q8_0 activation rule on four consecutive values of a block: lane m of an
 // aligned group of 8 lanes holds elements 4m..4m+3 of the same block.
 //   d = binary16(amax / 127) (widened back to fp32), q = round(x / d) half
@@ -73,11 +90,11 @@ __device__ __forceinline__ uint32_t dot_order_word(int8_t q0, int8_t q1, int8_t 
     const uint32_t ev = static_cast<uint8_t>(q0) | (static_cast<uint32_t>(static_cast<uint8_t>(q2)) << 8);
     const uint32_t od = static_cast<uint8_t>(q1) | (static_cast<uint32_t>(static_cast<uint8_t>(q3)) << 8);
     const uint32_t mine = ev | (od << 16);
-    const uint32_t other = static_cast<uint32_t>(__shfl_xor(static_cast<int>(mine), 1, 8));
+    const uint32_t other = static_cast<uint32_t>(dpp8_i<kDppXor1>(static_cast<int>(mine)));
     int sum = static_cast<int>(q0) + q1 + q2 + q3;
-    sum += __shfl_xor(sum, 1, 8);
-    sum += __shfl_xor(sum, 2, 8);
-    sum += __shfl_xor(sum, 4, 8);
+    sum += dpp8_i<kDppXor1>(sum);
+    sum += dpp8_i<kDppXor2>(sum);
+    sum += dpp8_i<kDppMirror8>(sum);
     bias = -8 * sum;
     return (m & 1) ? ((other >> 16) | (od << 16)) : (ev | (other << 16));
 }
@@ -85,9 +102,9 @@ __device__ __forceinline__ uint32_t dot_order_word(int8_t q0, int8_t q1, int8_t 
 __device__ __forceinline__ ActScale quant_act_quad(float x0, float x1, float x2, float x3, int m, uint32_t& word,
                                                    uint32_t& dbits) {
     float a = fmaxf(fmaxf(fabsf(x0), fabsf(x1)), fmaxf(fabsf(x2), fabsf(x3)));
-    a = fmaxf(a, __shfl_xor(a, 1, 8));
-    a = fmaxf(a, __shfl_xor(a, 2, 8));
-    a = fmaxf(a, __shfl_xor(a, 4, 8));
+    a = fmaxf(a, dpp8_f<kDppXor1>(a));
+    a = fmaxf(a, dpp8_f<kDppXor2>(a));
+    a = fmaxf(a, dpp8_f<kDppMirror8>(a));
     dbits = float_to_half_bits(a / 127.0f);
     const float d = half_bits_to_float(dbits);
     const int8_t q0 = q8_rule(x0, d), q1 = q8_rule(x1, d), q2 = q8_rule(x2, d), q3 = q8_rule(x3, d);
