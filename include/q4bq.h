@@ -250,8 +250,9 @@ int q4_0_q8_0_block_dots(const void *Wq, int64_t rows, int64_t K, const void *Xq
  *                      q4bq_fused_workspace_size(rows, K, N), apart from every
  *                      other buffer (the form for graph capture).
  * Other arguments and errors as for mul_mat_q4_0_q8_0 (a short workspace:
- * Q4BQ_ENOMEM); N < 2^31 with LayerNorm.  Launches: LayerNorm statistics (if
- * any), one quantization pass, the product with the epilogue in its store.
+ * Q4BQ_ENOMEM); N < 2^31 with LayerNorm.  Launches: one kernel that
+ * normalizes X (if asked) and quantizes it, then the product with the
+ * epilogue in its store.
  */
 #define Q4BQ_ACT_NONE 0
 #define Q4BQ_ACT_GELU 1

@@ -498,6 +498,6 @@ const char* q4bq_status_string(int status) {
     }
 }
 
-int q4bq_version(void) { return 100; }
+int q4bq_version(void) { return 200; }
 
 }  // extern "C"
