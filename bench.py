@@ -60,7 +60,51 @@ def parse():
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of this many MiB, 5 times (a known-size kernel for "
                          "scaling HBM byte counters)")
+    ap.add_argument("--profile-legs", action="store_true",
+                    help="only run the other legs' kernels (Q8_0 weights on the head at N=1 and N=8, the fused "
+                         "SwiGLU, get_rows) 20 times each, eagerly, for a profiler; prints no JSON line")
     return ap.parse_args()
+
+
+def profile_legs(hip, torch):
+    """Twenty eager calls of each of the bench's other legs, for rocprofv3
+    (kernel trace and byte counters; the copy calibration runs first)."""
+    import numpy as np
+    from q4_block_quantized_amd import inputs
+    dev = torch.device("cuda")
+    rows, K = inputs.WORKLOADS[4].mats[0]
+    Wt = torch.from_numpy(inputs.weights(4, 0, rows, K)).to(dev)
+    Wq8 = hip.q8_0_quantize(Wt)
+    T = hip.q4_0_quantize(Wt)
+    del Wt
+    for N in (1, 8):
+        X = torch.from_numpy(inputs.activations(4, 0, N, K)).to(dev)
+        Y = torch.empty(N, rows, device=dev)
+        for _ in range(20):
+            hip.mul_mat_q8_0_q8_0(Wq8, X, Y)
+        torch.cuda.synchronize()
+        log("Q8_0 weights %dx%d N=%d: 20 calls" % (rows, K, N))
+    del Wq8
+    torch.cuda.empty_cache()
+    r3, K3 = inputs.WORKLOADS[3].mats[1]  # 14336 x 4096
+    Wg = hip.q4_0_quantize(torch.from_numpy(inputs.weights(3, 1, r3, K3)).to(dev))
+    Wu = hip.q4_0_quantize(torch.from_numpy(inputs.weights(3, 2, r3, K3)).to(dev))
+    X = torch.from_numpy(inputs.activations(3, 1, 1, K3)).to(dev)
+    gamma = torch.linspace(0.5, 1.5, K3, device=dev)
+    beta = torch.linspace(-0.1, 0.1, K3, device=dev)
+    H = torch.empty(1, r3, device=dev)
+    ws = hip.fused_workspace(r3, K3, 1, device=dev)
+    for _ in range(20):
+        hip.mul_mat_q4_0_q8_0_swiglu(Wg, Wu, X, gamma, beta, 1e-5, H, ws)
+    torch.cuda.synchronize()
+    log("SwiGLU 2 x %dx%d N=1: 20 calls" % (r3, K3))
+    del Wg, Wu
+    ids = torch.from_numpy(np.random.default_rng(inputs.seed(4, 0, 9)).integers(0, rows, 512).astype(np.int32)).to(dev)
+    out = torch.empty(512, K, device=dev)
+    for _ in range(20):
+        hip.q4_0_get_rows(T, K, ids, out)
+    torch.cuda.synchronize()
+    log("get_rows 512 ids of %dx%d: 20 calls" % (rows, K))
 
 
 def q4_bytes(rows, K):
@@ -452,6 +496,9 @@ def main():
         torch.cuda.synchronize()
         log("copy calibration: 5 x %d bytes" % n)
         del src, dst
+    if args.profile_legs:
+        profile_legs(hip, torch)
+        return
     cid = int(args.workload[1])
     from q4_block_quantized_amd import inputs
     wl = inputs.WORKLOADS[cid]
