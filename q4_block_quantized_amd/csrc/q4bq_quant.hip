@@ -305,53 +305,50 @@ k_q4_0_get_rows(const uint8_t* __restrict__ Wq, int64_t rows, int64_t nb, const 
     }
 }
 
-// Prefill records are written block-major: the 8-lane group that handles
-// record o = block * N + token reads block `block` of token `token`.
-__device__ __forceinline__ int64_t act6_source(int64_t o, int64_t N, int64_t nb) {
-    const int64_t b = o / N;
-    return (o - b * N) * nb + b;
-}
+// Prefill records are written block-major (record o = block * N + token).
+// Grid: y walks the blocks, x the tokens 32 at a time (an 8-lane group per
+// token; both loop bounds are uniform over each wave), so no index is
+// divided.
+constexpr int kAct6Tokens = kThreads / 8;  // tokens per workgroup iteration
 
 // fp32 activations -> prefill records (fp6 operands + binary16 scale bits).
 __global__ void __launch_bounds__(kThreads)
 k_act6_from_f32(const float* __restrict__ X, int64_t N, int64_t nb, uint32_t* __restrict__ rec) {
-    const int64_t nblocks = N * nb;
     const int m = threadIdx.x & 7;
-    const int64_t first = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) >> 3;
-    const int64_t step = static_cast<int64_t>(gridDim.x) * (kThreads / 8);
-    const int64_t wave_first = first & ~static_cast<int64_t>(7);
-    for (int64_t o0 = wave_first; o0 < nblocks; o0 += step) {
-        const int64_t o = o0 + (first & 7);
-        const bool valid = o < nblocks;
+    const int64_t step = static_cast<int64_t>(gridDim.x) * kAct6Tokens;
+    const int64_t wave_first = static_cast<int64_t>(blockIdx.x) * kAct6Tokens + ((threadIdx.x >> 3) & ~7);
+    for (int64_t b = blockIdx.y; b < nb; b += gridDim.y)
+    for (int64_t n0 = wave_first; n0 < N; n0 += step) {
+        const int64_t n = n0 + ((threadIdx.x >> 3) & 7);
+        const bool valid = n < N;
         float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (valid) __builtin_memcpy(&x, X + act6_source(o, N, nb) * kQK + 4 * m, 16);
+        if (valid) __builtin_memcpy(&x, X + (n * nb + b) * kQK + 4 * m, 16);
         uint32_t word, dbits;
         quant_act_quad(x.x, x.y, x.z, x.w, m, word, dbits);
-        store_act6(m, word, dbits, valid, o, rec);
+        store_act6(m, word, dbits, valid, b * N + n, rec);
     }
 }
 
 // Q8_0 blocks -> prefill records.
 __global__ void __launch_bounds__(kThreads)
 k_act6_from_q8(const uint8_t* __restrict__ Xq, int64_t N, int64_t nb, uint32_t* __restrict__ rec) {
-    const int64_t nblocks = N * nb;
     const int m = threadIdx.x & 7;
-    const int64_t first = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) >> 3;
-    const int64_t step = static_cast<int64_t>(gridDim.x) * (kThreads / 8);
-    const int64_t wave_first = first & ~static_cast<int64_t>(7);
-    for (int64_t o0 = wave_first; o0 < nblocks; o0 += step) {
-        const int64_t o = o0 + (first & 7);
-        const bool valid = o < nblocks;
+    const int64_t step = static_cast<int64_t>(gridDim.x) * kAct6Tokens;
+    const int64_t wave_first = static_cast<int64_t>(blockIdx.x) * kAct6Tokens + ((threadIdx.x >> 3) & ~7);
+    for (int64_t b = blockIdx.y; b < nb; b += gridDim.y)
+    for (int64_t n0 = wave_first; n0 < N; n0 += step) {
+        const int64_t n = n0 + ((threadIdx.x >> 3) & 7);
+        const bool valid = n < N;
         int8_t q[4] = {0, 0, 0, 0};
         uint16_t h = 0;
         if (valid) {
-            const uint8_t* blk = Xq + act6_source(o, N, nb) * kQ8Bytes;
+            const uint8_t* blk = Xq + (n * nb + b) * kQ8Bytes;
             __builtin_memcpy(q, blk + 2 + 4 * m, 4);
             __builtin_memcpy(&h, blk, 2);
         }
         int bias;
         const uint32_t word = dot_order_word(q[0], q[1], q[2], q[3], m, bias);
-        store_act6(m, word, h, valid, o, rec);
+        store_act6(m, word, h, valid, b * N + n, rec);
     }
 }
 
@@ -440,10 +437,14 @@ hipError_t launch_q8_0_quantize(const float* X, int64_t nblocks, uint8_t* Xq, hi
 }
 
 namespace {
-int act_grid(int64_t nblocks) {
-    int64_t wgs = (nblocks + (kThreads / 8) - 1) / (kThreads / 8);
-    if (wgs > 8192) wgs = 8192;
-    return static_cast<int>(wgs < 1 ? 1 : wgs);
+// Prefill records: y = blocks (at most 8192), x = token groups of kAct6Tokens,
+// at most 8192 workgroups in all.
+dim3 act6_grid(int64_t N, int64_t nb) {
+    const int64_t y = nb < 8192 ? nb : 8192;
+    int64_t x = (N + kAct6Tokens - 1) / kAct6Tokens;
+    const int64_t xmax = 8192 / y > 0 ? 8192 / y : 1;
+    if (x > xmax) x = xmax;
+    return dim3(static_cast<uint32_t>(x < 1 ? 1 : x), static_cast<uint32_t>(y < 1 ? 1 : y));
 }
 }  // namespace
 
@@ -451,7 +452,7 @@ hipError_t launch_act_from_f32(const float* X, int64_t N, int64_t nb, void* act,
     const int64_t nblocks = N * nb;
     if (N > kGemvMaxN) {
         uint32_t* rec = static_cast<uint32_t*>(act);
-        hipLaunchKernelGGL(k_act6_from_f32, dim3(act_grid(nblocks)), dim3(kThreads), 0, s, X, N, nb, rec);
+        hipLaunchKernelGGL(k_act6_from_f32, act6_grid(N, nb), dim3(kThreads), 0, s, X, N, nb, rec);
         return hipGetLastError();
     }
     uint32_t* q = static_cast<uint32_t*>(act);
@@ -497,7 +498,7 @@ hipError_t launch_act_from_q8(const uint8_t* Xq, int64_t N, int64_t nb, void* ac
     const int64_t nblocks = N * nb;
     if (N > kGemvMaxN) {
         uint32_t* rec = static_cast<uint32_t*>(act);
-        hipLaunchKernelGGL(k_act6_from_q8, dim3(act_grid(nblocks)), dim3(kThreads), 0, s, Xq, N, nb, rec);
+        hipLaunchKernelGGL(k_act6_from_q8, act6_grid(N, nb), dim3(kThreads), 0, s, Xq, N, nb, rec);
         return hipGetLastError();
     }
     uint32_t* q = static_cast<uint32_t*>(act);
