@@ -149,6 +149,27 @@ def test_product_sweep(hip, orc, rows, K):
         assert_close(Y, orc.mul_mat_ref(Wq_o, Xq_o, K), "rows=%d K=%d N=%d" % (rows, K, N))
 
 
+def test_prefill_very_long_rows(hip, orc):
+    """More tokens than the decode kernels take on rows of 8200 blocks: the
+    prefill activation records walk the blocks in more than one pass of the
+    grid (at most 8192 blocks per pass), the prefill kernel runs 4100 stages.
+    Oracle bar, the block dots, and the same bits from the pre-quantized
+    input."""
+    rows, K = 3, 8200 * 32
+    for N in (9, 40):
+        print("very long rows rows=%d K=%d N=%d" % (rows, K, N), flush=True)
+        W, X = _case(rows, K, N, 4242 + N)
+        Wq_o, Xq_o = orc.q4_0_quantize(W), orc.q8_0_quantize(X)
+        Wq = hip.q4_0_quantize(dev(W))
+        Xt = dev(X)
+        Xq = hip.q8_0_quantize(Xt)
+        Y = host(hip.mul_mat_q4_0_q8_0(Wq, Xt))
+        assert_close(Y, orc.mul_mat_ref(Wq_o, Xq_o, K), "rows=%d K=%d N=%d" % (rows, K, N))
+        assert np.array_equal(host(hip.mul_mat_q4_0_q8_0_pq(Wq, Xq, K)), Y), (rows, K, N)
+        D = host(hip.q4_0_q8_0_block_dots(Wq, Xq, K))
+        assert np.array_equal(D, orc.block_dots(Wq_o, Xq_o, K)), (rows, K, N)
+
+
 def test_paths_agree_bitwise(hip, orc):
     """Fused quantization, pre-quantized input, caller workspace and the
     stream-ordered scratch give the same bits; so do repeated calls and a
