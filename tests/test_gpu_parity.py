@@ -149,6 +149,26 @@ def test_product_sweep(hip, orc, rows, K):
         assert_close(Y, orc.mul_mat_ref(Wq_o, Xq_o, K), "rows=%d K=%d N=%d" % (rows, K, N))
 
 
+@pytest.mark.parametrize("K", [65536, 98336])
+def test_decode_rows_beyond_lds(hip, orc, K):
+    """One to eight tokens on rows whose quantized activations exceed the
+    decode kernels' 64 KB LDS budget (K = 98336: an odd block count): the
+    activations are read from the quantizer's buffer in global memory.  Oracle
+    bar, and the same bits from every entry point."""
+    for rows in (3, 70):
+        for N in (1, 3, 8):
+            print("beyond lds rows=%d K=%d N=%d" % (rows, K, N), flush=True)
+            W, X = _case(rows, K, N, 777 + rows + 3 * N)
+            Wq_o, Xq_o = orc.q4_0_quantize(W), orc.q8_0_quantize(X)
+            Wq = hip.q4_0_quantize(dev(W))
+            Xt = dev(X)
+            Y = host(hip.mul_mat_q4_0_q8_0(Wq, Xt))
+            assert_close(Y, orc.mul_mat_ref(Wq_o, Xq_o, K), "rows=%d K=%d N=%d" % (rows, K, N))
+            assert np.array_equal(host(hip.mul_mat_q4_0_q8_0_pq(Wq, hip.q8_0_quantize(Xt), K)), Y), (rows, K, N)
+            assert np.array_equal(host(hip.mul_mat_q4_0_q8_0_ex(Wq, Xt, hip.workspace(rows, K, N))), Y), (rows, K, N)
+            assert np.array_equal(host(hip.mul_mat_q4_0r_q8_0(hip.q4_0_repack(Wq, K), Xt)), Y), (rows, K, N)
+
+
 def test_prefill_very_long_rows(hip, orc):
     """More tokens than the decode kernels take on rows of 8200 blocks: the
     prefill activation records walk the blocks in more than one pass of the
