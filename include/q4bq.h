@@ -140,9 +140,10 @@ int mul_mat_q4_0_q8_0_prepared(const void *Wq, int64_t rows, int64_t K,
  *                                 bytes; code c = 4*m + i stands for element
  *                                 8*(m/2) + 2*i + (m%2) of the block and is
  *                                 the FP6 E2M3 encoding of (nibble - 8)/8
- *                                 (exact: |nibble - 8| <= 8).  In rows with
- *                                 bit 3 of r set the record's two 16-byte
- *                                 halves are stored swapped.
+ *                                 (exact: |nibble - 8| <= 8).  In rows r
+ *                                 where bit 2 xor bit 3 of r is set the
+ *                                 record's two 16-byte halves are stored
+ *                                 swapped.
  * The bytes in [18*nblk, R) are zero.  q4bq_repack_size(rows, K) gives the
  * total (0 for invalid sizes).  Every
  * 16-byte nibble block is aligned, so the decode kernels read it with single

@@ -498,6 +498,6 @@ const char* q4bq_status_string(int status) {
     }
 }
 
-int q4bq_version(void) { return 200; }
+int q4bq_version(void) { return 201; }
 
 }  // extern "C"

@@ -21,7 +21,9 @@
 //    ([block][token][64 bytes], from the quantizer) keep 16-byte quarter q of
 //    token t at position q ^ ((t >> 2) & 3); weight records (32 bytes per
 //    (row, block): 6 dwords of codes, d bits, zero) swap their two halves in
-//    rows with bit 3 set.
+//    rows where bit 2 xor bit 3 is set, which keeps both the 16-lane reads
+//    and the staging waves' 16-byte writes (8 lanes per cycle over 32 banks)
+//    free of conflicts.
 //
 // Shape: a workgroup computes 128 tokens x 224 rows.  224 = 7 x 32 makes
 // 14336-row matrices split into 64 row tiles, so the 512-token prefill is 256
@@ -177,7 +179,7 @@ __device__ __forceinline__ void tile_step(const Operand& ak, const Operand& wk, 
 // dealt round-robin to the staging waves.
 constexpr int kRecDma = kBufB / 1024;
 static_assert(kBufB % 1024 == 0 && kPlaneB % 16 == 0, "record staging in 1 KB wave moves");
-static_assert(kTR % 16 == 0, "row tiles keep the record swizzle (bit 3 of the row)");
+static_assert(kTR % 16 == 0, "row tiles keep the record swizzle (bits 2 and 3 of the row)");
 
 template <bool DOTS, bool RP, bool EPI>
 __global__ void __launch_bounds__(kT)
@@ -279,13 +281,13 @@ k_prefill(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Wrec, int6
         }
         // weights: staging thread u < 224 converts row u's blocks of a stage.
         // LDS record: 6 dwords of fp6 codes, binary16 d bits, zero; the two
-        // 16-byte halves swap places in rows with bit 3 set.
+        // 16-byte halves swap places in rows where bit 2 xor bit 3 is set.
         const bool w_thread = u < kTR;
         const int w_row = w_thread ? u : 0;
         const bool w_row_ok = w_thread && r0 + w_row < rows;
         const int64_t w_row_first = (r0 + (w_row_ok ? w_row : 0)) * nb;
         const uint8_t* w_src = Wq + w_row_first * kQ4Bytes;
-        const int w_swap = (w_row >> 3) & 1;
+        const int w_swap = ((w_row >> 2) ^ (w_row >> 3)) & 1;
         Block4 rw[2][kKB];
         bool rw_ok[2][kKB];
         // loads are unconditional (block 0 of a valid row when the wanted block
@@ -367,7 +369,7 @@ k_prefill(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Wrec, int6
         a_p0[u] = a_row + 16 * ((2 * half) ^ a_sw);
         a_p1[u] = a_row + 16 * ((2 * half + 1) ^ a_sw);
     }
-    const int b_sw = (l32 >> 3) & 1;
+    const int b_sw = ((l32 >> 2) ^ (l32 >> 3)) & 1;
     const int b_row = l32 * kRecW;
     const int b_p0 = b_row + 16 * b_sw;
     const int b_p1 = b_row + 16 * (b_sw ^ 1);

@@ -231,8 +231,8 @@ k_act_from_f32(const float* __restrict__ X, int64_t nblocks, uint32_t* __restric
 //  * the binary16 scales in (row, block) order;
 //  * at rec_off, the matrix-core weight records of the prefill kernel, block
 //    major ([block][row], 32 bytes: 6 dwords of fp6 codes of (nibble - 8)/8,
-//    the scale bits, a zero dword; the two 16-byte halves swapped in rows with
-//    bit 3 set, the LDS order), followed by one plane of zero records that
+//    the scale bits, a zero dword; the two 16-byte halves swapped in rows where
+//    bit 2 xor bit 3 is set, the LDS order), followed by one plane of zero records that
 //    stands for blocks past the end.
 // The bytes between the scale stream and the records are zero.  No value
 // changes; the records are the kernel's own conversion, done once.
@@ -263,7 +263,7 @@ k_q4_0_repack(const uint8_t* __restrict__ Wq, int64_t rows, int64_t nb, int64_t 
             r = g - nblocks;  // the zero plane
             b = nb;
         }
-        const int swap = static_cast<int>((r >> 3) & 1);
+        const int swap = static_cast<int>(((r >> 2) ^ (r >> 3)) & 1);
         uint8_t* p = rec + (b * rows + r) * 32;
         *reinterpret_cast<u32x4*>(p + 16 * swap) = u32x4{d6[0], d6[1], d6[2], d6[3]};
         *reinterpret_cast<u32x4*>(p + 16 * (swap ^ 1)) = u32x4{d6[4], d6[5], dbits, 0u};

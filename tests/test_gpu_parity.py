@@ -296,7 +296,7 @@ def _repack_expected(Wq_h, rows, K):
     a multiple of 256, then the block-major 32-byte records (24 bytes of E2M3
     codes of (nibble - 8)/8, code c at bits 6c, code 4m + i for element
     8(m//2) + 2i + m%2; the scale bytes; 6 zero bytes; 16-byte halves swapped
-    in rows with bit 3 set) and one plane of zero records."""
+    in rows where bit 2 xor bit 3 is set) and one plane of zero records."""
     nb = K // 32
     blocks = Wq_h.reshape(rows * nb, 18)
     head = np.concatenate([blocks[:, 2:].reshape(-1), blocks[:, :2].reshape(-1)])
@@ -317,7 +317,8 @@ def _repack_expected(Wq_h, rows, K):
     rec[:, :24] = np.packbits(bits, axis=1, bitorder="little")
     rec[:, 24:26] = blocks[:, :2]
     rec = rec.reshape(rows, nb, 32)
-    swap = (np.arange(rows) & 8) != 0
+    r = np.arange(rows)
+    swap = (((r >> 2) ^ (r >> 3)) & 1) != 0
     rec[swap] = np.concatenate([rec[swap][:, :, 16:], rec[swap][:, :, :16]], axis=2)
     planes = np.zeros((nb + 1, rows, 32), dtype=np.uint8)
     planes[:nb] = rec.transpose(1, 0, 2)
