@@ -12,12 +12,15 @@
  * Sources (the pages the method is taken from):
  *   [P3-2]  "llama.cpp 深度解读" (luoboask.github.io), section 2
  *           "量化数据结构 — Q4_0 格式详解": the block_q4_0 struct (fp16 d + 16 bytes
- *           of nibbles, 32 weights), its 4-step encode and its decode
- *           (value = (nibble - 8) * d, low nibble = even element).
- *   [P3-3]  same page, section 3 "量化矩阵乘法 — 核心算子": ggml_vec_dot_q4_0_q8_0,
- *           per block d = d_x * d_y (both fp16 widened to fp32), integer sum of
- *           nibble * int8 products, then sumf += d * sumi.  Activations are
- *           Q8_0-quantized so the dot runs in the integer domain.
+ *           of nibbles, 32 weights), how a block is encoded (the scale from the
+ *           largest magnitude over 8, each weight rounded against it and offset
+ *           by 8) and its decode (value = (nibble - 8) * d, low nibble = even
+ *           element).
+ *   [P3-3]  same page, section 3 "量化矩阵乘法 — 核心算子": the Q4_0 x Q8_0 dot
+ *           product -- per pair of blocks an exact integer dot of the codes,
+ *           scaled by the product of the two fp16 scales and summed in fp32.
+ *           Activations are Q8_0-quantized so the dot runs in the integer
+ *           domain.
  *   [P3-1]  same page, section 1: the table of ggml quantization types, with
  *           Q8_0 (8 bits per weight) beside Q4_0 as a weight format.
  *   [P4]    ggml GPT-2 walkthrough (aicoding.csdn.net): section 3.1 LayerNorm
@@ -118,43 +121,78 @@ void orc_f32_to_f16_array(const float *x, int64_t n, uint16_t *out)
 }
 
 /* ------------------------------------------------------------------------ */
+/* Block codes and scales.                                                   */
+/*                                                                           */
+/* [P3-2] defines a Q4_0 block as a binary16 scale d followed by 32 four-bit */
+/* fields, element j in byte j/2 (low half for even j), whose value is       */
+/* (field - 8) * d.  A Q8_0 block is the same scale followed by 32 signed    */
+/* bytes, element j worth byte_j * d.  Below, "code" is the signed integer   */
+/* that multiplies d: field - 8 in [-8, 7] for Q4_0, the byte in [-127, 127] */
+/* for Q8_0.                                                                  */
+/* ------------------------------------------------------------------------ */
+
+static float orc_block_d(const uint8_t *blk)
+{
+    return orc_f16_to_f32((uint16_t)(blk[0] | (blk[1] << 8)));
+}
+
+static int orc_q4_0_code(const uint8_t *blk, int j)
+{
+    uint8_t byte = blk[2 + j / 2];
+    int field = (j % 2 == 0) ? (byte & 0x0f) : (byte >> 4);
+    return field - 8;
+}
+
+static int orc_q8_0_code(const uint8_t *blk, int j)
+{
+    return (int)(int8_t)blk[2 + j];
+}
+
+/* The scale of 32 values encoded with `top` positive steps (8 for Q4_0, 127
+ * for Q8_0): the largest magnitude divided by `top` in fp32, kept as the
+ * nearest binary16 (R6).  Returns its bits. */
+static uint16_t orc_scale_bits(const float *v, float top)
+{
+    float amax = 0.0f;
+    for (int k = 0; k < ORC_QK; ++k)
+        if (fabsf(v[k]) > amax)
+            amax = fabsf(v[k]);
+    return orc_f32_to_f16(amax / top);
+}
+
+/* The code of v against the STORED scale d (R2): v / d in fp32 rounded to the
+ * nearest integer, halves away from zero (R3), limited to [lo, hi] (G5 for
+ * Q4_0, R5 for Q8_0); 0 when d is 0 (R4). */
+static int orc_code(float v, float d, int lo, int hi)
+{
+    if (d == 0.0f)
+        return 0;
+    int c = (int)roundf(v / d);
+    return c < lo ? lo : (c > hi ? hi : c);
+}
+
+static void orc_put_scale(uint16_t dh, uint8_t *blk)
+{
+    blk[0] = (uint8_t)(dh & 0xffu);
+    blk[1] = (uint8_t)(dh >> 8);
+}
+
+/* ------------------------------------------------------------------------ */
 /* Q4_0 encode / decode, [P3-2].                                            */
 /* ------------------------------------------------------------------------ */
 
-/* One block of 32 weights -> 18 bytes. */
+/* One block of 32 weights -> 18 bytes: the binary16 scale amax / 8, then the
+ * 4-bit fields code + 8 (R1: element j in byte j/2, even j in the low half). */
 void orc_q4_0_quantize_block(const float *w, uint8_t *out)
 {
-    /* step 1: largest magnitude in the block */
-    float amax = 0.0f;
-    for (int k = 0; k < ORC_QK; ++k) {
-        float a = fabsf(w[k]);
-        if (a > amax)
-            amax = a;
-    }
-    /* step 2: scale = amax / 8, stored as fp16 (R6); divide by the stored value (R2) */
-    float scale = amax / 8.0f;
-    uint16_t dh = orc_f32_to_f16(scale);
+    uint16_t dh = orc_scale_bits(w, 8.0f);
     float d = orc_f16_to_f32(dh);
-    /* step 3: q = round(w / d) + 8, clamped into the nibble range (R3, R4, G5) */
-    int q[ORC_QK];
-    for (int k = 0; k < ORC_QK; ++k) {
-        if (d == 0.0f) {
-            q[k] = 8;
-        } else {
-            float t = w[k] / d;
-            int v = (int)roundf(t) + 8;
-            if (v < 0)
-                v = 0;
-            if (v > 15)
-                v = 15;
-            q[k] = v;
-        }
+    orc_put_scale(dh, out);
+    memset(out + 2, 0, ORC_QK / 2);
+    for (int j = 0; j < ORC_QK; ++j) {
+        int field = orc_code(w[j], d, -8, 7) + 8;
+        out[2 + j / 2] |= (uint8_t)(j % 2 == 0 ? field : field << 4);
     }
-    /* step 4: two nibbles per byte, even element in the low nibble (R1) */
-    out[0] = (uint8_t)(dh & 0xffu);
-    out[1] = (uint8_t)(dh >> 8);
-    for (int j = 0; j < ORC_QK / 2; ++j)
-        out[2 + j] = (uint8_t)(q[2 * j] | (q[2 * j + 1] << 4));
 }
 
 /* rows x K fp32 (row-major) -> rows x (K/32) blocks of 18 bytes. */
@@ -167,52 +205,31 @@ void orc_q4_0_quantize(const float *W, int64_t rows, int64_t K, uint8_t *Wq)
                                     Wq + (r * nb + b) * ORC_Q4_BYTES);
 }
 
-/* Decode: element j of a block is (nibble - 8) * d, nibble j taken from byte
- * j/2, low nibble for even j. */
+/* Decode: element j of a block is code_j * d. */
 void orc_q4_0_dequantize(const uint8_t *Wq, int64_t rows, int64_t K, float *W)
 {
     int64_t nb = K / ORC_QK;
     for (int64_t r = 0; r < rows; ++r) {
         for (int64_t b = 0; b < nb; ++b) {
             const uint8_t *blk = Wq + (r * nb + b) * ORC_Q4_BYTES;
-            float d = orc_f16_to_f32((uint16_t)(blk[0] | (blk[1] << 8)));
-            for (int j = 0; j < ORC_QK; ++j) {
-                uint8_t byte = blk[2 + j / 2];
-                int nib = (j % 2 == 0) ? (byte & 0x0f) : (byte >> 4);
-                W[r * K + b * ORC_QK + j] = (float)(nib - 8) * d;
-            }
+            float d = orc_block_d(blk);
+            for (int j = 0; j < ORC_QK; ++j)
+                W[r * K + b * ORC_QK + j] = (float)orc_q4_0_code(blk, j) * d;
         }
     }
 }
 
 /* ------------------------------------------------------------------------ */
-/* Q8_0 encode (R5).                                                         */
+/* Q8_0 encode (R5): the binary16 scale amax / 127, then the codes.          */
 /* ------------------------------------------------------------------------ */
 
 void orc_q8_0_quantize_block(const float *x, uint8_t *out)
 {
-    float amax = 0.0f;
-    for (int k = 0; k < ORC_QK; ++k) {
-        float a = fabsf(x[k]);
-        if (a > amax)
-            amax = a;
-    }
-    float scale = amax / 127.0f;
-    uint16_t dh = orc_f32_to_f16(scale);
+    uint16_t dh = orc_scale_bits(x, 127.0f);
     float d = orc_f16_to_f32(dh);
-    out[0] = (uint8_t)(dh & 0xffu);
-    out[1] = (uint8_t)(dh >> 8);
-    for (int k = 0; k < ORC_QK; ++k) {
-        int v = 0;
-        if (d != 0.0f) {
-            v = (int)roundf(x[k] / d);
-            if (v < -127)
-                v = -127;
-            if (v > 127)
-                v = 127;
-        }
-        out[2 + k] = (uint8_t)(int8_t)v;
-    }
+    orc_put_scale(dh, out);
+    for (int j = 0; j < ORC_QK; ++j)
+        out[2 + j] = (uint8_t)(int8_t)orc_code(x[j], d, -127, 127);
 }
 
 void orc_q8_0_quantize(const float *X, int64_t N, int64_t K, uint8_t *Xq)
@@ -225,20 +242,18 @@ void orc_q8_0_quantize(const float *X, int64_t N, int64_t K, uint8_t *Xq)
 }
 
 /* ------------------------------------------------------------------------ */
-/* Per-block integer dot, [P3-3] with the offset of [P3-2] (G1).             */
+/* Per-block integer dot, [P3-3].  The product of a weight block and an     */
+/* activation block is d_w * d_x * (sum over the 32 elements of code_w *     */
+/* code_x); with the weights' code being field - 8 by [P3-2]'s decode (G1),  */
+/* the sum is an exact integer.                                              */
 /* ------------------------------------------------------------------------ */
 
 int32_t orc_block_dot(const uint8_t *wblk, const uint8_t *xblk)
 {
-    const uint8_t *qs = wblk + 2;
-    const int8_t *y = (const int8_t *)(xblk + 2);
-    int32_t sumi = 0;
-    for (int j = 0; j < ORC_QK / 2; ++j) {
-        int v0 = (qs[j] & 0x0f) - 8; /* element 2j   */
-        int v1 = (qs[j] >> 4) - 8;   /* element 2j+1 */
-        sumi += v0 * y[2 * j] + v1 * y[2 * j + 1];
-    }
-    return sumi;
+    int32_t s = 0;
+    for (int j = 0; j < ORC_QK; ++j)
+        s += orc_q4_0_code(wblk, j) * orc_q8_0_code(xblk, j);
+    return s;
 }
 
 /* D[(n * rows + r) * nb + b] = dot of weight block (r, b) with activation
@@ -253,11 +268,6 @@ void orc_block_dots(const uint8_t *Wq, int64_t rows, int64_t K,
                 D[(n * rows + r) * nb + b] =
                     orc_block_dot(Wq + (r * nb + b) * ORC_Q4_BYTES,
                                   Xq + (n * nb + b) * ORC_Q8_BYTES);
-}
-
-static float orc_block_d(const uint8_t *blk)
-{
-    return orc_f16_to_f32((uint16_t)(blk[0] | (blk[1] << 8)));
 }
 
 /* ------------------------------------------------------------------------ */
@@ -286,23 +296,25 @@ void orc_mul_mat_ref(const uint8_t *Wq, int64_t rows, int64_t K,
     }
 }
 
-/* The page's own fp32 accumulation: d = d0 * d1 in fp32, sumf += d * sumi in
- * fp32, increasing block order ([P3-3] steps 3 and 5). */
+/* The same block terms accumulated in binary32, as the page's dot routine
+ * does it ([P3-3]): each term is the binary32 product of the two widened
+ * scales times the block's integer dot converted to binary32, and the terms
+ * are added into a binary32 running sum in increasing block order. */
 void orc_mul_mat_pages_f32(const uint8_t *Wq, int64_t rows, int64_t K,
                            const uint8_t *Xq, int64_t N, float *Y)
 {
     int64_t nb = K / ORC_QK;
     for (int64_t n = 0; n < N; ++n) {
         for (int64_t r = 0; r < rows; ++r) {
-            float sumf = 0.0f;
+            float acc = 0.0f;
             for (int64_t b = 0; b < nb; ++b) {
                 const uint8_t *wb = Wq + (r * nb + b) * ORC_Q4_BYTES;
                 const uint8_t *xb = Xq + (n * nb + b) * ORC_Q8_BYTES;
-                float d = orc_block_d(wb) * orc_block_d(xb);
-                int32_t sumi = orc_block_dot(wb, xb);
-                sumf += d * (float)sumi;
+                float scale = orc_block_d(wb) * orc_block_d(xb);
+                float term = scale * (float)orc_block_dot(wb, xb);
+                acc = acc + term;
             }
-            Y[n * rows + r] = sumf;
+            Y[n * rows + r] = acc;
         }
     }
 }
@@ -316,12 +328,10 @@ void orc_mul_mat_pages_f32(const uint8_t *Wq, int64_t rows, int64_t K,
 
 int32_t orc_block_dot_q8(const uint8_t *wblk, const uint8_t *xblk)
 {
-    const int8_t *w = (const int8_t *)(wblk + 2);
-    const int8_t *y = (const int8_t *)(xblk + 2);
-    int32_t sumi = 0;
+    int32_t s = 0;
     for (int j = 0; j < ORC_QK; ++j)
-        sumi += (int32_t)w[j] * (int32_t)y[j];
-    return sumi;
+        s += orc_q8_0_code(wblk, j) * orc_q8_0_code(xblk, j);
+    return s;
 }
 
 void orc_block_dots_q8(const uint8_t *Wq, int64_t rows, int64_t K,

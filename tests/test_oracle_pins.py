@@ -117,6 +117,35 @@ def test_p3_tie_rounding_matches_libm_round():
     assert libm.roundf(np.float32(0.49999997)) == 0.0
 
 
+def _units(s):
+    """Values given in units of 2^-24 (the smallest binary16 subnormal), as fp32."""
+    return np.array([float(t) for t in s.split()], np.float64) * 2.0 ** -24
+
+
+def test_p9_q8_0_subnormal_scale_clamp(orc):
+    """A Q8_0 block whose stored scale is the binary16 subnormal 2^-24: the
+    codes reach +-178 before the clamp to [-127, 127] (hand-worked)."""
+    g = read_golden("q8_0_subnormal_clamp_block.txt")
+    x = np.zeros(32, np.float32)
+    v = _units(g["units_of_2^-24"][0])
+    x[:v.size] = v
+    assert np.array_equal(x[:v.size].astype(np.float64), v)       # exact fp32 inputs
+    got = orc.q8_0_quantize(x[None])[0]
+    assert np.array_equal(got, hexbytes(g["bytes"][0]))
+    assert not np.array_equal(got, hexbytes(g["clamp_minus_128_bytes_rejected"][0]))
+
+
+def test_p9_q4_0_subnormal_scale_clamps_both_sides(orc):
+    """A Q4_0 block whose stored scale rounds down to the subnormal 2^-24, so
+    the most negative weight clips to nibble 0 as well (hand-worked)."""
+    g = read_golden("q4_0_subnormal_clamp_block.txt")
+    w = np.zeros(32, np.float32)
+    v = _units(g["units_of_2^-24"][0])
+    w[:v.size] = v
+    assert np.array_equal(w[:v.size].astype(np.float64), v)
+    assert np.array_equal(orc.q4_0_quantize(w[None])[0], hexbytes(g["bytes"][0]))
+
+
 def test_p9_zero_blocks(orc):
     g = read_golden("zero_blocks.txt")
     assert np.array_equal(orc.q4_0_quantize(np.zeros((1, 32), np.float32))[0],
@@ -548,6 +577,30 @@ def test_gelu_against_the_normal_cdf(orc):
         assert abs(orc.gelu(x) - orc.gelu(-x) - x) < 1e-12
         assert abs(orc.gelu(x) - x * ndtr(x)) < 1e-3
     assert orc.gelu(30.0) == 30.0 and orc.gelu(-30.0) == 0.0
+
+
+def test_gelu_tanh_form_golden_values(orc):
+    """GPT-2's tanh form at five points, worked out with its intermediates
+    (tests/golden/gelu_tanh_values.txt); the erf form and a mistyped
+    0.044715 both miss them by far more than the 1e-12 allowed here."""
+    for v in read_golden("gelu_tanh_values.txt")["value"]:
+        x, want = (float(t) for t in v.split("|"))
+        assert abs(orc.gelu(x) - want) <= 1e-12 * max(1.0, abs(want)), (x, orc.gelu(x), want)
+
+
+def test_layernorm_mean_off_the_fp32_grid(orc):
+    """A token whose mean 4096 + 2^-16 is not an fp32 value (hand-worked in
+    tests/golden/layernorm_offset_block.txt): the fp64 statistics give
+    sqrt(31) and -1/sqrt(31), rounded once to fp32; an fp32 mean would give
+    5.657 and 0."""
+    g = read_golden("layernorm_offset_block.txt")
+    K = int(g["K"][0])
+    x = np.full((1, K), 4096.0, np.float32)
+    x[0, 0] = np.float32(4096.0 + float(g["x0_above_4096"][0]))
+    assert float(x[0, 0]) - 4096.0 == 2.0 ** -11
+    out = orc.layernorm(x, np.ones(K, np.float32), np.zeros(K, np.float32), 0.0)
+    assert out[0, 0] == np.float32(float(g["out_first"][0]))
+    assert np.all(out[0, 1:] == np.float32(float(g["out_rest"][0])))
 
 
 def test_silu_is_x_times_sigmoid(orc):
