@@ -56,7 +56,7 @@ extern "C" {
 #define Q4BQ_Q8_0_BYTES 34
 
 /*
- * Q4_0 encode, "llama.cpp 深度解读" section 2, encode steps 1-4: per block of
+ * Q4_0 encode, "llama.cpp 深度解读" section 2 (the block encode): per block of
  * 32 weights, amax = max |w|; the scale amax / 8 is stored as binary16
  * (round to nearest even, subnormals kept); q = round(w / d) + 8 with d the
  * stored scale widened to fp32, round() half away from zero, clamped to
@@ -84,9 +84,11 @@ int q8_0_quantize(const float *X, int64_t N, int64_t K, void *Xq, void *stream);
  *   Wq  rows x (K/32) Q4_0 blocks, 2-byte aligned.
  *   X   fp32 N x K, 4-byte aligned.
  *   Y   fp32 N x rows, 4-byte aligned, overwritten; must not overlap Wq or X.
- * N <= 8 runs the streaming decode kernel; larger N the int8 matrix-core
- * kernel.  Needs stream-ordered scratch of q4bq_workspace_size(rows, K, N)
- * bytes, taken with hipMallocAsync on `stream` (Q4BQ_ENOMEM if that fails).
+ * N <= 8 runs the streaming decode kernel; larger N the matrix-core kernel,
+ * in ceil(rows / 224) * ceil(N / 128) workgroups of 512 threads: shapes whose
+ * grid would exceed HIP's 2^32 - 1 work-items return Q4BQ_EINVAL.  Needs
+ * stream-ordered scratch of q4bq_workspace_size(rows, K, N) bytes, taken with
+ * hipMallocAsync on `stream` (Q4BQ_ENOMEM if that fails).
  * The summation order is fixed for a given (rows, K, N, device), so repeated
  * calls give bitwise-identical Y.
  */
@@ -251,7 +253,8 @@ int q4_0_q8_0_block_dots(const void *Wq, int64_t rows, int64_t K, const void *Xq
  *                      q4bq_fused_workspace_size(rows, K, N), apart from every
  *                      other buffer (the form for graph capture).
  * Other arguments and errors as for mul_mat_q4_0_q8_0 (a short workspace:
- * Q4BQ_ENOMEM); N < 2^31 with LayerNorm.  Launches: one kernel that
+ * Q4BQ_ENOMEM); N < 2^22 with LayerNorm (one 1024-thread workgroup per
+ * token).  Launches: one kernel that
  * normalizes X (if asked) and quantizes it, then the product with the
  * epilogue in its store.
  */

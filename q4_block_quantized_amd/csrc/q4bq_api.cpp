@@ -178,7 +178,11 @@ int check_product(const void* Wq, int64_t rows, int64_t K, const void* Xany, Act
     const int64_t nb = K / kQK;
     if (too_big(rows, K, 1) || too_big(N, K, 4) || too_big(N, rows, 4)) return Q4BQ_EINVAL;
     if (dots && too_big(N * rows, nb, 4)) return Q4BQ_EINVAL;
-    if (N > kGemvMaxN && ((rows + 127) / 128) * ((N + 255) / 256) >= (int64_t(1) << 31)) return Q4BQ_EINVAL;
+    // the matrix-core kernel's grid must stay within HIP's work-item limit
+    if (N > kGemvMaxN &&
+        ((rows + kPrefillRows - 1) / kPrefillRows) * ((N + kPrefillTokens - 1) / kPrefillTokens) >
+            kMaxWorkItems / kPrefillThreads)
+        return Q4BQ_EINVAL;
     const uintptr_t x_align = kind == kF32 ? 4 : kind == kQ8 ? 2 : 16;
     if (!aligned(Wq, lay == kRepacked ? 16 : 2) || !aligned(Xany, x_align) || !aligned(out, 4)) return Q4BQ_EINVAL;
     if (lay == kRepacked && too_big(rows, K + kQK, 2)) return Q4BQ_EINVAL;
@@ -321,7 +325,7 @@ namespace {
 int check_fusion(int64_t K, int64_t rows, int64_t N, const float* ln_gamma, const float* ln_beta, float ln_eps,
                  const float* bias, int act, const float* mul, const float* Y) {
     if ((ln_gamma == nullptr) != (ln_beta == nullptr)) return Q4BQ_EINVAL;
-    if (ln_gamma && (!(ln_eps >= 0.0f) || ln_eps > 3.0e38f || N >= (int64_t(1) << 31))) return Q4BQ_EINVAL;
+    if (ln_gamma && (!(ln_eps >= 0.0f) || ln_eps > 3.0e38f || N > kMaxWorkItems / kLnActThreads)) return Q4BQ_EINVAL;
     if (act != kEpiNone && act != kEpiGelu && act != kEpiSilu) return Q4BQ_EINVAL;
     if (!aligned(ln_gamma, 4) || !aligned(ln_beta, 4) || !aligned(bias, 4) || !aligned(mul, 4)) return Q4BQ_EINVAL;
     const size_t y_bytes = static_cast<size_t>(N * rows) * 4;

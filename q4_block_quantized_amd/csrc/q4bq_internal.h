@@ -126,8 +126,19 @@ hipError_t launch_rows_x(const DeviceInfo* dev, int lay, const uint8_t* Wq, int6
 hipError_t launch_rows_act(const DeviceInfo* dev, int lay, const uint8_t* Wq, int64_t rows, int64_t nb,
                            const void* act, int64_t N, float* Y, const MultiDesc& md, hipStream_t s);
 
-// Matrix-core kernel (128-token x 224-row tiles), any N; the one the library
-// runs above kGemvMaxN.  D as above.
+// Matrix-core kernel geometry: a workgroup of kPrefillThreads threads computes
+// kPrefillTokens tokens x kPrefillRows rows, so a launch has
+// ceil(rows / kPrefillRows) * ceil(N / kPrefillTokens) workgroups.
+constexpr int kPrefillThreads = 512;
+constexpr int kPrefillTokens = 128;
+constexpr int kPrefillRows = 224;
+// LayerNorm + quantization kernel: one workgroup of kLnActThreads per token.
+constexpr int kLnActThreads = 1024;
+// HIP launches fewer than 2^32 work-items per grid dimension.
+constexpr int64_t kMaxWorkItems = (int64_t(1) << 32) - 1;
+
+// Matrix-core kernel, any N; the one the library runs above kGemvMaxN.  D as
+// above.
 hipError_t launch_prefill(const DeviceInfo* dev, WLayout lay, const uint8_t* Wq, int64_t rows, int64_t nb,
                           const void* act, int64_t N, float* Y, int32_t* D, hipStream_t s,
                           const Epilogue& epi = Epilogue{nullptr, nullptr, kEpiNone});

@@ -69,6 +69,8 @@ constexpr int kDma = kKB * 2;
 static_assert(kNS * kStage <= 160 * 1024, "LDS budget");
 static_assert(kDma * kCW * 16 == kKB * kTT, "activation staging covers the planes");
 static_assert(kTR <= kST, "one weight row per staging thread");
+static_assert(kT == kPrefillThreads && kTT == kPrefillTokens && kTR == kPrefillRows,
+              "launch geometry the argument checks bound");
 
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));

@@ -104,7 +104,6 @@ __device__ __forceinline__ float ln_value(float x, double mu, double rstd, float
 // holds quads t, t + T, ... (QPT of them, four values each, loaded in one
 // round); T is a multiple of 8, so the 8 lanes of a block are neighbours, as
 // the quantizer wants.  QPT = 0: rows too long for registers, re-read per pass.
-constexpr int kLnActThreads = 1024;
 
 __device__ __forceinline__ double block_sum_big(double v, double* red) {
 #pragma unroll

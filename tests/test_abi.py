@@ -78,6 +78,9 @@ def _bad_product_calls(L):
     yield f(A, 4, 64, B, 1, A + 8, None)           # Y overlaps the weights
     yield f(A, 4, 64, B, 2, B + 16, None)          # Y overlaps X
     yield f(A, 1 << 41, 64, B, 1, C, None)         # absurd row count
+    # a matrix-core grid of 2^22 * 2 workgroups x 512 threads = 2^32 work-items:
+    # one past HIP's limit (rows = 2^22 * 224, N = 129 -> 2 token tiles)
+    yield f(1 << 40, (1 << 22) * 224, 32, 2 << 40, 129, 3 << 40, None)
     g = L.mul_mat_q4_0_q8_0_pq
     yield g(A, 4, 64, B + 1, 1, C, None)           # Q8_0 data on an odd address
     yield g(A, 4, 80, B, 1, C, None)               # K % 32 != 0
@@ -141,6 +144,9 @@ def _bad_product_calls(L):
     yield fu(A, 4, 64, B, 1, None, None, ctypes.c_float(0.0), WS + 2, 0, None, C, None, 0, None)  # bias misaligned
     yield fu(A, 4, 64, B, 1, None, None, ctypes.c_float(0.0), None, 0, None, C, WS + 8, 1 << 20, None)  # ws misaligned
     yield fu(A, 4, 64, B, 1, None, None, ctypes.c_float(0.0), None, 0, None, C, C, 1 << 20, None)       # ws over Y
+    # LayerNorm runs one 1024-thread workgroup per token: N = 2^22 is past HIP's grid limit
+    yield fu(1 << 40, 4, 32, 2 << 40, 1 << 22, 3 << 40, (3 << 40) + 1024, ctypes.c_float(0.0), None, 0, None,
+             4 << 40, None, 0, None)
     sw = L.mul_mat_q4_0_q8_0_swiglu
     yield sw(A, None, 4, 64, B, 1, None, None, ctypes.c_float(0.0), C, None, 0, None)   # null up matrix
     yield sw(A, A + 4096, 4, 64, B, 1, WS, None, ctypes.c_float(0.0), C, None, 0, None)  # beta missing
