@@ -339,7 +339,7 @@ hipError_t fused_n(const DeviceInfo* dev, int lay, const uint8_t* Wq, int64_t ro
 
 hipError_t gemv_n(const DeviceInfo* dev, int lay, const uint8_t* Wq, int64_t rows, int64_t nb, const void* act,
                   int64_t N, float* Y, int32_t* D, const MultiDesc& md, hipStream_t s) {
-    if (!D && rows_apply(N, nb)) return launch_rows_act(dev, lay, Wq, rows, nb, act, N, Y, md, s);
+    if (rows_apply(N, nb)) return launch_rows_act(dev, lay, Wq, rows, nb, act, N, Y, md, s, D);
     switch (N) {
         case 1: return launch_n<1>(dev, lay, Wq, rows, nb, act, Y, D, md, s);
         case 2: return launch_n<2>(dev, lay, Wq, rows, nb, act, Y, D, md, s);

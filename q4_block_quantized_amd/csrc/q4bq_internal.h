@@ -123,8 +123,10 @@ enum DecodeLayout { kLayAoS = 0, kLayRepacked = 1, kLayMulti = 2 };
 bool rows_apply(int64_t N, int64_t nb);
 hipError_t launch_rows_x(const DeviceInfo* dev, int lay, const uint8_t* Wq, int64_t rows, int64_t nb, const float* X,
                          int64_t N, float* Y, const MultiDesc& md, hipStream_t s);
+// D != nullptr: the block-dot export (Q4_0 blocks, one matrix) instead of Y.
 hipError_t launch_rows_act(const DeviceInfo* dev, int lay, const uint8_t* Wq, int64_t rows, int64_t nb,
-                           const void* act, int64_t N, float* Y, const MultiDesc& md, hipStream_t s);
+                           const void* act, int64_t N, float* Y, const MultiDesc& md, hipStream_t s,
+                           int32_t* D = nullptr);
 
 // Matrix-core kernel geometry: a workgroup of kPrefillThreads threads computes
 // kPrefillTokens tokens x kPrefillRows rows, so a launch has

@@ -129,11 +129,15 @@ __device__ __forceinline__ int64_t uniform64(int64_t v) {
     return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
-template <int THREADS, int NT, int PPL, int D, int SRC, int LAY, bool EPI>
+// DOTS: instead of Y, every per-block integer dot goes to
+// Dots[(n * rows + r) * nb + b] (the test export; one matrix of Q4_0 blocks,
+// activations from the quantizer's buffer).
+template <int THREADS, int NT, int PPL, int D, int SRC, int LAY, bool EPI, bool DOTS = false>
 __global__ void __launch_bounds__(THREADS)
 k_gemv_rows(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __restrict__ src,
-            float* __restrict__ Y, const MultiDesc md) {
+            float* __restrict__ Y, int32_t* __restrict__ Dots, const MultiDesc md) {
     static_assert(SRC == kXF32 || SRC == kActGlobal, "activation source");
+    static_assert(!DOTS || (SRC == kActGlobal && LAY == kLayAoS && !EPI), "block-dot export form");
     constexpr bool RP = LAY == kLayRepacked;
     constexpr bool MULTI = LAY == kLayMulti;  // rows of md's matrices, concatenated (rows = their total)
     constexpr bool kActReg = PPL == 1;         // activations in registers, else read from LDS per row
@@ -303,6 +307,43 @@ k_gemv_rows(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __
     }
     if (nk == 0) return;
 
+    if constexpr (DOTS) {
+        // the same loads and block dots as the product, each dot stored
+        for (int64_t k = 0; k < nk; k += D) {
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                if (k + d < nk) {
+                    const int64_t r = w0 + (k + d) * S;
+#pragma unroll
+                    for (int i = 0; i < PPL; ++i) {
+                        if (!pv[i]) continue;
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+                            const Block4 blk = h ? pair_second(raw[d][i]) : pair_first(raw[d][i]);
+#pragma unroll
+                            for (int n = 0; n < NT; ++n) {
+                                int32_t sdot;
+                                if constexpr (kActReg) {
+                                    sdot = block_dot(blk, areg[n][h], sreg[n][h].bias);
+                                } else {
+                                    const int g = n * nb + 2 * pp[i] + h;
+                                    const u32x4 a0 = reinterpret_cast<const u32x4*>(sq)[g * 2];
+                                    const u32x4 a1 = reinterpret_cast<const u32x4*>(sq)[g * 2 + 1];
+                                    const uint32_t a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+                                    sdot = block_dot(blk, a, ss[g].bias);
+                                }
+                                Dots[(static_cast<int64_t>(n) * rows + r) * nb + 2 * pp[i] + h] = sdot;
+                            }
+                        }
+                    }
+                }
+                load_row(raw[d], k + d + D);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        return;
+    }
+
     // 4. the rolling loop
     auto fold = [&](const Pair36 (&q)[PPL], float (&part)[NT]) __attribute__((always_inline)) {
 #pragma unroll
@@ -385,12 +426,12 @@ constexpr int rows_threads() { return NT > (PPL == 1 ? 4 : PPL == 2 ? 6 : 4) ? 5
 template <int NT, int PPL>
 constexpr int rows_depth() { return PPL == 1 && NT > 4 ? 2 : 1; }
 
-template <int SRC, int LAY, bool EPI, int NT, int PPL>
+template <int SRC, int LAY, bool EPI, bool DOTS, int NT, int PPL>
 hipError_t launch_rows_k(const DeviceInfo* dev, const uint8_t* Wq, int64_t rows, int64_t nb, const void* src,
-                         float* Y, const MultiDesc& md, hipStream_t s) {
+                         float* Y, int32_t* dots, const MultiDesc& md, hipStream_t s) {
     constexpr int kThreads = rows_threads<NT, PPL>();
     constexpr int kDepth = rows_depth<NT, PPL>();
-    const auto kernel = k_gemv_rows<kThreads, NT, PPL, kDepth, SRC, LAY, EPI>;
+    const auto kernel = k_gemv_rows<kThreads, NT, PPL, kDepth, SRC, LAY, EPI, DOTS>;
     int64_t wgs = (rows + kThreads / 64 - 1) / (kThreads / 64);
     const int64_t cap = static_cast<int64_t>(dev->num_cu) * (1024 / kThreads);
     if (wgs > cap) wgs = cap;
@@ -403,33 +444,33 @@ hipError_t launch_rows_k(const DeviceInfo* dev, const uint8_t* Wq, int64_t rows,
         if (raised != hipSuccess) return raised;
     }
     hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(wgs)), dim3(kThreads), lds, s, Wq, rows,
-                       static_cast<int>(nb), src, Y, md);
+                       static_cast<int>(nb), src, Y, dots, md);
     return hipGetLastError();
 }
 
-template <int SRC, int LAY, bool EPI, int NT>
+template <int SRC, int LAY, bool EPI, bool DOTS, int NT>
 hipError_t launch_rows_nt(const DeviceInfo* dev, const uint8_t* Wq, int64_t rows, int64_t nb, const void* src,
-                          float* Y, const MultiDesc& md, hipStream_t s) {
+                          float* Y, int32_t* dots, const MultiDesc& md, hipStream_t s) {
     switch (rows_ppl(nb)) {
-        case 1: return launch_rows_k<SRC, LAY, EPI, NT, 1>(dev, Wq, rows, nb, src, Y, md, s);
-        case 2: return launch_rows_k<SRC, LAY, EPI, NT, 2>(dev, Wq, rows, nb, src, Y, md, s);
-        case 4: return launch_rows_k<SRC, LAY, EPI, NT, 4>(dev, Wq, rows, nb, src, Y, md, s);
+        case 1: return launch_rows_k<SRC, LAY, EPI, DOTS, NT, 1>(dev, Wq, rows, nb, src, Y, dots, md, s);
+        case 2: return launch_rows_k<SRC, LAY, EPI, DOTS, NT, 2>(dev, Wq, rows, nb, src, Y, dots, md, s);
+        case 4: return launch_rows_k<SRC, LAY, EPI, DOTS, NT, 4>(dev, Wq, rows, nb, src, Y, dots, md, s);
         default: return hipErrorInvalidValue;
     }
 }
 
-template <int SRC, int LAY, bool EPI = false>
+template <int SRC, int LAY, bool EPI = false, bool DOTS = false>
 hipError_t launch_rows_t(const DeviceInfo* dev, const uint8_t* Wq, int64_t rows, int64_t nb, const void* src,
-                         int64_t N, float* Y, const MultiDesc& md, hipStream_t s) {
+                         int64_t N, float* Y, const MultiDesc& md, hipStream_t s, int32_t* dots = nullptr) {
     switch (N) {
-        case 1: return launch_rows_nt<SRC, LAY, EPI, 1>(dev, Wq, rows, nb, src, Y, md, s);
-        case 2: return launch_rows_nt<SRC, LAY, EPI, 2>(dev, Wq, rows, nb, src, Y, md, s);
-        case 3: return launch_rows_nt<SRC, LAY, EPI, 3>(dev, Wq, rows, nb, src, Y, md, s);
-        case 4: return launch_rows_nt<SRC, LAY, EPI, 4>(dev, Wq, rows, nb, src, Y, md, s);
-        case 5: return launch_rows_nt<SRC, LAY, EPI, 5>(dev, Wq, rows, nb, src, Y, md, s);
-        case 6: return launch_rows_nt<SRC, LAY, EPI, 6>(dev, Wq, rows, nb, src, Y, md, s);
-        case 7: return launch_rows_nt<SRC, LAY, EPI, 7>(dev, Wq, rows, nb, src, Y, md, s);
-        case 8: return launch_rows_nt<SRC, LAY, EPI, 8>(dev, Wq, rows, nb, src, Y, md, s);
+        case 1: return launch_rows_nt<SRC, LAY, EPI, DOTS, 1>(dev, Wq, rows, nb, src, Y, dots, md, s);
+        case 2: return launch_rows_nt<SRC, LAY, EPI, DOTS, 2>(dev, Wq, rows, nb, src, Y, dots, md, s);
+        case 3: return launch_rows_nt<SRC, LAY, EPI, DOTS, 3>(dev, Wq, rows, nb, src, Y, dots, md, s);
+        case 4: return launch_rows_nt<SRC, LAY, EPI, DOTS, 4>(dev, Wq, rows, nb, src, Y, dots, md, s);
+        case 5: return launch_rows_nt<SRC, LAY, EPI, DOTS, 5>(dev, Wq, rows, nb, src, Y, dots, md, s);
+        case 6: return launch_rows_nt<SRC, LAY, EPI, DOTS, 6>(dev, Wq, rows, nb, src, Y, dots, md, s);
+        case 7: return launch_rows_nt<SRC, LAY, EPI, DOTS, 7>(dev, Wq, rows, nb, src, Y, dots, md, s);
+        case 8: return launch_rows_nt<SRC, LAY, EPI, DOTS, 8>(dev, Wq, rows, nb, src, Y, dots, md, s);
         default: return hipErrorInvalidValue;
     }
 }
