@@ -29,12 +29,11 @@ pytestmark = pytest.mark.gpu
 
 RTOL, ATOL = 1e-4, 1e-5
 
-# Per-block magnitudes (multipliers of N(0, 1) values).  Weights: 0 and 1e-9
-# give d_w = 0; 1e-4 and 3e-5 give fp16-subnormal d_w; 0.02 is the workloads'
-# scale; 50 is large.  Activations: 0 and 1e-9 give d_x = 0; 1e-3 and 2e-3
-# give subnormal d_x; 1 and 300 are normal.
-W_LEVELS = np.array([0.0, 1e-9, 1e-4, 3e-5, 0.02, 50.0], np.float32)
-X_LEVELS = np.array([0.0, 1e-9, 1e-3, 2e-3, 1.0, 300.0], np.float32)
+# Per-block magnitudes (multipliers of N(0, 1) values).  Tiny weights: 0 and
+# 1e-9 give d_w = 0, 1e-4 and 3e-5 an fp16-subnormal d_w; tiny activations: 0
+# and 1e-9 give d_x = 0, 1e-3 and 2e-3 a subnormal d_x.
+W_TINY = np.array([0.0, 1e-9, 1e-4, 3e-5], np.float32)
+X_TINY = np.array([0.0, 1e-9, 1e-3, 2e-3], np.float32)
 
 
 @pytest.fixture(scope="module")
@@ -69,24 +68,31 @@ def assert_close(Y, Yref, what, scale=1.0):
 
 
 def mixed_scales(rows, K, N, seed):
-    """W (rows x K) and X (N x K) whose blocks draw their magnitude from the
-    levels above: row 0 and token 0 all zero, row 1 all subnormal-scaled,
-    token 1 all subnormal-scaled, the rest mixed block by block (a third of
-    the blocks on the tiny levels)."""
-    rng = np.random.default_rng(seed)
+    """W (rows x K) and X (N x K) with zero and subnormal block scales whose
+    contributions are all visible: every block index b has one regime, shared
+    by all rows and tokens of this K -- tiny weights against activations of
+    magnitude 300, weights of magnitude 50 against tiny activations, or the
+    workloads' 0.02 against 1 -- so every block term is of order 0.1 to 1 (a
+    flushed subnormal scale moves Y by far more than the bar, and no term
+    dwarfs the sum, which an fp32 accumulation could not follow).  Row 0 and
+    (N >= 3) token 0 are all zero; row 1 and (N >= 2) token 1 are tiny in
+    every block."""
     nb = K // 32
+    regime = np.random.default_rng(K).choice(3, size=nb, p=[0.25, 0.25, 0.5])
+    rng = np.random.default_rng(seed)
     W = inputs.random_matrix(seed, rows, K, 1.0)
     X = inputs.random_matrix(seed + 1, N, K, 1.0)
-    wl = rng.choice(len(W_LEVELS), size=(rows, nb), p=[0.08, 0.08, 0.09, 0.09, 0.46, 0.20])
-    xl = rng.choice(len(X_LEVELS), size=(N, nb), p=[0.08, 0.08, 0.09, 0.09, 0.46, 0.20])
-    wl[0] = 0
+    wl = np.where(regime == 0, rng.choice(W_TINY, size=(rows, nb)), np.where(regime == 1, 50.0, 0.02))
+    xl = np.where(regime == 0, 300.0, np.where(regime == 1, rng.choice(X_TINY, size=(N, nb)), 1.0))
+    wl[0] = 0.0
     if rows > 1:
-        wl[1] = rng.choice([2, 3], size=nb)
-    xl[0] = 0
-    if N > 1:
-        xl[1] = rng.choice([2, 3], size=nb)
-    W *= np.repeat(W_LEVELS[wl], 32, axis=1)
-    X *= np.repeat(X_LEVELS[xl], 32, axis=1)
+        wl[1] = rng.choice(W_TINY[2:], size=nb)
+    if N >= 3:
+        xl[0] = 0.0
+    if N >= 2:
+        xl[1] = rng.choice(X_TINY[2:], size=nb)
+    W *= np.repeat(wl.astype(np.float32), 32, axis=1)
+    X *= np.repeat(xl.astype(np.float32), 32, axis=1)
     return W.astype(np.float32), X.astype(np.float32)
 
 
@@ -95,8 +101,8 @@ def all_subnormal(rows, K, N, seed):
     scale."""
     rng = np.random.default_rng(seed)
     nb = K // 32
-    W = inputs.random_matrix(seed, rows, K, 1.0) * np.repeat(rng.choice(W_LEVELS[2:4], size=(rows, nb)), 32, axis=1)
-    X = inputs.random_matrix(seed + 1, N, K, 1.0) * np.repeat(rng.choice(X_LEVELS[2:4], size=(N, nb)), 32, axis=1)
+    W = inputs.random_matrix(seed, rows, K, 1.0) * np.repeat(rng.choice(W_TINY[2:], size=(rows, nb)), 32, axis=1)
+    X = inputs.random_matrix(seed + 1, N, K, 1.0) * np.repeat(rng.choice(X_TINY[2:], size=(N, nb)), 32, axis=1)
     return W.astype(np.float32), X.astype(np.float32)
 
 
