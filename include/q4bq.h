@@ -50,6 +50,7 @@ extern "C" {
 #define Q4BQ_EINVAL (-1) /* bad argument: null, size < 1, K % 32 != 0, misaligned, overlap */
 #define Q4BQ_EHIP (-2)   /* HIP runtime / launch failure */
 #define Q4BQ_ENOMEM (-3) /* scratch allocation failed, or workspace too small */
+#define Q4BQ_ESCRATCH (-4) /* sizes beyond the no-allocation entry point's fixed scratch */
 
 #define Q4BQ_QK 32
 #define Q4BQ_Q4_0_BYTES 18
@@ -307,6 +308,24 @@ int mul_mat_q8_0_q8_0(const void *Wq8, int64_t rows, int64_t K, const float *X,
  */
 int q8_0_q8_0_block_dots(const void *Wq8, int64_t rows, int64_t K, const void *Xq,
                          int64_t N, int32_t *D, void *stream);
+
+/*
+ * For callers that cannot allocate memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): mul_mat_q4_0_q8_0 with its
+ * scratch in a fixed device array that the library holds on each GPU it runs
+ * on until the process ends (Q4BQ_NOALLOC_SCRATCH_BYTES = 16 MiB per GPU).
+ * Arguments, checks and results are those of mul_mat_q4_0_q8_0 (the same
+ * kernels; Y bit for bit that of mul_mat_q4_0_q8_0_ex); no hipMalloc,
+ * hipMallocAsync or hipFree is called.  Sizes whose scratch,
+ * q4bq_workspace_size(rows, K, N), exceeds the array return Q4BQ_ESCRATCH
+ * before anything is launched (N > 8 needs N * K/32 * 64 bytes: up to 512
+ * tokens at K = 16384).  Every call on one GPU shares that GPU's array, which
+ * keeps the last call's contents: calls that overlap in time on one GPU (two
+ * streams, or two host threads) race and must be serialized by the caller.
+ */
+#define Q4BQ_NOALLOC_SCRATCH_BYTES (16u * 1024u * 1024u)
+int mul_mat_q4_0_q8_0_noalloc(const void *Wq, int64_t rows, int64_t K, const float *X,
+                              int64_t N, float *Y, void *stream);
 
 /* Static text for a status code. */
 const char *q4bq_status_string(int status);

@@ -24,6 +24,8 @@ Q4BQ_OK = 0
 Q4BQ_EINVAL = -1
 Q4BQ_EHIP = -2
 Q4BQ_ENOMEM = -3
+Q4BQ_ESCRATCH = -4
+NOALLOC_SCRATCH_BYTES = 16 * 1024 * 1024
 
 EXPORTS = (
     "q4_0_quantize", "q8_0_quantize", "mul_mat_q4_0_q8_0", "q4bq_workspace_size",
@@ -32,6 +34,7 @@ EXPORTS = (
     "q4_0_repack", "mul_mat_q4_0r_q8_0", "mul_mat_q4_0r_q8_0_ex", "mul_mat_q4_0_q8_0_multi",
     "q4_0_get_rows", "q4bq_repack_size", "mul_mat_q8_0_q8_0", "q8_0_q8_0_block_dots",
     "mul_mat_q4_0_q8_0_fused", "mul_mat_q4_0_q8_0_swiglu", "q4bq_fused_workspace_size",
+    "mul_mat_q4_0_q8_0_noalloc",
 )
 
 ACT_NONE, ACT_GELU, ACT_SILU = 0, 1, 2
@@ -59,6 +62,7 @@ def lib() -> ctypes.CDLL:
         "q4_0_quantize": (I, [P, I64, I64, P, P]),
         "q8_0_quantize": (I, [P, I64, I64, P, P]),
         "mul_mat_q4_0_q8_0": (I, [P, I64, I64, P, I64, P, P]),
+        "mul_mat_q4_0_q8_0_noalloc": (I, [P, I64, I64, P, I64, P, P]),
         "q4bq_workspace_size": (ctypes.c_size_t, [I64, I64, I64]),
         "mul_mat_q4_0_q8_0_ex": (I, [P, I64, I64, P, I64, P, P, ctypes.c_size_t, P]),
         "mul_mat_q4_0_q8_0_pq": (I, [P, I64, I64, P, I64, P, P]),
@@ -175,6 +179,20 @@ def mul_mat_q4_0_q8_0(Wq: torch.Tensor, X: torch.Tensor, Y: torch.Tensor | None 
         Y = torch.empty((N, rows), dtype=torch.float32, device=X.device)
     _check(lib().mul_mat_q4_0_q8_0(_dev(Wq, torch.uint8, "Wq"), rows, K, _dev(X, torch.float32, "X"), N,
                                    _dev(Y, torch.float32, "Y"), _stream(stream)), "mul_mat_q4_0_q8_0")
+    return Y
+
+
+def mul_mat_q4_0_q8_0_noalloc(Wq: torch.Tensor, X: torch.Tensor, Y: torch.Tensor | None = None,
+                              stream=None) -> torch.Tensor:
+    """mul_mat_q4_0_q8_0 with the library's fixed per-GPU scratch: the call
+    allocates nothing (Y must be given where the caller cannot allocate)."""
+    N, K = X.shape
+    rows = _rows(Wq, K)
+    if Y is None:
+        Y = torch.empty((N, rows), dtype=torch.float32, device=X.device)
+    _check(lib().mul_mat_q4_0_q8_0_noalloc(_dev(Wq, torch.uint8, "Wq"), rows, K, _dev(X, torch.float32, "X"), N,
+                                           _dev(Y, torch.float32, "Y"), _stream(stream)),
+           "mul_mat_q4_0_q8_0_noalloc")
     return Y
 
 

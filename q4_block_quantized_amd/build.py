@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libq4bq.so")
 
 ARCH = "gfx950"
 SOURCES = ["q4bq_api.cpp", "q4bq_quant.hip", "q4bq_gemv.hip", "q4bq_rows_x.hip", "q4bq_rows_act.hip",
-           "q4bq_prefill.hip", "q4bq_q8w.hip"]
+           "q4bq_prefill.hip", "q4bq_q8w.hip", "q4bq_noalloc.hip"]
 
 # No fast-math anywhere: the quantizers need IEEE division and round-half-away.
 # Packed fp32 instructions are switched off for all device code.

@@ -308,6 +308,21 @@ int mul_mat_q4_0_q8_0_pq(const void* Wq, int64_t rows, int64_t K, const void* Xq
                             N, Y, nullptr, static_cast<hipStream_t>(stream));
 }
 
+int mul_mat_q4_0_q8_0_noalloc(const void* Wq, int64_t rows, int64_t K, const float* X, int64_t N, float* Y,
+                              void* stream) {
+    const int rc = check_product(Wq, rows, K, X, kF32, N, Y, false);
+    if (rc != Q4BQ_OK) return rc;
+    if (q4bq_workspace_size(rows, K, N) > Q4BQ_NOALLOC_SCRATCH_BYTES) return Q4BQ_ESCRATCH;
+    hipError_t err = hipSuccess;
+    const DeviceInfo* dev = current_device(&err);
+    if (!dev) return Q4BQ_EHIP;
+    void* ws = noalloc_scratch(dev->id, &err);
+    if (!ws) return Q4BQ_EHIP;
+    // the scratch is device memory of its own, apart from every caller buffer
+    return run_product(kAoS, static_cast<const uint8_t*>(Wq), rows, K, X, nullptr, N, Y, nullptr, ws,
+                       static_cast<hipStream_t>(stream));
+}
+
 int q4_0_q8_0_block_dots(const void* Wq, int64_t rows, int64_t K, const void* Xq, int64_t N, int32_t* D,
                          void* stream) {
     const int rc = check_product(Wq, rows, K, Xq, kQ8, N, D, true);
@@ -498,10 +513,12 @@ const char* q4bq_status_string(int status) {
                                  "misaligned pointer or overlapping buffers)";
         case Q4BQ_EHIP: return "HIP runtime or kernel launch failure";
         case Q4BQ_ENOMEM: return "scratch allocation failed or workspace too small";
+        case Q4BQ_ESCRATCH: return "sizes need more scratch than the no-allocation entry point holds "
+                                   "(Q4BQ_NOALLOC_SCRATCH_BYTES)";
         default: return "unknown status";
     }
 }
 
-int q4bq_version(void) { return 201; }
+int q4bq_version(void) { return 300; }
 
 }  // extern "C"

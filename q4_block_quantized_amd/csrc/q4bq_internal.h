@@ -52,6 +52,11 @@ struct DeviceInfo {
 // Launch parameters of the device current on this thread (cached).
 const DeviceInfo* current_device(hipError_t* err);
 
+// Device address of the no-allocation entry point's fixed scratch
+// (Q4BQ_NOALLOC_SCRATCH_BYTES) on `device`, which must be the current device;
+// looked up once per device.  nullptr and *err set on failure.
+void* noalloc_scratch(int device, hipError_t* err);
+
 // Internal activation buffer ([n][b], b fastest):
 //  N <= kGemvMaxN (decode kernel): N*nb blocks of 32 int8 bytes in dot order,
 //    then N*nb scale records of 8 bytes {float d; int32 -8*sum(q)};
