@@ -60,6 +60,9 @@ def parse():
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of this many MiB, 5 times (a known-size kernel for "
                          "scaling HBM byte counters)")
+    ap.add_argument("--profile-prefill", action="store_true",
+                    help="only run the 512-token prefill (14336 x 4096) 30 times eagerly on the pages' blocks, then 30 "
+                         "times on repacked weights, after a second of settling, for a profiler; prints no JSON line")
     ap.add_argument("--profile-legs", action="store_true",
                     help="only run the other legs' kernels (Q8_0 weights on the head at N=1 and N=8, the fused "
                          "SwiGLU, get_rows) 20 times each, eagerly, for a profiler; prints no JSON line")
@@ -105,6 +108,21 @@ def profile_legs(hip, torch):
         hip.q4_0_get_rows(T, K, ids, out)
     torch.cuda.synchronize()
     log("get_rows 512 ids of %dx%d: 20 calls" % (rows, K))
+
+
+def profile_prefill(hip, torch):
+    """Thirty eager prefill steps (activation records + k_prefill) on the
+    pages' blocks, then thirty on repacked weights, for rocprofv3 (kernel
+    trace and counters)."""
+    for repack in (False, True):
+        pm = Mats(hip, torch, 5, 512, repack=repack)
+        settle(torch, lambda i: pm.step(hip, i))
+        for i in range(30):
+            pm.step(hip, i)
+        torch.cuda.synchronize()
+        log("prefill 14336x4096 N=512%s: 30 steps" % (" (repacked weights)" if repack else ""))
+        del pm
+        torch.cuda.empty_cache()
 
 
 def q4_bytes(rows, K):
@@ -201,17 +219,40 @@ def settle(torch, fn, seconds=1.0):
         torch.cuda.synchronize()
 
 
+REPS = 7            # timed repetitions per measurement
+MIN_LOOP_MS = 20.0  # each repetition times a loop of at least this long
+
+
 def timed(torch, fn, steps, warmup):
+    """The timing protocol: `warmup` untimed steps, then REPS repetitions of a
+    loop of L >= `steps` steps lasting at least MIN_LOOP_MS, each bracketed by
+    HIP events on the current stream (the one the library launches on).
+    Returns {"median", "min"} in ms per step, the per-repetition figures and
+    L."""
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for i in range(steps):
-        fn(i)
-    end.record()
-    torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps  # ms
+
+    def loop(n, first):
+        start.record()
+        for i in range(n):
+            fn(first + i)
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end)
+
+    est = loop(steps, warmup) / steps
+    L = max(steps, int(np.ceil(MIN_LOOP_MS / max(est, 1e-6))))
+    reps = [loop(L, warmup + steps + r * L) / L for r in range(REPS)]
+    return {"median": float(np.median(reps)), "min": float(np.min(reps)), "reps_ms": [round(x, 6) for x in reps],
+            "steps_per_rep": L}
+
+
+def proto(t):
+    """The timing record as it goes into the JSON line (microseconds)."""
+    return {"median_us": round(t["median"] * 1e3, 3), "min_us": round(t["min"] * 1e3, 3), "reps": REPS,
+            "steps_per_rep": t["steps_per_rep"], "loop_ms_min": round(t["min"] * t["steps_per_rep"], 2)}
 
 
 def multi_matrix(hip, torch, args):
@@ -226,11 +267,12 @@ def multi_matrix(hip, torch, args):
     X = torch.from_numpy(inputs.activations(3, 0, max(wl.ns), 4096)[:1].copy()).cuda()
     Ys = [torch.empty((1, r), dtype=torch.float32, device="cuda") for _, (r, _k) in mats]
     ws = hip.workspace(max(r for _, (r, _k) in mats), 4096, 1)
-    ms_one = timed(torch, lambda i: hip.mul_mat_q4_0_q8_0_multi(sets[i % copies], X, Ys), args.steps, args.warmup)
+    ms_one = timed(torch, lambda i: hip.mul_mat_q4_0_q8_0_multi(sets[i % copies], X, Ys), args.steps,
+                   args.warmup)["median"]
     def sep(i):
         for w, y in zip(sets[i % copies], Ys):
             hip.mul_mat_q4_0_q8_0_ex(w, X, ws, y)
-    ms_sep = timed(torch, sep, args.steps, args.warmup)
+    ms_sep = timed(torch, sep, args.steps, args.warmup)["median"]
     nbytes = sum(step_bytes(r, k, 1) for _, (r, k) in mats)
     log("multi-matrix decode (%s): one launch %.2f us, one call per matrix %.2f us"
         % (" + ".join("%dx%d" % rk for _, rk in mats), ms_one * 1e3, ms_sep * 1e3))
@@ -450,29 +492,129 @@ def fused_leg(hip, torch):
     return res
 
 
-def cpu_baseline(cid, N):
-    """The oracle, as it stands, on a bounded row sample of the workload."""
-    import oracle
-    from q4_block_quantized_amd import inputs
-    wl = inputs.WORKLOADS[cid]
-    rows, K = wl.mats[0]
-    take = min(rows, 32768)
-    W = inputs.weights(cid, 0, rows, K, outliers=wl.outliers, row_slice=slice(0, take))
-    X = inputs.activations(cid, 0, max(wl.ns), K)[:N].copy()
-    Wq = oracle.q4_0_quantize(W)
-    threads = min(os.cpu_count() or 1, 16)
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_rate(fn, seconds):
+    """Runs fn until `seconds` have passed (at least once); seconds per run."""
     runs, t0 = 0, time.perf_counter()
     while True:
-        oracle.mul_mat(Wq, X, nthreads=threads)
+        fn()
         runs += 1
         el = time.perf_counter() - t0
-        if el >= 10.0 or runs >= 100000:
-            break
-    per = el / runs
-    return {"value": round(step_bytes(take, K, N) / per / 1e9, 3), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
-            "sample": "rows 0..%d of the %dx%d matrix, N=%d, %d runs in %.1f s (%.1f ms each), fp64 oracle"
-                      % (take - 1, rows, K, N, runs, el, per * 1e3)}
+        if el >= seconds:
+            return el / runs, runs, el
+
+
+def cpu_baseline(N_decode, seconds=3.0):
+    """The oracle as it stands (plain C loops, fp64 accumulation, threads over
+    rows) on bounded samples of the headline decode workload and of the
+    512-token prefill, each on one thread and on all the cores this process
+    may use (capped at 16: the share of a one-GPU job on a shared host).
+    Rates are scaled to the metrics' units: GB/s of the operator's
+    algorithmic bytes for the decode, int8-equivalent TOPS for the prefill."""
+    import oracle
+    from q4_block_quantized_amd import inputs
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    allc = max(1, min(avail, 16))
+    # decode: the first 16384 rows of the 128256 x 4096 head, one token
+    wl = inputs.WORKLOADS[4]
+    rows, K = wl.mats[0]
+    take = 16384
+    Wq = oracle.q4_0_quantize(inputs.weights(4, 0, rows, K, outliers=wl.outliers, row_slice=slice(0, take)))
+    X = inputs.activations(4, 0, max(wl.ns), K)[:N_decode].copy()
+    dec = {}
+    for label, th in (("one_thread", 1), ("all_cores", allc)):
+        per, runs, el = _oracle_rate(lambda: oracle.mul_mat(Wq, X, nthreads=th), seconds)
+        dec[label] = {"GB/s": round(step_bytes(take, K, N_decode) / per / 1e9, 3), "threads": th,
+                      "ms_per_run": round(per * 1e3, 2), "runs": runs}
+    # prefill: 112 rows of the 14336 x 4096 matrix against all 512 tokens
+    wl5 = inputs.WORKLOADS[5]
+    r5, K5 = wl5.mats[0]
+    t5 = 112
+    Wq5 = oracle.q4_0_quantize(inputs.weights(5, 0, r5, K5, outliers=wl5.outliers, row_slice=slice(0, t5)))
+    X5 = inputs.activations(5, 0, 512, K5)
+    pre = {}
+    for label, th in (("one_thread", 1), ("all_cores", allc)):
+        per, runs, el = _oracle_rate(lambda: oracle.mul_mat(Wq5, X5, nthreads=th), seconds)
+        pre[label] = {"TOPS": round(2 * t5 * K5 * 512 / per / 1e12, 5), "threads": th,
+                      "ms_per_run": round(per * 1e3, 1), "runs": runs}
+    return {"value": dec["all_cores"]["GB/s"], "unit": "GB/s", "cores": allc, "kind": "oracle",
+            "sample": "decode: rows 0..%d of the %dx%d head, N=%d (per leg >= %.0f s of runs); the whole operator "
+                      "(Q8_0 quantization of X, int32 block dots, fp64 accumulation)" % (take - 1, rows, K, N_decode,
+                                                                                      seconds),
+            "decode": dec,
+            "prefill": {"sample": "rows 0..%d of the %dx%d matrix x 512 tokens" % (t5 - 1, r5, K5), **pre},
+            "cpu_model": cpu_model(), "os_cpu_count": os.cpu_count(), "cores_available": avail}
+
+
+def measured_peaks(torch):
+    """Peak rates of this GPU for the instructions the kernels use (the probe
+    library), each the best of three launches timed with HIP events."""
+    import ctypes
+    from q4_block_quantized_amd import build as qb
+    L = ctypes.CDLL(qb.PROBE_LIB)
+    L.q4bq_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    L.q4bq_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    L.q4bq_probe_ops.restype = ctypes.c_double
+    L.q4bq_probe_ops.argtypes = [ctypes.c_int, ctypes.c_int64]
+    out = torch.empty(L.q4bq_probe_threads(), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def best(launch, count):
+        t = []
+        for _ in range(4):
+            ev0.record()
+            if launch() != 0:
+                raise RuntimeError("probe launch failed")
+            ev1.record()
+            torch.cuda.synchronize()
+            t.append(ev0.elapsed_time(ev1) * 1e-3)
+        return count / min(t[1:])
+
+    res = {}
+    for kind, name, iters in ((0, "mfma_int8_TOPS", 4000), (1, "mfma_fp6_TFLOPS", 4000),
+                              (2, "mfma_f16_32x32x8_TFLOPS", 4000), (3, "valu_fp32_fma_TFLOPS", 20000)):
+        ops = L.q4bq_probe_ops(kind, iters)
+        res[name] = round(best(lambda: L.q4bq_probe_mfma(kind, iters, out.data_ptr(), stream.cuda_stream), ops)
+                          / 1e12, 1)
+    buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    res["stream_read_GB/s"] = round(best(lambda: L.q4bq_probe_read(buf.data_ptr(), buf.numel(), out.data_ptr(),
+                                                                    stream.cuda_stream), buf.numel()) / 1e9, 1)
+    del buf
+    torch.cuda.empty_cache()
+    return res
+
+
+def prefill_ceiling(rows, K, N, peaks):
+    """Lower bounds on the prefill kernel's time from its work at the measured
+    peak rates: per 32-token x 32-row tile and 32-value block one fp6 MFMA
+    (32x32x64: the block dot, exact), one f16 MFMA (32x32x8: the 1024 scale
+    products) and 1024 fp32 FMAs on the vector ALU.  'overlapped' assumes the
+    matrix cores and the vector ALU run side by side, 'serial' one after the
+    other."""
+    tiles = (rows / 32) * (N / 32) * (K / 32)
+    t_fp6 = tiles * 2 * 32 * 32 * 64 / (peaks["mfma_fp6_TFLOPS"] * 1e12)
+    t_f16 = tiles * 2 * 32 * 32 * 8 / (peaks["mfma_f16_32x32x8_TFLOPS"] * 1e12)
+    t_valu = tiles * 1024 * 2 / (peaks["valu_fp32_fma_TFLOPS"] * 1e12)
+    ops = 2 * rows * K * N
+    over = max(t_fp6 + t_f16, t_valu)
+    return {"mfma_us": round((t_fp6 + t_f16) * 1e6, 2), "valu_us": round(t_valu * 1e6, 2),
+            "overlapped_us": round(over * 1e6, 2), "serial_us": round((t_fp6 + t_f16 + t_valu) * 1e6, 2),
+            "overlapped_TOPS": round(ops / over / 1e12, 1),
+            "overlapped_frac_of_int8_peak": round(ops / over / 1e12 / INT8_PEAK_TOPS, 4)}
 
 
 def main():
@@ -499,40 +641,48 @@ def main():
     if args.profile_legs:
         profile_legs(hip, torch)
         return
+    if args.profile_prefill:
+        profile_prefill(hip, torch)
+        return
     cid = int(args.workload[1])
     from q4_block_quantized_amd import inputs
     wl = inputs.WORKLOADS[cid]
     N = wl.ns[0]
 
+    peaks = measured_peaks(torch)
+    log("measured peaks: %s" % json.dumps(peaks))
+
     log("workload %s N=%d: preparing" % (wl.name, N))
     mats = Mats(hip, torch, cid, N)
     n_launch = len(mats.items)
     settle(torch, lambda i: mats.step(hip, i))
-    ms_step = timed(torch, lambda i: mats.step(hip, i), args.steps, args.warmup)
+    t_step = timed(torch, lambda i: mats.step(hip, i), args.steps, args.warmup)
+    ms_step = t_step["median"]
     gbs = mats.bytes_step() / (ms_step * 1e-3) / 1e9
     # two-phase form: activation quantizer once, then the product kernel alone
     mats.prepare(hip)
-    ms_kernel = timed(torch, lambda i: mats.kernel_only(hip, i), args.steps, args.warmup)
+    t_kernel = timed(torch, lambda i: mats.kernel_only(hip, i), args.steps, args.warmup)
+    ms_kernel = t_kernel["median"]
     kern_gbs = mats.bytes_kernel() / (ms_kernel * 1e-3) / 1e9
-    log("step %.2f us -> %.1f GB/s; two-phase product kernel %.2f us/launch -> %.1f GB/s"
-        % (ms_step * 1e3, gbs, ms_kernel * 1e3 / n_launch, kern_gbs))
+    log("step %.2f us (min %.2f) -> %.1f GB/s; two-phase product kernel %.2f us/launch -> %.1f GB/s"
+        % (ms_step * 1e3, t_step["min"] * 1e3, gbs, ms_kernel * 1e3 / n_launch, kern_gbs))
     if fused_step(N):
         # one kernel per matrix: the step is the dominant kernel
         roof = {"kernel": decode_kernel(mats.items[0][1], N) + " (fused activation quantizer)", "achieved": gbs,
-                "ms": ms_step,
+                "ms": ms_step, "t": t_step,
                 "bytes": mats.bytes_step() // n_launch}
     else:
         roof = {"kernel": decode_kernel(mats.items[0][1], N) + " (product kernel alone)", "achieved": kern_gbs,
-                "ms": ms_kernel,
+                "ms": ms_kernel, "t": t_kernel,
                 "bytes": mats.bytes_kernel() // n_launch}
     del mats
     torch.cuda.empty_cache()
     # the same step on repacked weights (q4_0_repack, done once, outside the timed region)
     rmats = Mats(hip, torch, cid, N, repack=True)
-    ms_rstep = timed(torch, lambda i: rmats.step(hip, i), args.steps, args.warmup)
-    rgbs = rmats.bytes_step() / (ms_rstep * 1e-3) / 1e9
-    log("repacked weights: step %.2f us -> %.1f GB/s" % (ms_rstep * 1e3, rgbs))
-    repacked = {"decode": {"ms_per_step": round(ms_rstep, 5), "GB/s": round(rgbs, 1)}}
+    t_r = timed(torch, lambda i: rmats.step(hip, i), args.steps, args.warmup)
+    rgbs = rmats.bytes_step() / (t_r["median"] * 1e-3) / 1e9
+    log("repacked weights: step %.2f us -> %.1f GB/s" % (t_r["median"] * 1e3, rgbs))
+    repacked = {"decode": {"ms_per_step": round(t_r["median"], 5), "GB/s": round(rgbs, 1), "timing": proto(t_r)}}
     del rmats
     torch.cuda.empty_cache()
 
@@ -551,29 +701,38 @@ def main():
         log("prefill: preparing")
         pm = Mats(hip, torch, 5, 512)
         settle(torch, lambda i: pm.step(hip, i))  # clocks settle again under the matrix-core load
-        ms_p = timed(torch, lambda i: pm.step(hip, i), max(10, args.steps // 4), max(3, args.warmup // 4))
+        t_p = timed(torch, lambda i: pm.step(hip, i), max(10, args.steps // 4), max(3, args.warmup // 4))
         pm.prepare(hip)
-        ms_pk = timed(torch, lambda i: pm.kernel_only(hip, i), max(10, args.steps // 4), max(3, args.warmup // 4))
+        t_pk = timed(torch, lambda i: pm.kernel_only(hip, i), max(10, args.steps // 4), max(3, args.warmup // 4))
+        ms_p, ms_pk = t_p["median"], t_pk["median"]
         tops = pm.ops() / (ms_p * 1e-3) / 1e12
         ktops = pm.ops() / (ms_pk * 1e-3) / 1e12
         log("prefill step %.2f us -> %.1f TOPS; kernel %.2f us -> %.1f TOPS" % (ms_p * 1e3, tops, ms_pk * 1e3, ktops))
+        ceil = prefill_ceiling(14336, 4096, 512, peaks)
         prefill = {"workload": "llama3_8b_prefill", "rows": 14336, "K": 4096, "N": 512,
                    "ms_per_step": round(ms_p, 5), "value": round(tops, 2), "unit": "TOPS (int8)",
+                   "timing": proto(t_p),
                    "roofline": {"bound": "mfma", "achieved": round(ktops, 2), "peak": INT8_PEAK_TOPS,
                                 "unit": "TOPS", "frac": round(ktops / INT8_PEAK_TOPS, 4),
-                                "traffic": TRAFFIC_BYTES.get(("llama3_8b_prefill", 512))}}
+                                "traffic": TRAFFIC_BYTES.get(("llama3_8b_prefill", 512)),
+                                "kernel": "k_prefill", "us_per_launch": round(ms_pk * 1e3, 3),
+                                "timing": proto(t_pk),
+                                "frac_of_measured_int8_peak": round(ktops / peaks["mfma_int8_TOPS"], 4),
+                                "ceiling_mfma_plus_valu": ceil,
+                                "frac_of_overlapped_ceiling": round(ktops / ceil["overlapped_TOPS"], 4)}}
         del pm
         torch.cuda.empty_cache()
         rpm = Mats(hip, torch, 5, 512, repack=True)
         settle(torch, lambda i: rpm.step(hip, i), 0.3)
-        ms_rp = timed(torch, lambda i: rpm.step(hip, i), max(10, args.steps // 4), max(3, args.warmup // 4))
-        rtops = rpm.ops() / (ms_rp * 1e-3) / 1e12
-        log("repacked weights: prefill step %.2f us -> %.1f TOPS" % (ms_rp * 1e3, rtops))
-        repacked["prefill"] = {"ms_per_step": round(ms_rp, 5), "TOPS": round(rtops, 2)}
+        t_rp = timed(torch, lambda i: rpm.step(hip, i), max(10, args.steps // 4), max(3, args.warmup // 4))
+        rtops = rpm.ops() / (t_rp["median"] * 1e-3) / 1e12
+        log("repacked weights: prefill step %.2f us -> %.1f TOPS" % (t_rp["median"] * 1e3, rtops))
+        repacked["prefill"] = {"ms_per_step": round(t_rp["median"], 5), "TOPS": round(rtops, 2),
+                               "timing": proto(t_rp)}
         del rpm
         torch.cuda.empty_cache()
 
-    cpu = None if args.no_cpu else cpu_baseline(cid, N)
+    cpu = None if args.no_cpu else cpu_baseline(N)
 
     out = {
         "metric": "Q4_0xQ8_0 mul_mat HBM bandwidth (GB/s, N=1 decode)",
@@ -582,13 +741,17 @@ def main():
         "dtype": "int4xint8->int32, fp32 scale/accumulate", "data": "synthetic (seeded N(0,0.02) weights, N(0,1) activations)",
         "config": {"workload": wl.name, "matrices": [list(m) for m in wl.mats], "N": N,
                    "weights_cold": "rotating copies >= 1 GiB"},
+        "timing": dict(proto(t_step), note="value and ms_per_step are the median of %d repetitions" % REPS),
         "roofline": {"bound": "hbm", "achieved": round(roof["achieved"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(roof["achieved"] / HBM_PEAK_GBS, 4),
                      "traffic": TRAFFIC_BYTES.get((wl.name, N)) if fused_step(N) else None,
                      "kernel": roof["kernel"], "bytes_per_launch": roof["bytes"],
-                     "us_per_launch": round(roof["ms"] * 1e3 / n_launch, 3)},
+                     "us_per_launch": round(roof["ms"] * 1e3 / n_launch, 3),
+                     "us_per_launch_min": round(roof["t"]["min"] * 1e3 / n_launch, 3),
+                     "frac_of_measured_stream_read": round(roof["achieved"] / peaks["stream_read_GB/s"], 4)},
         "two_phase_product_kernel": {"us_per_launch": round(ms_kernel * 1e3 / n_launch, 3),
-                                     "GB/s": round(kern_gbs, 1)},
+                                     "GB/s": round(kern_gbs, 1), "timing": proto(t_kernel)},
+        "measured_peaks": peaks,
         "prefill": prefill,
         "repacked_weights": repacked,
         "multi_matrix_decode": multi,

@@ -21,6 +21,9 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libq4bq.so")
 
 ARCH = "gfx950"
+# measurement probes for the benchmark (not linked into the product library)
+PROBE_SOURCE = "q4bq_probe.hip"
+PROBE_LIB = os.path.join(PKG, "libq4bq_probe.so")
 SOURCES = ["q4bq_api.cpp", "q4bq_quant.hip", "q4bq_gemv.hip", "q4bq_rows_x.hip", "q4bq_rows_act.hip",
            "q4bq_prefill.hip", "q4bq_q8w.hip", "q4bq_noalloc.hip"]
 
@@ -52,19 +55,26 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libq4bq.so; returns the library path."""
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source, link libq4bq.so (the product library) and
+    libq4bq_probe.so (the benchmark's peak-rate probes); returns the product
+    library's path."""
+    os.makedirs(BUILD, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES) + 1, os.cpu_count() or 4)) as ex:
+        objs = list(ex.map(_compile, SOURCES + [PROBE_SOURCE]))
+    _link(objs[:-1], LIB)
+    _link(objs[-1:], PROBE_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PROBE_LIB)
     return LIB
 
 
