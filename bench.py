@@ -63,6 +63,9 @@ def parse():
     ap.add_argument("--profile-prefill", action="store_true",
                     help="only run the 512-token prefill (14336 x 4096) 30 times eagerly on the pages' blocks, then 30 "
                          "times on repacked weights, after a second of settling, for a profiler; prints no JSON line")
+    ap.add_argument("--profile-decode", action="store_true",
+                    help="only run the decode configurations (GPT-2 matrix and layer, Llama layer at N=1 and 4, the "
+                         "vocabulary head at N=1 and 8) 30 steps each, eagerly, for a profiler; prints no JSON line")
     ap.add_argument("--profile-legs", action="store_true",
                     help="only run the other legs' kernels (Q8_0 weights on the head at N=1 and N=8, the fused "
                          "SwiGLU, get_rows) 20 times each, eagerly, for a profiler; prints no JSON line")
@@ -122,6 +125,22 @@ def profile_prefill(hip, torch):
         torch.cuda.synchronize()
         log("prefill 14336x4096 N=512%s: 30 steps" % (" (repacked weights)" if repack else ""))
         del pm
+        torch.cuda.empty_cache()
+
+
+def profile_decode(hip, torch):
+    """Thirty eager steps of each decode configuration (weights rotating over
+    >= 1 GiB of copies), for rocprofv3: kernel durations without the launch
+    gaps that the graph-timed figures include."""
+    from q4_block_quantized_amd import inputs
+    for cid, N in ((1, 1), (2, 1), (3, 1), (3, 4), (4, 1), (4, 8)):
+        mats = Mats(hip, torch, cid, N)
+        settle(torch, lambda i: mats.step(hip, i), 0.3)
+        for i in range(30):
+            mats.step(hip, i)
+        torch.cuda.synchronize()
+        log("%s N=%d: 30 steps" % (inputs.WORKLOADS[cid].name, N))
+        del mats
         torch.cuda.empty_cache()
 
 
@@ -410,6 +429,31 @@ def q8w_leg(hip, torch):
     return res
 
 
+def q8w_prefill_leg(hip, torch, args, peaks):
+    """Q8_0 weights against 512 tokens (14336 x 4096, the prefill shape) on the
+    int8 matrix-core kernel: the whole call (activation records + product),
+    timed by the protocol; weights rotate over >= 1 GiB.  Throughput in
+    int8-equivalent TOPS (2 rows K N), against the int8 MFMA peak."""
+    from q4_block_quantized_amd import inputs
+    rows, K, N = 14336, 4096, 512
+    Wq8 = hip.q8_0_quantize(torch.from_numpy(inputs.weights(5, 0, rows, K)).cuda())
+    copies = max(2, -(-ROTATE_BYTES // (rows * (K // 32) * 34)))
+    Ws = [Wq8] + [Wq8.clone() for _ in range(copies - 1)]
+    X = torch.from_numpy(inputs.activations(5, 0, N, K)).cuda()
+    Y = torch.empty((N, rows), dtype=torch.float32, device="cuda")
+    fn = lambda i: hip.mul_mat_q8_0_q8_0(Ws[i % copies], X, Y)
+    settle(torch, fn, 0.3)
+    t = timed(torch, fn, max(10, args.steps // 4), max(3, args.warmup // 4))
+    tops = 2 * rows * K * N / (t["median"] * 1e-3) / 1e12
+    log("Q8_0 weights prefill %dx%d N=%d: %.2f us -> %.1f TOPS" % (rows, K, N, t["median"] * 1e3, tops))
+    del Ws, Wq8
+    torch.cuda.empty_cache()
+    return {"matrix": [rows, K], "N": N, "kernel": "k_act8_from_f32 + k_q8w_mm (int8 MFMA)",
+            "us_per_call": round(t["median"] * 1e3, 3), "TOPS": round(tops, 1), "timing": proto(t),
+            "frac_of_int8_peak": round(tops / INT8_PEAK_TOPS, 4),
+            "frac_of_measured_int8_peak": round(tops / peaks["mfma_int8_TOPS"], 4)}
+
+
 def fused_leg(hip, torch):
     """The steps around the product, fused (HIP graphs, each replay checked
     against an eager call; weights rotate over >= 1 GiB):
@@ -641,6 +685,9 @@ def main():
     if args.profile_legs:
         profile_legs(hip, torch)
         return
+    if args.profile_decode:
+        profile_decode(hip, torch)
+        return
     if args.profile_prefill:
         profile_prefill(hip, torch)
         return
@@ -695,6 +742,7 @@ def main():
     rows_lookup = None if args.no_small else get_rows_leg(hip, torch)
     q8_weights = None if args.no_small else q8w_leg(hip, torch)
     fusion = None if args.no_small else fused_leg(hip, torch)
+    q8w_prefill = None if args.no_prefill else q8w_prefill_leg(hip, torch, args, peaks)
 
     prefill = None
     if not args.no_prefill:
@@ -758,6 +806,7 @@ def main():
         "decode_configs_graph": small,
         "get_rows_graph": rows_lookup,
         "q8_0_weights_graph": q8_weights,
+        "q8_0_weights_prefill": q8w_prefill,
         "fused_graph": fusion,
         "cpu_baseline": cpu,
     }

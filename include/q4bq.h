@@ -294,8 +294,12 @@ int mul_mat_q4_0_q8_0_swiglu(const void *Wgate, const void *Wup, int64_t rows, i
  *   Wq8  device, rows x (K/32) blocks of 34 bytes, 2-byte aligned.
  *   X, N, Y, stream  as for mul_mat_q4_0_q8_0 (X is quantized inside).
  * Requires K/32 <= 1024 (K <= 32768); other errors as for mul_mat_q4_0_q8_0.
- * Decode-shaped: one row-streaming launch per group of at most 8 tokens (fewer
- * for K above 14336), each reading all of Wq8.  No scratch memory.
+ * N <= 8: one row-streaming launch per group of tokens (fewer than 8 above
+ * K = 14336), no scratch memory.  N > 8: the activations are quantized into
+ * stream-ordered scratch of N * K/32 * 34 bytes (hipMallocAsync on `stream`,
+ * Q4BQ_ENOMEM if that fails), then the int8 matrix-core kernel reads Wq8 once
+ * per 128-token tile, in ceil(rows / 128) * ceil(N / 128) workgroups of 256
+ * threads (shapes past HIP's grid limit: Q4BQ_EINVAL).
  */
 int mul_mat_q8_0_q8_0(const void *Wq8, int64_t rows, int64_t K, const float *X,
                       int64_t N, float *Y, void *stream);
@@ -303,8 +307,9 @@ int mul_mat_q8_0_q8_0(const void *Wq8, int64_t rows, int64_t K, const float *X,
 /*
  * Test export for Q8_0 weights: D[(n * rows + r) * (K/32) + b] = the integer
  * dot of weight block (r, b) with activation block (n, b) of Xq (pages' Q8_0
- * layout), computed by the product kernel's dot function.  D: N*rows*(K/32)
- * int32, 4-byte aligned, must not overlap the inputs.
+ * layout): for N <= 8 by the decode kernel's dot function, above 8 by the
+ * matrix-core kernel's int8 MFMA (stream-ordered scratch as for the product).
+ * D: N*rows*(K/32) int32, 4-byte aligned, must not overlap the inputs.
  */
 int q8_0_q8_0_block_dots(const void *Wq8, int64_t rows, int64_t K, const void *Xq,
                          int64_t N, int32_t *D, void *stream);

@@ -447,10 +447,38 @@ int mul_mat_q4_0_q8_0_swiglu(const void* Wgate, const void* Wup, int64_t rows, i
                      static_cast<hipStream_t>(stream));
 }
 
+}  // extern "C"
+
+namespace {
+
+// The matrix-core grid for Q8_0 weights stays within HIP's work-item limit.
+bool q8w_mm_grid_ok(int64_t rows, int64_t N) {
+    return ((rows + kQ8wMmRows - 1) / kQ8wMmRows) * ((N + kQ8wMmTokens - 1) / kQ8wMmTokens) <=
+           kMaxWorkItems / kQ8wMmThreads;
+}
+
+// Runs the matrix-core Q8_0-weight product with stream-ordered scratch.
+int run_q8w_mm(const uint8_t* W, int64_t rows, int64_t nb, const float* X, const uint8_t* Xq, int64_t N, float* Y,
+               int32_t* D, hipStream_t s) {
+    void* ws = nullptr;
+    if (hipMallocAsync(&ws, q8w_mm_act_bytes(N, nb), s) != hipSuccess || ws == nullptr) {
+        (void)hipGetLastError();
+        return Q4BQ_ENOMEM;
+    }
+    const hipError_t err = launch_q8w_mm(W, rows, nb, X, Xq, N, Y, D, ws, s);
+    if (hipFreeAsync(ws, s) != hipSuccess) return Q4BQ_EHIP;
+    return status_of(err);
+}
+
+}  // namespace
+
+extern "C" {
+
 int mul_mat_q8_0_q8_0(const void* Wq8, int64_t rows, int64_t K, const float* X, int64_t N, float* Y, void* stream) {
     if (!Wq8 || !X || !Y || bad_dim(rows) || bad_dim(N) || bad_k(K)) return Q4BQ_EINVAL;
     const int64_t nb = K / kQK;
     if (!q8w_supported_k(nb) || too_big(rows, K, 2) || too_big(N, K, 4) || too_big(N, rows, 4)) return Q4BQ_EINVAL;
+    if (N > kGemvMaxN && !q8w_mm_grid_ok(rows, N)) return Q4BQ_EINVAL;
     if (!aligned(Wq8, 2) || !aligned(X, 4) || !aligned(Y, 4)) return Q4BQ_EINVAL;
     const size_t y_bytes = static_cast<size_t>(N * rows) * 4;
     if (overlap(Y, y_bytes, Wq8, static_cast<size_t>(rows * nb) * kQ8Bytes) ||
@@ -459,6 +487,9 @@ int mul_mat_q8_0_q8_0(const void* Wq8, int64_t rows, int64_t K, const float* X, 
     hipError_t err = hipSuccess;
     const DeviceInfo* dev = current_device(&err);
     if (!dev) return Q4BQ_EHIP;
+    if (N > kGemvMaxN)
+        return run_q8w_mm(static_cast<const uint8_t*>(Wq8), rows, nb, X, nullptr, N, Y, nullptr,
+                          static_cast<hipStream_t>(stream));
     return status_of(launch_q8w_product(dev, static_cast<const uint8_t*>(Wq8), rows, nb, X, N, Y,
                                         static_cast<hipStream_t>(stream)));
 }
@@ -473,8 +504,12 @@ int q8_0_q8_0_block_dots(const void* Wq8, int64_t rows, int64_t K, const void* X
     if (overlap(D, d_bytes, Wq8, static_cast<size_t>(rows * nb) * kQ8Bytes) ||
         overlap(D, d_bytes, Xq, static_cast<size_t>(N * nb) * kQ8Bytes))
         return Q4BQ_EINVAL;
+    if (N > kGemvMaxN && !q8w_mm_grid_ok(rows, N)) return Q4BQ_EINVAL;
     hipError_t err = hipSuccess;
     if (!current_device(&err)) return Q4BQ_EHIP;
+    if (N > kGemvMaxN)
+        return run_q8w_mm(static_cast<const uint8_t*>(Wq8), rows, nb, nullptr, static_cast<const uint8_t*>(Xq), N,
+                          nullptr, D, static_cast<hipStream_t>(stream));
     return status_of(launch_q8w_block_dots(static_cast<const uint8_t*>(Wq8), rows, nb,
                                            static_cast<const uint8_t*>(Xq), N, D, static_cast<hipStream_t>(stream)));
 }

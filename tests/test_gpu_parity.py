@@ -440,6 +440,47 @@ def test_q8w_full_size(hip, orc, rows, K):
         assert_close(Y[:, sample], orc.mul_mat_q8_ref(Ws, orc.q8_0_quantize(X[:N]), K), "q8w full N=%d" % N)
 
 
+@pytest.mark.parametrize("K", [32, 96, 160, 4096, 4128])
+def test_q8w_many_tokens(hip, orc, K):
+    """More than eight tokens (the int8 matrix-core kernel): ragged row and token
+    tiles, block counts that are not a multiple of the 4-block stage, the
+    oracle bar on Y and every block dot bit for bit."""
+    for rows in (1, 129, 300):
+        for N in (9, 64, 130, 257):
+            if rows * K * N > 20_000_000:
+                continue
+            print("q8w many tokens rows=%d K=%d N=%d" % (rows, K, N), flush=True)
+            W, X = _case(rows, K, N, 4400 + rows + K + N)
+            Wq8 = hip.q8_0_quantize(dev(W))
+            Wq8_o = orc.q8_0_quantize(W)
+            Xq_o = orc.q8_0_quantize(X)
+            Y = host(hip.mul_mat_q8_0_q8_0(Wq8, dev(X)))
+            assert Y.shape == (N, rows)
+            assert_close(Y, orc.mul_mat_q8_ref(Wq8_o, Xq_o, K), "q8w rows=%d K=%d N=%d" % (rows, K, N))
+            D = host(hip.q8_0_q8_0_block_dots(Wq8, dev(Xq_o), K))
+            assert np.array_equal(D, orc.block_dots_q8(Wq8_o, Xq_o, K)), (rows, K, N)
+
+
+def test_q8w_prefill_full_size(hip, orc):
+    """Q8_0 weights 14336 x 4096 against 512 tokens (the prefill shape), in the
+    benchmark's launch configuration; outputs sampled on the first, last and
+    random rows for every token, block dots sampled."""
+    rows, K, N = 14336, 4096, 512
+    W = inputs.weights(5, 0, rows, K)
+    X = inputs.activations(5, 0, N, K)
+    Wq8 = hip.q8_0_quantize(dev(W))
+    sample = _sample_rows(rows, 512, 4500)
+    Wq8_o = orc.q8_0_quantize(W[sample])
+    Xq_o = orc.q8_0_quantize(X)
+    print("q8w prefill full size", flush=True)
+    Y = host(hip.mul_mat_q8_0_q8_0(Wq8, dev(X)))
+    assert_close(Y[:, sample], orc.mul_mat_q8_ref(Wq8_o, Xq_o, K), "q8w prefill")
+    Dg = hip.q8_0_q8_0_block_dots(Wq8, dev(Xq_o), K)
+    tok = np.unique(np.r_[0, N - 1, np.arange(1, N, 37)])
+    Ds = host(Dg.index_select(0, torch.from_numpy(tok).cuda()).index_select(1, torch.from_numpy(sample).cuda()))
+    assert np.array_equal(Ds, orc.block_dots_q8(Wq8_o, Xq_o[tok], K))
+
+
 # ---------------------------------------------------------------------------
 # the steps around the product: LayerNorm before it, bias / activation /
 # element-wise factor after it, SwiGLU

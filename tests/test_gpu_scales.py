@@ -184,6 +184,22 @@ def test_multi_and_fused_with_edge_scales(hip, orc, N):
         assert_close(Yf, orc.epilogue(Yref, bias=bias, act=orc.ACT_SILU), "fused N=%d matrix %d" % (N, i))
 
 
+@pytest.mark.parametrize("rows,K,N", [(300, 4096, 1), (300, 4096, 8), (257, 768, 9), (300, 4096, 130)])
+def test_q8_0_weights_with_edge_scales(hip, orc, rows, K, N):
+    """Q8_0 weights (the same binary16 block scale) with zero and subnormal
+    scales on both sides, through the decode kernel (N <= 8) and the int8
+    matrix-core kernel (N > 8): Y against the oracle and the block dots."""
+    print("q8_0 weights edge scales rows=%d K=%d N=%d" % (rows, K, N), flush=True)
+    W, X = mixed_scales(rows, K, N, 65000 + rows + K + N)
+    Wq8_o, Xq_o = orc.q8_0_quantize(W), orc.q8_0_quantize(X)
+    assert _scale_kinds(Wq8_o, 34)[1] > 0 and _scale_kinds(Xq_o, 34)[1] > 0
+    Wq8 = hip.q8_0_quantize(dev(W))
+    assert np.array_equal(host(Wq8).reshape(-1), Wq8_o.reshape(-1))
+    Y = host(hip.mul_mat_q8_0_q8_0(Wq8, dev(X)))
+    assert_close(Y, orc.mul_mat_q8_ref(Wq8_o, Xq_o, K), "q8w edge N=%d" % N)
+    assert np.array_equal(host(hip.q8_0_q8_0_block_dots(Wq8, dev(Xq_o), K)), orc.block_dots_q8(Wq8_o, Xq_o, K))
+
+
 @pytest.mark.parametrize("N", [1, 3, 11])
 def test_layernorm_mean_off_the_fp32_grid(hip, orc, N):
     """Tokens whose mean is not an fp32 value (4096 plus a few fp32 ulps on a
