@@ -9,6 +9,8 @@
 // the task kernel in q4bq_gemv.hip.
 #pragma once
 
+#include <algorithm>
+
 #include "q4bq_device.h"
 #include "q4bq_internal.h"
 
@@ -41,9 +43,20 @@ namespace {
 // quantizer's buffer (kActGlobal).  Up to eight of X's 16-byte loads per
 // thread are issued before the first weight loads, so that waiting for them
 // does not wait for the weights.
+//
+// Few long rows (chunked form, C > 1): with more pairs than lanes and too few
+// rows to give each wave several, a row is cut into C chunks of 48..64
+// consecutive pairs and the grid walks "chunk rows" v = C r + c, one pair per
+// lane.  Wave w always meets chunk w mod C, so its activations stay in
+// registers; the grid still streams one contiguous band of the matrix at a
+// time, and each wave has several chunk rows to pipeline.  The C chunks of a
+// row belong to C neighbouring waves of one workgroup: each wave keeps its
+// per-round partial sums in registers, and at the end the workgroup adds a
+// row's C partials in chunk order through LDS and stores Y.
 // ---------------------------------------------------------------------------
 constexpr int kRowsMaxPPL = 4;
 constexpr size_t kRowsMaxLds = 128 * 1024;  // quantized activations in LDS (one workgroup per CU)
+constexpr int kSplitRounds = 8;              // chunk rows per wave, at most, in the chunked form
 
 template <int kCtrl, int kRowMask>
 __device__ __forceinline__ float dpp_f(float v) {
@@ -132,7 +145,7 @@ __device__ __forceinline__ int64_t uniform64(int64_t v) {
 // DOTS: instead of Y, every per-block integer dot goes to
 // Dots[(n * rows + r) * nb + b] (the test export; one matrix of Q4_0 blocks,
 // activations from the quantizer's buffer).
-template <int THREADS, int NT, int PPL, int D, int SRC, int LAY, bool EPI, bool DOTS = false>
+template <int THREADS, int NT, int PPL, int D, int SRC, int LAY, bool EPI, bool DOTS = false, int C = 1>
 __global__ void __launch_bounds__(THREADS)
 k_gemv_rows(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __restrict__ src,
             float* __restrict__ Y, int32_t* __restrict__ Dots, const MultiDesc md) {
@@ -143,6 +156,7 @@ k_gemv_rows(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __
     constexpr bool kActReg = PPL == 1;         // activations in registers, else read from LDS per row
     constexpr bool kUseLds = SRC == kXF32 || !kActReg;
     constexpr int kWaves = THREADS / 64;
+    static_assert(C == 1 || (PPL == 1 && !MULTI && !DOTS && kWaves % C == 0), "chunked form");
     extern __shared__ __align__(16) uint8_t smem[];
     uint32_t* sq = reinterpret_cast<uint32_t*>(smem);
     ActScale* ss = reinterpret_cast<ActScale*>(smem + static_cast<size_t>(NT) * nb * kActQBytes);
@@ -150,14 +164,16 @@ k_gemv_rows(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar row arithmetic
     const int P = nb >> 1;
+    const int Pc = P / C;                         // pairs per chunk (C divides P)
+    const int pbase = C > 1 ? (wave % C) * Pc : 0;  // this wave's chunk, as a pair offset in the row
     const int nblk = NT * nb;  // activation blocks, token-major
 
     // 1. activation loads (before any weight load)
     //    kXF32: thread t quantizes quad (t & 7) of blocks t / 8 + (THREADS / 8) j
     //    kActGlobal into LDS: thread t copies 16-byte piece t + THREADS j of
     //    the int8 blocks and scale record t + THREADS j
-    constexpr int kJ = (1024 * NT * PPL + THREADS - 1) / THREADS;  // nb <= 128 * PPL
-    constexpr int kJpreMax = PPL == 1 ? 8 : 4;
+    constexpr int kJ = (1024 * NT * PPL * C + THREADS - 1) / THREADS;  // nb <= 128 * PPL * C
+    constexpr int kJpreMax = PPL * C == 1 ? 8 : 4;
     constexpr int kJpre = kJ < kJpreMax ? kJ : kJpreMax;
     float4 xv[SRC == kXF32 ? kJpre : 1];
     if constexpr (SRC == kXF32) {
@@ -171,7 +187,7 @@ k_gemv_rows(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __
     uint32_t areg[kActReg ? NT : 1][2][8];
     ActScale sreg[kActReg ? NT : 1][2];
     if constexpr (SRC == kActGlobal && kActReg) {
-        const int p = min(lane, P - 1);
+        const int p = pbase + min(lane, Pc - 1);
         const u32x4* q = static_cast<const u32x4*>(src);
         const ActScale* sc = reinterpret_cast<const ActScale*>(static_cast<const uint8_t*>(src) +
                                                                static_cast<size_t>(nblk) * kActQBytes);
@@ -188,18 +204,20 @@ k_gemv_rows(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __
     }
 
     // 2. the first D rows of this wave
+    //    (rows of the chunked form are chunk rows v = C r + c)
+    const int64_t V = rows * C;
     const int64_t S = static_cast<int64_t>(gridDim.x) * kWaves;
     const int64_t w0 = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
-    const int64_t nk = w0 < rows ? (rows - 1 - w0) / S + 1 : 0;
+    const int64_t nk = w0 < V ? (V - 1 - w0) / S + 1 : 0;
     // a wave without rows (small matrices) still issues its loads, on the last
     // row, so that no branch leaves the load counters uncertain
-    const int64_t rlast = nk > 0 ? w0 + (nk - 1) * S : rows - 1;
+    const int64_t rlast = nk > 0 ? w0 + (nk - 1) * S : V - 1;
     int pp[PPL];
     bool pv[PPL];
 #pragma unroll
     for (int i = 0; i < PPL; ++i) {
-        pv[i] = lane + 64 * i < P;
-        pp[i] = min(lane + 64 * i, P - 1);
+        pv[i] = lane + 64 * i < Pc;
+        pp[i] = pbase + min(lane + 64 * i, Pc - 1);
     }
     // where a row's blocks and its output live; every value is wave-uniform
     // (scalar registers) and lanes add a 32-bit offset
@@ -229,10 +247,10 @@ k_gemv_rows(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __
             a.y = yb + (r - f);
             a.ystride = f1 - f;
         } else {
-            const int64_t rb = uniform64(r * nb);
+            const int64_t rb = uniform64(static_cast<int64_t>(static_cast<uint64_t>(r) / C) * nb);
             a.w = Wq + rb * (RP ? 16 : kQ4Bytes);
             a.sc = Wsc + rb * 2;
-            a.y = Y + r;
+            a.y = Y + static_cast<int64_t>(static_cast<uint64_t>(r) / C);
             a.ystride = rows;
         }
         return a;
@@ -271,8 +289,9 @@ k_gemv_rows(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __
 #pragma unroll
             for (int j = 0; j < kJpre; ++j) quantize(xv[j], j);
             // the rest of a long X (loaded after the weights: these wait for them)
+            const int jend = min(kJ, (nblk + THREADS / 8 - 1) / (THREADS / 8));
 #pragma unroll 2
-            for (int j = kJpre; j < kJ; ++j) {
+            for (int j = kJpre; j < jend; ++j) {
                 const int g = min(static_cast<int>(threadIdx.x >> 3) + (THREADS / 8) * j, nblk - 1);
                 float4 x;
                 __builtin_memcpy(&x, X + static_cast<int64_t>(g) * kQK + 4 * m, 16);
@@ -291,7 +310,7 @@ k_gemv_rows(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         if constexpr (kActReg) {
-            const int p = min(lane, P - 1);
+            const int p = pbase + min(lane, Pc - 1);
 #pragma unroll
             for (int n = 0; n < NT; ++n)
 #pragma unroll
@@ -305,7 +324,7 @@ k_gemv_rows(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __
                 }
         }
     }
-    if (nk == 0) return;
+    if (C == 1 && nk == 0) return;  // the chunked form's waves all meet the final barriers
 
     if constexpr (DOTS) {
         // the same loads and block dots as the product, each dot stored
@@ -388,6 +407,51 @@ k_gemv_rows(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __
         }
     };
     const int my_token = lane_token<NT>(lane);
+    if constexpr (C > 1) {
+        // per-round partial sums in registers (round k: chunk row w0 + k S)
+        float keep[kSplitRounds];
+#pragma unroll
+        for (int k = 0; k < kSplitRounds; k += D) {
+            if (k >= nk) break;
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                float part[NT];
+                fold(raw[d], part);
+                keep[k + d] = wave_sums<NT>(part, lane);
+                load_row(raw[d], k + d + D);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        // every wave is past its last LDS activation read: the partials take
+        // LDS, slot (k * kWaves + wave) * NT + token
+        float* pl = reinterpret_cast<float*>(smem);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int k = 0; k < kSplitRounds; ++k)
+            if (k < nk && my_token >= 0 && my_token < NT) pl[(k * kWaves + wave) * NT + my_token] = keep[k];
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        // this workgroup's outputs: round k, row q of the round (kWaves / C
+        // rows, from waves C q .. C q + C - 1), token n
+        constexpr int kRowsPerRound = kWaves / C;
+        for (int t = threadIdx.x; t < kSplitRounds * kRowsPerRound * NT; t += THREADS) {
+            const int n = t % NT, q = (t / NT) % kRowsPerRound, k = t / (NT * kRowsPerRound);
+            const int64_t v = static_cast<int64_t>(blockIdx.x) * kWaves + k * S + q * C;
+            if (v < V) {
+                const float* src_p = pl + (k * kWaves + q * C) * NT + n;
+                float y = src_p[0];
+#pragma unroll
+                for (int c = 1; c < C; ++c) y += src_p[c * NT];
+                const int64_t r = v / C;
+                Y[static_cast<int64_t>(n) * rows + r] = EPI ? apply_epilogue(y, n, r, rows, md.epi) : y;
+            }
+        }
+        return;
+    }
     for (int64_t k = 0; k < nk; k += D) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
@@ -417,6 +481,25 @@ inline int rows_ppl(int64_t nb) {
     return 0;
 }
 
+// Chunks per row for the chunked form, or 1: rows of 96..512 pairs (an even
+// block count) that split into C = 2, 4 or 8 chunks of 48..64 pairs, when
+// the grid gives no wave more than kSplitRounds chunk rows.  waves: per
+// workgroup of the one-pair-per-lane kernel for these tokens.
+inline int rows_split(int64_t rows, int64_t nb, int waves, int num_cu) {
+    if (nb & 1) return 1;
+    const int64_t P = nb >> 1;
+    if (P <= 64) return 1;
+    for (int C = 2; C <= 8; C *= 2) {
+        if (C > waves || P % C != 0 || P / C > 64 || P / C < 48) continue;
+        const int64_t V = rows * C;
+        int64_t wgs = (V + waves - 1) / waves;
+        const int64_t cap = static_cast<int64_t>(num_cu) * (16 / waves);
+        if (wgs > cap) wgs = cap;
+        return (V + wgs * waves - 1) / (wgs * waves) <= kSplitRounds ? C : 1;
+    }
+    return 1;
+}
+
 // Workgroup size: 16 waves per CU (at most 128 registers per lane), or 8 where
 // more tokens need more registers (token activations with one pair per lane;
 // per-token partial sums and LDS operands on longer rows).  Depth: rows in
@@ -426,16 +509,17 @@ constexpr int rows_threads() { return NT > (PPL == 1 ? 4 : PPL == 2 ? 6 : 4) ? 5
 template <int NT, int PPL>
 constexpr int rows_depth() { return PPL == 1 && NT > 4 ? 2 : 1; }
 
-template <int SRC, int LAY, bool EPI, bool DOTS, int NT, int PPL>
+template <int SRC, int LAY, bool EPI, bool DOTS, int NT, int PPL, int C = 1>
 hipError_t launch_rows_k(const DeviceInfo* dev, const uint8_t* Wq, int64_t rows, int64_t nb, const void* src,
                          float* Y, int32_t* dots, const MultiDesc& md, hipStream_t s) {
     constexpr int kThreads = rows_threads<NT, PPL>();
     constexpr int kDepth = rows_depth<NT, PPL>();
-    const auto kernel = k_gemv_rows<kThreads, NT, PPL, kDepth, SRC, LAY, EPI, DOTS>;
-    int64_t wgs = (rows + kThreads / 64 - 1) / (kThreads / 64);
+    const auto kernel = k_gemv_rows<kThreads, NT, PPL, kDepth, SRC, LAY, EPI, DOTS, C>;
+    int64_t wgs = (rows * C + kThreads / 64 - 1) / (kThreads / 64);
     const int64_t cap = static_cast<int64_t>(dev->num_cu) * (1024 / kThreads);
     if (wgs > cap) wgs = cap;
-    const size_t lds = (SRC == kXF32 || PPL > 1) ? static_cast<size_t>(NT) * nb * (kActQBytes + kActSBytes) : 0;
+    size_t lds = (SRC == kXF32 || PPL > 1) ? static_cast<size_t>(NT) * nb * (kActQBytes + kActSBytes) : 0;
+    if (C > 1) lds = std::max(lds, static_cast<size_t>(kSplitRounds) * (kThreads / 64) * NT * sizeof(float));
     if (lds > 64 * 1024) {
         // beyond the default dynamic LDS limit: raise it once for this kernel
         static const hipError_t raised = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
@@ -451,6 +535,14 @@ hipError_t launch_rows_k(const DeviceInfo* dev, const uint8_t* Wq, int64_t rows,
 template <int SRC, int LAY, bool EPI, bool DOTS, int NT>
 hipError_t launch_rows_nt(const DeviceInfo* dev, const uint8_t* Wq, int64_t rows, int64_t nb, const void* src,
                           float* Y, int32_t* dots, const MultiDesc& md, hipStream_t s) {
+    if constexpr (LAY != kLayMulti && !DOTS) {
+        switch (rows_split(rows, nb, rows_threads<NT, 1>() / 64, dev->num_cu)) {
+            case 2: return launch_rows_k<SRC, LAY, EPI, DOTS, NT, 1, 2>(dev, Wq, rows, nb, src, Y, dots, md, s);
+            case 4: return launch_rows_k<SRC, LAY, EPI, DOTS, NT, 1, 4>(dev, Wq, rows, nb, src, Y, dots, md, s);
+            case 8: return launch_rows_k<SRC, LAY, EPI, DOTS, NT, 1, 8>(dev, Wq, rows, nb, src, Y, dots, md, s);
+            default: break;
+        }
+    }
     switch (rows_ppl(nb)) {
         case 1: return launch_rows_k<SRC, LAY, EPI, DOTS, NT, 1>(dev, Wq, rows, nb, src, Y, dots, md, s);
         case 2: return launch_rows_k<SRC, LAY, EPI, DOTS, NT, 2>(dev, Wq, rows, nb, src, Y, dots, md, s);

@@ -115,6 +115,68 @@ def test_quantizers_fp16_scale_sweep(hip, orc):
     assert np.array_equal(host(hip.q8_0_quantize(dev(B))), orc.q8_0_quantize(B))
 
 
+def near_half_blocks(seed, N, K):
+    """N x K activations whose quotients x / d sit within a few ulps of a
+    half-integer, so that the rounding of the binary32 quotient decides each
+    code.  Element 0 of every block is +-127 d, which makes binary16(amax / 127)
+    exactly d; d spans normal and subnormal binary16 values; about a third of
+    the elements are ordinary values of the block's range."""
+    rng = np.random.default_rng(seed)
+    nb = K // 32
+    bits = np.where(rng.random((N, nb)) < 0.2, rng.integers(1, 0x400, (N, nb)), rng.integers(0x0400, 0x5BFF, (N, nb)))
+    d = bits.astype(np.uint16).view(np.float16).astype(np.float64)
+    k = rng.integers(-127, 127, (N, nb, 32))
+    x = ((k + 0.5) * d[..., None]).astype(np.float32)
+    nudge = rng.integers(-3, 4, (N, nb, 32))
+    for step in range(1, 4):
+        x = np.where(nudge >= step, np.nextafter(x, np.float32(np.inf)), x)
+        x = np.where(-nudge >= step, np.nextafter(x, np.float32(-np.inf)), x)
+    plain = (rng.uniform(-126.9, 126.9, (N, nb, 32)) * d[..., None]).astype(np.float32)
+    x = np.where(rng.random((N, nb, 32)) < 0.33, plain, x)
+    x[..., 0] = (np.where(rng.random((N, nb)) < 0.5, -127.0, 127.0) * d).astype(np.float32)
+    return np.ascontiguousarray(x.reshape(N, K), dtype=np.float32)
+
+
+def unit_code_weights(K):
+    """K x K Q4_0 blocks, all scales 1.0, whose row r has the single nonzero
+    code +1 at element r: every product element is then one activation code
+    times its block scale, exact in fp32, so Y shows each code."""
+    nb = K // 32
+    Wq = np.zeros((K, nb, 18), np.uint8)
+    Wq[:, :, 1] = 0x3C  # binary16 1.0, little-endian
+    Wq[:, :, 2:] = 0x88  # nibble 8 = code 0
+    r = np.arange(K)
+    j = r % 32
+    Wq[r, r // 32, 2 + j // 2] = np.where(j % 2 == 0, 0x89, 0x98)
+    return Wq.reshape(K, nb * 18)
+
+
+def test_quantizer_half_integer_quotients(hip, orc):
+    X = near_half_blocks(31, 64, 4096)
+    assert np.array_equal(host(hip.q8_0_quantize(dev(X))), orc.q8_0_quantize(X))
+
+
+@pytest.mark.parametrize("K", [768, 4096, 14336])
+def test_activation_codes_in_every_product_path(hip, orc, K):
+    """Quotients at half-integers through the activation quantizer of each
+    product kernel (streaming decode, task kernel, two-phase, matrix cores):
+    with unit_code_weights the fp32 result must equal the oracle's exactly."""
+    Wq_o = unit_code_weights(K)
+    dq = orc.q4_0_dequantize(Wq_o, K)
+    assert np.array_equal(dq, np.eye(K, dtype=np.float32))
+    Wq = dev(Wq_o)
+    for N in ((1, 8, 9) if K > 4096 else (1, 3, 8, 9, 130)):
+        print("half-integer quotients K=%d N=%d" % (K, N), flush=True)
+        X = near_half_blocks(4000 + K + N, N, K)
+        want = orc.mul_mat_ref(Wq_o, orc.q8_0_quantize(X), K)
+        Xt = dev(X)
+        got = host(hip.mul_mat_q4_0_q8_0(Wq, Xt)).astype(np.float64)
+        assert np.array_equal(got, want), (K, N, int((got != want).sum()))
+        ws = hip.workspace(K, K, N)
+        got = host(hip.mul_mat_q4_0_q8_0_prepared(Wq, hip.q4bq_quantize_activations(Xt, ws), N, K))
+        assert np.array_equal(got.astype(np.float64), want), ("two-phase", K, N)
+
+
 # ---------------------------------------------------------------------------
 # block dots and the product on a shape sweep (tiles, ragged tails, odd K/32)
 # ---------------------------------------------------------------------------
