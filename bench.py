@@ -39,8 +39,10 @@ ROTATE_BYTES = 1 << 30
 # are in profiles/.  They describe the kernels as profiled; re-profile after a
 # kernel change.
 TRAFFIC_BYTES = {
-    ("llama3_8b_head", 1): 296211489,      # profiles/k_gemv_rows_fused_vocab_head_128256x4096_N1.md
-    ("llama3_8b_prefill", 512): 98293810,   # profiles/k_prefill_14336x4096_N512.md
+    ("llama3_8b_head", 1): 296213669,      # profiles/k_gemv_rows_fused_vocab_head_128256x4096_N1.md
+    ("llama3_8b_prefill", 512): 98293485,   # profiles/k_prefill_14336x4096_N512.md
+    ("llama3_8b_prefill_repacked", 512): 122589802,  # profiles/k_prefill_repacked_14336x4096_N512.md
+    ("q8_0_weights_prefill", 512): 109773002,         # profiles/k_q8w_mm_q8_0_weights_prefill_14336x4096_N512.md
 }
 
 
@@ -451,7 +453,8 @@ def q8w_prefill_leg(hip, torch, args, peaks):
     return {"matrix": [rows, K], "N": N, "kernel": "k_act8_from_f32 + k_q8w_mm (int8 MFMA)",
             "us_per_call": round(t["median"] * 1e3, 3), "TOPS": round(tops, 1), "timing": proto(t),
             "frac_of_int8_peak": round(tops / INT8_PEAK_TOPS, 4),
-            "frac_of_measured_int8_peak": round(tops / peaks["mfma_int8_TOPS"], 4)}
+            "frac_of_measured_int8_peak": round(tops / peaks["mfma_int8_TOPS"], 4),
+            "traffic_k_q8w_mm": TRAFFIC_BYTES.get(("q8_0_weights_prefill", N))}
 
 
 def fused_leg(hip, torch):
@@ -776,7 +779,8 @@ def main():
         rtops = rpm.ops() / (t_rp["median"] * 1e-3) / 1e12
         log("repacked weights: prefill step %.2f us -> %.1f TOPS" % (t_rp["median"] * 1e3, rtops))
         repacked["prefill"] = {"ms_per_step": round(t_rp["median"], 5), "TOPS": round(rtops, 2),
-                               "timing": proto(t_rp)}
+                               "timing": proto(t_rp),
+                               "traffic_k_prefill": TRAFFIC_BYTES.get(("llama3_8b_prefill_repacked", 512))}
         del rpm
         torch.cuda.empty_cache()
 
