@@ -84,37 +84,6 @@ __device__ __forceinline__ int8_t q8_rule(float x, float d) {
     return static_cast<int8_t>(min(max(q, -127), 127));
 }
 
-// q8_rule on four values of one block, with one reciprocal instead of four
-// correctly rounded divisions.  The estimate e = x * rcp(d) is within
-// 2^-22 |x / d| of the exact quotient (the hardware reciprocal to 1 ulp, the
-// product to half an ulp) and so is the binary32 quotient (half an ulp);
-// since |x| <= amax and d is the binary16 rounding of amax / 127, |x / d| is
-// below 192 (binary16 subnormals lose at most a factor 1.5), so the two lie
-// within 2^-14 of each other.  The code only depends on which side of the
-// nearest half-integer the quotient falls, so e decides it whenever it is
-// more than 2^-12 away from one; otherwise all four values of the lane are
-// redone with q8_rule (a branch that only some waves take).  d == 0 gives a
-// zero reciprocal, hence zero codes, as q8_rule does.
-__device__ __forceinline__ void q8_codes4(float x0, float x1, float x2, float x3, float d, int8_t (&q)[4]) {
-    const float xs[4] = {x0, x1, x2, x3};
-    const float r = d == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(d);
-    bool near = false;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float e = xs[i] * r;
-        const float a = fabsf(e);
-        const float whole = floorf(a);
-        const float frac = a - whole;  // exact: a < 2^8
-        near |= fabsf(frac - 0.5f) <= 0x1p-12f;
-        const int c = min(static_cast<int>(whole) + (frac > 0.5f ? 1 : 0), 127);
-        q[i] = static_cast<int8_t>(e < 0.0f ? -c : c);
-    }
-    if (near) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) q[i] = q8_rule(xs[i], d);
-    }
-}
-
 // Four int8 values of lane m (elements 4m..4m+3) -> this lane's dot-order
 // dword, and the block's -8 * sum(q) (both over the 8-lane group).
 __device__ __forceinline__ uint32_t dot_order_word(int8_t q0, int8_t q1, int8_t q2, int8_t q3, int m, int& bias) {
@@ -138,10 +107,9 @@ __device__ __forceinline__ ActScale quant_act_quad(float x0, float x1, float x2,
     a = fmaxf(a, dpp8_f<kDppMirror8>(a));
     dbits = float_to_half_bits(a / 127.0f);
     const float d = half_bits_to_float(dbits);
-    int8_t q[4];
-    q8_codes4(x0, x1, x2, x3, d, q);
+    const int8_t q0 = q8_rule(x0, d), q1 = q8_rule(x1, d), q2 = q8_rule(x2, d), q3 = q8_rule(x3, d);
     int bias;
-    word = dot_order_word(q[0], q[1], q[2], q[3], m, bias);
+    word = dot_order_word(q0, q1, q2, q3, m, bias);
     return ActScale{d, bias};
 }
 

@@ -60,10 +60,9 @@ __device__ __forceinline__ uint32_t quant_q8_natural(float x0, float x1, float x
     a = fmaxf(a, __shfl_xor(a, 2, 8));
     a = fmaxf(a, __shfl_xor(a, 4, 8));
     d = half_bits_to_float(float_to_half_bits(a / 127.0f));
-    int8_t q[4];
-    q8_codes4(x0, x1, x2, x3, d, q);
-    return static_cast<uint32_t>(static_cast<uint8_t>(q[0])) | (static_cast<uint32_t>(static_cast<uint8_t>(q[1])) << 8) |
-           (static_cast<uint32_t>(static_cast<uint8_t>(q[2])) << 16) | (static_cast<uint32_t>(static_cast<uint8_t>(q[3])) << 24);
+    const uint32_t q0 = static_cast<uint8_t>(q8_rule(x0, d)), q1 = static_cast<uint8_t>(q8_rule(x1, d));
+    const uint32_t q2 = static_cast<uint8_t>(q8_rule(x2, d)), q3 = static_cast<uint8_t>(q8_rule(x3, d));
+    return q0 | (q1 << 8) | (q2 << 16) | (q3 << 24);
 }
 
 // LDS: NT x nb blocks of 8 dwords (token-major), then NT x nb fp32 scales.

@@ -273,12 +273,9 @@ k_act8_from_f32(const float* __restrict__ X, int64_t N, int64_t nb, uint8_t* __r
             a = fmaxf(a, dpp8_f<kDppMirror8>(a));
             const uint32_t dbits = float_to_half_bits(a / 127.0f);
             const float d = half_bits_to_float(dbits);
-            int8_t c[4];
-            q8_codes4(x.x, x.y, x.z, x.w, d, c);
-            const uint32_t q = static_cast<uint32_t>(static_cast<uint8_t>(c[0])) |
-                               (static_cast<uint32_t>(static_cast<uint8_t>(c[1])) << 8) |
-                               (static_cast<uint32_t>(static_cast<uint8_t>(c[2])) << 16) |
-                               (static_cast<uint32_t>(static_cast<uint8_t>(c[3])) << 24);
+            const uint32_t q = static_cast<uint8_t>(q8_rule(x.x, d)) | (static_cast<uint32_t>(static_cast<uint8_t>(q8_rule(x.y, d))) << 8) |
+                               (static_cast<uint32_t>(static_cast<uint8_t>(q8_rule(x.z, d))) << 16) |
+                               (static_cast<uint32_t>(static_cast<uint8_t>(q8_rule(x.w, d))) << 24);
             if (valid) {
                 codes[(b * N + n) * 8 + m] = q;
                 if (m == 0) scales[b * N + n] = static_cast<uint16_t>(dbits);
