@@ -255,9 +255,14 @@ int q4_0_q8_0_block_dots(const void *Wq, int64_t rows, int64_t K, const void *Xq
  *                      other buffer (the form for graph capture).
  * Other arguments and errors as for mul_mat_q4_0_q8_0 (a short workspace:
  * Q4BQ_ENOMEM); N < 2^22 with LayerNorm (one 1024-thread workgroup per
- * token).  Launches: one kernel that
- * normalizes X (if asked) and quantizes it, then the product with the
- * epilogue in its store.
+ * token).  Launches: with one token (N = 1) and rows of at most 128 blocks or
+ * a block count the task kernel takes (every K of the GPT-2 and Llama shapes),
+ * one launch per product: the decode kernel normalizes and quantizes the
+ * token in its prologue (each workgroup takes the statistics over the whole
+ * token itself) and applies the epilogue in its store, and the workspace is
+ * not touched.  Otherwise one kernel that normalizes X (if asked) and
+ * quantizes it into the workspace, then the product with the epilogue in its
+ * store.
  */
 #define Q4BQ_ACT_NONE 0
 #define Q4BQ_ACT_GELU 1
@@ -273,8 +278,10 @@ int mul_mat_q4_0_q8_0_fused(const void *Wq, int64_t rows, int64_t K, const float
  * up and gate projections of the same normalized input, then
  * SiLU(gate) * up):
  *   H = SiLU(LN(X) Wgate^T) * (LN(X) Wup^T)
- * X is normalized (optional, as above) and quantized once; the gate product
- * writes SiLU(gate) into H and the up product multiplies it in its store.
+ * X is normalized (optional, as above) and quantized, once (or, in the one-
+ * token form of mul_mat_q4_0_q8_0_fused, in the prologue of each of the two
+ * product launches); the gate product writes SiLU(gate) into H and the up
+ * product multiplies it in its store.
  *   Wgate, Wup  rows x (K/32) Q4_0 blocks each; H device fp32 N x rows.
  * Workspace and errors as for mul_mat_q4_0_q8_0_fused.
  */

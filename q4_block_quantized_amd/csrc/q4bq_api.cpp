@@ -363,6 +363,18 @@ int run_fused(int count, const uint8_t* const* Wq, int64_t rows, int64_t K, cons
     const DeviceInfo* dev = current_device(&err);
     if (!dev) return Q4BQ_EHIP;
     const int64_t nb = K / kQK;
+    if (N == 1 && gemv_fuses_epi(nb)) {
+        // one launch per matrix: the decode kernel normalizes and quantizes
+        // the token in its prologue (no scratch)
+        for (int i = 0; i < count && err == hipSuccess; ++i) {
+            Epilogue e = epi[i];
+            e.ln_gamma = ln_gamma;
+            e.ln_beta = ln_beta;
+            e.ln_eps = ln_eps;
+            err = launch_gemv_fused_epi(dev, Wq[i], rows, nb, X, Y[i], e, s);
+        }
+        return err == hipSuccess ? Q4BQ_OK : Q4BQ_EHIP;
+    }
     const size_t bytes = fused_act_bytes(N, nb);
     void* ws = workspace;
     if (ws) {
@@ -439,6 +451,21 @@ int mul_mat_q4_0_q8_0_swiglu(const void* Wgate, const void* Wup, int64_t rows, i
                             static_cast<size_t>(K) * 4, static_cast<size_t>(K) * 4};
     rc = check_workspace(workspace, rows, K, N, bufs, sizes, 6);
     if (rc != Q4BQ_OK) return rc;
+    if (N == 1) {
+        hipError_t err = hipSuccess;
+        const DeviceInfo* dev = current_device(&err);
+        if (!dev) return Q4BQ_EHIP;
+        if (rows_dual_apply(dev, rows, K / kQK)) {
+            // one launch: gate and up rows side by side, LayerNorm and
+            // quantization of the token in its prologue
+            Epilogue ln{nullptr, nullptr, kEpiNone};
+            ln.ln_gamma = ln_gamma;
+            ln.ln_beta = ln_beta;
+            ln.ln_eps = ln_eps;
+            return status_of(launch_rows_dual(dev, static_cast<const uint8_t*>(Wgate), static_cast<const uint8_t*>(Wup),
+                                              rows, K / kQK, X, H, ln, static_cast<hipStream_t>(stream)));
+        }
+    }
     // H = SiLU(gate) first, then H = up * H in place
     const uint8_t* w[2] = {static_cast<const uint8_t*>(Wgate), static_cast<const uint8_t*>(Wup)};
     const Epilogue epi[2] = {Epilogue{nullptr, nullptr, kEpiSilu}, Epilogue{nullptr, H, kEpiNone}};

@@ -342,15 +342,69 @@ __device__ __forceinline__ int32_t block_dot(const Block4& w, const uint32_t* a,
 // The epilogue of a product output y for token n, row r (rows per token:
 // rows): y + bias[r], then GELU (GPT-2's tanh form) or SiLU (x * sigmoid(x)),
 // then times mul[n][r].
-__device__ __forceinline__ float apply_epilogue(float y, int64_t n, int64_t r, int64_t rows, const Epilogue& e) {
-    if (e.bias) y += e.bias[r];
+// ---------------------------------------------------------------------------
+// LayerNorm before the product (the ggml GPT-2 walkthrough, section 3.1:
+// gamma * (x - mu) / sqrt(sigma^2 + eps) + beta over each token's K values).
+// The statistics are taken in fp64 and the normalized value is evaluated in
+// fp64 and rounded once to fp32: the fp32 value that decides the Q8_0 codes
+// then does not depend on the summation order.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float ln_value(float x, double mu, double rstd, float g, float b) {
+#pragma clang fp contract(off)
+    return static_cast<float>(static_cast<double>(g) * ((static_cast<double>(x) - mu) * rstd) +
+                              static_cast<double>(b));
+}
+
+// Sum of one fp64 value per thread over a workgroup of THREADS threads; red:
+// THREADS / 64 doubles of LDS.  Every thread of the workgroup calls it (one
+// workgroup barrier) and gets the total, added in wave order.  A later call
+// must use other LDS (or come after another barrier): slow waves may still be
+// reading red.
+template <int THREADS>
+__device__ __forceinline__ double wg_sum_f64(double v, double* red) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    double t = 0.0;
+#pragma unroll
+    for (int i = 0; i < THREADS / 64; ++i) t += red[i];
+    return t;
+}
+
+__device__ __forceinline__ double quad_sum_f64(float4 v) {
+    return (static_cast<double>(v.x) + static_cast<double>(v.y)) + (static_cast<double>(v.z) + static_cast<double>(v.w));
+}
+__device__ __forceinline__ double quad_sqdev_f64(float4 v, double mu) {
+    const double a = static_cast<double>(v.x) - mu, b = static_cast<double>(v.y) - mu;
+    const double c = static_cast<double>(v.z) - mu, d = static_cast<double>(v.w) - mu;
+    return (a * a + b * b) + (c * c + d * d);
+}
+__device__ __forceinline__ float4 ln_quad(float4 v, double mu, double rstd, float4 g, float4 b) {
+    return make_float4(ln_value(v.x, mu, rstd, g.x, b.x), ln_value(v.y, mu, rstd, g.y, b.y),
+                       ln_value(v.z, mu, rstd, g.z, b.z), ln_value(v.w, mu, rstd, g.w, b.w));
+}
+
+// The epilogue with its operands already loaded: b = bias[r], m = mul[n][r]
+// (either ignored when its pointer is null), so that a kernel can fetch them
+// with the row's weights instead of at the store.
+__device__ __forceinline__ float epilogue_with(float y, float b, float m, const Epilogue& e) {
+    if (e.bias) y += b;
     if (e.act == kEpiGelu) {
         y = 0.5f * y * (1.0f + tanhf(0.7978845608028654f * (y + 0.044715f * y * y * y)));
     } else if (e.act == kEpiSilu) {
         y = y / (1.0f + expf(-y));
     }
-    if (e.mul) y *= e.mul[n * rows + r];
+    if (e.mul) y *= m;
     return y;
+}
+__device__ __forceinline__ float epi_bias(const Epilogue& e, int64_t r) { return e.bias ? e.bias[r] : 0.0f; }
+__device__ __forceinline__ float epi_mul(const Epilogue& e, int64_t n, int64_t r, int64_t rows) {
+    return e.mul ? e.mul[n * rows + r] : 1.0f;
+}
+
+__device__ __forceinline__ float apply_epilogue(float y, int64_t n, int64_t r, int64_t rows, const Epilogue& e) {
+    return epilogue_with(y, epi_bias(e, r), epi_mul(e, n, r, rows), e);
 }
 
 }  // namespace q4bq

@@ -66,11 +66,91 @@ k_gemv(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __restr
             const float* X = static_cast<const float*>(src);
             const int m = threadIdx.x & 7;
             const int nblk = NT * nb;
-            for (int g0 = (threadIdx.x >> 3) & ~7; g0 < nblk; g0 += THREADS / 8) {
+            // the fused form may LayerNorm the one token first: fp64 mean and
+            // population variance over the workgroup, then each value
+            // normalized in fp64 and rounded once to fp32
+            constexpr bool kLn = EPI && NT == 1;
+            const bool do_ln = kLn && md.epi.ln_gamma != nullptr;
+            double mu = 0.0, rstd = 0.0;
+            // a token of at most kLnRegQ quads per thread is read once, into
+            // registers, with its gamma and beta; longer ones in three passes
+            constexpr int kLnRegQ = 4;
+            bool ln_done = false;
+            if constexpr (kLn) {
+                if (do_ln && nblk <= kLnRegQ * (THREADS / 8)) {
+                    __shared__ double redr[2][THREADS / 64];
+                    const int qn = (nblk + THREADS / 8 - 1) / (THREADS / 8);  // quad rounds, <= kLnRegQ
+                    float4 xr[kLnRegQ], gr[kLnRegQ], br[kLnRegQ];
+#pragma unroll
+                    for (int i = 0; i < kLnRegQ; ++i) {
+                        if (i >= qn) break;
+                        const int g = min(static_cast<int>(threadIdx.x >> 3) + (THREADS / 8) * i, nblk - 1);
+                        const int64_t k = static_cast<int64_t>(g) * kQK + 4 * m;
+                        __builtin_memcpy(&xr[i], X + k, 16);
+                        __builtin_memcpy(&gr[i], md.epi.ln_gamma + k, 16);
+                        __builtin_memcpy(&br[i], md.epi.ln_beta + k, 16);
+                    }
+                    const double kk = static_cast<double>(nb) * kQK;
+                    double s1 = 0.0;
+#pragma unroll
+                    for (int i = 0; i < kLnRegQ; ++i) {
+                        if (i >= qn) break;
+                        if (static_cast<int>(threadIdx.x >> 3) + (THREADS / 8) * i < nblk) s1 += quad_sum_f64(xr[i]);
+                    }
+                    mu = wg_sum_f64<THREADS>(s1, redr[0]) / kk;
+                    double s2 = 0.0;
+#pragma unroll
+                    for (int i = 0; i < kLnRegQ; ++i) {
+                        if (i >= qn) break;
+                        if (static_cast<int>(threadIdx.x >> 3) + (THREADS / 8) * i < nblk)
+                            s2 += quad_sqdev_f64(xr[i], mu);
+                    }
+                    rstd = 1.0 / sqrt(wg_sum_f64<THREADS>(s2, redr[1]) / kk + static_cast<double>(md.epi.ln_eps));
+#pragma unroll
+                    for (int i = 0; i < kLnRegQ; ++i) {
+                        if (i >= qn) break;
+                        const int g = static_cast<int>(threadIdx.x >> 3) + (THREADS / 8) * i;
+                        const float4 x = ln_quad(xr[i], mu, rstd, gr[i], br[i]);
+                        uint32_t word;
+                        const ActScale sc = quant_act_quad(x.x, x.y, x.z, x.w, m, word);
+                        if (g < nblk) {
+                            sq[g * 8 + m] = word;
+                            if (m == 0) ss[g] = sc;
+                        }
+                    }
+                    ln_done = true;
+                } else if (do_ln) {
+                    __shared__ double red[2][THREADS / 64];
+                    const double kk = static_cast<double>(nb) * kQK;
+                    double s1 = 0.0;
+                    for (int g = threadIdx.x >> 3; g < nblk; g += THREADS / 8) {
+                        float4 x;
+                        __builtin_memcpy(&x, X + static_cast<int64_t>(g) * kQK + 4 * m, 16);
+                        s1 += quad_sum_f64(x);
+                    }
+                    mu = wg_sum_f64<THREADS>(s1, red[0]) / kk;
+                    double s2 = 0.0;
+                    for (int g = threadIdx.x >> 3; g < nblk; g += THREADS / 8) {
+                        float4 x;
+                        __builtin_memcpy(&x, X + static_cast<int64_t>(g) * kQK + 4 * m, 16);
+                        s2 += quad_sqdev_f64(x, mu);
+                    }
+                    rstd = 1.0 / sqrt(wg_sum_f64<THREADS>(s2, red[1]) / kk + static_cast<double>(md.epi.ln_eps));
+                }
+            }
+            for (int g0 = (threadIdx.x >> 3) & ~7; !ln_done && g0 < nblk; g0 += THREADS / 8) {
                 const int g = g0 + ((threadIdx.x >> 3) & 7);
                 const bool valid = g < nblk;
                 float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
                 if (valid) __builtin_memcpy(&x, X + static_cast<int64_t>(g) * kQK + 4 * m, 16);
+                if constexpr (kLn) {
+                    if (do_ln && valid) {
+                        float4 gq, bq;
+                        __builtin_memcpy(&gq, md.epi.ln_gamma + static_cast<int64_t>(g) * kQK + 4 * m, 16);
+                        __builtin_memcpy(&bq, md.epi.ln_beta + static_cast<int64_t>(g) * kQK + 4 * m, 16);
+                        x = ln_quad(x, mu, rstd, gq, bq);
+                    }
+                }
                 uint32_t word;
                 const ActScale sc = quant_act_quad(x.x, x.y, x.z, x.w, m, word);
                 if (valid) {
@@ -124,6 +204,17 @@ k_gemv(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __restr
                 wrow[j] = Wq + r[j] * nb * kQ4Bytes;
                 yrow[j] = Y + r[j];
                 ystride[j] = rows;
+            }
+        }
+        // fused forms: the rows' epilogue operands, fetched before the weights
+        float eb[EPI ? kRmax : 1], em[EPI ? kRmax : 1][EPI ? NT : 1];
+        if constexpr (EPI) {
+#pragma unroll
+            for (int j = 0; j < kRmax; ++j) {
+                const int64_t rr = rv[j] ? r[j] : 0;
+                eb[j] = epi_bias(md.epi, rr);
+#pragma unroll
+                for (int n = 0; n < NT; ++n) em[j][n] = epi_mul(md.epi, n, rr, rows);
             }
         }
         float acc[kRmax][NT];
@@ -217,7 +308,7 @@ k_gemv(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __restr
 #pragma unroll
                     for (int n = 0; n < NT; ++n)
                         yrow[j][static_cast<int64_t>(n) * ystride[j]] =
-                            EPI ? apply_epilogue(acc[j][n], n, r[j], rows, md.epi) : acc[j][n];
+                            EPI ? epilogue_with(acc[j][n], eb[j], em[j][n], md.epi) : acc[j][n];
                 }
             }
         }
@@ -283,7 +374,7 @@ hipError_t launch_v(const Shape& sh, int lay, const uint8_t* Wq, int64_t rows, i
                     float* Y, int32_t* D, const MultiDesc& md, hipStream_t s) {
     const size_t lds = SRC == kActGlobal ? 0 : static_cast<size_t>(NT) * nb * (kActQBytes + kActSBytes);
     const int nbi = static_cast<int>(nb);
-    const bool fused = md.epi.bias || md.epi.mul || md.epi.act != kEpiNone;
+    const bool fused = md.epi.bias || md.epi.mul || md.epi.act != kEpiNone || md.epi.ln_gamma;
     if (lay == kLayRepacked) {
         if (fused) return hipErrorInvalidValue;  // the fused forms take the pages' blocks
         hipLaunchKernelGGL((k_gemv<NT, THREADS, SRC, DOTS, kLayRepacked, false>), dim3(sh.wgs), dim3(THREADS), lds, s,
@@ -295,9 +386,12 @@ hipError_t launch_v(const Shape& sh, int lay, const uint8_t* Wq, int64_t rows, i
             hipLaunchKernelGGL((k_gemv<NT, THREADS, SRC, false, kLayMulti, false>), dim3(sh.wgs), dim3(THREADS), lds,
                                s, Wq, rows, nbi, src, Y, D, sh.log2G, sh.rpi, md);
         }
-    } else if (fused && SRC != kXF32 && !DOTS) {
-        hipLaunchKernelGGL((k_gemv<NT, THREADS, SRC, false, kLayAoS, true>), dim3(sh.wgs), dim3(THREADS), lds, s, Wq,
-                           rows, nbi, src, Y, D, sh.log2G, sh.rpi, md);
+    } else if (fused && !DOTS && (SRC != kXF32 || NT == 1)) {
+        if constexpr (!DOTS && (SRC != kXF32 || NT == 1)) {
+            if (md.epi.ln_gamma && SRC != kXF32) return hipErrorInvalidValue;  // LayerNorm: fp32 X only
+            hipLaunchKernelGGL((k_gemv<NT, THREADS, SRC, false, kLayAoS, true>), dim3(sh.wgs), dim3(THREADS), lds, s,
+                               Wq, rows, nbi, src, Y, D, sh.log2G, sh.rpi, md);
+        }
     } else {
         if (fused) return hipErrorInvalidValue;
         hipLaunchKernelGGL((k_gemv<NT, THREADS, SRC, DOTS, kLayAoS, false>), dim3(sh.wgs), dim3(THREADS), lds, s, Wq,
@@ -377,6 +471,16 @@ bool gemv_prefers_fused(int64_t N, int64_t nb) {
 hipError_t launch_gemv_fused(const DeviceInfo* dev, WLayout lay, const uint8_t* Wq, int64_t rows, int64_t nb,
                              const float* X, int64_t N, float* Y, hipStream_t s) {
     return fused_n(dev, lay_of(lay), Wq, rows, nb, X, N, Y, kNoMulti, s);
+}
+
+bool gemv_fuses_epi(int64_t nb) { return rows_apply(1, nb) ? rows_fuse_prologue(nb) : gemv_fuses(1, nb); }
+
+hipError_t launch_gemv_fused_epi(const DeviceInfo* dev, const uint8_t* Wq, int64_t rows, int64_t nb, const float* X,
+                                 float* Y, const Epilogue& epi, hipStream_t s) {
+    if (!gemv_fuses_epi(nb)) return hipErrorInvalidValue;
+    MultiDesc md = kNoMulti;
+    md.epi = epi;
+    return fused_n(dev, kLayAoS, Wq, rows, nb, X, 1, Y, md, s);
 }
 
 hipError_t launch_gemv(const DeviceInfo* dev, WLayout lay, const uint8_t* Wq, int64_t rows, int64_t nb,

@@ -27,12 +27,17 @@ constexpr int kMaxMulti = 8;
 // What a product kernel applies to each output before it stores it: the bias
 // add and activation after GPT-2's c_mlp_fc, or the element-wise factor of
 // SiLU(gate) * up: y = act(y + bias[r]) * mul[n][r], every part optional
-// (null pointers, kEpiNone).  Single-matrix launches only.
+// (null pointers, kEpiNone).  Single-matrix launches only.  ln_gamma set: the
+// decode kernels that quantize one fp32 token themselves first LayerNorm it
+// with ln_gamma, ln_beta, ln_eps (the host routes only those launches here).
 enum EpiAct { kEpiNone = 0, kEpiGelu = 1, kEpiSilu = 2 };
 struct Epilogue {
     const float* bias;
     const float* mul;
     int act;
+    const float* ln_gamma = nullptr;
+    const float* ln_beta = nullptr;
+    float ln_eps = 0.0f;
 };
 
 struct MultiDesc {
@@ -121,6 +126,13 @@ bool gemv_fuses(int64_t N, int64_t nb);
 bool gemv_prefers_fused(int64_t N, int64_t nb);
 hipError_t launch_gemv_fused(const DeviceInfo* dev, WLayout lay, const uint8_t* Wq, int64_t rows, int64_t nb,
                              const float* X, int64_t N, float* Y, hipStream_t s);
+// One token, the pages' blocks, with an epilogue and optionally LayerNorm:
+// the decode kernel normalizes (epi.ln_gamma set) and quantizes the fp32 token
+// in its prologue and applies the epilogue at its stores, in one launch, for
+// block counts where gemv_fuses_epi(nb).
+bool gemv_fuses_epi(int64_t nb);
+hipError_t launch_gemv_fused_epi(const DeviceInfo* dev, const uint8_t* Wq, int64_t rows, int64_t nb, const float* X,
+                                 float* Y, const Epilogue& epi, hipStream_t s);
 
 // The decode kernel over the rows of several matrices (N <= kGemvMaxN; AoS
 // blocks).  X fp32 is quantized in the kernel when gemv_fuses(N, nb), else
@@ -137,6 +149,15 @@ enum DecodeLayout { kLayAoS = 0, kLayRepacked = 1, kLayMulti = 2 };
 // rows_apply(N, nb): from fp32 X quantized in the kernel, or from the
 // quantizer's buffer.  `lay` is a DecodeLayout; Wq/Y unused for kLayMulti.
 bool rows_apply(int64_t N, int64_t nb);
+// Whether the row kernel's fused form (epilogue, LayerNorm of the one token in
+// its prologue) covers this block count: one pair per lane.
+bool rows_fuse_prologue(int64_t nb);
+// SiLU(LN(x) Wgate^T) * (LN(x) Wup^T) for one token in one launch (the row
+// kernel's gate-and-up form), where rows_dual_apply; ln: LayerNorm operands
+// (ln.ln_gamma null: none), its other fields unused.
+bool rows_dual_apply(const DeviceInfo* dev, int64_t rows, int64_t nb);
+hipError_t launch_rows_dual(const DeviceInfo* dev, const uint8_t* Wgate, const uint8_t* Wup, int64_t rows, int64_t nb,
+                            const float* X, float* H, const Epilogue& ln, hipStream_t s);
 hipError_t launch_rows_x(const DeviceInfo* dev, int lay, const uint8_t* Wq, int64_t rows, int64_t nb, const float* X,
                          int64_t N, float* Y, const MultiDesc& md, hipStream_t s);
 // D != nullptr: the block-dot export (Q4_0 blocks, one matrix) instead of Y.

@@ -84,20 +84,6 @@ k_q8_0_quantize(const float* __restrict__ X, int64_t nblocks, uint8_t* __restric
     }
 }
 
-// ---------------------------------------------------------------------------
-// LayerNorm before the product (the ggml GPT-2 walkthrough, section 3.1:
-// gamma * (x - mu) / sqrt(sigma^2 + eps) + beta over each token's K values).
-// The statistics are taken in fp64, one workgroup per token, and the
-// quantizers below evaluate the normalized value in fp64 and round it once to
-// fp32: the fp32 value that decides the Q8_0 codes then does not depend on the
-// summation order.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ float ln_value(float x, double mu, double rstd, float g, float b) {
-#pragma clang fp contract(off)
-    return static_cast<float>(static_cast<double>(g) * ((static_cast<double>(x) - mu) * rstd) +
-                              static_cast<double>(b));
-}
-
 // One workgroup per token: the statistics (fp64, two passes), then the token's
 // blocks normalized and quantized, into the decode layout (token-major blocks
 // g = n nb + b, PREFILL false) or the prefill records (o = b N + n).  Thread t
@@ -105,24 +91,11 @@ __device__ __forceinline__ float ln_value(float x, double mu, double rstd, float
 // round); T is a multiple of 8, so the 8 lanes of a block are neighbours, as
 // the quantizer wants.  QPT = 0: rows too long for registers, re-read per pass.
 
-__device__ __forceinline__ double block_sum_big(double v, double* red) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-    const int w = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) red[w] = v;
-    __syncthreads();
-    double t = 0.0;
-#pragma unroll
-    for (int i = 0; i < kLnActThreads / 64; ++i) t += red[i];
-    __syncthreads();
-    return t;
-}
-
 template <bool PREFILL, int QPT>
 __global__ void __launch_bounds__(kLnActThreads)
 k_ln_act(const float* __restrict__ X, int64_t N, int64_t nb, const float* __restrict__ gamma,
          const float* __restrict__ beta, float eps, uint32_t* __restrict__ act_q, ActScale* __restrict__ act_s) {
-    __shared__ double red[kLnActThreads / 64];
+    __shared__ double red[2][kLnActThreads / 64];
     const int64_t n = blockIdx.x;
     const int64_t nq = nb * 8;  // quads of the token
     const float* x = X + n * nb * kQK;
@@ -148,7 +121,7 @@ k_ln_act(const float* __restrict__ X, int64_t N, int64_t nb, const float* __rest
         }
     }
     const double K = static_cast<double>(nb * kQK);
-    const double mu = block_sum_big(s, red) / K;
+    const double mu = wg_sum_f64<kLnActThreads>(s, red[0]) / K;
     auto sq = [&](const float4& v) __attribute__((always_inline)) {
         const double a = static_cast<double>(v.x) - mu, b = static_cast<double>(v.y) - mu;
         const double c = static_cast<double>(v.z) - mu, d = static_cast<double>(v.w) - mu;
@@ -166,7 +139,7 @@ k_ln_act(const float* __restrict__ X, int64_t N, int64_t nb, const float* __rest
             v2 += sq(v);
         }
     }
-    const double rstd = 1.0 / sqrt(block_sum_big(v2, red) / K + static_cast<double>(eps));
+    const double rstd = 1.0 / sqrt(wg_sum_f64<kLnActThreads>(v2, red[1]) / K + static_cast<double>(eps));
     const int m = threadIdx.x & 7;
     auto emit = [&](float4 v, int64_t q) __attribute__((always_inline)) {
         const int64_t k = 4 * q;

@@ -53,6 +53,11 @@ namespace {
 // row belong to C neighbouring waves of one workgroup: each wave keeps its
 // per-round partial sums in registers, and at the end the workgroup adds a
 // row's C partials in chunk order through LDS and stores Y.
+//
+// Gate and up of a feed-forward (DUAL, C = 2): the two chunk rows of row r are
+// row r of the gate matrix (md.w[0]) and row r of the up matrix (md.w[1]),
+// each whole; the workgroup stores SiLU(gate) * up.  One launch reads both
+// matrices, quantizing (and normalizing) the token once per workgroup.
 // ---------------------------------------------------------------------------
 constexpr int kRowsMaxPPL = 4;
 constexpr size_t kRowsMaxLds = 128 * 1024;  // quantized activations in LDS (one workgroup per CU)
@@ -145,7 +150,8 @@ __device__ __forceinline__ int64_t uniform64(int64_t v) {
 // DOTS: instead of Y, every per-block integer dot goes to
 // Dots[(n * rows + r) * nb + b] (the test export; one matrix of Q4_0 blocks,
 // activations from the quantizer's buffer).
-template <int THREADS, int NT, int PPL, int D, int SRC, int LAY, bool EPI, bool DOTS = false, int C = 1>
+template <int THREADS, int NT, int PPL, int D, int SRC, int LAY, bool EPI, bool DOTS = false, int C = 1,
+          bool DUAL = false>
 __global__ void __launch_bounds__(THREADS)
 k_gemv_rows(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __restrict__ src,
             float* __restrict__ Y, int32_t* __restrict__ Dots, const MultiDesc md) {
@@ -157,6 +163,12 @@ k_gemv_rows(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __
     constexpr bool kUseLds = SRC == kXF32 || !kActReg;
     constexpr int kWaves = THREADS / 64;
     static_assert(C == 1 || (PPL == 1 && !MULTI && !DOTS && kWaves % C == 0), "chunked form");
+    static_assert(!DUAL || (C == 2 && EPI && SRC == kXF32 && NT == 1 && LAY == kLayAoS), "gate and up form");
+    // LayerNorm of the one token in the prologue (md.epi.ln_gamma set): the
+    // fused instantiation with one pair per lane, where each thread holds its
+    // quads of X in registers
+    constexpr bool kLn = EPI && SRC == kXF32 && NT == 1 && PPL == 1 && (C == 1 || DUAL);
+    constexpr int kCK = DUAL ? 1 : C;  // K-chunks per row
     extern __shared__ __align__(16) uint8_t smem[];
     uint32_t* sq = reinterpret_cast<uint32_t*>(smem);
     ActScale* ss = reinterpret_cast<ActScale*>(smem + static_cast<size_t>(NT) * nb * kActQBytes);
@@ -164,24 +176,40 @@ k_gemv_rows(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar row arithmetic
     const int P = nb >> 1;
-    const int Pc = P / C;                         // pairs per chunk (C divides P)
-    const int pbase = C > 1 ? (wave % C) * Pc : 0;  // this wave's chunk, as a pair offset in the row
+    const int Pc = P / kCK;                          // pairs per chunk (kCK divides P)
+    const int pbase = kCK > 1 ? (wave % C) * Pc : 0;  // this wave's chunk, as a pair offset in the row
     const int nblk = NT * nb;  // activation blocks, token-major
 
     // 1. activation loads (before any weight load)
     //    kXF32: thread t quantizes quad (t & 7) of blocks t / 8 + (THREADS / 8) j
     //    kActGlobal into LDS: thread t copies 16-byte piece t + THREADS j of
     //    the int8 blocks and scale record t + THREADS j
-    constexpr int kJ = (1024 * NT * PPL * C + THREADS - 1) / THREADS;  // nb <= 128 * PPL * C
-    constexpr int kJpreMax = PPL * C == 1 ? 8 : 4;
+    constexpr int kJ = (1024 * NT * PPL * kCK + THREADS - 1) / THREADS;  // nb <= 128 * PPL * kCK
+    constexpr int kJpreMax = PPL * kCK == 1 ? 8 : 4;
     constexpr int kJpre = kJ < kJpreMax ? kJ : kJpreMax;
     float4 xv[SRC == kXF32 ? kJpre : 1];
+    static_assert(!kLn || kJ == kJpre, "LayerNorm needs every quad of X in registers");
+    float4 gv[kLn ? kJpre : 1], bv[kLn ? kJpre : 1];
+    const bool do_ln = kLn && md.epi.ln_gamma != nullptr;
     if constexpr (SRC == kXF32) {
         const float* X = static_cast<const float*>(src);
 #pragma unroll
         for (int j = 0; j < kJpre; ++j) {
             const int g = min(static_cast<int>(threadIdx.x >> 3) + (THREADS / 8) * j, nblk - 1);
             __builtin_memcpy(&xv[j], X + static_cast<int64_t>(g) * kQK + 4 * (threadIdx.x & 7), 16);
+        }
+        if constexpr (kLn) {
+            // unconditional (X itself stands in without LayerNorm): a branch
+            // here made the compiler wait for these loads before the weights'
+            const float* gp = do_ln ? md.epi.ln_gamma : X;
+            const float* bp = do_ln ? md.epi.ln_beta : X;
+#pragma unroll
+            for (int j = 0; j < kJpre; ++j) {
+                const int g = min(static_cast<int>(threadIdx.x >> 3) + (THREADS / 8) * j, nblk - 1);
+                const int64_t k = static_cast<int64_t>(g) * kQK + 4 * (threadIdx.x & 7);
+                __builtin_memcpy(&gv[j], gp + k, 16);
+                __builtin_memcpy(&bv[j], bp + k, 16);
+            }
         }
     }
     uint32_t areg[kActReg ? NT : 1][2][8];
@@ -248,7 +276,8 @@ k_gemv_rows(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __
             a.ystride = f1 - f;
         } else {
             const int64_t rb = uniform64(static_cast<int64_t>(static_cast<uint64_t>(r) / C) * nb);
-            a.w = Wq + rb * (RP ? 16 : kQ4Bytes);
+            const uint8_t* wb = DUAL && (static_cast<uint64_t>(r) & 1) ? md.w[1] : Wq;
+            a.w = wb + rb * (RP ? 16 : kQ4Bytes);
             a.sc = Wsc + rb * 2;
             a.y = Y + static_cast<int64_t>(static_cast<uint64_t>(r) / C);
             a.ystride = rows;
@@ -286,6 +315,29 @@ k_gemv_rows(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __
                     if (m == 0) ss[g] = sc;
                 }
             };
+            if constexpr (kLn) {
+                if (do_ln) {
+                    // fp64 mean and population variance of the token over the
+                    // workgroup, then the normalized values (fp64, rounded
+                    // once to fp32)
+                    __shared__ double red[2][THREADS / 64];
+                    double s1 = 0.0;
+#pragma unroll
+                    for (int j = 0; j < kJpre; ++j)
+                        if (static_cast<int>(threadIdx.x >> 3) + (THREADS / 8) * j < nblk) s1 += quad_sum_f64(xv[j]);
+                    const double kk = static_cast<double>(nb) * kQK;
+                    const double mu = wg_sum_f64<THREADS>(s1, red[0]) / kk;
+                    double s2 = 0.0;
+#pragma unroll
+                    for (int j = 0; j < kJpre; ++j)
+                        if (static_cast<int>(threadIdx.x >> 3) + (THREADS / 8) * j < nblk)
+                            s2 += quad_sqdev_f64(xv[j], mu);
+                    const double rstd =
+                        1.0 / sqrt(wg_sum_f64<THREADS>(s2, red[1]) / kk + static_cast<double>(md.epi.ln_eps));
+#pragma unroll
+                    for (int j = 0; j < kJpre; ++j) xv[j] = ln_quad(xv[j], mu, rstd, gv[j], bv[j]);
+                }
+            }
 #pragma unroll
             for (int j = 0; j < kJpre; ++j) quantize(xv[j], j);
             // the rest of a long X (loaded after the weights: these wait for them)
@@ -422,6 +474,22 @@ k_gemv_rows(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
+        // this workgroup's outputs: round k, row q of the round (kWaves / C
+        // rows, from waves C q .. C q + C - 1), token n; at most one per thread
+        constexpr int kRowsPerRound = kWaves / C;
+        constexpr int kOuts = kSplitRounds * kRowsPerRound * NT;
+        static_assert(kOuts <= THREADS, "one output per thread");
+        const int on = threadIdx.x % NT, oq = (threadIdx.x / NT) % kRowsPerRound, ok = threadIdx.x / (NT * kRowsPerRound);
+        const int64_t ov = static_cast<int64_t>(blockIdx.x) * kWaves + ok * S + oq * C;
+        const bool has_out = threadIdx.x < kOuts && ov < V;
+        const int64_t orow = has_out ? ov / C : 0;
+        float eb = 0.0f, em = 1.0f;
+        if constexpr (EPI && !DUAL) {
+            if (has_out) {
+                eb = epi_bias(md.epi, orow);
+                em = epi_mul(md.epi, on, orow, rows);
+            }
+        }
         // every wave is past its last LDS activation read: the partials take
         // LDS, slot (k * kWaves + wave) * NT + token
         float* pl = reinterpret_cast<float*>(smem);
@@ -435,23 +503,35 @@ k_gemv_rows(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        // this workgroup's outputs: round k, row q of the round (kWaves / C
-        // rows, from waves C q .. C q + C - 1), token n
-        constexpr int kRowsPerRound = kWaves / C;
-        for (int t = threadIdx.x; t < kSplitRounds * kRowsPerRound * NT; t += THREADS) {
-            const int n = t % NT, q = (t / NT) % kRowsPerRound, k = t / (NT * kRowsPerRound);
-            const int64_t v = static_cast<int64_t>(blockIdx.x) * kWaves + k * S + q * C;
-            if (v < V) {
-                const float* src_p = pl + (k * kWaves + q * C) * NT + n;
-                float y = src_p[0];
+        if (has_out) {
+            const float* src_p = pl + (ok * kWaves + oq * C) * NT + on;
+            float y = src_p[0];
+            if constexpr (DUAL) {
+                // SiLU(gate), then times up: the two fused stores' arithmetic
+                y = y / (1.0f + expf(-y));
+                y *= src_p[NT];
+            } else {
 #pragma unroll
                 for (int c = 1; c < C; ++c) y += src_p[c * NT];
-                const int64_t r = v / C;
-                Y[static_cast<int64_t>(n) * rows + r] = EPI ? apply_epilogue(y, n, r, rows, md.epi) : y;
+                if constexpr (EPI) y = epilogue_with(y, eb, em, md.epi);
             }
+            Y[static_cast<int64_t>(on) * rows + orow] = y;
         }
         return;
     }
+    // fused forms: each row's epilogue operands (bias, factor of this lane's
+    // token) are loaded with the row's weights, not at its store
+    float eb[EPI ? D : 1], em[EPI ? D : 1];
+    const int etok = my_token >= 0 && my_token < NT ? my_token : 0;
+    auto load_epi = [&](int d, int64_t k) __attribute__((always_inline)) {
+        if constexpr (EPI) {
+            const int64_t r = min(w0 + k * S, rlast);
+            eb[d] = epi_bias(md.epi, r);
+            em[d] = epi_mul(md.epi, etok, r, rows);
+        }
+    };
+#pragma unroll
+    for (int d = 0; d < D; ++d) load_epi(d, d);
     for (int64_t k = 0; k < nk; k += D) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
@@ -461,10 +541,10 @@ k_gemv_rows(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __
             if (k + d < nk && my_token >= 0 && my_token < NT) {
                 const int64_t r = w0 + (k + d) * S;
                 const RowAt a = row_at(r);
-                a.y[static_cast<int64_t>(my_token) * a.ystride] =
-                    EPI ? apply_epilogue(t, my_token, r, rows, md.epi) : t;
+                a.y[static_cast<int64_t>(my_token) * a.ystride] = EPI ? epilogue_with(t, eb[d], em[d], md.epi) : t;
             }
             load_row(raw[d], k + d + D);
+            load_epi(d, k + d + D);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -509,12 +589,12 @@ constexpr int rows_threads() { return NT > (PPL == 1 ? 4 : PPL == 2 ? 6 : 4) ? 5
 template <int NT, int PPL>
 constexpr int rows_depth() { return PPL == 1 && NT > 4 ? 2 : 1; }
 
-template <int SRC, int LAY, bool EPI, bool DOTS, int NT, int PPL, int C = 1>
+template <int SRC, int LAY, bool EPI, bool DOTS, int NT, int PPL, int C = 1, bool DUAL = false>
 hipError_t launch_rows_k(const DeviceInfo* dev, const uint8_t* Wq, int64_t rows, int64_t nb, const void* src,
                          float* Y, int32_t* dots, const MultiDesc& md, hipStream_t s) {
     constexpr int kThreads = rows_threads<NT, PPL>();
     constexpr int kDepth = rows_depth<NT, PPL>();
-    const auto kernel = k_gemv_rows<kThreads, NT, PPL, kDepth, SRC, LAY, EPI, DOTS, C>;
+    const auto kernel = k_gemv_rows<kThreads, NT, PPL, kDepth, SRC, LAY, EPI, DOTS, C, DUAL>;
     int64_t wgs = (rows * C + kThreads / 64 - 1) / (kThreads / 64);
     const int64_t cap = static_cast<int64_t>(dev->num_cu) * (1024 / kThreads);
     if (wgs > cap) wgs = cap;
