@@ -360,10 +360,35 @@ __device__ __forceinline__ float ln_value(float x, double mu, double rstd, float
 // workgroup barrier) and gets the total, added in wave order.  A later call
 // must use other LDS (or come after another barrier): slow waves may still be
 // reading red.
+// One DPP move of an fp64 value (both 32-bit halves); lanes outside kRowMask
+// read 0.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ double dpp_f64(double v) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(u), kCtrl, kRowMask, 0xF, false));
+    const uint32_t hi = static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(u >> 32), kCtrl, kRowMask, 0xF, false));
+    return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// Sum over the 64 lanes of a wave, returned in every lane: DPP adds inside
+// rows of 16 lanes, two row broadcasts into lane 63, then lane 63's value.
+__device__ __forceinline__ double wave_total_f64(double v) {
+    v += dpp_f64<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+    v += dpp_f64<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+    v += dpp_f64<0x141, 0xF>(v);  // row_half_mirror
+    v += dpp_f64<0x140, 0xF>(v);  // row_mirror: each row of 16 holds its sum
+    v += dpp_f64<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+    v += dpp_f64<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(u), 63);
+    const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(u >> 32), 63);
+    return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 template <int THREADS>
 __device__ __forceinline__ double wg_sum_f64(double v, double* red) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    v = wave_total_f64(v);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
     __syncthreads();
     double t = 0.0;
