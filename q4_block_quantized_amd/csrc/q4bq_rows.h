@@ -594,17 +594,24 @@ hipError_t launch_rows_k(const DeviceInfo* dev, const uint8_t* Wq, int64_t rows,
                          float* Y, int32_t* dots, const MultiDesc& md, hipStream_t s) {
     constexpr int kThreads = rows_threads<NT, PPL>();
     constexpr int kDepth = rows_depth<NT, PPL>();
-    const auto kernel = k_gemv_rows<kThreads, NT, PPL, kDepth, SRC, LAY, EPI, DOTS, C, DUAL>;
     int64_t wgs = (rows * C + kThreads / 64 - 1) / (kThreads / 64);
     const int64_t cap = static_cast<int64_t>(dev->num_cu) * (1024 / kThreads);
     if (wgs > cap) wgs = cap;
+    // many tokens with one pair per lane (two waves per SIMD): four rows in
+    // flight per wave where every wave has at least 16 rows (the vocabulary
+    // head at N = 8: 88 -> 83 us); shorter matrices keep two, since a wave
+    // re-reads its last row for each extra slot
+    constexpr bool kDeep = kDepth == 2 && C == 1 && !DOTS;
+    const bool deep = kDeep && rows >= 16 * wgs * (kThreads / 64);
+    const auto kernel = deep ? k_gemv_rows<kThreads, NT, PPL, kDeep ? 4 : kDepth, SRC, LAY, EPI, DOTS, C, DUAL>
+                             : k_gemv_rows<kThreads, NT, PPL, kDepth, SRC, LAY, EPI, DOTS, C, DUAL>;
     size_t lds = (SRC == kXF32 || PPL > 1) ? static_cast<size_t>(NT) * nb * (kActQBytes + kActSBytes) : 0;
     if (C > 1) lds = std::max(lds, static_cast<size_t>(kSplitRounds) * (kThreads / 64) * NT * sizeof(float));
     if (lds > 64 * 1024) {
         // beyond the default dynamic LDS limit: raise it once for this kernel
-        static const hipError_t raised = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                             static_cast<int>(kRowsMaxLds));
+        const hipError_t raised = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                                      hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                      static_cast<int>(kRowsMaxLds));
         if (raised != hipSuccess) return raised;
     }
     hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(wgs)), dim3(kThreads), lds, s, Wq, rows,
