@@ -49,7 +49,7 @@ int run_product(WLayout lay, const uint8_t* Wq, int64_t rows, int64_t K, const f
     const int64_t nb = K / kQK;
     // without a workspace the fused kernel runs whenever it fits (run_with_scratch
     // passes none in exactly that case)
-    if (X && !D && (ws ? gemv_prefers_fused(N, nb) : gemv_fuses(N, nb)))
+    if (X && !D && (ws ? gemv_prefers_fused(N, nb, rows) : gemv_fuses(N, nb, rows)))
         return status_of(launch_gemv_fused(dev, lay, Wq, rows, nb, X, N, Y, s));
     err = X ? launch_act_from_f32(X, N, nb, ws, s) : launch_act_from_q8(Xq, N, nb, ws, s);
     if (err != hipSuccess) return Q4BQ_EHIP;
@@ -65,7 +65,7 @@ int run_with_scratch(WLayout lay, const uint8_t* Wq, int64_t rows, int64_t K, co
                      int64_t N, float* Y, int32_t* D, hipStream_t s) {
     hipError_t err = hipSuccess;
     if (!current_device(&err)) return Q4BQ_EHIP;
-    if (X && !D && gemv_fuses(N, K / kQK)) return run_product(lay, Wq, rows, K, X, Xq, N, Y, D, nullptr, s);
+    if (X && !D && gemv_fuses(N, K / kQK, rows)) return run_product(lay, Wq, rows, K, X, Xq, N, Y, D, nullptr, s);
     const size_t bytes = q4bq_workspace_size(rows, K, N);
     void* ws = nullptr;
     if (hipMallocAsync(&ws, bytes, s) != hipSuccess || ws == nullptr) {
@@ -280,7 +280,8 @@ int mul_mat_q4_0_q8_0_multi(int count, const void* const* Wq, const int64_t* row
     const DeviceInfo* dev = current_device(&err);
     if (!dev) return Q4BQ_EHIP;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    if (N <= kGemvMaxN && (workspace ? gemv_prefers_fused(N, nb) : gemv_fuses(N, nb)))
+    const int64_t total = md.first[count];
+    if (N <= kGemvMaxN && (workspace ? gemv_prefers_fused(N, nb, total) : gemv_fuses(N, nb, total)))
         return status_of(launch_gemv_multi(dev, md, nb, X, nullptr, N, s));
     void* ws = workspace;
     if (!ws && (hipMallocAsync(&ws, need, s) != hipSuccess || ws == nullptr)) {
@@ -363,7 +364,7 @@ int run_fused(int count, const uint8_t* const* Wq, int64_t rows, int64_t K, cons
     const DeviceInfo* dev = current_device(&err);
     if (!dev) return Q4BQ_EHIP;
     const int64_t nb = K / kQK;
-    if (N == 1 && gemv_fuses_epi(nb)) {
+    if (N == 1 && gemv_fuses_epi(nb, rows)) {
         // one launch per matrix: the decode kernel normalizes and quantizes
         // the token in its prologue (no scratch)
         for (int i = 0; i < count && err == hipSuccess; ++i) {

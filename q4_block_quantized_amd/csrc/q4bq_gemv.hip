@@ -422,7 +422,7 @@ int lay_of(WLayout lay) { return lay == kRepacked ? kLayRepacked : kLayAoS; }
 // instead, spread over more CUs.
 hipError_t fused_n(const DeviceInfo* dev, int lay, const uint8_t* Wq, int64_t rows, int64_t nb, const float* X,
                    int64_t N, float* Y, const MultiDesc& md, hipStream_t s) {
-    if (rows_apply(N, nb)) return launch_rows_x(dev, lay, Wq, rows, nb, X, N, Y, md, s);
+    if (rows_apply(N, nb, rows)) return launch_rows_x(dev, lay, Wq, rows, nb, X, N, Y, md, s);
     if (N != 1) return hipErrorInvalidValue;
     const Shape big = pick_shape(dev, rows, nb, 1024, 1, 1);
     if (big.ntasks >= static_cast<int64_t>(dev->num_cu) * 16)
@@ -433,7 +433,7 @@ hipError_t fused_n(const DeviceInfo* dev, int lay, const uint8_t* Wq, int64_t ro
 
 hipError_t gemv_n(const DeviceInfo* dev, int lay, const uint8_t* Wq, int64_t rows, int64_t nb, const void* act,
                   int64_t N, float* Y, int32_t* D, const MultiDesc& md, hipStream_t s) {
-    if (rows_apply(N, nb)) return launch_rows_act(dev, lay, Wq, rows, nb, act, N, Y, md, s, D);
+    if (rows_apply(N, nb, rows)) return launch_rows_act(dev, lay, Wq, rows, nb, act, N, Y, md, s, D);
     switch (N) {
         case 1: return launch_n<1>(dev, lay, Wq, rows, nb, act, Y, D, md, s);
         case 2: return launch_n<2>(dev, lay, Wq, rows, nb, act, Y, D, md, s);
@@ -451,8 +451,8 @@ const MultiDesc kNoMulti{};
 
 }  // namespace
 
-bool gemv_fuses(int64_t N, int64_t nb) {
-    return rows_apply(N, nb) ||
+bool gemv_fuses(int64_t N, int64_t nb, int64_t rows) {
+    return rows_apply(N, nb, rows) ||
            (N <= kGemvFusedMaxN && static_cast<size_t>(N) * nb * (kActQBytes + kActSBytes) <= kMaxActLds);
 }
 
@@ -464,8 +464,8 @@ bool gemv_fuses(int64_t N, int64_t nb) {
 // kernel is faster).
 constexpr int64_t kFusedMaxValues = 16384;
 
-bool gemv_prefers_fused(int64_t N, int64_t nb) {
-    return gemv_fuses(N, nb) && (N == 1 || N * nb * kQK <= kFusedMaxValues);
+bool gemv_prefers_fused(int64_t N, int64_t nb, int64_t rows) {
+    return gemv_fuses(N, nb, rows) && (N == 1 || N * nb * kQK <= kFusedMaxValues);
 }
 
 hipError_t launch_gemv_fused(const DeviceInfo* dev, WLayout lay, const uint8_t* Wq, int64_t rows, int64_t nb,
@@ -473,11 +473,13 @@ hipError_t launch_gemv_fused(const DeviceInfo* dev, WLayout lay, const uint8_t* 
     return fused_n(dev, lay_of(lay), Wq, rows, nb, X, N, Y, kNoMulti, s);
 }
 
-bool gemv_fuses_epi(int64_t nb) { return rows_apply(1, nb) ? rows_fuse_prologue(nb) : gemv_fuses(1, nb); }
+bool gemv_fuses_epi(int64_t nb, int64_t rows) {
+    return rows_apply(1, nb, rows) ? rows_fuse_prologue(nb, rows) : gemv_fuses(1, nb, rows);
+}
 
 hipError_t launch_gemv_fused_epi(const DeviceInfo* dev, const uint8_t* Wq, int64_t rows, int64_t nb, const float* X,
                                  float* Y, const Epilogue& epi, hipStream_t s) {
-    if (!gemv_fuses_epi(nb)) return hipErrorInvalidValue;
+    if (!gemv_fuses_epi(nb, rows)) return hipErrorInvalidValue;
     MultiDesc md = kNoMulti;
     md.epi = epi;
     return fused_n(dev, kLayAoS, Wq, rows, nb, X, 1, Y, md, s);
@@ -493,7 +495,7 @@ hipError_t launch_gemv(const DeviceInfo* dev, WLayout lay, const uint8_t* Wq, in
 hipError_t launch_gemv_multi(const DeviceInfo* dev, const MultiDesc& md, int64_t nb, const float* X, const void* act,
                              int64_t N, hipStream_t s) {
     const int64_t rows = md.first[md.count];
-    if (X && gemv_fuses(N, nb)) return fused_n(dev, kLayMulti, nullptr, rows, nb, X, N, nullptr, md, s);
+    if (X && gemv_fuses(N, nb, rows)) return fused_n(dev, kLayMulti, nullptr, rows, nb, X, N, nullptr, md, s);
     return gemv_n(dev, kLayMulti, nullptr, rows, nb, act, N, nullptr, nullptr, md, s);
 }
 

@@ -120,17 +120,17 @@ hipError_t launch_gemv(const DeviceInfo* dev, WLayout lay, const uint8_t* Wq, in
 // N <= kGemvFusedMaxN when the quantized activations fit in LDS.  Same bits
 // as launch_act_from_f32 followed by launch_gemv.
 constexpr int64_t kGemvFusedMaxN = 1;
-bool gemv_fuses(int64_t N, int64_t nb);
+bool gemv_fuses(int64_t N, int64_t nb, int64_t rows);
 // Whether the fused kernel is also the faster choice when the caller has a
 // workspace for a separate quantizer launch.
-bool gemv_prefers_fused(int64_t N, int64_t nb);
+bool gemv_prefers_fused(int64_t N, int64_t nb, int64_t rows);
 hipError_t launch_gemv_fused(const DeviceInfo* dev, WLayout lay, const uint8_t* Wq, int64_t rows, int64_t nb,
                              const float* X, int64_t N, float* Y, hipStream_t s);
 // One token, the pages' blocks, with an epilogue and optionally LayerNorm:
 // the decode kernel normalizes (epi.ln_gamma set) and quantizes the fp32 token
 // in its prologue and applies the epilogue at its stores, in one launch, for
-// block counts where gemv_fuses_epi(nb).
-bool gemv_fuses_epi(int64_t nb);
+// shapes where gemv_fuses_epi(nb, rows).
+bool gemv_fuses_epi(int64_t nb, int64_t rows);
 hipError_t launch_gemv_fused_epi(const DeviceInfo* dev, const uint8_t* Wq, int64_t rows, int64_t nb, const float* X,
                                  float* Y, const Epilogue& epi, hipStream_t s);
 
@@ -148,10 +148,10 @@ enum DecodeLayout { kLayAoS = 0, kLayRepacked = 1, kLayMulti = 2 };
 // Row-streaming decode (whole waves per row), for N tokens when
 // rows_apply(N, nb): from fp32 X quantized in the kernel, or from the
 // quantizer's buffer.  `lay` is a DecodeLayout; Wq/Y unused for kLayMulti.
-bool rows_apply(int64_t N, int64_t nb);
+bool rows_apply(int64_t N, int64_t nb, int64_t rows);
 // Whether the row kernel's fused form (epilogue, LayerNorm of the one token in
 // its prologue) covers this block count: one pair per lane.
-bool rows_fuse_prologue(int64_t nb);
+bool rows_fuse_prologue(int64_t nb, int64_t rows);
 // SiLU(LN(x) Wgate^T) * (LN(x) Wup^T) for one token in one launch (the row
 // kernel's gate-and-up form), where rows_dual_apply; ln: LayerNorm operands
 // (ln.ln_gamma null: none), its other fields unused.

@@ -3,15 +3,15 @@
 
 namespace q4bq {
 
-bool rows_apply(int64_t N, int64_t nb) {
-    return rows_ppl(nb) > 0 && N >= 1 && N <= 8 &&
+bool rows_apply(int64_t N, int64_t nb, int64_t rows) {
+    return rows_ppl(nb, rows) > 0 && N >= 1 && N <= 8 &&
            static_cast<size_t>(N) * nb * (kActQBytes + kActSBytes) <= kRowsMaxLds;
 }
 
-bool rows_fuse_prologue(int64_t nb) { return rows_ppl(nb) == 1; }
+bool rows_fuse_prologue(int64_t nb, int64_t rows) { return rows_ppl(nb, rows) == 1; }
 
 bool rows_dual_apply(const DeviceInfo* dev, int64_t rows, int64_t nb) {
-    if (!rows_fuse_prologue(nb)) return false;
+    if (!rows_fuse_prologue(nb, rows)) return false;
     constexpr int kWaves = rows_threads<1, 1>() / 64;
     int64_t wgs = (2 * rows + kWaves - 1) / kWaves;
     if (wgs > dev->num_cu) wgs = dev->num_cu;
@@ -33,7 +33,7 @@ hipError_t launch_rows_x(const DeviceInfo* dev, int lay, const uint8_t* Wq, int6
     const Epilogue& e = md.epi;
     if (e.bias || e.mul || e.act != kEpiNone || e.ln_gamma) {
         // the fused forms: one token, the pages' blocks, one pair per lane
-        if (lay != kLayAoS || N != 1 || !rows_fuse_prologue(nb)) return hipErrorInvalidValue;
+        if (lay != kLayAoS || N != 1 || !rows_fuse_prologue(nb, rows)) return hipErrorInvalidValue;
         return launch_rows_nt<kXF32, kLayAoS, true, false, 1>(dev, Wq, rows, nb, src, Y, nullptr, md, s);
     }
     switch (lay) {

@@ -282,14 +282,34 @@ def test_long_rows_few_tokens(hip, orc, K):
     """One to eight tokens on long rows, where whole waves stream each row: the
     oracle bar on ragged row counts, and the same bits from fused quantization,
     the pre-quantized input and the repacked weights.  K = 3008 (47 pairs per
-    row), K = 16416 (an odd block count) and the larger token counts on the
-    longest rows sit outside that kernel's range and check the other one."""
+    row) takes that kernel's short-row form; K = 16416 (an odd block count) and
+    the larger token counts on the longest rows sit outside its range and check
+    the other one."""
     for rows in (1, 17, 300):
         for N in (1, 2, 3, 4, 8):
             if rows * K * N > 12_000_000:
                 continue
             print("long rows rows=%d K=%d N=%d" % (rows, K, N), flush=True)
             W, X = _case(rows, K, N, 900 + rows + K + 7 * N)
+            Wq_o, Xq_o = orc.q4_0_quantize(W), orc.q8_0_quantize(X)
+            Wq = hip.q4_0_quantize(dev(W))
+            Xt = dev(X)
+            Y = host(hip.mul_mat_q4_0_q8_0(Wq, Xt))
+            assert_close(Y, orc.mul_mat_ref(Wq_o, Xq_o, K), "rows=%d K=%d N=%d" % (rows, K, N))
+            assert np.array_equal(host(hip.mul_mat_q4_0_q8_0_pq(Wq, hip.q8_0_quantize(Xt), K)), Y), (rows, K, N)
+            assert np.array_equal(host(hip.mul_mat_q4_0r_q8_0(hip.q4_0_repack(Wq, K), Xt)), Y), (rows, K, N)
+
+
+@pytest.mark.parametrize("K", [448, 512, 768, 3008])
+def test_short_rows_either_side_of_row_limit(hip, orc, K):
+    """Rows of 7 to 47 block pairs: whole waves stream each row (most lanes
+    idle) on matrices of up to 16384 rows, the task kernel above that and
+    below 8 pairs.  Both sides of the row limit against the oracle, and the
+    same bits from the pre-quantized input and the repacked weights."""
+    for rows in (16384, 16385):
+        for N in (1, 3):
+            print("short rows rows=%d K=%d N=%d" % (rows, K, N), flush=True)
+            W, X = _case(rows, K, N, 4100 + rows + K + N)
             Wq_o, Xq_o = orc.q4_0_quantize(W), orc.q8_0_quantize(X)
             Wq = hip.q4_0_quantize(dev(W))
             Xt = dev(X)
