@@ -281,7 +281,7 @@ int mul_mat_q4_0_q8_0_multi(int count, const void* const* Wq, const int64_t* row
     if (!dev) return Q4BQ_EHIP;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t total = md.first[count];
-    if (N <= kGemvMaxN && (workspace ? gemv_prefers_fused(N, nb, total) : gemv_fuses(N, nb, total)))
+    if (N <= kGemvMaxN && (workspace ? gemv_prefers_fused(N, nb, total, &md) : gemv_fuses(N, nb, total, &md)))
         return status_of(launch_gemv_multi(dev, md, nb, X, nullptr, N, s));
     void* ws = workspace;
     if (!ws && (hipMallocAsync(&ws, need, s) != hipSuccess || ws == nullptr)) {

@@ -422,6 +422,8 @@ int lay_of(WLayout lay) { return lay == kRepacked ? kLayRepacked : kLayAoS; }
 // instead, spread over more CUs.
 hipError_t fused_n(const DeviceInfo* dev, int lay, const uint8_t* Wq, int64_t rows, int64_t nb, const float* X,
                    int64_t N, float* Y, const MultiDesc& md, hipStream_t s) {
+    const MultiDesc* mdp = lay == kLayMulti ? &md : nullptr;
+    if (mma_apply(N, nb, rows, mdp)) return launch_gemv_mma(dev, lay, Wq, rows, nb, X, true, N, Y, md, s);
     if (rows_apply(N, nb, rows)) return launch_rows_x(dev, lay, Wq, rows, nb, X, N, Y, md, s);
     if (N != 1) return hipErrorInvalidValue;
     const Shape big = pick_shape(dev, rows, nb, 1024, 1, 1);
@@ -433,6 +435,8 @@ hipError_t fused_n(const DeviceInfo* dev, int lay, const uint8_t* Wq, int64_t ro
 
 hipError_t gemv_n(const DeviceInfo* dev, int lay, const uint8_t* Wq, int64_t rows, int64_t nb, const void* act,
                   int64_t N, float* Y, int32_t* D, const MultiDesc& md, hipStream_t s) {
+    if (!D && mma_apply(N, nb, rows, lay == kLayMulti ? &md : nullptr))
+        return launch_gemv_mma(dev, lay, Wq, rows, nb, act, false, N, Y, md, s);
     if (rows_apply(N, nb, rows)) return launch_rows_act(dev, lay, Wq, rows, nb, act, N, Y, md, s, D);
     switch (N) {
         case 1: return launch_n<1>(dev, lay, Wq, rows, nb, act, Y, D, md, s);
@@ -451,8 +455,8 @@ const MultiDesc kNoMulti{};
 
 }  // namespace
 
-bool gemv_fuses(int64_t N, int64_t nb, int64_t rows) {
-    return rows_apply(N, nb, rows) ||
+bool gemv_fuses(int64_t N, int64_t nb, int64_t rows, const MultiDesc* md) {
+    return mma_apply(N, nb, rows, md) || rows_apply(N, nb, rows) ||
            (N <= kGemvFusedMaxN && static_cast<size_t>(N) * nb * (kActQBytes + kActSBytes) <= kMaxActLds);
 }
 
@@ -464,8 +468,8 @@ bool gemv_fuses(int64_t N, int64_t nb, int64_t rows) {
 // kernel is faster).
 constexpr int64_t kFusedMaxValues = 16384;
 
-bool gemv_prefers_fused(int64_t N, int64_t nb, int64_t rows) {
-    return gemv_fuses(N, nb, rows) && (N == 1 || N * nb * kQK <= kFusedMaxValues);
+bool gemv_prefers_fused(int64_t N, int64_t nb, int64_t rows, const MultiDesc* md) {
+    return gemv_fuses(N, nb, rows, md) && (N == 1 || N * nb * kQK <= kFusedMaxValues);
 }
 
 hipError_t launch_gemv_fused(const DeviceInfo* dev, WLayout lay, const uint8_t* Wq, int64_t rows, int64_t nb,
@@ -495,7 +499,7 @@ hipError_t launch_gemv(const DeviceInfo* dev, WLayout lay, const uint8_t* Wq, in
 hipError_t launch_gemv_multi(const DeviceInfo* dev, const MultiDesc& md, int64_t nb, const float* X, const void* act,
                              int64_t N, hipStream_t s) {
     const int64_t rows = md.first[md.count];
-    if (X && gemv_fuses(N, nb, rows)) return fused_n(dev, kLayMulti, nullptr, rows, nb, X, N, nullptr, md, s);
+    if (X && gemv_fuses(N, nb, rows, &md)) return fused_n(dev, kLayMulti, nullptr, rows, nb, X, N, nullptr, md, s);
     return gemv_n(dev, kLayMulti, nullptr, rows, nb, act, N, nullptr, nullptr, md, s);
 }
 

@@ -120,10 +120,11 @@ hipError_t launch_gemv(const DeviceInfo* dev, WLayout lay, const uint8_t* Wq, in
 // N <= kGemvFusedMaxN when the quantized activations fit in LDS.  Same bits
 // as launch_act_from_f32 followed by launch_gemv.
 constexpr int64_t kGemvFusedMaxN = 1;
-bool gemv_fuses(int64_t N, int64_t nb, int64_t rows);
+// md: the multi-matrix form's table, else nullptr.
+bool gemv_fuses(int64_t N, int64_t nb, int64_t rows, const MultiDesc* md = nullptr);
 // Whether the fused kernel is also the faster choice when the caller has a
 // workspace for a separate quantizer launch.
-bool gemv_prefers_fused(int64_t N, int64_t nb, int64_t rows);
+bool gemv_prefers_fused(int64_t N, int64_t nb, int64_t rows, const MultiDesc* md = nullptr);
 hipError_t launch_gemv_fused(const DeviceInfo* dev, WLayout lay, const uint8_t* Wq, int64_t rows, int64_t nb,
                              const float* X, int64_t N, float* Y, hipStream_t s);
 // One token, the pages' blocks, with an epilogue and optionally LayerNorm:
@@ -164,6 +165,24 @@ hipError_t launch_rows_x(const DeviceInfo* dev, int lay, const uint8_t* Wq, int6
 hipError_t launch_rows_act(const DeviceInfo* dev, int lay, const uint8_t* Wq, int64_t rows, int64_t nb,
                            const void* act, int64_t N, float* Y, const MultiDesc& md, hipStream_t s,
                            int32_t* D = nullptr);
+
+// Decode on the matrix cores (`k_gemv_mma`): one v_mfma_i32_32x32x32_i8 per
+// 32-row tile and block, for the shapes where mma_apply (kMmaMinN..kGemvMaxN
+// tokens, at least kMmaMinRows rows, even block counts up to kMmaMaxBlocks,
+// kMmaLongMinN tokens from kMmaLongRows rows on).  src is fp32 X (src_f32) or
+// the quantizer's buffer; `lay` a DecodeLayout; md.epi applies at the store
+// (single matrix).
+constexpr int kMmaThreads = 1024;
+constexpr int64_t kMmaMinN = 5;
+constexpr int64_t kMmaMinRows = 2048;
+constexpr int64_t kMmaMaxBlocks = 256;
+constexpr int64_t kMmaLongRows = 32768;
+constexpr int64_t kMmaLongMinN = 7;
+// md: the multi-matrix form's table (its matrices must start on 32-row
+// boundaries), else nullptr.
+bool mma_apply(int64_t N, int64_t nb, int64_t rows, const MultiDesc* md = nullptr);
+hipError_t launch_gemv_mma(const DeviceInfo* dev, int lay, const uint8_t* Wq, int64_t rows, int64_t nb,
+                           const void* src, bool src_f32, int64_t N, float* Y, const MultiDesc& md, hipStream_t s);
 
 // Matrix-core kernel geometry: a workgroup of kPrefillThreads threads computes
 // kPrefillTokens tokens x kPrefillRows rows, so a launch has

@@ -319,6 +319,53 @@ def test_short_rows_either_side_of_row_limit(hip, orc, K):
             assert np.array_equal(host(hip.mul_mat_q4_0r_q8_0(hip.q4_0_repack(Wq, K), Xt)), Y), (rows, K, N)
 
 
+@pytest.mark.parametrize("rows,K", [(2048, 64), (2049, 192), (3000, 768), (2080, 4096), (4100, 8192), (2048, 8256)])
+def test_matrix_core_decode(hip, orc, rows, K):
+    """Five to eight tokens on matrices of 2048 rows and more (the matrix-core
+    decode kernel, one 32-row tile and block per instruction): the oracle bar,
+    ragged row counts (tiles cut by the end of a workgroup's rows or of the
+    matrix), short rows (a chunk of four blocks past the row end), K = 8192
+    (the longest rows it takes) and K = 8256 (past it: the other kernels); the
+    same bits from fused quantization, the pre-quantized input, a caller's
+    workspace and the repacked weights."""
+    for N in (5, 6, 8):
+        if rows * K * N > 160_000_000:
+            continue
+        print("matrix-core decode rows=%d K=%d N=%d" % (rows, K, N), flush=True)
+        W, X = _case(rows, K, N, 6100 + rows + K + N)
+        Wq_o, Xq_o = orc.q4_0_quantize(W), orc.q8_0_quantize(X)
+        Wq = hip.q4_0_quantize(dev(W))
+        Xt = dev(X)
+        Y = host(hip.mul_mat_q4_0_q8_0(Wq, Xt))
+        assert_close(Y, orc.mul_mat_ref(Wq_o, Xq_o, K), "rows=%d K=%d N=%d" % (rows, K, N))
+        assert np.array_equal(host(hip.mul_mat_q4_0_q8_0_pq(Wq, hip.q8_0_quantize(Xt), K)), Y), (rows, K, N)
+        assert np.array_equal(host(hip.mul_mat_q4_0_q8_0_ex(Wq, Xt, hip.workspace(rows, K, N))), Y), (rows, K, N)
+        assert np.array_equal(host(hip.mul_mat_q4_0r_q8_0(hip.q4_0_repack(Wq, K), Xt)), Y), (rows, K, N)
+
+
+def test_matrix_core_decode_multi(hip, orc):
+    """The multi-matrix form on the matrix cores: matrices starting on 32-row
+    boundaries share its 32-row tiles' loop (a tile never spans two matrices);
+    with a matrix that does not, the other kernels run.  Every output against
+    the oracle, with and without a workspace."""
+    K = 4096
+    for shapes in ([2048, 1024, 1024], [2048, 1000, 1024]):
+        Ws = [_case(r, K, 1, 6300 + 7 * r)[0] for r in shapes]
+        X = inputs.random_matrix(6400, 8, K)
+        Wqs = [hip.q4_0_quantize(dev(W)) for W in Ws]
+        Wq_os = [orc.q4_0_quantize(W) for W in Ws]
+        for N in (6, 8):
+            print("matrix-core multi %s N=%d" % (shapes, N), flush=True)
+            Xt = dev(X[:N])
+            Xq_o = orc.q8_0_quantize(X[:N])
+            Ys = hip.mul_mat_q4_0_q8_0_multi(Wqs, Xt)
+            Ys_ws = hip.mul_mat_q4_0_q8_0_multi(Wqs, Xt, ws=hip.workspace(1, K, N))
+            for i, r in enumerate(shapes):
+                Y = host(Ys[i])
+                assert np.array_equal(host(Ys_ws[i]), Y), (shapes, N, i)
+                assert_close(Y, orc.mul_mat_ref(Wq_os[i], Xq_o, K), "multi %s N=%d matrix %d" % (shapes, N, i))
+
+
 @pytest.mark.parametrize("rows,K,n", [(1, 32, 1), (37, 96, 50), (1000, 768, 7), (300, 4096, 513),
                                       (32768, 4096, 512)])
 def test_get_rows(hip, orc, rows, K, n):
@@ -579,7 +626,7 @@ def _fusion_inputs(rows, K, N, seed):
 
 
 # decode task kernel (K = 768), row kernel (K = 4096), prefill kernel (N > 8)
-@pytest.mark.parametrize("rows,K,N", [(3072, 768, 1), (3072, 768, 4), (300, 4096, 1), (300, 4096, 5),
+@pytest.mark.parametrize("rows,K,N", [(3072, 768, 1), (3072, 768, 4), (2304, 768, 6), (300, 4096, 1), (300, 4096, 5),
                                       (1000, 4096, 9), (777, 768, 130)])
 def test_fused_product(hip, orc, rows, K, N):
     W, X, gamma, beta, bias, mul = _fusion_inputs(rows, K, N, 5100 + rows + K + N)
@@ -628,7 +675,8 @@ def test_fused_layernorm_k_sweep(hip, orc, K):
         assert_close(Y, ref, "layernorm K=%d N=%d" % (K, N))
 
 
-@pytest.mark.parametrize("rows,K,N", [(1000, 4096, 1), (1000, 4096, 3), (600, 768, 2), (300, 4096, 40)])
+@pytest.mark.parametrize("rows,K,N", [(1000, 4096, 1), (1000, 4096, 3), (600, 768, 2), (2048, 4096, 7),
+                                      (300, 4096, 40)])
 def test_swiglu(hip, orc, rows, K, N):
     Wg, X, gamma, beta, _, _ = _fusion_inputs(rows, K, N, 5300 + rows + N)
     Wu = _case(rows, K, 1, 5400 + rows)[0]
