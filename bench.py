@@ -39,10 +39,11 @@ ROTATE_BYTES = 1 << 30
 # are in profiles/.  They describe the kernels as profiled; re-profile after a
 # kernel change.
 TRAFFIC_BYTES = {
-    ("llama3_8b_head", 1): 296213669,      # profiles/k_gemv_rows_fused_vocab_head_128256x4096_N1.md
-    ("llama3_8b_prefill", 512): 98293485,   # profiles/k_prefill_14336x4096_N512.md
-    ("llama3_8b_prefill_repacked", 512): 122589802,  # profiles/k_prefill_repacked_14336x4096_N512.md
-    ("q8_0_weights_prefill", 512): 109773002,         # profiles/k_q8w_mm_q8_0_weights_prefill_14336x4096_N512.md
+    ("llama3_8b_head", 1): 296210021,      # profiles/k_gemv_rows_fused_vocab_head_128256x4096_N1.md
+    ("llama3_8b_head", 8): 300084518,      # profiles/k_gemv_mma_vocab_head_128256x4096_N8.md (k_gemv_mma)
+    ("llama3_8b_prefill", 512): 98299615,   # profiles/k_prefill_14336x4096_N512.md
+    ("llama3_8b_prefill_repacked", 512): 122591664,  # profiles/k_prefill_repacked_14336x4096_N512.md
+    ("q8_0_weights_prefill", 512): 109785279,         # profiles/k_q8w_mm_q8_0_weights_prefill_14336x4096_N512.md
 }
 
 
@@ -358,6 +359,8 @@ def decode_configs(hip, torch):
         res.append({"workload": wl.name, "N": N, "matrices": [list(m) for m in wl.mats],
                     "us_per_step": round(ms * 1e3, 3), "GB/s": round(gbs, 1),
                     "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)})
+        if N > 1 and (wl.name, N) in TRAFFIC_BYTES:  # the product kernel's counted HBM bytes per launch
+            res[-1]["traffic_product_kernel"] = TRAFFIC_BYTES[(wl.name, N)]
         del g, mats
         torch.cuda.empty_cache()
     return res
