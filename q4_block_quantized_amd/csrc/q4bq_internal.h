@@ -166,18 +166,23 @@ hipError_t launch_rows_act(const DeviceInfo* dev, int lay, const uint8_t* Wq, in
                            const void* act, int64_t N, float* Y, const MultiDesc& md, hipStream_t s,
                            int32_t* D = nullptr);
 
-// Decode on the matrix cores (`k_gemv_mma`): one v_mfma_i32_32x32x32_i8 per
-// 32-row tile and block, for the shapes where mma_apply (kMmaMinN..kGemvMaxN
-// tokens, at least kMmaMinRows rows, even block counts up to kMmaMaxBlocks,
-// kMmaLongMinN tokens from kMmaLongRows rows on).  src is fp32 X (src_f32) or
-// the quantizer's buffer; `lay` a DecodeLayout; md.epi applies at the store
+// Decode on the matrix cores (`k_gemv_mma_tr` with contiguous weight loads
+// where a row is whole chunks of 8 blocks, at least 64 blocks, and its LDS
+// fits; `k_gemv_mma` with 36-byte lane loads otherwise): one
+// v_mfma_i32_32x32x32_i8 per 32-row tile and block, for the shapes where
+// mma_apply (up to kGemvMaxN tokens, at least kMmaMinRows rows, even block
+// counts up to kMmaMaxBlocks; from kMmaMinN tokens, or on matrices of
+// kMmaLongRows rows and more from kMmaLongMinN tokens with contiguous loads,
+// kMmaLongMinNPairs with lane loads).  src is fp32 X (src_f32) or the
+// quantizer's buffer; `lay` a DecodeLayout; md.epi applies at the store
 // (single matrix).
 constexpr int kMmaThreads = 1024;
 constexpr int64_t kMmaMinN = 5;
 constexpr int64_t kMmaMinRows = 2048;
 constexpr int64_t kMmaMaxBlocks = 256;
 constexpr int64_t kMmaLongRows = 32768;
-constexpr int64_t kMmaLongMinN = 7;
+constexpr int64_t kMmaLongMinN = 4;
+constexpr int64_t kMmaLongMinNPairs = 7;
 // md: the multi-matrix form's table (its matrices must start on 32-row
 // boundaries), else nullptr.
 bool mma_apply(int64_t N, int64_t nb, int64_t rows, const MultiDesc* md = nullptr);

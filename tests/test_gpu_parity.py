@@ -319,17 +319,22 @@ def test_short_rows_either_side_of_row_limit(hip, orc, K):
             assert np.array_equal(host(hip.mul_mat_q4_0r_q8_0(hip.q4_0_repack(Wq, K), Xt)), Y), (rows, K, N)
 
 
-@pytest.mark.parametrize("rows,K", [(2048, 64), (2049, 192), (3000, 768), (2080, 4096), (4100, 8192), (2048, 8256)])
-def test_matrix_core_decode(hip, orc, rows, K):
-    """Five to eight tokens on matrices of 2048 rows and more (the matrix-core
-    decode kernel, one 32-row tile and block per instruction): the oracle bar,
+@pytest.mark.parametrize("rows,K,Ns", [(2048, 64, (5, 6, 8)), (2049, 192, (5, 6, 8)), (3000, 768, (5, 6, 8)),
+                                       (2080, 2048, (5, 6, 8)), (2080, 4096, (5, 6, 8)), (4100, 8192, (5, 6, 8)),
+                                       (2048, 8256, (5, 6, 8)), (32800, 2048, (4, 8))])
+def test_matrix_core_decode(hip, orc, rows, K, Ns):
+    """Four to eight tokens on matrices of 2048 rows and more (the matrix-core
+    decode kernels, one 32-row tile and block per instruction): the oracle bar,
     ragged row counts (tiles cut by the end of a workgroup's rows or of the
-    matrix), short rows (a chunk of four blocks past the row end), K = 8192
-    (the longest rows it takes) and K = 8256 (past it: the other kernels); the
-    same bits from fused quantization, the pre-quantized input, a caller's
-    workspace and the repacked weights."""
-    for N in (5, 6, 8):
-        if rows * K * N > 160_000_000:
+    matrix), short rows (block counts under 64 or not a multiple of 8 take the
+    kernel with 36-byte lane loads, whose last chunk of four blocks can pass
+    the row end), K = 2048 (the shortest rows of the contiguous-load kernel),
+    K = 8192 (the longest rows the matrix cores take) and K = 8256 (past it:
+    the other kernels), 32800 rows (long enough for four tokens on the matrix
+    cores; 1025 tiles over the grid); the same bits from fused quantization,
+    the pre-quantized input, a caller's workspace and the repacked weights."""
+    for N in Ns:
+        if rows * K * N > 600_000_000:
             continue
         print("matrix-core decode rows=%d K=%d N=%d" % (rows, K, N), flush=True)
         W, X = _case(rows, K, N, 6100 + rows + K + N)
@@ -346,16 +351,16 @@ def test_matrix_core_decode(hip, orc, rows, K):
 def test_matrix_core_decode_multi(hip, orc):
     """The multi-matrix form on the matrix cores: matrices starting on 32-row
     boundaries share its 32-row tiles' loop (a tile never spans two matrices);
-    with a matrix that does not, the other kernels run.  Every output against
-    the oracle, with and without a workspace."""
-    K = 4096
-    for shapes in ([2048, 1024, 1024], [2048, 1000, 1024]):
+    with a matrix that does not, the other kernels run; 32768 rows in all take
+    six tokens on the matrix cores.  Every output against the oracle, with and
+    without a workspace."""
+    for K, shapes in ((4096, [2048, 1024, 1024]), (4096, [2048, 1000, 1024]), (2048, [16384, 8192, 8192])):
         Ws = [_case(r, K, 1, 6300 + 7 * r)[0] for r in shapes]
         X = inputs.random_matrix(6400, 8, K)
         Wqs = [hip.q4_0_quantize(dev(W)) for W in Ws]
         Wq_os = [orc.q4_0_quantize(W) for W in Ws]
         for N in (6, 8):
-            print("matrix-core multi %s N=%d" % (shapes, N), flush=True)
+            print("matrix-core multi %s K=%d N=%d" % (shapes, K, N), flush=True)
             Xt = dev(X[:N])
             Xq_o = orc.q8_0_quantize(X[:N])
             Ys = hip.mul_mat_q4_0_q8_0_multi(Wqs, Xt)
