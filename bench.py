@@ -138,11 +138,14 @@ def profile_decode(hip, torch):
     from q4_block_quantized_amd import inputs
     for cid, N in ((1, 1), (2, 1), (3, 1), (3, 4), (4, 1), (4, 8)):
         mats = Mats(hip, torch, cid, N)
-        settle(torch, lambda i: mats.step(hip, i), 0.3)
-        for i in range(30):
-            mats.step(hip, i)
-        torch.cuda.synchronize()
-        log("%s N=%d: 30 steps" % (inputs.WORKLOADS[cid].name, N))
+        # several products of one token: the one-launch set as well
+        fns = [mats.step] + ([mats.step_set] if N == 1 and len(mats.items) > 1 else [])
+        for fn in fns:
+            settle(torch, lambda i: fn(hip, i), 0.3)
+            for i in range(30):
+                fn(hip, i)
+            torch.cuda.synchronize()
+            log("%s N=%d: 30 steps%s" % (inputs.WORKLOADS[cid].name, N, " (one launch)" if fn == mats.step_set else ""))
         del mats
         torch.cuda.empty_cache()
 
@@ -192,6 +195,12 @@ class Mats:
         f = hip.mul_mat_q4_0r_q8_0_ex if self.repack else hip.mul_mat_q4_0_q8_0_ex
         for rows, K, Wqs, X, Y, ws in self.items:
             f(Wqs[i % self.copies], X, ws, Y)
+
+    def step_set(self, hip, i):
+        """One token per product, every product of the workload in one launch."""
+        hip.mul_mat_q4_0_q8_0_set([Wqs[i % self.copies] for rows, K, Wqs, X, Y, ws in self.items],
+                                  [X for rows, K, Wqs, X, Y, ws in self.items],
+                                  [Y for rows, K, Wqs, X, Y, ws in self.items])
 
     def kernel_only(self, hip, i):
         for rows, K, Wqs, X, Y, ws in self.items:
@@ -343,25 +352,46 @@ def decode_configs(hip, torch):
     for cid, N in ((1, 1), (2, 1), (3, 1), (3, 4), (4, 8)):
         wl = inputs.WORKLOADS[cid]
         mats = Mats(hip, torch, cid, N)
-        mats.step(hip, 0)
-        torch.cuda.synchronize()
-        ref = [it[4].clone() for it in mats.items]
-        settle(torch, lambda i: mats.step(hip, i), 0.3)
-        n_steps = mats.copies
-        replays = max(3, int(0.05 / max(n_steps * len(mats.items) * 4e-6, 1e-9)))
-        ms, g = graph_timed(torch, lambda i: mats.step(hip, i), n_steps, replays)
-        same = all(torch.equal(it[4], r) for it, r in zip(mats.items, ref))
-        if not same:
-            raise RuntimeError("graph replay of %s N=%d differs from the eager call" % (wl.name, N))
+        # several products of one token: one launch for all of them
+        # (mul_mat_q4_0_q8_0_set), the separate calls timed beside it
+        paths = [("separate", mats.step)]
+        if N == 1 and len(mats.items) > 1:
+            paths.insert(0, ("set", mats.step_set))
+        timed_paths = {}
+        for pname, fn in paths:
+            fn(hip, 0)
+            torch.cuda.synchronize()
+            ref = [it[4].clone() for it in mats.items]
+            settle(torch, lambda i: fn(hip, i), 0.3)
+            n_steps = mats.copies
+            replays = max(3, int(0.05 / max(n_steps * len(mats.items) * 4e-6, 1e-9)))
+            ms, g = graph_timed(torch, lambda i: fn(hip, i), n_steps, replays)
+            same = all(torch.equal(it[4], r) for it, r in zip(mats.items, ref))
+            if not same:
+                raise RuntimeError("graph replay of %s N=%d (%s) differs from the eager call" % (wl.name, N, pname))
+            timed_paths[pname] = (ms, ref)
+            del g
+        if "set" in timed_paths and not all(torch.equal(a, b) for a, b in zip(timed_paths["set"][1],
+                                                                             timed_paths["separate"][1])):
+            raise RuntimeError("%s: the one-launch set differs from the separate calls" % wl.name)
+        # the step: the faster of the library's two forms (both are reported)
+        pname = min(timed_paths, key=lambda k: timed_paths[k][0])
+        ms = timed_paths[pname][0]
         gbs = mats.bytes_step() / (ms * 1e-3) / 1e9
-        log("%s N=%d: %.2f us per step (%d launches, HIP graph) -> %.1f GB/s"
-            % (wl.name, N, ms * 1e3, len(mats.items), gbs))
+        log("%s N=%d: %.2f us per step (%s, HIP graph) -> %.1f GB/s"
+            % (wl.name, N, ms * 1e3, "one launch" if pname == "set" else "%d launches" % len(mats.items), gbs))
         res.append({"workload": wl.name, "N": N, "matrices": [list(m) for m in wl.mats],
                     "us_per_step": round(ms * 1e3, 3), "GB/s": round(gbs, 1),
-                    "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)})
+                    "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                    "form": "mul_mat_q4_0_q8_0_set (one launch)" if pname == "set" else "one call per matrix"})
+        if "set" in timed_paths:
+            res[-1]["set_us_per_step"] = round(timed_paths["set"][0] * 1e3, 3)
+            res[-1]["separate_calls_us_per_step"] = round(timed_paths["separate"][0] * 1e3, 3)
+            log("   one launch: %.2f us, separate calls: %.2f us per step"
+                % (timed_paths["set"][0] * 1e3, timed_paths["separate"][0] * 1e3))
         if N > 1 and (wl.name, N) in TRAFFIC_BYTES:  # the product kernel's counted HBM bytes per launch
             res[-1]["traffic_product_kernel"] = TRAFFIC_BYTES[(wl.name, N)]
-        del g, mats
+        del mats
         torch.cuda.empty_cache()
     return res
 

@@ -213,6 +213,35 @@ int mul_mat_q4_0_q8_0_multi(int count, const void *const *Wq, const int64_t *row
                             void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * Several independent one-token products in one launch: Y[i] = mul_mat(Wq[i],
+ * X[i]) with N = 1 for i < count, each with its own K and its own token --
+ * a decode step's products as "llama.cpp 深度解读" section 4 ("计算图构建 — 以
+ * Llama 模型为例") lists them (Q, K, V, output, gate, up and down
+ * projections), with the operator of section 3 ("量化矩阵乘法 — 核心算子").
+ *   count          1 <= count <= 8.
+ *   Wq, rows, K,   HOST arrays of count entries: device pointers to each
+ *   X, Y           product's Q4_0 blocks (rows[i] x K[i]/32, 2-byte aligned),
+ *                  its fp32 token (K[i] values, 4-byte aligned) and its fp32
+ *                  output (rows[i] values, 4-byte aligned, overwritten);
+ *                  K[i] a positive multiple of 32; no output may overlap any
+ *                  input or another output.
+ * The workgroups quantize every token once and stream the products' weights
+ * in one pass, where every block count is even, a row is at most 16 chunks of
+ * 64 block pairs (K <= 65536), the tokens hold at most 1024 blocks in all
+ * (32768 values) and the rows at most 64 rounds of 16 chunk rows per
+ * workgroup (the one launch allocates nothing); other sets run as count
+ * separate products.  Each Y[i] equals mul_mat_q4_0_q8_0(Wq[i], rows[i], K[i],
+ * X[i], 1, Y[i]) within the operator's tolerance (the same block terms), and
+ * bitwise where that call runs the row kernel with one block pair per lane and
+ * the same chunks (the GPT-2- and Llama-3-8B-shaped matrices).  Errors as
+ * mul_mat_q4_0_q8_0: nothing is launched for an invalid argument; products
+ * enqueued before a failed launch may have run.
+ */
+int mul_mat_q4_0_q8_0_set(int count, const void *const *Wq, const int64_t *rows,
+                          const int64_t *K, const float *const *X, float *const *Y,
+                          void *stream);
+
+/*
  * The operator with pre-quantized activations: Xq holds N x (K/32) Q8_0 blocks
  * (2-byte aligned), otherwise as mul_mat_q4_0_q8_0.  Feeding it the output of
  * q8_0_quantize(X) gives exactly the Y of mul_mat_q4_0_q8_0(X).

@@ -31,7 +31,7 @@ EXPORTS = (
     "q4_0_quantize", "q8_0_quantize", "mul_mat_q4_0_q8_0", "q4bq_workspace_size",
     "mul_mat_q4_0_q8_0_ex", "mul_mat_q4_0_q8_0_pq", "q4_0_q8_0_block_dots",
     "q4bq_status_string", "q4bq_version", "q4bq_quantize_activations", "mul_mat_q4_0_q8_0_prepared",
-    "q4_0_repack", "mul_mat_q4_0r_q8_0", "mul_mat_q4_0r_q8_0_ex", "mul_mat_q4_0_q8_0_multi",
+    "q4_0_repack", "mul_mat_q4_0r_q8_0", "mul_mat_q4_0r_q8_0_ex", "mul_mat_q4_0_q8_0_multi", "mul_mat_q4_0_q8_0_set",
     "q4_0_get_rows", "q4bq_repack_size", "mul_mat_q8_0_q8_0", "q8_0_q8_0_block_dots",
     "mul_mat_q4_0_q8_0_fused", "mul_mat_q4_0_q8_0_swiglu", "q4bq_fused_workspace_size",
     "mul_mat_q4_0_q8_0_noalloc",
@@ -76,6 +76,7 @@ def lib() -> ctypes.CDLL:
         "q8_0_q8_0_block_dots": (I, [P, I64, I64, P, I64, P, P]),
         "q4_0_get_rows": (I, [P, I64, I64, P, I64, P, P]),
         "mul_mat_q4_0_q8_0_multi": (I, [ctypes.c_int, P, P, I64, P, I64, P, P, ctypes.c_size_t, P]),
+        "mul_mat_q4_0_q8_0_set": (I, [ctypes.c_int, P, P, P, P, P, P]),
         "mul_mat_q4_0r_q8_0": (I, [P, I64, I64, P, I64, P, P]),
         "mul_mat_q4_0r_q8_0_ex": (I, [P, I64, I64, P, I64, P, P, ctypes.c_size_t, P]),
         "q4_0_q8_0_block_dots": (I, [P, I64, I64, P, I64, P, P]),
@@ -364,6 +365,27 @@ def mul_mat_q4_0_q8_0_multi(Wqs, X: torch.Tensor, Ys=None, ws: torch.Tensor | No
     _check(lib().mul_mat_q4_0_q8_0_multi(count, ctypes.cast(wp, ctypes.c_void_p), ctypes.cast(rp, ctypes.c_void_p), K,
                                          _dev(X, torch.float32, "X"), N, ctypes.cast(yp, ctypes.c_void_p), wsp, wsn,
                                          _stream(stream)), "mul_mat_q4_0_q8_0_multi")
+    return Ys
+
+
+def mul_mat_q4_0_q8_0_set(Wqs, Xs, Ys=None, stream=None) -> list:
+    """Y[i] = mul_mat_q4_0_q8_0(Wqs[i], Xs[i]) for every i, one token each (Xs[i]: 1 x K_i or K_i values),
+    in one launch where the set fits it."""
+    count = len(Wqs)
+    if len(Xs) != count:
+        raise ValueError("mul_mat_q4_0_q8_0_set: %d weight matrices, %d tokens" % (count, len(Xs)))
+    Ks = [int(X.numel()) for X in Xs]
+    rows = [_rows(W, K) for W, K in zip(Wqs, Ks)]
+    if Ys is None:
+        Ys = [torch.empty((1, r), dtype=torch.float32, device=X.device) for r, X in zip(rows, Xs)]
+    wp = (ctypes.c_void_p * count)(*[_dev(W, torch.uint8, "Wq[%d]" % i) for i, W in enumerate(Wqs)])
+    xp = (ctypes.c_void_p * count)(*[_dev(X, torch.float32, "X[%d]" % i) for i, X in enumerate(Xs)])
+    yp = (ctypes.c_void_p * count)(*[_dev(Y, torch.float32, "Y[%d]" % i) for i, Y in enumerate(Ys)])
+    rp = (ctypes.c_int64 * count)(*rows)
+    kp = (ctypes.c_int64 * count)(*Ks)
+    _check(lib().mul_mat_q4_0_q8_0_set(count, ctypes.cast(wp, ctypes.c_void_p), ctypes.cast(rp, ctypes.c_void_p),
+                                       ctypes.cast(kp, ctypes.c_void_p), ctypes.cast(xp, ctypes.c_void_p),
+                                       ctypes.cast(yp, ctypes.c_void_p), _stream(stream)), "mul_mat_q4_0_q8_0_set")
     return Ys
 
 

@@ -25,7 +25,7 @@ ARCH = "gfx950"
 PROBE_SOURCE = "q4bq_probe.hip"
 PROBE_LIB = os.path.join(PKG, "libq4bq_probe.so")
 SOURCES = ["q4bq_api.cpp", "q4bq_quant.hip", "q4bq_gemv.hip", "q4bq_rows_x.hip", "q4bq_rows_act.hip",
-           "q4bq_prefill.hip", "q4bq_q8w.hip", "q4bq_q8w_mm.hip", "q4bq_noalloc.hip", "q4bq_mma.hip"]
+           "q4bq_prefill.hip", "q4bq_q8w.hip", "q4bq_q8w_mm.hip", "q4bq_noalloc.hip", "q4bq_mma.hip", "q4bq_set.hip"]
 
 # No fast-math anywhere: the quantizers need IEEE division and round-half-away.
 # Packed fp32 instructions are switched off for all device code.

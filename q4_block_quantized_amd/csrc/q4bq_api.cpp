@@ -301,6 +301,43 @@ int mul_mat_q4_0_q8_0_multi(int count, const void* const* Wq, const int64_t* row
     return status_of(err);
 }
 
+int mul_mat_q4_0_q8_0_set(int count, const void* const* Wq, const int64_t* rows, const int64_t* K,
+                          const float* const* X, float* const* Y, void* stream) {
+    if (count < 1 || count > kMaxMulti || !Wq || !rows || !K || !X || !Y) return Q4BQ_EINVAL;
+    SetDesc sd{};
+    sd.count = count;
+    for (int i = 0; i < count; ++i) {
+        const int rc = check_product(Wq[i], rows[i], K[i], X[i], kF32, 1, Y[i], false);
+        if (rc != Q4BQ_OK) return rc;
+        sd.w[i] = static_cast<const uint8_t*>(Wq[i]);
+        sd.x[i] = X[i];
+        sd.y[i] = Y[i];
+        sd.rows[i] = rows[i];
+        sd.nb[i] = static_cast<int>(K[i] / kQK);
+    }
+    // no output may overlap another product's weights, activations or output
+    for (int i = 0; i < count; ++i)
+        for (int j = 0; j < count; ++j) {
+            if (i == j) continue;
+            const size_t yb = static_cast<size_t>(rows[i]) * 4;
+            if (overlap(Y[i], yb, Wq[j], static_cast<size_t>(rows[j] * (K[j] / kQK)) * kQ4Bytes) ||
+                overlap(Y[i], yb, X[j], static_cast<size_t>(K[j]) * 4) ||
+                overlap(Y[i], yb, Y[j], static_cast<size_t>(rows[j]) * 4))
+                return Q4BQ_EINVAL;
+        }
+    hipError_t err = hipSuccess;
+    const DeviceInfo* dev = current_device(&err);
+    if (!dev) return Q4BQ_EHIP;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (set_plan(sd, dev->num_cu)) return status_of(launch_gemv_set(dev, sd, s));
+    // shapes the one launch does not take: the products one by one
+    for (int i = 0; i < count; ++i) {
+        const int rc = run_with_scratch(kAoS, sd.w[i], rows[i], K[i], X[i], nullptr, 1, Y[i], nullptr, s);
+        if (rc != Q4BQ_OK) return rc;
+    }
+    return Q4BQ_OK;
+}
+
 int mul_mat_q4_0_q8_0_pq(const void* Wq, int64_t rows, int64_t K, const void* Xq, int64_t N, float* Y,
                          void* stream) {
     const int rc = check_product(Wq, rows, K, Xq, kQ8, N, Y, false);
@@ -582,6 +619,6 @@ const char* q4bq_status_string(int status) {
     }
 }
 
-int q4bq_version(void) { return 300; }
+int q4bq_version(void) { return 400; }
 
 }  // extern "C"

@@ -141,6 +141,31 @@ hipError_t launch_gemv_fused_epi(const DeviceInfo* dev, const uint8_t* Wq, int64
 hipError_t launch_gemv_multi(const DeviceInfo* dev, const MultiDesc& md, int64_t nb, const float* X, const void* act,
                              int64_t N, hipStream_t s);
 
+// Several independent one-token products in one launch (`k_gemv_set`):
+// product m multiplies its Q4_0 blocks w[m] (rows[m] x nb[m]) with its own
+// fp32 token x[m] (nb[m] * 32 values) into y[m] (rows[m]).  set_plan fills
+// C, Pc, boff, round0 and nblk from count, w, x, y, rows, nb and returns
+// false where the launch does not apply (an odd block count, a row of more
+// than 16 chunks of 64 pairs, more than kSetMaxBlocks activation blocks in
+// all, or more than kSetMaxRounds rounds for a workgroup).
+constexpr int kSetMaxBlocks = 1024;  // activation blocks of all products (LDS)
+constexpr int kSetMaxRounds = 64;    // rounds of 16 chunk rows per workgroup
+struct SetDesc {
+    const uint8_t* w[kMaxMulti];
+    const float* x[kMaxMulti];
+    float* y[kMaxMulti];
+    int64_t rows[kMaxMulti];
+    int nb[kMaxMulti];
+    int C[kMaxMulti];      // chunks per row (a power of two, at most 16)
+    int Pc[kMaxMulti];     // block pairs per chunk (at most 64)
+    int boff[kMaxMulti];   // first activation block of the product in LDS
+    int64_t round0[kMaxMulti + 1];  // first round of each product; round0[count]: all rounds
+    int count;
+    int nblk;              // activation blocks of all products
+};
+bool set_plan(SetDesc& sd, int64_t num_cu);
+hipError_t launch_gemv_set(const DeviceInfo* dev, const SetDesc& sd, hipStream_t s);
+
 // Decode kernels: activation sources and weight layouts (the rows of several
 // matrices, MultiDesc, count as one more layout).
 enum DecodeSrc { kActGlobal = 0, kActLds = 1, kXF32 = 2 };

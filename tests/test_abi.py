@@ -124,6 +124,18 @@ def _bad_product_calls(L):
     yield mm(2, ptrs(A, A + 4096), i64s(4, 0), 64, B, 1, ptrs(C, C + 256), None, 0, None)     # a matrix with 0 rows
     yield mm(2, ptrs(A, A + 4096), i64s(4, 4), 48, B, 1, ptrs(C, C + 256), None, 0, None)     # K % 32 != 0
     yield mm(2, ptrs(A, A + 4096), i64s(4, 4), 64, B, 1, ptrs(C, C + 256), WS + 8, 1 << 20, None)  # workspace misaligned
+    st = L.mul_mat_q4_0_q8_0_set
+    yield st(0, ptrs(A), i64s(4), i64s(64), ptrs(B), ptrs(C), None)                                # count < 1
+    yield st(9, ptrs(*[A] * 9), i64s(*[4] * 9), i64s(*[64] * 9), ptrs(*[B] * 9),
+             ptrs(*[C + 256 * i for i in range(9)]), None)                                             # count > 8
+    yield st(2, None, i64s(4, 4), i64s(64, 64), ptrs(B, B + 256), ptrs(C, C + 256), None)             # null weight array
+    yield st(2, ptrs(A, A + 4096), i64s(4, 4), None, ptrs(B, B + 256), ptrs(C, C + 256), None)        # null K array
+    yield st(2, ptrs(A, A + 4096), i64s(4, 4), i64s(64, 48), ptrs(B, B + 256), ptrs(C, C + 256), None)  # K % 32 != 0
+    yield st(2, ptrs(A, A + 4096), i64s(4, 0), i64s(64, 64), ptrs(B, B + 256), ptrs(C, C + 256), None)  # 0 rows
+    yield st(2, ptrs(A, A + 4096), i64s(4, 4), i64s(64, 64), ptrs(B, None), ptrs(C, C + 256), None)    # null token
+    yield st(2, ptrs(A, A + 4096), i64s(4, 4), i64s(64, 64), ptrs(B, B + 256), ptrs(C, C + 8), None)   # outputs overlap
+    yield st(2, ptrs(A, A + 4096), i64s(4, 4), i64s(64, 64), ptrs(B, B + 256), ptrs(B + 260, C), None)  # output in a token
+    yield st(2, ptrs(A, A + 4096), i64s(4, 4), i64s(64, 64), ptrs(B, B + 256), ptrs(C, A + 8), None)   # output in weights
     gr = L.q4_0_get_rows
     yield gr(None, 4, 64, B, 3, C, None)           # null table
     yield gr(A, 4, 64, None, 3, C, None)           # null ids

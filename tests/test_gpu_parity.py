@@ -348,6 +348,41 @@ def test_matrix_core_decode(hip, orc, rows, K, Ns):
         assert np.array_equal(host(hip.mul_mat_q4_0r_q8_0(hip.q4_0_repack(Wq, K), Xt)), Y), (rows, K, N)
 
 
+SET_CASES = [
+    ("gpt2_layer", [(2304, 768), (768, 768), (3072, 768), (768, 3072)], True),
+    ("llama3_8b_decode", [(4096, 4096), (14336, 4096), (4096, 14336)], True),
+    ("ragged", [(37, 64), (1000, 2048), (2049, 1536), (5, 16384)], False),
+    ("one", [(300, 4096)], True),
+    ("odd_blocks", [(100, 96), (64, 4096)], False),        # K = 96: three blocks, the products one by one
+    ("long_tokens", [(64, 32768), (64, 4096)], False),     # 1152 activation blocks: one by one
+]
+
+
+@pytest.mark.parametrize("name,shapes,same_bits", SET_CASES, ids=[c[0] for c in SET_CASES])
+def test_product_set(hip, orc, name, shapes, same_bits):
+    """Independent one-token products in one launch (mul_mat_q4_0_q8_0_set):
+    every output against the oracle; on the GPT-2- and Llama-3-8B-shaped
+    matrices (and a single product) bitwise equal to separate calls, which run
+    the row kernel with the same chunks; sets the launch does not take (an odd
+    block count, more than 1024 activation blocks in all) run one by one."""
+    print("product set %s %s" % (name, shapes), flush=True)
+    Ws = [_case(r, K, 1, 8100 + 13 * i + r + K)[0] for i, (r, K) in enumerate(shapes)]
+    Xs = [inputs.random_matrix(8200 + 13 * i + K, 1, K) for i, (r, K) in enumerate(shapes)]
+    Wqs = [hip.q4_0_quantize(dev(W)) for W in Ws]
+    Xts = [dev(X) for X in Xs]
+    Ys = hip.mul_mat_q4_0_q8_0_set(Wqs, Xts)
+    for i, (r, K) in enumerate(shapes):
+        Y = host(Ys[i])
+        assert Y.shape == (1, r)
+        assert_close(Y, orc.mul_mat_ref(orc.q4_0_quantize(Ws[i]), orc.q8_0_quantize(Xs[i]), K),
+                     "set %s product %d" % (name, i))
+        Y1 = host(hip.mul_mat_q4_0_q8_0(Wqs[i], Xts[i]))
+        if same_bits:
+            assert np.array_equal(Y, Y1), (name, i)
+        else:
+            assert_close(Y, Y1.astype(np.float64), "set %s product %d against its own call" % (name, i))
+
+
 def test_matrix_core_decode_multi(hip, orc):
     """The multi-matrix form on the matrix cores: matrices starting on 32-row
     boundaries share its 32-row tiles' loop (a tile never spans two matrices);
