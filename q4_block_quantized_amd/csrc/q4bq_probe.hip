@@ -16,8 +16,9 @@
 //   buffer of q4bq_probe_threads() floats.
 //
 //   q4bq_probe_read(src, bytes, out, stream): streams `bytes` (a multiple of
-//   16, src 16-byte aligned) with 16-byte loads, grid-stride, and writes one
-//   xor per thread to `out` (q4bq_probe_threads() floats): the streaming-read
+//   16, src 16-byte aligned) with 16-byte non-temporal loads, each wave
+//   instruction reading 1 KB contiguous, grid-stride, and writes one xor per
+//   thread to `out` (q4bq_probe_threads() floats): the streaming-read
 //   bandwidth the decode kernels are measured against.
 //
 // Returns 0, -1 (bad argument) or -2 (HIP error).
@@ -107,25 +108,31 @@ __global__ void __launch_bounds__(kThreads) k_probe_valu(int64_t iters, float* _
     out[blockIdx.x * kThreads + threadIdx.x] = s;
 }
 
-__global__ void __launch_bounds__(kThreads)
+// 1024 threads a workgroup, 256 workgroups (the same thread count as the
+// other probes): chunks of 4 x 1024 consecutive 16-byte pieces, lane t taking
+// pieces t, t + 1024, t + 2048, t + 3072 of a chunk (each load instruction one
+// contiguous 1 KB per wave), non-temporal, grid-stride over the chunks.
+// Measured on this GPU: ~6.9 TB/s over 1 GiB, against ~5.7 TB/s with the four
+// loads of a lane a grid stride apart and ~6.2 TB/s with plain loads.
+constexpr int kReadThreads = 1024;
+constexpr int kReadBlocks = kBlocks * kThreads / kReadThreads;
+__global__ void __launch_bounds__(kReadThreads)
 k_probe_read(const u32x4* __restrict__ src, int64_t n16, float* __restrict__ out) {
     uint32_t acc = 0;
-    const int64_t step = static_cast<int64_t>(gridDim.x) * kThreads;
-    int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-    // four independent 16-byte loads in flight per lane
-    for (; i + 3 * step < n16; i += 4 * step) {
-        const u32x4 v0 = __builtin_nontemporal_load(src + i);
-        const u32x4 v1 = __builtin_nontemporal_load(src + i + step);
-        const u32x4 v2 = __builtin_nontemporal_load(src + i + 2 * step);
-        const u32x4 v3 = __builtin_nontemporal_load(src + i + 3 * step);
-        acc ^= (v0.x ^ v0.y ^ v0.z ^ v0.w) ^ (v1.x ^ v1.y ^ v1.z ^ v1.w) ^ (v2.x ^ v2.y ^ v2.z ^ v2.w) ^
-               (v3.x ^ v3.y ^ v3.z ^ v3.w);
+    constexpr int kU = 4;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kReadThreads * kU;
+    for (int64_t base = static_cast<int64_t>(blockIdx.x) * kReadThreads * kU + threadIdx.x; base < n16;
+         base += stride) {
+        u32x4 v[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int64_t i = base + static_cast<int64_t>(u) * kReadThreads;
+            v[u] = i < n16 ? __builtin_nontemporal_load(src + i) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
     }
-    for (; i < n16; i += step) {
-        const u32x4 v = __builtin_nontemporal_load(src + i);
-        acc ^= v.x ^ v.y ^ v.z ^ v.w;
-    }
-    out[blockIdx.x * kThreads + threadIdx.x] = static_cast<float>(acc);
+    out[blockIdx.x * kReadThreads + threadIdx.x] = static_cast<float>(acc);
 }
 
 }  // namespace
@@ -154,7 +161,7 @@ int q4bq_probe_mfma(int kind, int64_t iters, float* out, void* stream) {
 
 int q4bq_probe_read(const void* src, int64_t bytes, float* out, void* stream) {
     if (!src || !out || bytes < 16 || bytes % 16 || (reinterpret_cast<uintptr_t>(src) & 15)) return -1;
-    hipLaunchKernelGGL(k_probe_read, dim3(kBlocks), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
+    hipLaunchKernelGGL(k_probe_read, dim3(kReadBlocks), dim3(kReadThreads), 0, static_cast<hipStream_t>(stream),
                        static_cast<const u32x4*>(src), bytes / 16, out);
     return hipGetLastError() == hipSuccess ? 0 : -2;
 }
