@@ -147,11 +147,28 @@ __device__ __forceinline__ int64_t uniform64(int64_t v) {
     return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
+// NTL (one pair per lane, the pages' blocks, rows or chunks of a multiple of
+// 4 pairs): a wave loads its row (chunk) as consecutive 16-byte pieces with
+// non-temporal loads -- each instruction one contiguous 1 KB -- writes them to
+// its own LDS area in order and reads its lane's 36-byte pair back (rows 9
+// dwords apart per lane: no bank conflicts).  Measured on the vocabulary head
+// (loads alone): 36-byte pairs loaded by the lanes directly stream at ~5.8
+// TB/s, the contiguous non-temporal pieces with the reordering at ~6.6 TB/s
+// (non-temporal loads of the pairs themselves are slower: several load
+// instructions touch each line).  The block dots see the same bytes.
+constexpr int kNtlRowBytes = 64 * 36;  // a row or chunk of at most 64 pairs
+__host__ __device__ inline size_t rows_ntl_offset(int nt, int64_t nb, int C, int waves, bool act_lds) {
+    size_t a = act_lds ? static_cast<size_t>(nt) * nb * (kActQBytes + kActSBytes) : 0;
+    const size_t p = C > 1 ? static_cast<size_t>(kSplitRounds) * waves * nt * sizeof(float) : 0;
+    if (p > a) a = p;
+    return (a + 15) / 16 * 16;
+}
+
 // DOTS: instead of Y, every per-block integer dot goes to
 // Dots[(n * rows + r) * nb + b] (the test export; one matrix of Q4_0 blocks,
 // activations from the quantizer's buffer).
 template <int THREADS, int NT, int PPL, int D, int SRC, int LAY, bool EPI, bool DOTS = false, int C = 1,
-          bool DUAL = false>
+          bool DUAL = false, bool NTL = false>
 __global__ void __launch_bounds__(THREADS)
 k_gemv_rows(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __restrict__ src,
             float* __restrict__ Y, int32_t* __restrict__ Dots, const MultiDesc md) {
@@ -164,6 +181,7 @@ k_gemv_rows(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __
     constexpr int kWaves = THREADS / 64;
     static_assert(C == 1 || (PPL == 1 && !MULTI && !DOTS && kWaves % C == 0), "chunked form");
     static_assert(!DUAL || (C == 2 && EPI && SRC == kXF32 && NT == 1 && LAY == kLayAoS), "gate and up form");
+    static_assert(!NTL || (PPL == 1 && !RP && !DOTS), "contiguous row loads");
     // LayerNorm of the one token in the prologue (md.epi.ln_gamma set): the
     // fused instantiation with one pair per lane, where each thread holds its
     // quads of X in registers
@@ -292,10 +310,40 @@ k_gemv_rows(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __
             dst[i] = RP ? load_pair_rp(a.w + 32 * p, a.sc + 4 * p) : load_pair(a.w + 36 * p);
         }
     };
+    // NTL: the row's (chunk's) 9 Pc / 4 pieces; the lanes past them re-read
+    // its last piece (unconditional loads), and only pieces inside are written
+    const int npc = 9 * Pc / 4;
+    uint8_t* const wrow =
+        smem + rows_ntl_offset(NT, nb, C, kWaves, kUseLds) + static_cast<size_t>(wave) * kNtlRowBytes;
+    auto load_row_ntl = [&](u32x4 (&dst)[3], int64_t k) __attribute__((always_inline)) {
+        typedef u32x4 u32x4_a2 __attribute__((aligned(2)));
+        const RowAt a = row_at(min(w0 + k * S, rlast));
+        const uint8_t* base = a.w + 36 * pbase;
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+            const int pc = min(lane + 64 * i, npc - 1);
+            dst[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_a2*>(base + 16 * pc));
+        }
+    };
+    auto unpack_row = [&](const u32x4 (&src)[3], Pair36 (&q)[PPL]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 3; ++i)
+            if (lane + 64 * i < npc) reinterpret_cast<u32x4*>(wrow)[lane + 64 * i] = src[i];
+        __builtin_amdgcn_wave_barrier();
+        const uint32_t* p = reinterpret_cast<const uint32_t*>(wrow + 36 * (pp[0] - pbase));
+#pragma unroll
+        for (int j = 0; j < 9; ++j) q[0].w[j] = p[j];
+        __builtin_amdgcn_wave_barrier();
+    };
     Pair36 raw[D][PPL];
+    u32x4 rawn[NTL ? D : 1][3];
+    auto load_next = [&](int d, int64_t k) __attribute__((always_inline)) {
+        if constexpr (NTL) load_row_ntl(rawn[d], k);
+        else load_row(raw[d], k);
+    };
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-        load_row(raw[d], d);
+        load_next(d, d);
         __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -468,9 +516,10 @@ k_gemv_rows(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __
 #pragma unroll
             for (int d = 0; d < D; ++d) {
                 float part[NT];
+                if constexpr (NTL) unpack_row(rawn[d], raw[d]);
                 fold(raw[d], part);
                 keep[k + d] = wave_sums<NT>(part, lane);
-                load_row(raw[d], k + d + D);
+                load_next(d, k + d + D);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -536,6 +585,7 @@ k_gemv_rows(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             float part[NT];
+            if constexpr (NTL) unpack_row(rawn[d], raw[d]);
             fold(raw[d], part);
             const float t = wave_sums<NT>(part, lane);
             if (k + d < nk && my_token >= 0 && my_token < NT) {
@@ -543,7 +593,7 @@ k_gemv_rows(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __
                 const RowAt a = row_at(r);
                 a.y[static_cast<int64_t>(my_token) * a.ystride] = EPI ? epilogue_with(t, eb[d], em[d], md.epi) : t;
             }
-            load_row(raw[d], k + d + D);
+            load_next(d, k + d + D);
             load_epi(d, k + d + D);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -609,10 +659,27 @@ hipError_t launch_rows_k(const DeviceInfo* dev, const uint8_t* Wq, int64_t rows,
     // re-reads its last row for each extra slot
     constexpr bool kDeep = kDepth == 2 && C == 1 && !DOTS;
     const bool deep = kDeep && rows >= 16 * wgs * (kThreads / 64);
-    const auto kernel = deep ? k_gemv_rows<kThreads, NT, PPL, kDeep ? 4 : kDepth, SRC, LAY, EPI, DOTS, C, DUAL>
-                             : k_gemv_rows<kThreads, NT, PPL, kDepth, SRC, LAY, EPI, DOTS, C, DUAL>;
+    // contiguous non-temporal row loads through LDS where a row (chunk) is
+    // whole 16-byte pieces and every wave has 16 rows or more (measured: the
+    // vocabulary head at N = 1 / 2, 52.0 -> 46.7 / 55.3 -> 50.0 us; with a few
+    // rows per wave the extra LDS round trip per row costs more than the
+    // loads save: 14336 x 4096 at N = 1 8.1 -> 8.3 us, 4096 x 4096 at N = 2
+    // 5.4 -> 6.0 us)
+    constexpr bool kNtlForm = PPL == 1 && LAY != kLayRepacked && !DOTS;
+    const bool ntl = kNtlForm && ((nb / 2) / C) % 4 == 0 && rows * C >= 16 * wgs * (kThreads / 64) &&
+                     rows_ntl_offset(NT, nb, C, kThreads / 64, SRC == kXF32 || PPL > 1) +
+                             static_cast<size_t>(kThreads / 64) * kNtlRowBytes <=
+                         kRowsMaxLds;
+    const auto kernel =
+        ntl ? (deep ? k_gemv_rows<kThreads, NT, PPL, kDeep ? 4 : kDepth, SRC, LAY, EPI, DOTS, C, DUAL, kNtlForm>
+                    : k_gemv_rows<kThreads, NT, PPL, kDepth, SRC, LAY, EPI, DOTS, C, DUAL, kNtlForm>)
+            : (deep ? k_gemv_rows<kThreads, NT, PPL, kDeep ? 4 : kDepth, SRC, LAY, EPI, DOTS, C, DUAL>
+                    : k_gemv_rows<kThreads, NT, PPL, kDepth, SRC, LAY, EPI, DOTS, C, DUAL>);
     size_t lds = (SRC == kXF32 || PPL > 1) ? static_cast<size_t>(NT) * nb * (kActQBytes + kActSBytes) : 0;
     if (C > 1) lds = std::max(lds, static_cast<size_t>(kSplitRounds) * (kThreads / 64) * NT * sizeof(float));
+    if (ntl)
+        lds = rows_ntl_offset(NT, nb, C, kThreads / 64, SRC == kXF32 || PPL > 1) +
+              static_cast<size_t>(kThreads / 64) * kNtlRowBytes;
     if (lds > 64 * 1024) {
         // beyond the default dynamic LDS limit: raise it once for this kernel
         const hipError_t raised = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),

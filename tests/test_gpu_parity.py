@@ -348,6 +348,32 @@ def test_matrix_core_decode(hip, orc, rows, K, Ns):
         assert np.array_equal(host(hip.mul_mat_q4_0r_q8_0(hip.q4_0_repack(Wq, K), Xt)), Y), (rows, K, N)
 
 
+@pytest.mark.parametrize("rows,K,Ns", [(66000, 3072, (1, 2, 4)), (70000, 4096, (1,))])
+def test_long_matrices_contiguous_row_loads(hip, orc, rows, K, Ns):
+    """One to four tokens on matrices with 16 rows or more per wave: the row
+    kernel loads each row as consecutive 16-byte pieces and reorders them
+    through LDS (rows of 108 and 144 pieces: two and three load instructions,
+    the last one partly used; ragged row counts).  Against the oracle, and bit
+    for bit against the repacked weights (which keep the lanes' own pair
+    loads), the pre-quantized input and a caller's workspace; the multi-matrix
+    form over two such matrices against separate calls."""
+    for N in Ns:
+        print("contiguous row loads rows=%d K=%d N=%d" % (rows, K, N), flush=True)
+        W, X = _case(rows, K, N, 9300 + rows + K + N)
+        Wq_o, Xq_o = orc.q4_0_quantize(W), orc.q8_0_quantize(X)
+        Wq = hip.q4_0_quantize(dev(W))
+        Xt = dev(X)
+        Y = host(hip.mul_mat_q4_0_q8_0(Wq, Xt))
+        assert_close(Y, orc.mul_mat_ref(Wq_o, Xq_o, K), "rows=%d K=%d N=%d" % (rows, K, N))
+        assert np.array_equal(host(hip.mul_mat_q4_0r_q8_0(hip.q4_0_repack(Wq, K), Xt)), Y), (rows, K, N)
+        assert np.array_equal(host(hip.mul_mat_q4_0_q8_0_pq(Wq, hip.q8_0_quantize(Xt), K)), Y), (rows, K, N)
+        assert np.array_equal(host(hip.mul_mat_q4_0_q8_0_ex(Wq, Xt, hip.workspace(rows, K, N))), Y), (rows, K, N)
+        if N == 1:
+            half = rows // 2 // 32 * 32
+            Ys = hip.mul_mat_q4_0_q8_0_multi([Wq[:half], Wq[half:]], Xt)
+            assert np.array_equal(np.concatenate([host(Ys[0]), host(Ys[1])], axis=1), Y), (rows, K, N)
+
+
 SET_CASES = [
     ("gpt2_layer", [(2304, 768), (768, 768), (3072, 768), (768, 3072)], True),
     ("llama3_8b_decode", [(4096, 4096), (14336, 4096), (4096, 14336)], True),
