@@ -84,6 +84,40 @@ __device__ __forceinline__ int8_t q8_rule(float x, float d) {
     return static_cast<int8_t>(min(max(q, -127), 127));
 }
 
+// The same codes for four values sharing d, with one reciprocal instead of a
+// correctly rounded division per value.  r = 1/d from the hardware
+// reciprocal refined by one Newton step has a relative error of about 2^-24,
+// so y = x r is within 2^-15 of x/d, and the rounded quotient fl(x/d) within
+// 2^-17 of it, as long as |x/d| < 256 (d is amax/127 rounded to binary16:
+// about amax/127 in the normal range, at least two thirds of it among the
+// subnormals, so |x/d| <= 190.5).  When y lies farther than 2^-13 from every half-integer, y and
+// fl(x/d) therefore fall strictly inside the same rounding interval, so
+// round(fl(x/d)) (half away from zero) is trunc(y + copysign(1/2, y)): that
+// sum stays 2^-13 clear of the integers, more than its rounding error.  A
+// wave in which any value comes that close takes the division for its four
+// values instead, so the codes equal q8_rule's for every input.
+__device__ __forceinline__ void q8_rule4(float x0, float x1, float x2, float x3, float d, int8_t q[4]) {
+    const bool zero = d == 0.0f;
+    const float dd = zero ? 1.0f : d;
+    float r = __builtin_amdgcn_rcpf(dd);
+    r = fmaf(fmaf(-dd, r, 1.0f), r, r);
+    const float x[4] = {x0, x1, x2, x3};
+    int k[4];
+    bool close = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float y = x[i] * r;
+        close |= fabsf(__builtin_amdgcn_fractf(y) - 0.5f) <= 0x1p-13f;
+        k[i] = static_cast<int>(fminf(fmaxf(y + copysignf(0.5f, y), -127.0f), 127.0f));
+    }
+    if (__builtin_amdgcn_ballot_w64(close) != 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) k[i] = q8_rule(x[i], d);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) q[i] = static_cast<int8_t>(zero ? 0 : k[i]);
+}
+
 // Four int8 values of lane m (elements 4m..4m+3) -> this lane's dot-order
 // dword, and the block's -8 * sum(q) (both over the 8-lane group).
 __device__ __forceinline__ uint32_t dot_order_word(int8_t q0, int8_t q1, int8_t q2, int8_t q3, int m, int& bias) {
@@ -101,15 +135,19 @@ __device__ __forceinline__ uint32_t dot_order_word(int8_t q0, int8_t q1, int8_t 
 
 __device__ __forceinline__ ActScale quant_act_quad(float x0, float x1, float x2, float x3, int m, uint32_t& word,
                                                    uint32_t& dbits) {
-    float a = fmaxf(fmaxf(fabsf(x0), fabsf(x1)), fmaxf(fabsf(x2), fabsf(x3)));
-    a = fmaxf(a, dpp8_f<kDppXor1>(a));
-    a = fmaxf(a, dpp8_f<kDppXor2>(a));
-    a = fmaxf(a, dpp8_f<kDppMirror8>(a));
-    dbits = float_to_half_bits(a / 127.0f);
+    // amax over the group: non-negative floats order as their bit patterns,
+    // so the cross-lane steps are integer maxima
+    const float a4 = fmaxf(fmaxf(fabsf(x0), fabsf(x1)), fmaxf(fabsf(x2), fabsf(x3)));
+    uint32_t ab = __builtin_bit_cast(uint32_t, a4);
+    ab = max(ab, static_cast<uint32_t>(dpp8_i<kDppXor1>(static_cast<int>(ab))));
+    ab = max(ab, static_cast<uint32_t>(dpp8_i<kDppXor2>(static_cast<int>(ab))));
+    ab = max(ab, static_cast<uint32_t>(dpp8_i<kDppMirror8>(static_cast<int>(ab))));
+    dbits = float_to_half_bits(__builtin_bit_cast(float, ab) / 127.0f);
     const float d = half_bits_to_float(dbits);
-    const int8_t q0 = q8_rule(x0, d), q1 = q8_rule(x1, d), q2 = q8_rule(x2, d), q3 = q8_rule(x3, d);
+    int8_t q[4];
+    q8_rule4(x0, x1, x2, x3, d, q);
     int bias;
-    word = dot_order_word(q0, q1, q2, q3, m, bias);
+    word = dot_order_word(q[0], q[1], q[2], q[3], m, bias);
     return ActScale{d, bias};
 }
 

@@ -118,7 +118,7 @@ def test_quantizers_fp16_scale_sweep(hip, orc):
 def near_half_blocks(seed, N, K):
     """N x K activations whose quotients x / d sit within a few ulps of a
     half-integer, so that the rounding of the binary32 quotient decides each
-    code.  Element 0 of every block is +-127 d, which makes binary16(amax / 127)
+    code.  Element 0 of most blocks is +-127 d, which makes binary16(amax / 127)
     exactly d; d spans normal and subnormal binary16 values; about a third of
     the elements are ordinary values of the block's range."""
     rng = np.random.default_rng(seed)
@@ -133,6 +133,35 @@ def near_half_blocks(seed, N, K):
         x = np.where(-nudge >= step, np.nextafter(x, np.float32(-np.inf)), x)
     plain = (rng.uniform(-126.9, 126.9, (N, nb, 32)) * d[..., None]).astype(np.float32)
     x = np.where(rng.random((N, nb, 32)) < 0.33, plain, x)
+    x[..., 0] = (np.where(rng.random((N, nb)) < 0.5, -127.0, 127.0) * d).astype(np.float32)
+    # A quarter of the blocks: amax / 127 = (m + u) 2^-24 with u < 1/2 rounds
+    # down to the binary16 subnormal d = m 2^-24, so quotients reach 127 (1 + u/m)
+    # (up to ~184, clamped to 127 when rounded), near half-integers up there too.
+    m = rng.integers(1, 24, (N, nb)).astype(np.float64)
+    u = rng.uniform(0.0, 0.45, (N, nb))
+    top = 127.0 * (m + u) / m  # amax / d
+    kk = np.floor(rng.uniform(-1.0, 1.0, (N, nb, 32)) * (top[..., None] - 1.0))
+    xs = ((kk + 0.5) * (m * 2.0 ** -24)[..., None]).astype(np.float32)
+    for step in range(1, 4):
+        xs = np.where(nudge >= step, np.nextafter(xs, np.float32(np.inf)), xs)
+        xs = np.where(-nudge >= step, np.nextafter(xs, np.float32(-np.inf)), xs)
+    xs[..., 0] = (np.where(rng.random((N, nb)) < 0.5, -1.0, 1.0) * top * m * 2.0 ** -24).astype(np.float32)
+    x = np.where((rng.random((N, nb)) < 0.25)[..., None], xs, x)
+    return np.ascontiguousarray(x.reshape(N, K), dtype=np.float32)
+
+
+def margin_blocks(seed, N, K):
+    """N x K activations whose quotients x / d all lie between 2^-12.6 and
+    2^-9 from a half-integer (never closer): the quantizers round these
+    without a division, and a wrong direction would change the code.
+    Element 0 of every block is +-127 d (d exact, as in near_half_blocks)."""
+    rng = np.random.default_rng(seed)
+    nb = K // 32
+    bits = np.where(rng.random((N, nb)) < 0.2, rng.integers(1, 0x400, (N, nb)), rng.integers(0x0400, 0x5BFF, (N, nb)))
+    d = bits.astype(np.uint16).view(np.float16).astype(np.float64)
+    k = rng.integers(-127, 127, (N, nb, 32))
+    off = 2.0 ** rng.uniform(-12.6, -9.0, (N, nb, 32)) * np.where(rng.random((N, nb, 32)) < 0.5, -1.0, 1.0)
+    x = ((k + 0.5 + off) * d[..., None]).astype(np.float32)
     x[..., 0] = (np.where(rng.random((N, nb)) < 0.5, -127.0, 127.0) * d).astype(np.float32)
     return np.ascontiguousarray(x.reshape(N, K), dtype=np.float32)
 
@@ -154,6 +183,8 @@ def unit_code_weights(K):
 def test_quantizer_half_integer_quotients(hip, orc):
     X = near_half_blocks(31, 64, 4096)
     assert np.array_equal(host(hip.q8_0_quantize(dev(X))), orc.q8_0_quantize(X))
+    X = margin_blocks(32, 64, 4096)
+    assert np.array_equal(host(hip.q8_0_quantize(dev(X))), orc.q8_0_quantize(X))
 
 
 @pytest.mark.parametrize("K", [768, 4096, 14336])
@@ -165,9 +196,10 @@ def test_activation_codes_in_every_product_path(hip, orc, K):
     dq = orc.q4_0_dequantize(Wq_o, K)
     assert np.array_equal(dq, np.eye(K, dtype=np.float32))
     Wq = dev(Wq_o)
-    for N in ((1, 8, 9) if K > 4096 else (1, 3, 8, 9, 130)):
-        print("half-integer quotients K=%d N=%d" % (K, N), flush=True)
-        X = near_half_blocks(4000 + K + N, N, K)
+    for N, make in [(n, f) for n in ((1, 8, 9) if K > 4096 else (1, 3, 8, 9, 130))
+                    for f in (near_half_blocks, margin_blocks)]:
+        print("%s K=%d N=%d" % (make.__name__, K, N), flush=True)
+        X = make(4000 + K + N, N, K)
         want = orc.mul_mat_ref(Wq_o, orc.q8_0_quantize(X), K)
         Xt = dev(X)
         got = host(hip.mul_mat_q4_0_q8_0(Wq, Xt)).astype(np.float64)
