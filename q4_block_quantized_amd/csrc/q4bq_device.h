@@ -133,10 +133,13 @@ __device__ __forceinline__ uint32_t dot_order_word(int8_t q0, int8_t q1, int8_t 
     return (m & 1) ? ((other >> 16) | (od << 16)) : (ev | (other << 16));
 }
 
-__device__ __forceinline__ ActScale quant_act_quad(float x0, float x1, float x2, float x3, int m, uint32_t& word,
-                                                   uint32_t& dbits) {
-    // amax over the group: non-negative floats order as their bit patterns,
-    // so the cross-lane steps are integer maxima
+// The Q8_0 rule for one block held by an aligned group of 8 lanes (lane m:
+// elements 4m..4m+3; the whole group active): the block's binary16 scale
+// (bits and value) and this lane's four codes.  amax is taken over the
+// group with integer maxima (non-negative floats order as their bit
+// patterns).
+__device__ __forceinline__ float q8_block_quad(float x0, float x1, float x2, float x3, uint32_t& dbits,
+                                               int8_t q[4]) {
     const float a4 = fmaxf(fmaxf(fabsf(x0), fabsf(x1)), fmaxf(fabsf(x2), fabsf(x3)));
     uint32_t ab = __builtin_bit_cast(uint32_t, a4);
     ab = max(ab, static_cast<uint32_t>(dpp8_i<kDppXor1>(static_cast<int>(ab))));
@@ -144,8 +147,21 @@ __device__ __forceinline__ ActScale quant_act_quad(float x0, float x1, float x2,
     ab = max(ab, static_cast<uint32_t>(dpp8_i<kDppMirror8>(static_cast<int>(ab))));
     dbits = float_to_half_bits(__builtin_bit_cast(float, ab) / 127.0f);
     const float d = half_bits_to_float(dbits);
-    int8_t q[4];
     q8_rule4(x0, x1, x2, x3, d, q);
+    return d;
+}
+
+// The same codes as one dword in element order (byte i: element 4m + i).
+__device__ __forceinline__ uint32_t q8_natural_word(const int8_t q[4]) {
+    return static_cast<uint32_t>(static_cast<uint8_t>(q[0])) | (static_cast<uint32_t>(static_cast<uint8_t>(q[1])) << 8) |
+           (static_cast<uint32_t>(static_cast<uint8_t>(q[2])) << 16) |
+           (static_cast<uint32_t>(static_cast<uint8_t>(q[3])) << 24);
+}
+
+__device__ __forceinline__ ActScale quant_act_quad(float x0, float x1, float x2, float x3, int m, uint32_t& word,
+                                                   uint32_t& dbits) {
+    int8_t q[4];
+    const float d = q8_block_quad(x0, x1, x2, x3, dbits, q);
     int bias;
     word = dot_order_word(q[0], q[1], q[2], q[3], m, bias);
     return ActScale{d, bias};

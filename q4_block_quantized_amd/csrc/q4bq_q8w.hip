@@ -55,14 +55,10 @@ __device__ __forceinline__ Q8Block load_q8_block(const uint8_t* p) {
 // Q8_0 of one block by its 8-lane group: lane m holds elements 4m..4m+3 and
 // gets their four int8 as one dword (element order), plus the block's scale.
 __device__ __forceinline__ uint32_t quant_q8_natural(float x0, float x1, float x2, float x3, float& d) {
-    float a = fmaxf(fmaxf(fabsf(x0), fabsf(x1)), fmaxf(fabsf(x2), fabsf(x3)));
-    a = fmaxf(a, __shfl_xor(a, 1, 8));
-    a = fmaxf(a, __shfl_xor(a, 2, 8));
-    a = fmaxf(a, __shfl_xor(a, 4, 8));
-    d = half_bits_to_float(float_to_half_bits(a / 127.0f));
-    const uint32_t q0 = static_cast<uint8_t>(q8_rule(x0, d)), q1 = static_cast<uint8_t>(q8_rule(x1, d));
-    const uint32_t q2 = static_cast<uint8_t>(q8_rule(x2, d)), q3 = static_cast<uint8_t>(q8_rule(x3, d));
-    return q0 | (q1 << 8) | (q2 << 16) | (q3 << 24);
+    uint32_t dbits;
+    int8_t q[4];
+    d = q8_block_quad(x0, x1, x2, x3, dbits, q);
+    return q8_natural_word(q);
 }
 
 // LDS: NT x nb blocks of 8 dwords (token-major), then NT x nb fp32 scales.
@@ -115,9 +111,21 @@ struct Q8Slot<true> {
     Q8Pair p;
 };
 
-template <int THREADS, int NT, int SPL, int D, bool PAIRED>
+// NTL (pairs, one per lane: rows of at most 128 blocks, a multiple of 8):
+// a wave loads its row as 17 nb / 8 consecutive 16-byte pieces with
+// non-temporal loads -- each instruction one contiguous 1 KB, the lanes past
+// the row re-reading its last piece -- writes them to its own LDS area in
+// order and reads its lane's 68-byte pair back (17 dwords apart per lane: no
+// bank conflicts).  The folds see the same bytes.
+constexpr int kQ8wNtlLoads = 5;  // 17 * 128 / 8 = 272 pieces at most
+__host__ __device__ inline size_t q8w_ntl_offset(int nt, int64_t nb) {
+    return (static_cast<size_t>(nt) * nb * kQ8wActBytes + 15) / 16 * 16;
+}
+
+template <int THREADS, int NT, int SPL, int D, bool PAIRED, bool NTL = false>
 __global__ void __launch_bounds__(THREADS)
 k_q8w_rows(const uint8_t* __restrict__ W, int64_t rows, int nb, const float* __restrict__ X, float* __restrict__ Y) {
+    static_assert(!NTL || (PAIRED && SPL == 1), "contiguous row loads: one pair per lane");
     constexpr int kWaves = THREADS / 64;
     constexpr int kBps = PAIRED ? 2 : 1;              // blocks per slot
     constexpr int BPL = SPL * kBps;
@@ -159,10 +167,39 @@ k_q8w_rows(const uint8_t* __restrict__ W, int64_t rows, int nb, const float* __r
                 dst[i].b = load_q8_block(p);
         }
     };
+    const int npc = 17 * nb / 8;
+    uint8_t* const wrow = smem + q8w_ntl_offset(NT, nb) + static_cast<size_t>(wave) * nb * kQ8Bytes;
+    auto load_row_ntl = [&](u32x4 (&dst)[kQ8wNtlLoads], int64_t k) __attribute__((always_inline)) {
+        typedef u32x4 u32x4_a2 __attribute__((aligned(2)));
+        const int64_t r = min(w0 + k * S, rlast);
+        const uint8_t* base = W + uniform64(r * nb) * kQ8Bytes;
+#pragma unroll
+        for (int i = 0; i < kQ8wNtlLoads; ++i) {
+            const int pc = min(lane + 64 * i, npc - 1);
+            dst[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_a2*>(base + 16 * pc));
+        }
+    };
+    auto unpack_row = [&](const u32x4 (&src)[kQ8wNtlLoads], Q8Slot<PAIRED> (&q)[SPL]) __attribute__((always_inline)) {
+        if constexpr (NTL) {
+#pragma unroll
+            for (int i = 0; i < kQ8wNtlLoads; ++i)
+                if (lane + 64 * i < npc) reinterpret_cast<u32x4*>(wrow)[lane + 64 * i] = src[i];
+            __builtin_amdgcn_wave_barrier();
+            const uint32_t* p = reinterpret_cast<const uint32_t*>(wrow + 2 * kQ8Bytes * ss[0]);
+#pragma unroll
+            for (int j = 0; j < 17; ++j) q[0].p.w[j] = p[j];
+            __builtin_amdgcn_wave_barrier();
+        }
+    };
     Q8Slot<PAIRED> raw[D][SPL];
+    u32x4 rawn[NTL ? D : 1][kQ8wNtlLoads];
+    auto load_next = [&](int d, int64_t k) __attribute__((always_inline)) {
+        if constexpr (NTL) load_row_ntl(rawn[d], k);
+        else load_row(raw[d], k);
+    };
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-        load_row(raw[d], d);
+        load_next(d, d);
         __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -238,11 +275,12 @@ k_q8w_rows(const uint8_t* __restrict__ W, int64_t rows, int nb, const float* __r
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             float part[NT];
+            if constexpr (NTL) unpack_row(rawn[d], raw[d]);
             fold(raw[d], part);
             const float t = wave_sums<NT>(part, lane);
             if (k + d < nk && my_token >= 0 && my_token < NT)
                 Y[static_cast<int64_t>(my_token) * rows + w0 + (k + d) * S] = t;
-            load_row(raw[d], k + d + D);
+            load_next(d, k + d + D);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -275,15 +313,31 @@ hipError_t launch_q8w_k(const DeviceInfo* dev, const uint8_t* W, int64_t rows, i
     constexpr int BPL = SPL * (PAIRED ? 2 : 1);
     constexpr int kThreads = q8w_threads<BPL>(NT);
     constexpr int kDepth = BPL <= 2 ? 2 : 1;
-    const auto kernel = k_q8w_rows<kThreads, NT, SPL, kDepth, PAIRED>;
     int64_t wgs = (rows + kThreads / 64 - 1) / (kThreads / 64);
     const int64_t cap = static_cast<int64_t>(dev->num_cu) * (1024 / kThreads);
     if (wgs > cap) wgs = cap;
-    const size_t lds = static_cast<size_t>(NT) * nb * kQ8wActBytes;
+    // contiguous non-temporal row loads where rows are whole 16-byte pieces
+    // and every wave has 16 rows or more (as for the Q4_0 row kernel), up to
+    // four tokens (measured, graph-timed, 128256 x 4096: N = 1 99.6 -> 88.8
+    // us, N = 4 113.5 -> 98.3 us; at N = 8, where the vector ALU bounds the
+    // 512-thread kernel, the LDS pass costs more than it saves: 153.6 ->
+    // 165.9 us)
+    constexpr bool kNtlForm = PAIRED && SPL == 1 && kThreads == 1024;
+    const size_t ntl_lds = q8w_ntl_offset(NT, nb) + static_cast<size_t>(kThreads / 64) * nb * kQ8Bytes;
+    const bool ntl = kNtlForm && nb % 8 == 0 && rows >= 16 * wgs * (kThreads / 64) && ntl_lds <= kRowsMaxLds;
+    const auto plain = k_q8w_rows<kThreads, NT, SPL, kDepth, PAIRED>;
+    const auto contiguous = k_q8w_rows<kThreads, NT, SPL, kDepth, PAIRED, kNtlForm>;
+    const auto kernel = ntl ? contiguous : plain;
+    const size_t lds = ntl ? ntl_lds : static_cast<size_t>(NT) * nb * kQ8wActBytes;
     if (lds > 64 * 1024) {
-        static const hipError_t raised = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                             static_cast<int>(kRowsMaxLds));
+        static const hipError_t raised = [&] {
+            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(plain),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kRowsMaxLds));
+            if (e == hipSuccess)
+                e = hipFuncSetAttribute(reinterpret_cast<const void*>(contiguous),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kRowsMaxLds));
+            return e;
+        }();
         if (raised != hipSuccess) return raised;
     }
     hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(wgs)), dim3(kThreads), lds, s, W, rows,

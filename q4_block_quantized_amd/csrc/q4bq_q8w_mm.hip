@@ -267,15 +267,10 @@ k_act8_from_f32(const float* __restrict__ X, int64_t N, int64_t nb, uint8_t* __r
             const bool valid = n < N;
             float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
             if (valid) __builtin_memcpy(&x, X + (n * nb + b) * kQK + 4 * m, 16);
-            float a = fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w)));
-            a = fmaxf(a, dpp8_f<kDppXor1>(a));
-            a = fmaxf(a, dpp8_f<kDppXor2>(a));
-            a = fmaxf(a, dpp8_f<kDppMirror8>(a));
-            const uint32_t dbits = float_to_half_bits(a / 127.0f);
-            const float d = half_bits_to_float(dbits);
-            const uint32_t q = static_cast<uint8_t>(q8_rule(x.x, d)) | (static_cast<uint32_t>(static_cast<uint8_t>(q8_rule(x.y, d))) << 8) |
-                               (static_cast<uint32_t>(static_cast<uint8_t>(q8_rule(x.z, d))) << 16) |
-                               (static_cast<uint32_t>(static_cast<uint8_t>(q8_rule(x.w, d))) << 24);
+            uint32_t dbits;
+            int8_t qq[4];
+            q8_block_quad(x.x, x.y, x.z, x.w, dbits, qq);
+            const uint32_t q = q8_natural_word(qq);
             if (valid) {
                 codes[(b * N + n) * 8 + m] = q;
                 if (m == 0) scales[b * N + n] = static_cast<uint16_t>(dbits);

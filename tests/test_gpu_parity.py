@@ -667,6 +667,29 @@ def test_q8w_full_size(hip, orc, rows, K):
         assert_close(Y[:, sample], orc.mul_mat_q8_ref(Ws, orc.q8_0_quantize(X[:N]), K), "q8w full N=%d" % N)
 
 
+@pytest.mark.parametrize("rows,K,Ns", [(66000, 3072, (1, 2, 4, 8)), (70000, 4096, (1, 3, 8))])
+def test_q8w_long_matrices_contiguous_row_loads(hip, orc, rows, K, Ns):
+    """Q8_0 weights on matrices long enough for the contiguous row loads (16
+    rows per wave or more): sampled rows against the oracle, and every row of
+    a 20000-row prefix bit for bit against the product on that prefix alone
+    (too few rows for that form: each lane loads its own blocks; the folds are
+    the same)."""
+    W, X = _case(rows, K, max(Ns), 4600 + rows)
+    Wq8 = hip.q8_0_quantize(dev(W))
+    sample = _sample_rows(rows, 200, 4601 + rows)
+    Ws = orc.q8_0_quantize(W[sample])
+    assert np.array_equal(host(Wq8)[sample], Ws.reshape(len(sample), -1))
+    del W
+    head = 20000
+    for N in Ns:
+        print("q8w contiguous row loads rows=%d K=%d N=%d" % (rows, K, N), flush=True)
+        Xn = dev(X[:N])
+        Y = host(hip.mul_mat_q8_0_q8_0(Wq8, Xn))
+        assert_close(Y[:, sample], orc.mul_mat_q8_ref(Ws, orc.q8_0_quantize(X[:N]), K), "q8w long N=%d" % N)
+        Yh = host(hip.mul_mat_q8_0_q8_0(Wq8[:head], Xn))
+        assert np.array_equal(Y[:, :head], Yh), ("prefix", rows, K, N)
+
+
 @pytest.mark.parametrize("K", [32, 96, 160, 4096, 4128])
 def test_q8w_many_tokens(hip, orc, K):
     """More than eight tokens (the int8 matrix-core kernel): ragged row and token
