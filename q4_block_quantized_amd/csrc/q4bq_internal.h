@@ -197,8 +197,9 @@ hipError_t launch_rows_act(const DeviceInfo* dev, int lay, const uint8_t* Wq, in
 // v_mfma_i32_32x32x32_i8 per 32-row tile and block, for the shapes where
 // mma_apply (up to kGemvMaxN tokens, at least kMmaMinRows rows, even block
 // counts up to kMmaMaxBlocks; from kMmaMinN tokens, or on matrices of
-// kMmaLongRows rows and more from kMmaLongMinN tokens with contiguous loads,
-// kMmaLongMinNPairs with lane loads).  src is fp32 X (src_f32) or the
+// kMmaLongRows rows and more from kMmaLongMinN tokens with contiguous loads
+// -- kMmaMinN where the row kernel loads rows whole --, kMmaLongMinNPairs
+// with lane loads).  src is fp32 X (src_f32) or the
 // quantizer's buffer; `lay` a DecodeLayout; md.epi applies at the store
 // (single matrix).
 constexpr int kMmaThreads = 1024;
@@ -208,6 +209,7 @@ constexpr int64_t kMmaMaxBlocks = 256;
 constexpr int64_t kMmaLongRows = 32768;
 constexpr int64_t kMmaLongMinN = 4;
 constexpr int64_t kMmaLongMinNPairs = 7;
+constexpr int64_t kMmaRowsContiguousRows = 65536;  // below: kMmaLongMinN even where the row kernel loads rows whole
 // md: the multi-matrix form's table (its matrices must start on 32-row
 // boundaries), else nullptr.
 bool mma_apply(int64_t N, int64_t nb, int64_t rows, const MultiDesc* md = nullptr);

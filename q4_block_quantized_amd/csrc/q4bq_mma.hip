@@ -715,13 +715,18 @@ bool mma_apply(int64_t N, int64_t nb, int64_t rows, const MultiDesc* md) {
     // Llama-3-8B, GPT-2 and vocabulary-head shapes): the matrix cores win from
     // five tokens on matrices of at least 2048 rows and K <= 8192; on the
     // longest matrices the row kernel streams at nearly full rate up to three
-    // tokens (the vocabulary head at N = 4: 64.3 us against 62.6 on the
-    // contiguous-load kernel), up to six against the lane-load kernel; fewer
-    // rows leave CUs idle (one workgroup per 32 rows), longer rows put most of
-    // the time into the per-workgroup activation copy
+    // tokens, up to six against the lane-load kernel, and up to four where it
+    // loads whole rows contiguously (one pair per lane, 16 rows per wave on a
+    // full chip: the vocabulary head at N = 4 58.5 us against 61.2 on the
+    // contiguous-load matrix-core kernel, 66000 x 3072 30.4 against 31.1);
+    // fewer rows leave CUs idle (one workgroup per 32 rows), longer rows put
+    // most of the time into the per-workgroup activation copy
     if (N > kGemvMaxN || nb % 2 != 0 || nb > kMmaMaxBlocks || rows < kMmaMinRows) return false;
     if (mma_lds_bytes<kMmaThreads>(N, nb) > kMmaMaxLds) return false;
-    const int64_t min_n = rows < kMmaLongRows ? kMmaMinN : (mma_tr_takes(N, nb) ? kMmaLongMinN : kMmaLongMinNPairs);
+    const bool rows_contiguous = rows >= kMmaRowsContiguousRows && rows_fuse_prologue(nb, rows) && (nb / 2) % 4 == 0;
+    const int64_t min_n = rows < kMmaLongRows ? kMmaMinN
+                          : mma_tr_takes(N, nb) ? (rows_contiguous ? kMmaMinN : kMmaLongMinN)
+                                                : kMmaLongMinNPairs;
     return N >= min_n;
 }
 
