@@ -705,6 +705,169 @@ k_gemv_mma_tr(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* 
     }
 }
 
+// ---------------------------------------------------------------------------
+// The same product with whole tiles loaded contiguously (`k_gemv_mma_tile`:
+// the pages' blocks, 64..128 blocks a row in whole chunks of 8, many tiles
+// per workgroup).  A tile's 32 rows are one contiguous run of 32 * 18 nb
+// bytes: thread t of the workgroup loads its 16-byte pieces t, t + 1024, ...
+// (each instruction of a wave one contiguous 1 KB, every cache line whole),
+// and the workgroup writes them into one LDS tile whose rows are TS bytes
+// apart (TS / 16 odd: the 16-byte reads of 16 consecutive rows hit 16
+// distinct bank groups).  After a barrier every wave reads its chunks
+// (32 rows x 144 bytes) from there, as `k_gemv_mma_tr` reads its own item,
+// while the next tiles' loads are in flight (D tiles per workgroup); a
+// second barrier, after the partial sums, frees the tile for the next one.
+// Same chunks per wave, same steps in the same order: the same bits as
+// `k_gemv_mma_tr`.  Measured (graph-timed, workspace form): the vocabulary
+// head at N = 5 / 8 61.8 / 63.5 -> 61.2 / 62.6 us, 66000 x 3072 30.6 / 31.6 ->
+// 29.3 / 29.9 us; without the matrix-core work the head still takes 56-57 us:
+// every wave waits at the two barriers for the slowest wave's pieces, so
+// the loads leave in bursts (a second LDS tile that would drop one barrier
+// does not fit beside the activations).
+constexpr int kTlThreads = 1024;
+constexpr int kTlMaxBlocks = 128;
+constexpr int kTlLoads = (36 * kTlMaxBlocks + kTlThreads - 1) / kTlThreads;  // 5: a tile is 36 nb pieces
+__host__ __device__ inline int64_t mma_tile_stride(int64_t nb) {
+    const int64_t p = nb * kQ4Bytes / 16;  // pieces a row
+    return 16 * (p + 1 + (p & 1));
+}
+template <int THREADS>
+inline int64_t mma_tile_lds_bytes(int64_t N, int64_t nb) {
+    return mma_lds_bytes<THREADS>(N, nb) + 32 * mma_tile_stride(nb);
+}
+// Many tiles per workgroup (the pipeline fills), rows of 64..128 blocks.
+inline bool mma_tile_takes(int64_t N, int64_t nb, int64_t ntiles, int64_t grid) {
+    return nb % kTrBlocks == 0 && nb >= 8 * kTrBlocks && nb <= kTlMaxBlocks && ntiles >= 8 * grid &&
+           mma_tile_lds_bytes<kTlThreads>(N, nb) <= kMmaMaxLds;
+}
+
+template <int THREADS, int D, int SRC, int LAY, bool EPI>
+__global__ void __launch_bounds__(THREADS)
+k_gemv_mma_tile(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* __restrict__ src, int N,
+                float* __restrict__ Y, const MultiDesc md) {
+    static_assert(SRC == kXF32 || SRC == kActGlobal, "activation source");
+    static_assert(LAY == kLayAoS || LAY == kLayMulti, "the pages' blocks");
+    static_assert(THREADS == kTlThreads, "a tile's pieces per thread");
+    constexpr bool MULTI = LAY == kLayMulti;
+    constexpr int kWaves = THREADS / 64;
+    extern __shared__ __align__(16) uint8_t smem[];
+    const MmaLds L = mma_lds<THREADS>(smem, N, nb);
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int l32 = lane & 31, h = lane >> 5;
+    const int TS = static_cast<int>(mma_tile_stride(nb));
+    uint8_t* const tile = reinterpret_cast<uint8_t*>(L.part + 2 * kWaves * 4 * 64);
+    const int nc = nb / kTrBlocks;  // chunks per row
+    const int64_t G = gridDim.x;
+    const int64_t ntiles = (rows + 31) >> 5;
+    const int64_t ntq = blockIdx.x < ntiles ? (ntiles - 1 - blockIdx.x) / G + 1 : 0;
+    const int rowbytes = nb * kQ4Bytes;
+    const int tpieces = 2 * rowbytes;  // 32 rows of rowbytes / 16 pieces
+
+    // this thread's pieces of a tile: byte offset in the tile's run (loads
+    // past the tile read nothing) and in the LDS tile
+    uint32_t loff[kTlLoads];
+#pragma unroll
+    for (int i = 0; i < kTlLoads; ++i) {
+        const int p = static_cast<int>(threadIdx.x) + THREADS * i;
+        const int row = p / (rowbytes / 16), pc = p - row * (rowbytes / 16);
+        loff[i] = static_cast<uint32_t>(row * TS + pc * 16);
+    }
+    // tile k of this workgroup into dst (a buffer resource over the tile's
+    // rows: zero bytes past the last row, or for k >= ntq)
+    auto load_tile = [&](u32x4 (&dst)[kTlLoads], int64_t k) __attribute__((always_inline)) {
+        const int64_t r0 = (static_cast<int64_t>(blockIdx.x) + k * G) * 32;
+        const int64_t nr = k < ntq ? min(static_cast<int64_t>(32), rows - r0) : 0;
+        const uint8_t* wb = Wq;
+        int64_t f = 0;
+        if constexpr (MULTI) {
+            wb = md.w[0];
+#pragma unroll
+            for (int m = 1; m < kMaxMulti; ++m)
+                if (m < md.count && r0 >= md.first[m]) {
+                    wb = md.w[m];
+                    f = md.first[m];
+                }
+        }
+        const uint8_t* base = wb + (nr > 0 ? (r0 - f) * rowbytes : 0);
+        const auto rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), static_cast<short>(0),
+                                                           static_cast<int>(nr * rowbytes), kRsrcFlags);
+#pragma unroll
+        for (int i = 0; i < kTlLoads; ++i)
+            dst[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   rw, 16 * (static_cast<int>(threadIdx.x) + THREADS * i), 0, 0));
+    };
+    u32x4 raw[D][kTlLoads];
+    auto prefetch = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            load_tile(raw[d], d);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    mma_stage_activations<THREADS, SRC>(src, N, nb, L, prefetch);
+
+    if (ntq == 0) return;  // the whole workgroup: no rows
+
+    const int a_tok = min(lane & 7, N - 1);
+    const int a_half = h ^ ((lane >> 3) & 1);
+    const uint8_t* a_base = L.a + a_tok * L.S + 16 * a_half;
+
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    int buf = 0;
+    for (int64_t k = 0; k < ntq; k += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            if (k + d >= ntq) break;  // (uniform)
+            // tile k + d into LDS, then its registers take tile k + d + D
+#pragma unroll
+            for (int i = 0; i < kTlLoads; ++i)
+                if (static_cast<int>(threadIdx.x) + THREADS * i < tpieces)
+                    *reinterpret_cast<u32x4*>(tile + loff[i]) = raw[d][i];
+            lds_barrier();
+            load_tile(raw[d], k + d + D);
+            __builtin_amdgcn_sched_barrier(0);
+            for (int c = wave; c < nc; c += kWaves) {
+                const u32x4* rp = reinterpret_cast<const u32x4*>(tile + l32 * TS + c * kTrRowBytes);
+#pragma unroll
+                for (int g = 0; g < 2; ++g) {
+                    uint32_t w0[4], w1[4], dd[4];
+                    uint32_t win[20];
+#pragma unroll
+                    for (int m = 0; m < 5; ++m) {
+                        const u32x4 v = rp[4 * g + m];
+                        win[4 * m] = v.x; win[4 * m + 1] = v.y; win[4 * m + 2] = v.z; win[4 * m + 3] = v.w;
+                    }
+                    auto sel = [&](int q) __attribute__((always_inline)) { return h ? win[q + 2] : win[q]; };
+                    const int o = 2 * g;
+                    w0[0] = __builtin_amdgcn_alignbit(sel(o + 1), sel(o), 16);
+                    w1[0] = __builtin_amdgcn_alignbit(sel(o + 2), sel(o + 1), 16);
+                    w0[1] = sel(o + 5);
+                    w1[1] = sel(o + 6);
+                    w0[2] = __builtin_amdgcn_alignbit(sel(o + 10), sel(o + 9), 16);
+                    w1[2] = __builtin_amdgcn_alignbit(sel(o + 11), sel(o + 10), 16);
+                    w0[3] = sel(o + 14);
+                    w1[3] = sel(o + 15);
+                    dd[0] = win[o] & 0xFFFFu; dd[1] = win[o + 4] >> 16;
+                    dd[2] = win[o + 9] & 0xFFFFu; dd[3] = win[o + 13] >> 16;
+                    const int b0 = kTrBlocks * c + 4 * g;
+                    const uint8_t* ab = a_base + b0 * kActQBytes;
+                    const int pb = b0 * kMmaSlots + 4 * h;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        mma_block(L, ab + i * kActQBytes, pb + i * kMmaSlots, w0[i], w1[i], dd[i], acc);
+                }
+            }
+            mma_put_partials<kWaves>(L, buf, wave, lane, acc);
+            lds_barrier();
+            mma_store_tile<kWaves, MULTI, EPI>(L, buf, (static_cast<int64_t>(blockIdx.x) + (k + d) * G) * 32, rows,
+                                               N, Y, md);
+            buf ^= 1;
+        }
+    }
+}
+
 }  // namespace
 
 bool mma_apply(int64_t N, int64_t nb, int64_t rows, const MultiDesc* md) {
@@ -738,8 +901,19 @@ hipError_t launch_mma_k(const DeviceInfo* dev, const uint8_t* Wq, int64_t rows, 
     const int64_t ntiles = (rows + 31) / 32;
     const int64_t grid = ntiles < dev->num_cu ? ntiles : dev->num_cu;
     {
-        // one wave per tile where that still gives (nearly) every CU a round
-        // of 16 tiles, else 16 waves per tile
+        if constexpr (LAY != kLayRepacked) {
+            if (mma_tile_takes(N, nb, ntiles, grid)) {
+                constexpr int kTlD = 1;  // tiles in flight per workgroup (two: 1-3 % slower)
+                const size_t lds = static_cast<size_t>(mma_tile_lds_bytes<kTlThreads>(N, nb));
+                const auto kernel = k_gemv_mma_tile<kTlThreads, kTlD, SRC, LAY, EPI>;
+                const hipError_t raised = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                                              hipFuncAttributeMaxDynamicSharedMemorySize, kMmaMaxLds);
+                if (raised != hipSuccess) return raised;
+                hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(grid)), dim3(kTlThreads), lds, s, Wq, rows,
+                                   static_cast<int>(nb), src, static_cast<int>(N), Y, md);
+                return hipGetLastError();
+            }
+        }
         if (mma_tr_takes(N, nb)) {
             constexpr int kTrD = 2;  // items in flight per wave
             const size_t lds = static_cast<size_t>(mma_tr_lds_bytes<kTrThreads>(N, nb));

@@ -406,6 +406,35 @@ def test_long_matrices_contiguous_row_loads(hip, orc, rows, K, Ns):
             assert np.array_equal(np.concatenate([host(Ys[0]), host(Ys[1])], axis=1), Y), (rows, K, N)
 
 
+@pytest.mark.parametrize("rows,K,Ns", [(66001, 4096, (5, 8)), (70000, 3072, (6,)), (68000, 2048, (4, 7))])
+def test_matrix_core_whole_tiles(hip, orc, rows, K, Ns):
+    """Matrix-core decode with 8 tiles of 32 rows or more per workgroup: the
+    workgroup loads each tile as one contiguous run into an LDS tile (rows of
+    64, 96 and 128 blocks; a ragged last tile).  Sampled rows against the
+    oracle; bit for bit against the per-wave item kernel (a 40000-row prefix:
+    too few tiles for this form), the repacked weights, the pre-quantized
+    input and a caller's workspace; the multi-matrix form over two halves
+    against the single call."""
+    head = 40000
+    for N in Ns:
+        print("whole-tile matrix-core decode rows=%d K=%d N=%d" % (rows, K, N), flush=True)
+        W, X = _case(rows, K, N, 9500 + rows + K + N)
+        sample = _sample_rows(rows, 1500, 9501 + rows + N)
+        Wq_o, Xq_o = orc.q4_0_quantize(W[sample]), orc.q8_0_quantize(X)
+        Wq = hip.q4_0_quantize(dev(W))
+        del W
+        Xt = dev(X)
+        Y = host(hip.mul_mat_q4_0_q8_0(Wq, Xt))
+        assert_close(Y[:, sample], orc.mul_mat_ref(Wq_o, Xq_o, K), "rows=%d K=%d N=%d" % (rows, K, N))
+        assert np.array_equal(host(hip.mul_mat_q4_0_q8_0(Wq[:head], Xt)), Y[:, :head]), ("prefix", rows, K, N)
+        assert np.array_equal(host(hip.mul_mat_q4_0r_q8_0(hip.q4_0_repack(Wq, K), Xt)), Y), (rows, K, N)
+        assert np.array_equal(host(hip.mul_mat_q4_0_q8_0_pq(Wq, hip.q8_0_quantize(Xt), K)), Y), (rows, K, N)
+        assert np.array_equal(host(hip.mul_mat_q4_0_q8_0_ex(Wq, Xt, hip.workspace(rows, K, N))), Y), (rows, K, N)
+        half = rows // 2 // 32 * 32
+        Ys = hip.mul_mat_q4_0_q8_0_multi([Wq[:half], Wq[half:]], Xt)
+        assert np.array_equal(np.concatenate([host(Ys[0]), host(Ys[1])], axis=1), Y), ("multi", rows, K, N)
+
+
 SET_CASES = [
     ("gpt2_layer", [(2304, 768), (768, 768), (3072, 768), (768, 3072)], True),
     ("llama3_8b_decode", [(4096, 4096), (14336, 4096), (4096, 14336)], True),
