@@ -40,7 +40,7 @@ ROTATE_BYTES = 1 << 30
 # kernel change.
 TRAFFIC_BYTES = {
     ("llama3_8b_head", 1): 300651896,      # profiles/k_gemv_rows_fused_vocab_head_128256x4096_N1.md
-    ("llama3_8b_head", 8): 300090508,      # profiles/k_gemv_mma_tr_vocab_head_128256x4096_N8.md (k_gemv_mma_tr)
+    ("llama3_8b_head", 8): 300048299,      # profiles/k_gemv_mma_tile_vocab_head_128256x4096_N8.md (k_gemv_mma_tile)
     ("llama3_8b_prefill", 512): 98299615,   # profiles/k_prefill_14336x4096_N512.md
     ("llama3_8b_prefill_repacked", 512): 122591664,  # profiles/k_prefill_repacked_14336x4096_N512.md
     ("q8_0_weights_prefill", 512): 109785279,         # profiles/k_q8w_mm_q8_0_weights_prefill_14336x4096_N512.md
