@@ -710,7 +710,8 @@ k_gemv_mma_tr(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* 
 // the pages' blocks, 64..128 blocks a row in whole chunks of 8, many tiles
 // per workgroup).  A tile's 32 rows are one contiguous run of 32 * 18 nb
 // bytes: thread t of the workgroup loads its 16-byte pieces t, t + 1024, ...
-// (each instruction of a wave one contiguous 1 KB, every cache line whole),
+// with non-temporal loads (each instruction of a wave one contiguous 1 KB,
+// every cache line whole),
 // and the workgroup writes them into one LDS tile whose rows are TS bytes
 // apart (TS / 16 odd: the 16-byte reads of 16 consecutive rows hit 16
 // distinct bank groups).  After a barrier every wave reads its chunks
@@ -719,11 +720,11 @@ k_gemv_mma_tr(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void* 
 // second barrier, after the partial sums, frees the tile for the next one.
 // Same chunks per wave, same steps in the same order: the same bits as
 // `k_gemv_mma_tr`.  Measured (graph-timed, workspace form): the vocabulary
-// head at N = 5 / 8 61.8 / 63.5 -> 61.2 / 62.6 us, 66000 x 3072 30.6 / 31.6 ->
-// 29.3 / 29.9 us; without the matrix-core work the head still takes 56-57 us:
-// every wave waits at the two barriers for the slowest wave's pieces, so
-// the loads leave in bursts (a second LDS tile that would drop one barrier
-// does not fit beside the activations).
+// head at N = 5 / 8 61.8 / 63.5 -> 61.2 / 62.6 us with plain loads, another
+// 5 % off with non-temporal ones (59.9 / 61.4 -> 57.0 / 57.9 us in one run);
+// 66000 x 3072 at N = 8 31.6 -> 27.5 us.  Without the matrix-core work the
+// head takes 52 us, with or without the barriers: the loads set the floor.
+constexpr int kNonTemporal = 2;  // buffer load cache policy: nt (whole lines streamed once)
 constexpr int kTlThreads = 1024;
 constexpr int kTlMaxBlocks = 128;
 constexpr int kTlLoads = (36 * kTlMaxBlocks + kTlThreads - 1) / kTlThreads;  // 5: a tile is 36 nb pieces
@@ -796,7 +797,8 @@ k_gemv_mma_tile(const uint8_t* __restrict__ Wq, int64_t rows, int nb, const void
 #pragma unroll
         for (int i = 0; i < kTlLoads; ++i)
             dst[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                   rw, 16 * (static_cast<int>(threadIdx.x) + THREADS * i), 0, 0));
+                                                   rw, 16 * (static_cast<int>(threadIdx.x) + THREADS * i), 0,
+                                                   kNonTemporal));
     };
     u32x4 raw[D][kTlLoads];
     auto prefetch = [&]() __attribute__((always_inline)) {
