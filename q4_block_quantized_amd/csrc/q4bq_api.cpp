@@ -41,6 +41,22 @@ bool too_big(int64_t a, int64_t b, int64_t bytes_per) {
     return v >= 4.0e18;
 }
 
+// A few more tokens than the decode kernels take at once run as groups of up
+// to kGemvMaxN through the decode path, where the row-streaming or the
+// matrix-core decode kernel takes the shape: the prefill kernel's workgroup
+// always computes 224 rows x 128 tokens over all of K, so below a few dozen
+// tokens most of its work is padding, and matrices of few row tiles leave CUs
+// idle.  Measured (graph-timed, workspace form), prefill -> groups: 14336 x
+// 4096 at N = 9 / 32 86.4 / 87.6 -> 22.1 / 50.8 us; 4096 x 14336 278 / 279 ->
+// 65 / 215 us; the 128256 x 4096 head 255 / 259 -> 105 / 233 us; 2304 x 768
+// 23.8 / 24.7 -> 9.8 / 24.5 us.
+constexpr int64_t kDecodeGroupsMaxN = 32;
+constexpr int64_t kQ8wGroupsMaxN = 32;
+constexpr int64_t kQ8wGroupsLongRows = 65536;
+bool decode_groups_pay(int64_t N, int64_t nb, int64_t rows) {
+    return N <= kDecodeGroupsMaxN && (rows_apply(kGemvMaxN, nb, rows) || mma_apply(kGemvMaxN, nb, rows));
+}
+
 int run_product(WLayout lay, const uint8_t* Wq, int64_t rows, int64_t K, const float* X, const uint8_t* Xq,
                 int64_t N, float* Y, int32_t* D, void* ws, hipStream_t s) {
     hipError_t err = hipSuccess;
@@ -51,6 +67,17 @@ int run_product(WLayout lay, const uint8_t* Wq, int64_t rows, int64_t K, const f
     // passes none in exactly that case)
     if (X && !D && (ws ? gemv_prefers_fused(N, nb, rows) : gemv_fuses(N, nb, rows)))
         return status_of(launch_gemv_fused(dev, lay, Wq, rows, nb, X, N, Y, s));
+    if (N > kGemvMaxN && !D && decode_groups_pay(N, nb, rows)) {
+        // up to kGemvMaxN tokens at a time through the decode path: token n0's
+        // inputs and outputs start n0 rows into X (Xq) and Y
+        for (int64_t n0 = 0; n0 < N; n0 += kGemvMaxN) {
+            const int64_t g = N - n0 < kGemvMaxN ? N - n0 : kGemvMaxN;
+            const int rc = run_product(lay, Wq, rows, K, X ? X + n0 * K : nullptr,
+                                       Xq ? Xq + n0 * nb * kQ8Bytes : nullptr, g, Y + n0 * rows, nullptr, ws, s);
+            if (rc != Q4BQ_OK) return rc;
+        }
+        return Q4BQ_OK;
+    }
     err = X ? launch_act_from_f32(X, N, nb, ws, s) : launch_act_from_q8(Xq, N, nb, ws, s);
     if (err != hipSuccess) return Q4BQ_EHIP;
     if (N <= kGemvMaxN)
@@ -281,23 +308,39 @@ int mul_mat_q4_0_q8_0_multi(int count, const void* const* Wq, const int64_t* row
     if (!dev) return Q4BQ_EHIP;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t total = md.first[count];
-    if (N <= kGemvMaxN && (workspace ? gemv_prefers_fused(N, nb, total, &md) : gemv_fuses(N, nb, total, &md)))
-        return status_of(launch_gemv_multi(dev, md, nb, X, nullptr, N, s));
+    auto fuses = [&](int64_t n, const MultiDesc& m) {
+        return n <= kGemvMaxN && (workspace ? gemv_prefers_fused(n, nb, total, &m) : gemv_fuses(n, nb, total, &m));
+    };
+    // more tokens than one decode launch takes: groups of up to kGemvMaxN
+    // (as in run_product), each on its rows of X and of every Y
+    const bool groups = N > kGemvMaxN && decode_groups_pay(N, nb, total);
+    const int64_t step = groups ? kGemvMaxN : N;
+    bool need_ws = false;
+    for (int64_t n0 = 0; n0 < N; n0 += step) need_ws = need_ws || !fuses(N - n0 < step ? N - n0 : step, md);
     void* ws = workspace;
-    if (!ws && (hipMallocAsync(&ws, need, s) != hipSuccess || ws == nullptr)) {
+    if (need_ws && !ws && (hipMallocAsync(&ws, need, s) != hipSuccess || ws == nullptr)) {
         (void)hipGetLastError();
         return Q4BQ_ENOMEM;
     }
-    err = launch_act_from_f32(X, N, nb, ws, s);
-    if (err == hipSuccess) {
-        if (N <= kGemvMaxN) {
-            err = launch_gemv_multi(dev, md, nb, nullptr, ws, N, s);
+    for (int64_t n0 = 0; n0 < N && err == hipSuccess; n0 += step) {
+        const int64_t g = N - n0 < step ? N - n0 : step;
+        MultiDesc mg = md;
+        for (int i = 0; i < count; ++i) mg.y[i] = Y[i] + n0 * rows[i];
+        const float* Xg = X + n0 * K;
+        if (fuses(g, mg)) {
+            err = launch_gemv_multi(dev, mg, nb, Xg, nullptr, g, s);
+            continue;
+        }
+        err = launch_act_from_f32(Xg, g, nb, ws, s);
+        if (err != hipSuccess) break;
+        if (g <= kGemvMaxN) {
+            err = launch_gemv_multi(dev, mg, nb, nullptr, ws, g, s);
         } else {
             for (int i = 0; i < count && err == hipSuccess; ++i)
-                err = launch_prefill(dev, kAoS, md.w[i], rows[i], nb, ws, N, md.y[i], nullptr, s);
+                err = launch_prefill(dev, kAoS, mg.w[i], rows[i], nb, ws, g, mg.y[i], nullptr, s);
         }
     }
-    if (!workspace && hipFreeAsync(ws, s) != hipSuccess) return Q4BQ_EHIP;
+    if (need_ws && !workspace && hipFreeAsync(ws, s) != hipSuccess) return Q4BQ_EHIP;
     return status_of(err);
 }
 
@@ -421,14 +464,25 @@ int run_fused(int count, const uint8_t* const* Wq, int64_t rows, int64_t K, cons
         (void)hipGetLastError();
         return Q4BQ_ENOMEM;
     }
-    if (ln_gamma) {
-        err = launch_ln_act(X, N, nb, ln_gamma, ln_beta, ln_eps, ws, s);
-    } else {
-        err = launch_act_from_f32(X, N, nb, ws, s);
+    // more tokens than one decode launch takes: groups of up to kGemvMaxN
+    // (as in run_product), each on its rows of X, Y and the factor
+    const int64_t step = N > kGemvMaxN && decode_groups_pay(N, nb, rows) ? kGemvMaxN : N;
+    for (int64_t n0 = 0; n0 < N && err == hipSuccess; n0 += step) {
+        const int64_t g = N - n0 < step ? N - n0 : step;
+        const float* Xg = X + n0 * K;
+        if (ln_gamma) {
+            err = launch_ln_act(Xg, g, nb, ln_gamma, ln_beta, ln_eps, ws, s);
+        } else {
+            err = launch_act_from_f32(Xg, g, nb, ws, s);
+        }
+        for (int i = 0; i < count && err == hipSuccess; ++i) {
+            Epilogue e = epi[i];
+            if (e.mul) e.mul += n0 * rows;
+            float* Yg = Y[i] + n0 * rows;
+            err = g <= kGemvMaxN ? launch_gemv(dev, kAoS, Wq[i], rows, nb, ws, g, Yg, nullptr, s, e)
+                                 : launch_prefill(dev, kAoS, Wq[i], rows, nb, ws, g, Yg, nullptr, s, e);
+        }
     }
-    for (int i = 0; i < count && err == hipSuccess; ++i)
-        err = N <= kGemvMaxN ? launch_gemv(dev, kAoS, Wq[i], rows, nb, ws, N, Y[i], nullptr, s, epi[i])
-                             : launch_prefill(dev, kAoS, Wq[i], rows, nb, ws, N, Y[i], nullptr, s, epi[i]);
     const hipError_t ferr = workspace ? hipSuccess : hipFreeAsync(ws, s);
     if (err != hipSuccess) return Q4BQ_EHIP;
     return ferr == hipSuccess ? Q4BQ_OK : Q4BQ_EHIP;
@@ -543,7 +597,14 @@ int mul_mat_q8_0_q8_0(const void* Wq8, int64_t rows, int64_t K, const float* X, 
     if (!Wq8 || !X || !Y || bad_dim(rows) || bad_dim(N) || bad_k(K)) return Q4BQ_EINVAL;
     const int64_t nb = K / kQK;
     if (!q8w_supported_k(nb) || too_big(rows, K, 2) || too_big(N, K, 4) || too_big(N, rows, 4)) return Q4BQ_EINVAL;
-    if (N > kGemvMaxN && !q8w_mm_grid_ok(rows, N)) return Q4BQ_EINVAL;
+    // a few more tokens than one decode launch takes: groups of up to 8 on the
+    // row kernel rather than the matrix-core kernel, whose workgroups cover 128
+    // tokens (measured, graph-timed: 14336 x 4096 at N = 9 / 16 125 -> ~47 / 62
+    // us; the 128256 x 4096 head only breaks even beyond 9 tokens: 8 tokens
+    // take 149 us there)
+    const bool groups = N > kGemvMaxN && N <= kQ8wGroupsMaxN && q8w_tokens_per_launch(nb) == kGemvMaxN &&
+                        (rows < kQ8wGroupsLongRows || N <= kGemvMaxN + 1);
+    if (N > kGemvMaxN && !groups && !q8w_mm_grid_ok(rows, N)) return Q4BQ_EINVAL;
     if (!aligned(Wq8, 2) || !aligned(X, 4) || !aligned(Y, 4)) return Q4BQ_EINVAL;
     const size_t y_bytes = static_cast<size_t>(N * rows) * 4;
     if (overlap(Y, y_bytes, Wq8, static_cast<size_t>(rows * nb) * kQ8Bytes) ||
@@ -552,7 +613,7 @@ int mul_mat_q8_0_q8_0(const void* Wq8, int64_t rows, int64_t K, const float* X, 
     hipError_t err = hipSuccess;
     const DeviceInfo* dev = current_device(&err);
     if (!dev) return Q4BQ_EHIP;
-    if (N > kGemvMaxN)
+    if (N > kGemvMaxN && !groups)
         return run_q8w_mm(static_cast<const uint8_t*>(Wq8), rows, nb, X, nullptr, N, Y, nullptr,
                           static_cast<hipStream_t>(stream));
     return status_of(launch_q8w_product(dev, static_cast<const uint8_t*>(Wq8), rows, nb, X, N, Y,

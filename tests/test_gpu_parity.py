@@ -435,6 +435,32 @@ def test_matrix_core_whole_tiles(hip, orc, rows, K, Ns):
         assert np.array_equal(np.concatenate([host(Ys[0]), host(Ys[1])], axis=1), Y), ("multi", rows, K, N)
 
 
+@pytest.mark.parametrize("rows,K", [(14336, 4096), (2304, 768), (300, 3072)])
+def test_decode_groups_between_9_and_32_tokens(hip, orc, rows, K):
+    """9..32 tokens run as groups of up to 8 through the decode kernels: every
+    output against the oracle, and bit for bit against separate calls on each
+    group of tokens, and across the workspace, pre-quantized, repacked and
+    multi-matrix forms."""
+    W, X = _case(rows, K, 32, 9700 + rows + K)
+    Wq_o = orc.q4_0_quantize(W)
+    Wq = hip.q4_0_quantize(dev(W))
+    Wr = hip.q4_0_repack(Wq, K)
+    for N in (9, 17, 31, 32):
+        print("decode groups rows=%d K=%d N=%d" % (rows, K, N), flush=True)
+        Xt = dev(X[:N])
+        Y = host(hip.mul_mat_q4_0_q8_0(Wq, Xt))
+        assert_close(Y, orc.mul_mat_ref(Wq_o, orc.q8_0_quantize(X[:N]), K), "rows=%d K=%d N=%d" % (rows, K, N))
+        parts = [host(hip.mul_mat_q4_0_q8_0_ex(Wq, dev(X[n0:min(N, n0 + 8)]), hip.workspace(rows, K, 8)))
+                 for n0 in range(0, N, 8)]
+        assert np.array_equal(Y, np.concatenate(parts, axis=0)), ("groups", rows, K, N)
+        assert np.array_equal(host(hip.mul_mat_q4_0_q8_0_ex(Wq, Xt, hip.workspace(rows, K, N))), Y), (rows, K, N)
+        assert np.array_equal(host(hip.mul_mat_q4_0_q8_0_pq(Wq, hip.q8_0_quantize(Xt), K)), Y), (rows, K, N)
+        assert np.array_equal(host(hip.mul_mat_q4_0r_q8_0(Wr, Xt)), Y), (rows, K, N)
+        half = rows // 2 // 32 * 32
+        Ys = hip.mul_mat_q4_0_q8_0_multi([Wq[:half], Wq[half:]], Xt)
+        assert np.array_equal(np.concatenate([host(Ys[0]), host(Ys[1])], axis=1), Y), ("multi", rows, K, N)
+
+
 SET_CASES = [
     ("gpt2_layer", [(2304, 768), (768, 768), (3072, 768), (768, 3072)], True),
     ("llama3_8b_decode", [(4096, 4096), (14336, 4096), (4096, 14336)], True),
