@@ -61,8 +61,22 @@ __device__ __forceinline__ uint32_t quant_q8_natural(float x0, float x1, float x
     return q8_natural_word(q);
 }
 
-// LDS: NT x nb blocks of 8 dwords (token-major), then NT x nb fp32 scales.
-constexpr int kQ8wActBytes = 36;
+// LDS: NT x nb blocks of 8 dwords of codes (token-major), then NT x nb fp32
+// scales.  With an even block count each pair of blocks takes 80 bytes (64 of
+// codes, 16 unused): lane l reads blocks 2l and 2l + 1, and at a 64-byte lane
+// stride every fourth lane's 16-byte read would meet the same four banks; at
+// 80 bytes the 16 lanes of one LDS cycle cover all 64 banks (this matters to
+// the 5..8-token kernels, which read the codes for every row: 128256 x 4096
+// at N = 8 149.8 -> 135.7 us, graph-timed).
+__host__ __device__ inline int q8w_code_dword(int g, bool padded) {
+    return padded ? (g >> 1) * 20 + (g & 1) * 8 : g * 8;
+}
+__host__ __device__ inline size_t q8w_code_bytes(int64_t nblk, bool padded) {
+    return static_cast<size_t>(nblk) * (padded ? 40 : 32);
+}
+__host__ __device__ inline size_t q8w_act_lds(int64_t nt, int64_t nb) {
+    return q8w_code_bytes(nt * nb, nb % 2 == 0) + static_cast<size_t>(nt) * nb * 4;
+}
 
 // Two consecutive blocks (68 bytes) from a 4-byte aligned address: four
 // 16-byte loads and one 4-byte load.  Block 0: scale in bytes 0-1, values in
@@ -119,7 +133,7 @@ struct Q8Slot<true> {
 // bank conflicts).  The folds see the same bytes.
 constexpr int kQ8wNtlLoads = 5;  // 17 * 128 / 8 = 272 pieces at most
 __host__ __device__ inline size_t q8w_ntl_offset(int nt, int64_t nb) {
-    return (static_cast<size_t>(nt) * nb * kQ8wActBytes + 15) / 16 * 16;
+    return (q8w_act_lds(nt, nb) + 15) / 16 * 16;
 }
 
 template <int THREADS, int NT, int SPL, int D, bool PAIRED, bool NTL = false>
@@ -132,7 +146,7 @@ k_q8w_rows(const uint8_t* __restrict__ W, int64_t rows, int nb, const float* __r
     constexpr bool kActReg = NT * BPL <= 8;  // activations in registers, else read from LDS per row
     extern __shared__ __align__(16) uint8_t smem[];
     uint32_t* sq = reinterpret_cast<uint32_t*>(smem);
-    float* sd = reinterpret_cast<float*>(smem + static_cast<size_t>(NT) * nb * 32);
+    float* sd = reinterpret_cast<float*>(smem + q8w_code_bytes(static_cast<int64_t>(NT) * nb, PAIRED));
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nblk = NT * nb;
@@ -212,7 +226,7 @@ k_q8w_rows(const uint8_t* __restrict__ W, int64_t rows, int nb, const float* __r
             __builtin_memcpy(&x, X + static_cast<int64_t>(g) * kQK + 4 * m, 16);
             float d;
             const uint32_t word = quant_q8_natural(x.x, x.y, x.z, x.w, d);
-            sq[g * 8 + m] = word;
+            sq[q8w_code_dword(g, PAIRED) + m] = word;
             if (m == 0) sd[g] = d;
         }
         // LDS writes done, then the workgroup barrier; no wait on the weight loads
@@ -229,8 +243,8 @@ k_q8w_rows(const uint8_t* __restrict__ W, int64_t rows, int nb, const float* __r
 #pragma unroll
             for (int i = 0; i < BPL; ++i) {
                 const int g = n * nb + bb[i];
-                const u32x4 a0 = reinterpret_cast<const u32x4*>(sq)[g * 2];
-                const u32x4 a1 = reinterpret_cast<const u32x4*>(sq)[g * 2 + 1];
+                const u32x4 a0 = *reinterpret_cast<const u32x4*>(sq + q8w_code_dword(g, PAIRED));
+                const u32x4 a1 = *reinterpret_cast<const u32x4*>(sq + q8w_code_dword(g, PAIRED) + 4);
                 areg[n][i][0] = a0.x; areg[n][i][1] = a0.y; areg[n][i][2] = a0.z; areg[n][i][3] = a0.w;
                 areg[n][i][4] = a1.x; areg[n][i][5] = a1.y; areg[n][i][6] = a1.z; areg[n][i][7] = a1.w;
                 dreg[n][i] = sd[g];
@@ -258,8 +272,8 @@ k_q8w_rows(const uint8_t* __restrict__ W, int64_t rows, int nb, const float* __r
                     dx = dreg[n][i];
                 } else {
                     const int g = n * nb + bb[i];
-                    const u32x4 a0 = reinterpret_cast<const u32x4*>(sq)[g * 2];
-                    const u32x4 a1 = reinterpret_cast<const u32x4*>(sq)[g * 2 + 1];
+                    const u32x4 a0 = *reinterpret_cast<const u32x4*>(sq + q8w_code_dword(g, PAIRED));
+                    const u32x4 a1 = *reinterpret_cast<const u32x4*>(sq + q8w_code_dword(g, PAIRED) + 4);
                     const uint32_t a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
                     s = q8w_block_dot(blk.q, a);
                     dx = sd[g];
@@ -328,7 +342,7 @@ hipError_t launch_q8w_k(const DeviceInfo* dev, const uint8_t* W, int64_t rows, i
     const auto plain = k_q8w_rows<kThreads, NT, SPL, kDepth, PAIRED>;
     const auto contiguous = k_q8w_rows<kThreads, NT, SPL, kDepth, PAIRED, kNtlForm>;
     const auto kernel = ntl ? contiguous : plain;
-    const size_t lds = ntl ? ntl_lds : static_cast<size_t>(NT) * nb * kQ8wActBytes;
+    const size_t lds = ntl ? ntl_lds : q8w_act_lds(NT, nb);
     if (lds > 64 * 1024) {
         static const hipError_t raised = [&] {
             hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(plain),
@@ -372,7 +386,7 @@ hipError_t launch_q8w_nt(const DeviceInfo* dev, const uint8_t* W, int64_t rows, 
 // Tokens per launch: their quantized blocks fit the LDS budget; rows longer
 // than 512 blocks (16 per lane) take at most two (register budget).
 int64_t q8w_tokens_per_launch(int64_t nb) {
-    int64_t t = static_cast<int64_t>(kRowsMaxLds) / (nb * kQ8wActBytes);
+    int64_t t = static_cast<int64_t>(kRowsMaxLds / q8w_act_lds(1, nb));
     if (t > 8) t = 8;
     if (nb > 512 && t > 2) t = 2;
     return t;
