@@ -136,6 +136,14 @@ __host__ __device__ inline size_t q8w_ntl_offset(int nt, int64_t nb) {
     return (q8w_act_lds(nt, nb) + 15) / 16 * 16;
 }
 
+// 5..8 tokens on one block pair per lane: the tokens' 16 activation blocks
+// stay in registers and the 512-thread workgroups run one per CU (measured,
+// graph-timed: 14336 x 4096 at N = 8 27.0 -> 23.3 us, the 128256 x 4096 head
+// 136.1 -> 131.0 us, against two workgroups per CU reading the blocks from
+// LDS for every row)
+template <int THREADS, int BPL>
+constexpr bool kRegPairs = THREADS == 512 && BPL == 2;
+
 template <int THREADS, int NT, int SPL, int D, bool PAIRED, bool NTL = false>
 __global__ void __launch_bounds__(THREADS)
 k_q8w_rows(const uint8_t* __restrict__ W, int64_t rows, int nb, const float* __restrict__ X, float* __restrict__ Y) {
@@ -143,7 +151,10 @@ k_q8w_rows(const uint8_t* __restrict__ W, int64_t rows, int nb, const float* __r
     constexpr int kWaves = THREADS / 64;
     constexpr int kBps = PAIRED ? 2 : 1;              // blocks per slot
     constexpr int BPL = SPL * kBps;
-    constexpr bool kActReg = NT * BPL <= 8;  // activations in registers, else read from LDS per row
+    // activations in registers (up to 16 blocks in the one-pair 512-thread
+    // form, which then runs one workgroup per CU: two waves per SIMD have the
+    // registers), else read from LDS per row
+    constexpr bool kActReg = NT * BPL <= (kRegPairs<THREADS, BPL> ? 16 : 8);
     extern __shared__ __align__(16) uint8_t smem[];
     uint32_t* sq = reinterpret_cast<uint32_t*>(smem);
     float* sd = reinterpret_cast<float*>(smem + q8w_code_bytes(static_cast<int64_t>(NT) * nb, PAIRED));
@@ -328,7 +339,7 @@ hipError_t launch_q8w_k(const DeviceInfo* dev, const uint8_t* W, int64_t rows, i
     constexpr int kThreads = q8w_threads<BPL>(NT);
     constexpr int kDepth = BPL <= 2 ? 2 : 1;
     int64_t wgs = (rows + kThreads / 64 - 1) / (kThreads / 64);
-    const int64_t cap = static_cast<int64_t>(dev->num_cu) * (1024 / kThreads);
+    const int64_t cap = static_cast<int64_t>(dev->num_cu) * (kRegPairs<kThreads, BPL> ? 1 : 1024 / kThreads);
     if (wgs > cap) wgs = cap;
     // contiguous non-temporal row loads where rows are whole 16-byte pieces
     // and every wave has 16 rows or more (as for the Q4_0 row kernel), up to
