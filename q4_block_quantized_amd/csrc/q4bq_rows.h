@@ -649,7 +649,10 @@ template <int SRC, int LAY, bool EPI, bool DOTS, int NT, int PPL, int C = 1, boo
 hipError_t launch_rows_k(const DeviceInfo* dev, const uint8_t* Wq, int64_t rows, int64_t nb, const void* src,
                          float* Y, int32_t* dots, const MultiDesc& md, hipStream_t s) {
     constexpr int kThreads = rows_threads<NT, PPL>();
-    constexpr int kDepth = rows_depth<NT, PPL>();
+    // one token in the chunked form: two chunk rows in flight per wave (each
+    // wave has only a few: 4096 x 14336 at N = 1 10.0 -> 9.5 us; whole rows
+    // keep one: 4096 x 4096 4.1 -> 5.2 us with two)
+    constexpr int kDepth = NT == 1 && C > 1 && !DUAL ? 2 : rows_depth<NT, PPL>();
     int64_t wgs = (rows * C + kThreads / 64 - 1) / (kThreads / 64);
     const int64_t cap = static_cast<int64_t>(dev->num_cu) * (1024 / kThreads);
     if (wgs > cap) wgs = cap;
