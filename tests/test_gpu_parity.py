@@ -801,7 +801,8 @@ def _fusion_inputs(rows, K, N, seed):
     return W, X.astype(np.float32), gamma, beta, bias, mul
 
 
-# decode task kernel (K = 768), row kernel (K = 4096), prefill kernel (N > 8)
+# decode task kernel (K = 768), row kernel (K = 4096), groups of 8 tokens through
+# the decode kernels (N = 9), prefill kernel (N = 130)
 @pytest.mark.parametrize("rows,K,N", [(3072, 768, 1), (3072, 768, 4), (2304, 768, 6), (300, 4096, 1), (300, 4096, 5),
                                       (1000, 4096, 9), (777, 768, 130)])
 def test_fused_product(hip, orc, rows, K, N):
@@ -839,7 +840,9 @@ def test_fused_product(hip, orc, rows, K, N):
 def test_fused_layernorm_k_sweep(hip, orc, K):
     """The LayerNorm + quantization kernel at every register layout (1, 2, 4, 8
     quads per thread, and re-reading above 32768 values), into both activation
-    layouts (N <= 8 and N > 8)."""
+    layouts: the decode kernels' (N = 1, and N = 11 as groups of 8 and 3 tokens
+    where a decode kernel takes the rows) and the prefill kernel's (N = 11 at
+    K = 32 and K >= 32768)."""
     rows = 37
     W, X, gamma, beta, _, _ = _fusion_inputs(rows, K, 11, 5700 + K)
     Wq = hip.q4_0_quantize(dev(W))
