@@ -85,11 +85,15 @@ int q8_0_quantize(const float *X, int64_t N, int64_t K, void *Xq, void *stream);
  *   Wq  rows x (K/32) Q4_0 blocks, 2-byte aligned.
  *   X   fp32 N x K, 4-byte aligned.
  *   Y   fp32 N x rows, 4-byte aligned, overwritten; must not overlap Wq or X.
- * N <= 8 runs the streaming decode kernel; larger N the matrix-core kernel,
+ * N <= 8 runs the streaming decode kernel (9..32 tokens run as groups of up
+ * to 8 through it where it takes the shape); larger N the matrix-core kernel,
  * in ceil(rows / 224) * ceil(N / 128) workgroups of 512 threads: shapes whose
- * grid would exceed HIP's 2^32 - 1 work-items return Q4BQ_EINVAL.  Needs
- * stream-ordered scratch of q4bq_workspace_size(rows, K, N) bytes, taken with
- * hipMallocAsync on `stream` (Q4BQ_ENOMEM if that fails).
+ * grid would exceed HIP's 2^32 - 1 work-items return Q4BQ_EINVAL.  When that
+ * is fewer than 256 workgroups, K is split into up to 4 ranges (as many
+ * workgroups more) whose fp32 sums a second kernel adds in range order.
+ * Needs stream-ordered scratch of q4bq_workspace_size(rows, K, N) bytes (the
+ * activations and room for those sums), taken with hipMallocAsync on
+ * `stream` (Q4BQ_ENOMEM if that fails).
  * The summation order is fixed for a given (rows, K, N, device), so repeated
  * calls give bitwise-identical Y.
  */
@@ -118,7 +122,9 @@ int mul_mat_q4_0_q8_0_ex(const void *Wq, int64_t rows, int64_t K, const float *X
  * to the library).  mul_mat_q4_0_q8_0_prepared then computes Y from Wq and
  * that workspace; it may be called any number of times, for different Wq with
  * the same K, while the workspace is left untouched.  Running the two in
- * sequence gives exactly the Y of mul_mat_q4_0_q8_0.
+ * sequence gives exactly the Y of mul_mat_q4_0_q8_0 (where that splits K,
+ * mul_mat_q4_0_q8_0_prepared takes the buffer for the range sums
+ * stream-ordered on `stream`).
  */
 int q4bq_quantize_activations(const float *X, int64_t N, int64_t K, void *workspace,
                               size_t ws_bytes, void *stream);
@@ -357,10 +363,11 @@ int q8_0_q8_0_block_dots(const void *Wq8, int64_t rows, int64_t K, const void *X
  * on until the process ends (Q4BQ_NOALLOC_SCRATCH_BYTES = 16 MiB per GPU).
  * Arguments, checks and results are those of mul_mat_q4_0_q8_0 (the same
  * kernels; Y bit for bit that of mul_mat_q4_0_q8_0_ex); no hipMalloc,
- * hipMallocAsync or hipFree is called.  Sizes whose scratch,
- * q4bq_workspace_size(rows, K, N), exceeds the array return Q4BQ_ESCRATCH
- * before anything is launched (N > 8 needs N * K/32 * 64 bytes: up to 512
- * tokens at K = 16384).  Every call on one GPU shares that GPU's array, which
+ * hipMallocAsync or hipFree is called.  Sizes whose scratch exceeds the
+ * array return Q4BQ_ESCRATCH before anything is launched: above 8 tokens the
+ * activations take N * K/32 * 64 bytes (up to 512 tokens at K = 16384), and
+ * where the matrix-core kernel splits K (fewer than 256 workgroup tiles) its
+ * range sums splits * N * rows * 4 bytes more.  Every call on one GPU shares that GPU's array, which
  * keeps the last call's contents: calls that overlap in time on one GPU (two
  * streams, or two host threads) race and must be serialized by the caller.
  */

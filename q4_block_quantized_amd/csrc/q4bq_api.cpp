@@ -57,8 +57,14 @@ bool decode_groups_pay(int64_t N, int64_t nb, int64_t rows) {
     return N <= kDecodeGroupsMaxN && (rows_apply(kGemvMaxN, nb, rows) || mma_apply(kGemvMaxN, nb, rows));
 }
 
+// Workspace layout: the activations (act_bytes, rounded up to 256 bytes), then
+// room for the prefill kernel's split sums.
+size_t act_ws_bytes(int64_t N, int64_t nb) { return (act_bytes(N, nb) + 255) & ~static_cast<size_t>(255); }
+
+// ws_bytes: the workspace's size (the prefill kernel splits K only where its
+// partial sums fit behind the activations).
 int run_product(WLayout lay, const uint8_t* Wq, int64_t rows, int64_t K, const float* X, const uint8_t* Xq,
-                int64_t N, float* Y, int32_t* D, void* ws, hipStream_t s) {
+                int64_t N, float* Y, int32_t* D, void* ws, size_t ws_bytes, hipStream_t s) {
     hipError_t err = hipSuccess;
     const DeviceInfo* dev = current_device(&err);
     if (!dev) return Q4BQ_EHIP;
@@ -73,17 +79,22 @@ int run_product(WLayout lay, const uint8_t* Wq, int64_t rows, int64_t K, const f
         for (int64_t n0 = 0; n0 < N; n0 += kGemvMaxN) {
             const int64_t g = N - n0 < kGemvMaxN ? N - n0 : kGemvMaxN;
             const int rc = run_product(lay, Wq, rows, K, X ? X + n0 * K : nullptr,
-                                       Xq ? Xq + n0 * nb * kQ8Bytes : nullptr, g, Y + n0 * rows, nullptr, ws, s);
+                                       Xq ? Xq + n0 * nb * kQ8Bytes : nullptr, g, Y + n0 * rows, nullptr, ws,
+                                       ws_bytes, s);
             if (rc != Q4BQ_OK) return rc;
         }
         return Q4BQ_OK;
     }
     err = X ? launch_act_from_f32(X, N, nb, ws, s) : launch_act_from_q8(Xq, N, nb, ws, s);
     if (err != hipSuccess) return Q4BQ_EHIP;
-    if (N <= kGemvMaxN)
+    if (N <= kGemvMaxN) {
         err = launch_gemv(dev, lay, Wq, rows, nb, ws, N, Y, D, s);
-    else
-        err = launch_prefill(dev, lay, Wq, rows, nb, ws, N, Y, D, s);
+    } else {
+        const size_t off = act_ws_bytes(N, nb);
+        float* partial = ws_bytes > off ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + off) : nullptr;
+        err = launch_prefill(dev, lay, Wq, rows, nb, ws, N, Y, D, s, Epilogue{nullptr, nullptr, kEpiNone}, partial,
+                             partial ? ws_bytes - off : 0);
+    }
     return status_of(err);
 }
 
@@ -92,14 +103,14 @@ int run_with_scratch(WLayout lay, const uint8_t* Wq, int64_t rows, int64_t K, co
                      int64_t N, float* Y, int32_t* D, hipStream_t s) {
     hipError_t err = hipSuccess;
     if (!current_device(&err)) return Q4BQ_EHIP;
-    if (X && !D && gemv_fuses(N, K / kQK, rows)) return run_product(lay, Wq, rows, K, X, Xq, N, Y, D, nullptr, s);
+    if (X && !D && gemv_fuses(N, K / kQK, rows)) return run_product(lay, Wq, rows, K, X, Xq, N, Y, D, nullptr, 0, s);
     const size_t bytes = q4bq_workspace_size(rows, K, N);
     void* ws = nullptr;
     if (hipMallocAsync(&ws, bytes, s) != hipSuccess || ws == nullptr) {
         (void)hipGetLastError();
         return Q4BQ_ENOMEM;
     }
-    const int rc = run_product(lay, Wq, rows, K, X, Xq, N, Y, D, ws, s);
+    const int rc = run_product(lay, Wq, rows, K, X, Xq, N, Y, D, ws, bytes, s);
     if (hipFreeAsync(ws, s) != hipSuccess) return Q4BQ_EHIP;
     return rc;
 }
@@ -185,8 +196,10 @@ int q4_0_get_rows(const void* Wq, int64_t rows, int64_t K, const int32_t* ids, i
 
 size_t q4bq_workspace_size(int64_t rows, int64_t K, int64_t N) {
     if (bad_dim(rows) || bad_dim(N) || bad_k(K) || too_big(N, K, 4)) return 0;
-    const size_t b = act_bytes(N, K / kQK);
-    return (b + 255) & ~static_cast<size_t>(255);
+    const int64_t nb = K / kQK;
+    size_t b = act_ws_bytes(N, nb);
+    if (N > kGemvMaxN && !too_big(N, rows, 4 * kPrefillMaxSplits)) b += prefill_partial_bytes(rows, nb, N);
+    return b;
 }
 
 }  // extern "C"
@@ -245,7 +258,8 @@ int mul_mat_q4_0_q8_0_ex(const void* Wq, int64_t rows, int64_t K, const float* X
         overlap(workspace, need, X, static_cast<size_t>(N * K) * 4) ||
         overlap(workspace, need, Wq, static_cast<size_t>(rows * nb) * kQ4Bytes))
         return Q4BQ_EINVAL;
-    return run_product(kAoS, static_cast<const uint8_t*>(Wq), rows, K, X, nullptr, N, Y, nullptr, workspace,
+    // (only the checked `need` bytes are used)
+    return run_product(kAoS, static_cast<const uint8_t*>(Wq), rows, K, X, nullptr, N, Y, nullptr, workspace, need,
                        static_cast<hipStream_t>(stream));
 }
 
@@ -269,7 +283,7 @@ int mul_mat_q4_0r_q8_0_ex(const void* Wr, int64_t rows, int64_t K, const float* 
         overlap(workspace, need, Wr, repack_bytes(rows, nb)))
         return Q4BQ_EINVAL;
     return run_product(kRepacked, static_cast<const uint8_t*>(Wr), rows, K, X, nullptr, N, Y, nullptr, workspace,
-                       static_cast<hipStream_t>(stream));
+                       need, static_cast<hipStream_t>(stream));
 }
 
 int mul_mat_q4_0_q8_0_multi(int count, const void* const* Wq, const int64_t* rows, int64_t K, const float* X,
@@ -393,15 +407,19 @@ int mul_mat_q4_0_q8_0_noalloc(const void* Wq, int64_t rows, int64_t K, const flo
                               void* stream) {
     const int rc = check_product(Wq, rows, K, X, kF32, N, Y, false);
     if (rc != Q4BQ_OK) return rc;
-    if (q4bq_workspace_size(rows, K, N) > Q4BQ_NOALLOC_SCRATCH_BYTES) return Q4BQ_ESCRATCH;
     hipError_t err = hipSuccess;
     const DeviceInfo* dev = current_device(&err);
     if (!dev) return Q4BQ_EHIP;
+    // the activations and, where the prefill kernel splits K, its partial sums
+    const int64_t nb = K / kQK;
+    size_t need = act_ws_bytes(N, nb);
+    if (N > kGemvMaxN && !decode_groups_pay(N, nb, rows)) need += prefill_split_bytes(dev, rows, nb, N);
+    if (need > Q4BQ_NOALLOC_SCRATCH_BYTES) return Q4BQ_ESCRATCH;
     void* ws = noalloc_scratch(dev->id, &err);
     if (!ws) return Q4BQ_EHIP;
     // the scratch is device memory of its own, apart from every caller buffer
     return run_product(kAoS, static_cast<const uint8_t*>(Wq), rows, K, X, nullptr, N, Y, nullptr, ws,
-                       static_cast<hipStream_t>(stream));
+                       Q4BQ_NOALLOC_SCRATCH_BYTES, static_cast<hipStream_t>(stream));
 }
 
 int q4_0_q8_0_block_dots(const void* Wq, int64_t rows, int64_t K, const void* Xq, int64_t N, int32_t* D,

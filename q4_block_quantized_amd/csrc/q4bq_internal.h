@@ -228,10 +228,24 @@ constexpr int kLnActThreads = 1024;
 constexpr int64_t kMaxWorkItems = (int64_t(1) << 32) - 1;
 
 // Matrix-core kernel, any N; the one the library runs above kGemvMaxN.  D as
-// above.
+// above.  With fewer than kPrefillSplitTiles workgroup tiles, K is split in up
+// to kPrefillMaxSplits ranges of at least kPrefillMinSplitBlocks blocks (one
+// workgroup per tile and range, as many as the CUs take; the shape alone
+// decides); the ranges' sums go to a buffer of splits * N * rows floats --
+// `partial` where partial_bytes holds them, else one taken stream-ordered --
+// and a second kernel adds them in range order and applies the epilogue.
+constexpr int64_t kPrefillSplitTiles = 256;
+constexpr int64_t kPrefillMaxSplits = 4;
+constexpr int64_t kPrefillMinSplitBlocks = 16;
+int prefill_splits(int64_t rows, int64_t nb, int64_t N, int num_cu, int* kbs);
+// Room for the largest split of these sizes on any device (0 where none can
+// happen), and the bytes this device's split takes.
+size_t prefill_partial_bytes(int64_t rows, int64_t nb, int64_t N);
+size_t prefill_split_bytes(const DeviceInfo* dev, int64_t rows, int64_t nb, int64_t N);
 hipError_t launch_prefill(const DeviceInfo* dev, WLayout lay, const uint8_t* Wq, int64_t rows, int64_t nb,
                           const void* act, int64_t N, float* Y, int32_t* D, hipStream_t s,
-                          const Epilogue& epi = Epilogue{nullptr, nullptr, kEpiNone});
+                          const Epilogue& epi = Epilogue{nullptr, nullptr, kEpiNone}, float* partial = nullptr,
+                          size_t partial_bytes = 0);
 
 constexpr int64_t kGemvMaxN = 8;
 

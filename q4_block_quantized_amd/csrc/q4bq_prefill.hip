@@ -187,17 +187,23 @@ template <bool DOTS, bool RP, bool EPI>
 __global__ void __launch_bounds__(kT)
 k_prefill(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Wrec, int64_t rows, int nb,
           const uint8_t* __restrict__ act, int64_t N, float* __restrict__ Y, int32_t* __restrict__ D,
-          const Epilogue epi) {
+          const Epilogue epi, int kbs, int splits) {
     __shared__ __align__(16) uint8_t smem[kNS * kStage];
 
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    // workgroup tile: token tile (fastest), then split, then row tile; split s
+    // takes blocks [kb0, kb1) of every row and writes its sums to slice s of Y
     const int64_t ntt = (N + kTT - 1) / kTT;
     const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
     const int64_t n0 = (tile % ntt) * kTT;
-    const int64_t r0 = (tile / ntt) * kTR;
-    const int nst = (nb + kKB - 1) / kKB;
+    const int64_t rs = tile / ntt;
+    const int split = __builtin_amdgcn_readfirstlane(static_cast<int>(rs % splits));
+    const int64_t r0 = (rs / splits) * kTR;
+    const int kb0 = __builtin_amdgcn_readfirstlane(split * kbs);
+    const int kb1 = __builtin_amdgcn_readfirstlane(min(nb, kb0 + kbs));
+    const int nst = (kb1 - kb0 + kKB - 1) / kKB;
 
     if (wave >= kCW) {
         // ====================== staging waves ====================================
@@ -218,8 +224,8 @@ k_prefill(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Wrec, int6
 #pragma unroll
             for (int i = 0; i < kDma; ++i) {
                 const int blk = i >> 1, e = i & 1;
-                int b = st * kKB + blk;
-                if (b > nb - 1) b = nb - 1;  // past the end: neutralised by zero weight scales
+                int b = kb0 + st * kKB + blk;
+                if (b > kb1 - 1) b = kb1 - 1;  // past the range: neutralised by zero weight scales
                 const uint8_t* src = act + static_cast<int64_t>(b) * N * kAct6Bytes + dma_off[e];
                 dma16(src, sA + blk * kPlaneA + (sw * 32 + e * 16) * kAct6Bytes);
             }
@@ -250,8 +256,8 @@ k_prefill(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Wrec, int6
 #pragma unroll
                 for (int m = 0; m < kPer; ++m) {
                     if (m < nrec) {  // wave-uniform
-                        int b = st * kKB + rec_blk[m];
-                        if (b > nb) b = nb;
+                        int b = kb0 + st * kKB + rec_blk[m];
+                        if (b >= kb1) b = nb;  // past the range: the zero plane
                         const int g = sw + kCW * m;
                         dma16(Wrec + static_cast<int64_t>(b) * rows * kRecW + rec_off[m], sB + g * 1024);
                     }
@@ -298,8 +304,8 @@ k_prefill(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Wrec, int6
             constexpr int S = decltype(set)::value;
 #pragma unroll
             for (int k = 0; k < kKB; ++k) {
-                const int b = st * kKB + k;
-                rw_ok[S][k] = w_row_ok && b < nb;
+                const int b = kb0 + st * kKB + k;
+                rw_ok[S][k] = w_row_ok && b < kb1;
                 const int64_t bo = rw_ok[S][k] ? b : 0;
                 rw[S][k] = load_block(w_src + bo * kQ4Bytes);
             }
@@ -439,9 +445,9 @@ k_prefill(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Wrec, int6
                 } else {
                     sr[cur] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fp6_operand(ak), fp6_operand(wk), zero,
                                                                               2, 2, 0, scale_a, 0, kScaleW);
-                    const int b = st * kKB + blk;
+                    const int b = kb0 + st * kKB + blk;
                     const int64_t r = r0 + kSeqR[p] * 32 + l32;
-                    if (b < nb && r < rows) {
+                    if (b < kb1 && r < rows) {
 #pragma unroll
                         for (int v = 0; v < 16; ++v) {
                             const int64_t n = n0 + (2 * tp + kSeqT[p]) * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
@@ -464,6 +470,7 @@ k_prefill(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Wrec, int6
             // step count is even)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[kPos - 1][v] = fmaf(sr[1][v], pr[1][v], acc[kPos - 1][v]);
+            float* const Yo = Y + static_cast<int64_t>(split) * N * rows;  // this split's slice
 #pragma unroll
             for (int j = 0; j < kPos; ++j) {
                 const int64_t r = r0 + kSeqR[j] * 32 + l32;
@@ -471,7 +478,7 @@ k_prefill(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Wrec, int6
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int64_t n = n0 + (2 * tp + kSeqT[j]) * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-                    if (n < N) Y[n * rows + r] = EPI ? apply_epilogue(acc[j][v], n, r, rows, epi) : acc[j][v];
+                    if (n < N) Yo[n * rows + r] = EPI ? apply_epilogue(acc[j][v], n, r, rows, epi) : acc[j][v];
                 }
             }
         }
@@ -483,30 +490,109 @@ k_prefill(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Wrec, int6
 }
 
 
+// Y = the splits' slices of P added in split order (then the epilogue).
+template <bool EPI>
+__global__ void __launch_bounds__(256)
+k_prefill_sum(const float* __restrict__ P, int splits, int64_t N, int64_t rows, float* __restrict__ Y,
+              const Epilogue epi) {
+    const int64_t total = N * rows;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < total;
+         i += static_cast<int64_t>(gridDim.x) * 256) {
+        float y = P[i];
+        for (int k = 1; k < splits; ++k) y += P[k * total + i];
+        const int64_t n = i / rows, r = i - n * rows;
+        Y[i] = EPI ? apply_epilogue(y, n, r, rows, epi) : y;
+    }
+}
+
 }  // namespace
 
+int prefill_splits(int64_t rows, int64_t nb, int64_t N, int num_cu, int* kbs) {
+    const int64_t tiles = ((rows + kTR - 1) / kTR) * ((N + kTT - 1) / kTT);
+    *kbs = static_cast<int>(nb);
+    if (tiles >= kPrefillSplitTiles) return 1;
+    int64_t S = num_cu / tiles;
+    if (S > kPrefillMaxSplits) S = kPrefillMaxSplits;
+    if (S > nb / kPrefillMinSplitBlocks) S = nb / kPrefillMinSplitBlocks;
+    if (S < 2) return 1;
+    int64_t kb = (nb + S - 1) / S;
+    kb += kb & 1;  // whole stages of two blocks
+    S = (nb + kb - 1) / kb;
+    if (S < 2) return 1;
+    *kbs = static_cast<int>(kb);
+    return static_cast<int>(S);
+}
+
+size_t prefill_partial_bytes(int64_t rows, int64_t nb, int64_t N) {
+    const int64_t tiles = ((rows + kTR - 1) / kTR) * ((N + kTT - 1) / kTT);
+    if (tiles >= kPrefillSplitTiles || nb < 2 * kPrefillMinSplitBlocks) return 0;
+    return static_cast<size_t>(kPrefillMaxSplits) * static_cast<size_t>(N * rows) * sizeof(float);
+}
+
 hipError_t launch_prefill(const DeviceInfo* dev, WLayout lay, const uint8_t* Wq, int64_t rows, int64_t nb,
-                          const void* act, int64_t N, float* Y, int32_t* D, hipStream_t s, const Epilogue& epi) {
-    (void)dev;
+                          const void* act, int64_t N, float* Y, int32_t* D, hipStream_t s, const Epilogue& epi,
+                          float* partial, size_t partial_bytes) {
     const uint8_t* rec = static_cast<const uint8_t*>(act);
-    const dim3 grid(static_cast<uint32_t>(((rows + kTR - 1) / kTR) * ((N + kTT - 1) / kTT)));
     const int nbi = static_cast<int>(nb);
     const bool fused = epi.bias || epi.mul || epi.act != kEpiNone;
+    if (fused && lay == kRepacked) return hipErrorInvalidValue;  // the fused forms take the pages' blocks
+    // few workgroup tiles: split K (each split's sums into its slice of the
+    // partial buffer, added in split order by k_prefill_sum).  The split
+    // depends on the shape alone, so every entry point gives the same bits;
+    // without room in `partial` the buffer is taken stream-ordered.
+    int kbs = nbi, splits = 1;
+    if (!D) splits = prefill_splits(rows, nb, N, dev->num_cu, &kbs);
+    const size_t need = splits > 1 ? static_cast<size_t>(splits) * static_cast<size_t>(N * rows) * sizeof(float) : 0;
+    bool owned = false;
+    if (splits > 1 && (!partial || partial_bytes < need)) {
+        void* p = nullptr;
+        if (hipMallocAsync(&p, need, s) != hipSuccess || p == nullptr) return hipErrorOutOfMemory;
+        partial = static_cast<float*>(p);
+        owned = true;
+    }
+    const dim3 grid(static_cast<uint32_t>(((rows + kTR - 1) / kTR) * ((N + kTT - 1) / kTT) * splits));
+    float* out = splits > 1 ? partial : Y;
+    const bool epi_here = fused && splits == 1;
     if (D)
-        hipLaunchKernelGGL((k_prefill<true, false, false>), grid, dim3(kT), 0, s, Wq, nullptr, rows, nbi, rec, N, Y, D,
-                           epi);
-    else if (fused && lay == kRepacked)
-        return hipErrorInvalidValue;  // the fused forms take the pages' blocks
-    else if (fused)
-        hipLaunchKernelGGL((k_prefill<false, false, true>), grid, dim3(kT), 0, s, Wq, nullptr, rows, nbi, rec, N, Y,
-                           D, epi);
+        hipLaunchKernelGGL((k_prefill<true, false, false>), grid, dim3(kT), 0, s, Wq, nullptr, rows, nbi, rec, N, out,
+                           D, epi, kbs, splits);
+    else if (epi_here)
+        hipLaunchKernelGGL((k_prefill<false, false, true>), grid, dim3(kT), 0, s, Wq, nullptr, rows, nbi, rec, N, out,
+                           D, epi, kbs, splits);
     else if (lay == kRepacked)
         hipLaunchKernelGGL((k_prefill<false, true, false>), grid, dim3(kT), 0, s, Wq,
-                           Wq + repack_records_offset(rows, nb), rows, nbi, rec, N, Y, D, epi);
+                           Wq + repack_records_offset(rows, nb), rows, nbi, rec, N, out, D, epi, kbs, splits);
     else
-        hipLaunchKernelGGL((k_prefill<false, false, false>), grid, dim3(kT), 0, s, Wq, nullptr, rows, nbi, rec, N, Y,
-                           D, epi);
-    return hipGetLastError();
+        hipLaunchKernelGGL((k_prefill<false, false, false>), grid, dim3(kT), 0, s, Wq, nullptr, rows, nbi, rec, N,
+                           out, D, epi, kbs, splits);
+    hipError_t err = hipGetLastError();
+    if (splits == 1) return err;
+    if (err != hipSuccess) {
+        if (owned) (void)hipFreeAsync(partial, s);
+        return err;
+    }
+    const int64_t total = N * rows;
+    int64_t blocks = (total + 255) / 256;
+    const int64_t cap = static_cast<int64_t>(dev->num_cu) * 8;
+    if (blocks > cap) blocks = cap;
+    if (fused)
+        hipLaunchKernelGGL((k_prefill_sum<true>), dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, s, partial, splits,
+                           N, rows, Y, epi);
+    else
+        hipLaunchKernelGGL((k_prefill_sum<false>), dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, s, partial,
+                           splits, N, rows, Y, epi);
+    err = hipGetLastError();
+    if (owned) {
+        const hipError_t ferr = hipFreeAsync(partial, s);
+        if (err == hipSuccess) err = ferr;
+    }
+    return err;
+}
+
+size_t prefill_split_bytes(const DeviceInfo* dev, int64_t rows, int64_t nb, int64_t N) {
+    int kbs = 0;
+    const int splits = prefill_splits(rows, nb, N, dev->num_cu, &kbs);
+    return splits > 1 ? static_cast<size_t>(splits) * static_cast<size_t>(N * rows) * sizeof(float) : 0;
 }
 
 }  // namespace q4bq

@@ -461,6 +461,36 @@ def test_decode_groups_between_9_and_32_tokens(hip, orc, rows, K):
         assert np.array_equal(np.concatenate([host(Ys[0]), host(Ys[1])], axis=1), Y), ("multi", rows, K, N)
 
 
+@pytest.mark.parametrize("rows,K,N", [(4096, 4096, 512), (2000, 4160, 200)])
+def test_prefill_split_k(hip, orc, rows, K, N):
+    """Matrix-core kernel with K split into ranges (fewer than 256 workgroup
+    tiles: 3 ranges of 44, 44 and 40 blocks; 4 of 34, 34, 34 and 28 over 130
+    blocks and two token tiles, the second ragged): sampled rows against the
+    oracle; the repacked weights, the pre-quantized input and the prepared form
+    bit for bit; the fused LayerNorm + GELU form against the oracle."""
+    print("split K rows=%d K=%d N=%d" % (rows, K, N), flush=True)
+    W, X = _case(rows, K, N, 9900 + rows + K)
+    sample = _sample_rows(rows, 300, 9901 + rows)
+    Wq_o = orc.q4_0_quantize(W[sample])
+    Xq_o = orc.q8_0_quantize(X)
+    Wq = hip.q4_0_quantize(dev(W))
+    del W
+    Xt = dev(X)
+    Y = host(hip.mul_mat_q4_0_q8_0(Wq, Xt))
+    assert_close(Y[:, sample], orc.mul_mat_ref(Wq_o, Xq_o, K), "split K rows=%d K=%d N=%d" % (rows, K, N))
+    assert np.array_equal(host(hip.mul_mat_q4_0r_q8_0(hip.q4_0_repack(Wq, K), Xt)), Y)
+    assert np.array_equal(host(hip.mul_mat_q4_0_q8_0_pq(Wq, hip.q8_0_quantize(Xt), K)), Y)
+    ws = hip.workspace(1, K, N)
+    assert np.array_equal(host(hip.mul_mat_q4_0_q8_0_prepared(Wq, hip.q4bq_quantize_activations(Xt, ws), N, K)), Y)
+    gamma = inputs.random_matrix(9902, 1, K, 0.5)[0] + 1.0
+    beta = inputs.random_matrix(9903, 1, K, 0.1)[0]
+    bias = inputs.random_matrix(9904, 1, rows, 0.1)[0]
+    Yf = host(hip.mul_mat_q4_0_q8_0_fused(Wq, Xt, dev(gamma), dev(beta), 1e-5, dev(bias), hip.ACT_GELU, None))
+    ref = orc.epilogue(orc.mul_mat_ref(Wq_o, orc.q8_0_quantize(orc.layernorm(X, gamma, beta, 1e-5)), K),
+                       bias=bias[sample], act=hip.ACT_GELU, mul=None)
+    assert_close(Yf[:, sample], ref, "fused split K")
+
+
 SET_CASES = [
     ("gpt2_layer", [(2304, 768), (768, 768), (3072, 768), (768, 3072)], True),
     ("llama3_8b_decode", [(4096, 4096), (14336, 4096), (4096, 14336)], True),
