@@ -44,17 +44,23 @@ bool too_big(int64_t a, int64_t b, int64_t bytes_per) {
 // A few more tokens than the decode kernels take at once run as groups of up
 // to kGemvMaxN through the decode path, where the row-streaming or the
 // matrix-core decode kernel takes the shape: the prefill kernel's workgroup
-// always computes 224 rows x 128 tokens over all of K, so below a few dozen
-// tokens most of its work is padding, and matrices of few row tiles leave CUs
-// idle.  Measured (graph-timed, workspace form), prefill -> groups: 14336 x
+// always computes 224 rows x 128 tokens, so below a few dozen tokens most of
+// its work is padding.  Up to 16 tokens, and up to 32 where the prefill
+// kernel would not split K.  Measured (graph-timed, workspace form), prefill -> groups: 14336 x
 // 4096 at N = 9 / 32 86.4 / 87.6 -> 22.1 / 50.8 us; 4096 x 14336 278 / 279 ->
 // 65 / 215 us; the 128256 x 4096 head 255 / 259 -> 105 / 233 us; 2304 x 768
 // 23.8 / 24.7 -> 9.8 / 24.5 us.
+// (Where the prefill kernel splits K, from 17 tokens on it is the faster one:
+// 14336 x 4096 at N = 32 ~40 against 51 us as groups, 4096 x 14336 at N = 16
+// 85 against 110 us.)
 constexpr int64_t kDecodeGroupsMaxN = 32;
+constexpr int64_t kDecodeGroupsSplitMaxN = 16;
 constexpr int64_t kQ8wGroupsMaxN = 32;
 constexpr int64_t kQ8wGroupsLongRows = 65536;
-bool decode_groups_pay(int64_t N, int64_t nb, int64_t rows) {
-    return N <= kDecodeGroupsMaxN && (rows_apply(kGemvMaxN, nb, rows) || mma_apply(kGemvMaxN, nb, rows));
+bool decode_groups_pay(const DeviceInfo* dev, int64_t N, int64_t nb, int64_t rows) {
+    if (N > kDecodeGroupsMaxN || !(rows_apply(kGemvMaxN, nb, rows) || mma_apply(kGemvMaxN, nb, rows))) return false;
+    int kbs = 0;
+    return N <= kDecodeGroupsSplitMaxN || prefill_splits(rows, nb, N, dev->num_cu, &kbs) == 1;
 }
 
 // Workspace layout: the activations (act_bytes, rounded up to 256 bytes), then
@@ -73,7 +79,7 @@ int run_product(WLayout lay, const uint8_t* Wq, int64_t rows, int64_t K, const f
     // passes none in exactly that case)
     if (X && !D && (ws ? gemv_prefers_fused(N, nb, rows) : gemv_fuses(N, nb, rows)))
         return status_of(launch_gemv_fused(dev, lay, Wq, rows, nb, X, N, Y, s));
-    if (N > kGemvMaxN && !D && decode_groups_pay(N, nb, rows)) {
+    if (N > kGemvMaxN && !D && decode_groups_pay(dev, N, nb, rows)) {
         // up to kGemvMaxN tokens at a time through the decode path: token n0's
         // inputs and outputs start n0 rows into X (Xq) and Y
         for (int64_t n0 = 0; n0 < N; n0 += kGemvMaxN) {
@@ -327,7 +333,7 @@ int mul_mat_q4_0_q8_0_multi(int count, const void* const* Wq, const int64_t* row
     };
     // more tokens than one decode launch takes: groups of up to kGemvMaxN
     // (as in run_product), each on its rows of X and of every Y
-    const bool groups = N > kGemvMaxN && decode_groups_pay(N, nb, total);
+    const bool groups = N > kGemvMaxN && decode_groups_pay(dev, N, nb, total);
     const int64_t step = groups ? kGemvMaxN : N;
     bool need_ws = false;
     for (int64_t n0 = 0; n0 < N; n0 += step) need_ws = need_ws || !fuses(N - n0 < step ? N - n0 : step, md);
@@ -413,7 +419,7 @@ int mul_mat_q4_0_q8_0_noalloc(const void* Wq, int64_t rows, int64_t K, const flo
     // the activations and, where the prefill kernel splits K, its partial sums
     const int64_t nb = K / kQK;
     size_t need = act_ws_bytes(N, nb);
-    if (N > kGemvMaxN && !decode_groups_pay(N, nb, rows)) need += prefill_split_bytes(dev, rows, nb, N);
+    if (N > kGemvMaxN && !decode_groups_pay(dev, N, nb, rows)) need += prefill_split_bytes(dev, rows, nb, N);
     if (need > Q4BQ_NOALLOC_SCRATCH_BYTES) return Q4BQ_ESCRATCH;
     void* ws = noalloc_scratch(dev->id, &err);
     if (!ws) return Q4BQ_EHIP;
@@ -484,7 +490,7 @@ int run_fused(int count, const uint8_t* const* Wq, int64_t rows, int64_t K, cons
     }
     // more tokens than one decode launch takes: groups of up to kGemvMaxN
     // (as in run_product), each on its rows of X, Y and the factor
-    const int64_t step = N > kGemvMaxN && decode_groups_pay(N, nb, rows) ? kGemvMaxN : N;
+    const int64_t step = N > kGemvMaxN && decode_groups_pay(dev, N, nb, rows) ? kGemvMaxN : N;
     for (int64_t n0 = 0; n0 < N && err == hipSuccess; n0 += step) {
         const int64_t g = N - n0 < step ? N - n0 : step;
         const float* Xg = X + n0 * K;

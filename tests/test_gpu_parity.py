@@ -435,17 +435,18 @@ def test_matrix_core_whole_tiles(hip, orc, rows, K, Ns):
         assert np.array_equal(np.concatenate([host(Ys[0]), host(Ys[1])], axis=1), Y), ("multi", rows, K, N)
 
 
-@pytest.mark.parametrize("rows,K", [(14336, 4096), (2304, 768), (300, 3072)])
-def test_decode_groups_between_9_and_32_tokens(hip, orc, rows, K):
-    """9..32 tokens run as groups of up to 8 through the decode kernels: every
-    output against the oracle, and bit for bit against separate calls on each
-    group of tokens, and across the workspace, pre-quantized, repacked and
+@pytest.mark.parametrize("rows,K,Ns", [(14336, 4096, (9, 16)), (2304, 768, (9, 17, 31, 32)), (300, 3072, (9, 15, 16))])
+def test_decode_groups_between_9_and_32_tokens(hip, orc, rows, K, Ns):
+    """9..16 tokens (up to 32 where the matrix-core kernel would not split K:
+    the 2304 x 768 matrix) run as groups of up to 8 through the decode kernels:
+    every output against the oracle, and bit for bit against separate calls on
+    each group of tokens, and across the workspace, pre-quantized, repacked and
     multi-matrix forms."""
     W, X = _case(rows, K, 32, 9700 + rows + K)
     Wq_o = orc.q4_0_quantize(W)
     Wq = hip.q4_0_quantize(dev(W))
     Wr = hip.q4_0_repack(Wq, K)
-    for N in (9, 17, 31, 32):
+    for N in Ns:
         print("decode groups rows=%d K=%d N=%d" % (rows, K, N), flush=True)
         Xt = dev(X[:N])
         Y = host(hip.mul_mat_q4_0_q8_0(Wq, Xt))
