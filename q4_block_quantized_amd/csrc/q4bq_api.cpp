@@ -313,7 +313,7 @@ int mul_mat_q4_0_q8_0_multi(int count, const void* const* Wq, const int64_t* row
             if (overlap(Y[i], yb, Wq[j], static_cast<size_t>(rows[j] * nb) * kQ4Bytes)) return Q4BQ_EINVAL;
             if (i != j && overlap(Y[i], yb, Y[j], static_cast<size_t>(N * rows[j]) * 4)) return Q4BQ_EINVAL;
         }
-    const size_t need = q4bq_workspace_size(1, K, N);
+    const size_t need = act_ws_bytes(N, K / kQK);  // the activations alone (no rows: no split sums here)
     if (workspace) {
         if (!aligned(workspace, 16)) return Q4BQ_EINVAL;
         if (ws_bytes < need) return Q4BQ_ENOMEM;
@@ -668,7 +668,7 @@ int q4bq_quantize_activations(const float* X, int64_t N, int64_t K, void* worksp
                               void* stream) {
     if (!X || !workspace || bad_dim(N) || bad_k(K) || too_big(N, K, 4)) return Q4BQ_EINVAL;
     if (!aligned(X, 4) || !aligned(workspace, 16)) return Q4BQ_EINVAL;
-    const size_t need = q4bq_workspace_size(1, K, N);
+    const size_t need = act_ws_bytes(N, K / kQK);  // the activations alone (no rows: no split sums here)
     if (ws_bytes < need) return Q4BQ_ENOMEM;
     if (overlap(workspace, need, X, static_cast<size_t>(N * K) * 4)) return Q4BQ_EINVAL;
     hipError_t err = hipSuccess;

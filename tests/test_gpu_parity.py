@@ -492,6 +492,22 @@ def test_prefill_split_k(hip, orc, rows, K, N):
     assert_close(Yf[:, sample], ref, "fused split K")
 
 
+def test_prepared_workspace_sized_for_its_matrix(hip, orc):
+    """The two-phase form with a workspace sized for the matrix it serves
+    (q4bq_workspace_size(14336, K, 512): 256 workgroup tiles, no room for split
+    sums) rather than for one row (whose size does hold such room): the
+    activations fit, and the prepared product equals the operator bit for
+    bit."""
+    rows, K, N = 14336, 1024, 512
+    W, X = _case(rows, K, N, 9950)
+    Wq = hip.q4_0_quantize(dev(W))
+    Xt = dev(X)
+    ws = hip.workspace(rows, K, N)
+    assert ws.numel() < hip.q4bq_workspace_size(1, K, N)
+    Y = host(hip.mul_mat_q4_0_q8_0_prepared(Wq, hip.q4bq_quantize_activations(Xt, ws), N, K))
+    assert np.array_equal(Y, host(hip.mul_mat_q4_0_q8_0(Wq, Xt)))
+
+
 SET_CASES = [
     ("gpt2_layer", [(2304, 768), (768, 768), (3072, 768), (768, 3072)], True),
     ("llama3_8b_decode", [(4096, 4096), (14336, 4096), (4096, 14336)], True),
