@@ -603,12 +603,16 @@ bool q8w_mm_grid_ok(int64_t rows, int64_t N) {
 // Runs the matrix-core Q8_0-weight product with stream-ordered scratch.
 int run_q8w_mm(const uint8_t* W, int64_t rows, int64_t nb, const float* X, const uint8_t* Xq, int64_t N, float* Y,
                int32_t* D, hipStream_t s) {
+    hipError_t derr = hipSuccess;
+    const DeviceInfo* dev = current_device(&derr);
+    if (!dev) return Q4BQ_EHIP;
     void* ws = nullptr;
-    if (hipMallocAsync(&ws, q8w_mm_act_bytes(N, nb), s) != hipSuccess || ws == nullptr) {
+    const size_t bytes = D ? q8w_mm_act_bytes(N, nb) : q8w_mm_scratch_bytes(rows, nb, N, dev->num_cu);
+    if (hipMallocAsync(&ws, bytes, s) != hipSuccess || ws == nullptr) {
         (void)hipGetLastError();
         return Q4BQ_ENOMEM;
     }
-    const hipError_t err = launch_q8w_mm(W, rows, nb, X, Xq, N, Y, D, ws, s);
+    const hipError_t err = launch_q8w_mm(dev, W, rows, nb, X, Xq, N, Y, D, ws, s);
     if (hipFreeAsync(ws, s) != hipSuccess) return Q4BQ_EHIP;
     return status_of(err);
 }

@@ -90,14 +90,20 @@ hipError_t launch_q8w_block_dots(const uint8_t* W, int64_t rows, int64_t nb, con
 // Q8_0 weights x Q8_0 activations on the matrix cores (N > kGemvMaxN): the
 // activations (fp32 X, or Q8_0 blocks Xq) are first laid out in `ws`
 // (q8w_mm_act_bytes), then one launch of ceil(rows / kQ8wMmRows) *
-// ceil(N / kQ8wMmTokens) workgroups of kQ8wMmThreads.  D != nullptr: the
-// block-dot export instead of Y.
+// ceil(N / kQ8wMmTokens) workgroups of kQ8wMmThreads, times the K ranges
+// (q8w_mm_splits: up to kQ8wMmMaxSplits, so that there are about two
+// workgroups per CU) whose sums a second kernel adds in range order from
+// the rest of `ws` (q8w_mm_scratch_bytes in all).  D != nullptr: the
+// block-dot export instead of Y (no split).
 constexpr int kQ8wMmThreads = 256;
 constexpr int kQ8wMmRows = 128;
 constexpr int kQ8wMmTokens = 128;
+constexpr int64_t kQ8wMmMaxSplits = 4;
 size_t q8w_mm_act_bytes(int64_t N, int64_t nb);
-hipError_t launch_q8w_mm(const uint8_t* W, int64_t rows, int64_t nb, const float* X, const uint8_t* Xq, int64_t N,
-                         float* Y, int32_t* D, void* ws, hipStream_t s);
+int q8w_mm_splits(int64_t rows, int64_t nb, int64_t N, int num_cu, int* kbs);
+size_t q8w_mm_scratch_bytes(int64_t rows, int64_t nb, int64_t N, int num_cu);
+hipError_t launch_q8w_mm(const DeviceInfo* dev, const uint8_t* W, int64_t rows, int64_t nb, const float* X,
+                         const uint8_t* Xq, int64_t N, float* Y, int32_t* D, void* ws, hipStream_t s);
 hipError_t launch_q4_0_get_rows(const uint8_t* Wq, int64_t rows, int64_t nb, const int32_t* ids, int64_t n,
                                 float* out, hipStream_t s);
 

@@ -64,16 +64,22 @@ __device__ __forceinline__ int64_t mm_tile(uint32_t x, uint32_t grid) {
 template <bool DOTS>
 __global__ void __launch_bounds__(kMmThreads)
 k_q8w_mm(const uint8_t* __restrict__ W, int64_t rows, int nb, const uint8_t* __restrict__ acts, int64_t N,
-         float* __restrict__ Y, int32_t* __restrict__ D) {
+         float* __restrict__ Y, int32_t* __restrict__ D, int kbs, int splits) {
     __shared__ __align__(16) uint8_t smem[2 * kMmStage];
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    // workgroup tile: token tile (fastest), then split, then row tile; split s
+    // takes blocks [kb0, kb1) of every row and writes its sums to slice s of Y
     const int64_t ntt = (N + kMmTok - 1) / kMmTok;
     const int64_t tile = mm_tile(blockIdx.x, gridDim.x);
     const int64_t n0 = (tile % ntt) * kMmTok;
-    const int64_t r0 = (tile / ntt) * kMmRows;
-    const int nst = (nb + kMmKB - 1) / kMmKB;
+    const int64_t rs = tile / ntt;
+    const int split = __builtin_amdgcn_readfirstlane(static_cast<int>(rs % splits));
+    const int64_t r0 = (rs / splits) * kMmRows;
+    const int kb0 = __builtin_amdgcn_readfirstlane(split * kbs);
+    const int kb1 = __builtin_amdgcn_readfirstlane(min(nb, kb0 + kbs));
+    const int nst = (kb1 - kb0 + kMmKB - 1) / kMmKB;
     const uint8_t* __restrict__ act_codes = acts;
     const uint16_t* __restrict__ act_scales =
         reinterpret_cast<const uint16_t*>(acts + static_cast<int64_t>(nb) * N * 32);
@@ -81,7 +87,7 @@ k_q8w_mm(const uint8_t* __restrict__ W, int64_t rows, int nb, const uint8_t* __r
     // ---- staging: what this thread moves each stage ---------------------------
     // activations: 16-byte piece c = t + 256 i (i < 4) of the stage's 4 planes:
     // plane c / 256, token (c % 256) / 2, half c % 2.  Tokens past N read the
-    // last token (never stored); blocks past nb read block nb - 1 with a zero
+    // last token (never stored); blocks past the range read its last block with a zero
     // scale (see below).
     int a_tok[4], a_half[4], a_blk[4];
 #pragma unroll
@@ -118,27 +124,27 @@ k_q8w_mm(const uint8_t* __restrict__ W, int64_t rows, int nb, const uint8_t* __r
     auto load_stage = [&](int st) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int b = min(st * kMmKB + a_blk[i], nb - 1);
+            const int b = min(kb0 + st * kMmKB + a_blk[i], kb1 - 1);
             __builtin_memcpy(&ra[i], a_base[i] + static_cast<int64_t>(b) * planeA, 16);
         }
         {
             // two scales (tokens n, n + 1) as one dword; past N or past the
             // last block: zero scale
-            const int b = st * kMmKB + as_blk;
-            const uint16_t* p = s_base + static_cast<int64_t>(min(b, nb - 1)) * N;
+            const int b = kb0 + st * kMmKB + as_blk;
+            const uint16_t* p = s_base + static_cast<int64_t>(min(b, kb1 - 1)) * N;
             const uint32_t s0 = s_ok0 ? p[0] : 0u;
             const uint32_t s1 = s_ok1 ? p[1] : 0u;
-            ras = b < nb ? (s0 | (s1 << 16)) : 0u;
+            ras = b < kb1 ? (s0 | (s1 << 16)) : 0u;
         }
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
-            const int b = st * kMmKB + w_blk0 + k;
-            const uint8_t* p = w_base + min(b, nb - 1) * kQ8Bytes;
+            const int b = kb0 + st * kMmKB + w_blk0 + k;
+            const uint8_t* p = w_base + min(b, kb1 - 1) * kQ8Bytes;
             uint16_t d;
             __builtin_memcpy(&d, p, 2);
             __builtin_memcpy(&rwq[k][0], p + 2, 16);
             __builtin_memcpy(&rwq[k][1], p + 18, 16);
-            rwd[k] = b < nb ? d : 0u;
+            rwd[k] = b < kb1 ? d : 0u;
         }
     };
     auto store_stage = [&](int buf) __attribute__((always_inline)) {
@@ -200,9 +206,9 @@ k_q8w_mm(const uint8_t* __restrict__ W, int64_t rows, int nb, const uint8_t* __r
                 for (int j = 0; j < 2; ++j) {
                     const i32x16 sdot = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], izero, 0, 0, 0);
                     if constexpr (DOTS) {
-                        const int blk = st * kMmKB + kb;
+                        const int blk = kb0 + st * kMmKB + kb;
                         const int64_t r = r0 + 32 * (rt0 + j) + l32;
-                        if (blk < nb && r < rows) {
+                        if (blk < kb1 && r < rows) {
 #pragma unroll
                             for (int v = 0; v < 16; ++v) {
                                 const int64_t n = n0 + 32 * (tt0 + i) + 8 * (v >> 2) + 4 * half + (v & 3);
@@ -236,6 +242,7 @@ k_q8w_mm(const uint8_t* __restrict__ W, int64_t rows, int nb, const uint8_t* __r
     }
 
     if constexpr (!DOTS) {
+        float* const Yo = Y + static_cast<int64_t>(split) * N * rows;  // this split's slice
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -245,9 +252,20 @@ k_q8w_mm(const uint8_t* __restrict__ W, int64_t rows, int nb, const uint8_t* __r
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int64_t n = n0 + 32 * (tt0 + i) + 8 * (v >> 2) + 4 * half + (v & 3);
-                    if (n < N) Y[n * rows + r] = acc[i][j][v];
+                    if (n < N) Yo[n * rows + r] = acc[i][j][v];
                 }
             }
+    }
+}
+
+// Y = the splits' slices of P added in split order.
+__global__ void __launch_bounds__(256)
+k_q8w_mm_sum(const float* __restrict__ P, int splits, int64_t total, float* __restrict__ Y) {
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < total;
+         i += static_cast<int64_t>(gridDim.x) * 256) {
+        float y = P[i];
+        for (int k = 1; k < splits; ++k) y += P[k * total + i];
+        Y[i] = y;
     }
 }
 
@@ -314,8 +332,29 @@ size_t q8w_mm_act_bytes(int64_t N, int64_t nb) {
     return (static_cast<size_t>(N * nb) * (32 + 2) + 255) & ~static_cast<size_t>(255);
 }
 
-hipError_t launch_q8w_mm(const uint8_t* W, int64_t rows, int64_t nb, const float* X, const uint8_t* Xq, int64_t N,
-                         float* Y, int32_t* D, void* ws, hipStream_t s) {
+int q8w_mm_splits(int64_t rows, int64_t nb, int64_t N, int num_cu, int* kbs) {
+    const int64_t tiles = ((rows + kMmRows - 1) / kMmRows) * ((N + kMmTok - 1) / kMmTok);
+    *kbs = static_cast<int>(nb);
+    int64_t S = 2 * static_cast<int64_t>(num_cu) / tiles;  // two workgroups per CU
+    if (S > kQ8wMmMaxSplits) S = kQ8wMmMaxSplits;
+    if (S > nb / 16) S = nb / 16;
+    if (S < 2) return 1;
+    int64_t kb = (nb + S - 1) / S;
+    kb = (kb + kMmKB - 1) / kMmKB * kMmKB;  // whole stages
+    S = (nb + kb - 1) / kb;
+    if (S < 2) return 1;
+    *kbs = static_cast<int>(kb);
+    return static_cast<int>(S);
+}
+
+size_t q8w_mm_scratch_bytes(int64_t rows, int64_t nb, int64_t N, int num_cu) {
+    int kbs = 0;
+    const int S = q8w_mm_splits(rows, nb, N, num_cu, &kbs);
+    return q8w_mm_act_bytes(N, nb) + (S > 1 ? static_cast<size_t>(S) * static_cast<size_t>(N * rows) * 4 : 0);
+}
+
+hipError_t launch_q8w_mm(const DeviceInfo* dev, const uint8_t* W, int64_t rows, int64_t nb, const float* X,
+                         const uint8_t* Xq, int64_t N, float* Y, int32_t* D, void* ws, hipStream_t s) {
     uint8_t* acts = static_cast<uint8_t*>(ws);
     if (X)
         hipLaunchKernelGGL(k_act8_from_f32, act8_grid(N, nb), dim3(256), 0, s, X, N, nb, acts);
@@ -323,13 +362,27 @@ hipError_t launch_q8w_mm(const uint8_t* W, int64_t rows, int64_t nb, const float
         hipLaunchKernelGGL(k_act8_from_q8, act8_grid(N, nb), dim3(256), 0, s, Xq, N, nb, acts);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const dim3 grid(static_cast<uint32_t>(((rows + kMmRows - 1) / kMmRows) * ((N + kMmTok - 1) / kMmTok)));
+    // few workgroup tiles: K split into ranges, each range's sums into its
+    // slice of the buffer behind the activation records (q8w_mm_scratch_bytes),
+    // added in range order by k_q8w_mm_sum; the block-dot export never splits
+    int kbs = static_cast<int>(nb), splits = 1;
+    if (!D) splits = q8w_mm_splits(rows, nb, N, dev->num_cu, &kbs);
+    float* partial = reinterpret_cast<float*>(acts + q8w_mm_act_bytes(N, nb));
+    const dim3 grid(
+        static_cast<uint32_t>(((rows + kMmRows - 1) / kMmRows) * ((N + kMmTok - 1) / kMmTok) * splits));
     if (D)
         hipLaunchKernelGGL(k_q8w_mm<true>, grid, dim3(kMmThreads), 0, s, W, rows, static_cast<int>(nb), acts, N, Y,
-                           D);
+                           D, kbs, splits);
     else
-        hipLaunchKernelGGL(k_q8w_mm<false>, grid, dim3(kMmThreads), 0, s, W, rows, static_cast<int>(nb), acts, N, Y,
-                           D);
+        hipLaunchKernelGGL(k_q8w_mm<false>, grid, dim3(kMmThreads), 0, s, W, rows, static_cast<int>(nb), acts, N,
+                           splits > 1 ? partial : Y, D, kbs, splits);
+    e = hipGetLastError();
+    if (e != hipSuccess || splits == 1) return e;
+    const int64_t total = N * rows;
+    int64_t blocks = (total + 255) / 256;
+    const int64_t cap = static_cast<int64_t>(dev->num_cu) * 8;
+    if (blocks > cap) blocks = cap;
+    hipLaunchKernelGGL(k_q8w_mm_sum, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, s, partial, splits, total, Y);
     return hipGetLastError();
 }
 
