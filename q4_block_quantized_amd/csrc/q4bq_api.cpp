@@ -56,6 +56,7 @@ bool too_big(int64_t a, int64_t b, int64_t bytes_per) {
 constexpr int64_t kDecodeGroupsMaxN = 32;
 constexpr int64_t kDecodeGroupsSplitMaxN = 16;
 constexpr int64_t kQ8wGroupsMaxN = 32;
+constexpr int64_t kQ8wGroupsSplitMaxN = 16;
 constexpr int64_t kQ8wGroupsLongRows = 65536;
 bool decode_groups_pay(const DeviceInfo* dev, int64_t N, int64_t nb, int64_t rows) {
     if (N > kDecodeGroupsMaxN || !(rows_apply(kGemvMaxN, nb, rows) || mma_apply(kGemvMaxN, nb, rows))) return false;
@@ -627,12 +628,14 @@ int mul_mat_q8_0_q8_0(const void* Wq8, int64_t rows, int64_t K, const float* X, 
     if (!q8w_supported_k(nb) || too_big(rows, K, 2) || too_big(N, K, 4) || too_big(N, rows, 4)) return Q4BQ_EINVAL;
     // a few more tokens than one decode launch takes: groups of up to 8 on the
     // row kernel rather than the matrix-core kernel, whose workgroups cover 128
-    // tokens (measured, graph-timed: 14336 x 4096 at N = 9 / 16 125 -> ~47 / 62
-    // us; the 128256 x 4096 head only breaks even beyond 9 tokens: 8 tokens
-    // take 149 us there)
-    const bool groups = N > kGemvMaxN && N <= kQ8wGroupsMaxN && q8w_tokens_per_launch(nb) == kGemvMaxN &&
-                        (rows < kQ8wGroupsLongRows || N <= kGemvMaxN + 1);
-    if (N > kGemvMaxN && !groups && !q8w_mm_grid_ok(rows, N)) return Q4BQ_EINVAL;
+    // tokens -- up to 16 tokens where that kernel splits K, up to 32 elsewhere
+    // (measured, graph-timed, groups against the matrix cores: 14336 x 4096 at
+    // N = 16 / 24 43.9 / 65.1 against 51.5 / 52.3 us, 3072 x 768 at N = 32 24.6
+    // against 34.7 us); on the 128256 x 4096 head only at 9 tokens (8 tokens
+    // take 127-149 us there)
+    const bool may_group = N > kGemvMaxN && N <= kQ8wGroupsMaxN && q8w_tokens_per_launch(nb) == kGemvMaxN &&
+                           (rows < kQ8wGroupsLongRows || N <= kGemvMaxN + 1);
+    if (N > kGemvMaxN && !may_group && !q8w_mm_grid_ok(rows, N)) return Q4BQ_EINVAL;
     if (!aligned(Wq8, 2) || !aligned(X, 4) || !aligned(Y, 4)) return Q4BQ_EINVAL;
     const size_t y_bytes = static_cast<size_t>(N * rows) * 4;
     if (overlap(Y, y_bytes, Wq8, static_cast<size_t>(rows * nb) * kQ8Bytes) ||
@@ -641,6 +644,9 @@ int mul_mat_q8_0_q8_0(const void* Wq8, int64_t rows, int64_t K, const float* X, 
     hipError_t err = hipSuccess;
     const DeviceInfo* dev = current_device(&err);
     if (!dev) return Q4BQ_EHIP;
+    int kbs = 0;
+    const bool groups =
+        may_group && (N <= kQ8wGroupsSplitMaxN || q8w_mm_splits(rows, nb, N, dev->num_cu, &kbs) == 1);
     if (N > kGemvMaxN && !groups)
         return run_q8w_mm(static_cast<const uint8_t*>(Wq8), rows, nb, X, nullptr, N, Y, nullptr,
                           static_cast<hipStream_t>(stream));
