@@ -208,6 +208,8 @@ int mul_mat_q4_0r_q8_0_ex(const void *Wr, int64_t rows, int64_t K, const float *
  *   workspace     NULL, or a device buffer of ws_bytes >=
  *                 q4bq_workspace_size(1, K, N), 16-byte aligned; with NULL the
  *                 scratch (not needed for N = 1) is taken with hipMallocAsync.
+ *                 Above 8 tokens, where the matrix-core kernel splits K (few
+ *                 row tiles), its range sums take stream-ordered scratch too.
  * For N <= 8 the decode kernel runs once over the concatenated rows; larger N
  * runs the matrix-core kernel per matrix on the shared quantized X.  Each
  * Y[i] equals mul_mat_q4_0_q8_0(Wq[i], X) within the operator's tolerance

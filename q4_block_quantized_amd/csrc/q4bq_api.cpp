@@ -461,6 +461,10 @@ int check_fusion(int64_t K, int64_t rows, int64_t N, const float* ln_gamma, cons
 // LayerNorm (optional) + Q8_0 of X into stream-ordered scratch, then the
 // products of `count` matrices on it, each with its epilogue.
 size_t fused_act_bytes(int64_t N, int64_t nb) { return (act_bytes(N, nb) + 255) & ~static_cast<size_t>(255); }
+// ... and room for the matrix-core kernel's range sums where it may split K
+size_t fused_ws_bytes(int64_t rows, int64_t N, int64_t nb) {
+    return fused_act_bytes(N, nb) + (N > kGemvMaxN ? prefill_partial_bytes(rows, nb, N) : 0);
+}
 
 int run_fused(int count, const uint8_t* const* Wq, int64_t rows, int64_t K, const float* X, int64_t N,
               const float* ln_gamma, const float* ln_beta, float ln_eps, const Epilogue* epi, float* const* Y,
@@ -481,7 +485,8 @@ int run_fused(int count, const uint8_t* const* Wq, int64_t rows, int64_t K, cons
         }
         return err == hipSuccess ? Q4BQ_OK : Q4BQ_EHIP;
     }
-    const size_t bytes = fused_act_bytes(N, nb);
+    const size_t bytes = fused_ws_bytes(rows, N, nb);
+    const size_t act_b = fused_act_bytes(N, nb);
     void* ws = workspace;
     if (ws) {
         if (ws_bytes < bytes) return Q4BQ_ENOMEM;
@@ -504,8 +509,11 @@ int run_fused(int count, const uint8_t* const* Wq, int64_t rows, int64_t K, cons
             Epilogue e = epi[i];
             if (e.mul) e.mul += n0 * rows;
             float* Yg = Y[i] + n0 * rows;
+            // (the range sums, where K is split, behind the activations)
             err = g <= kGemvMaxN ? launch_gemv(dev, kAoS, Wq[i], rows, nb, ws, g, Yg, nullptr, s, e)
-                                 : launch_prefill(dev, kAoS, Wq[i], rows, nb, ws, g, Yg, nullptr, s, e);
+                                 : launch_prefill(dev, kAoS, Wq[i], rows, nb, ws, g, Yg, nullptr, s, e,
+                                                  reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + act_b),
+                                                  bytes - act_b);
         }
     }
     const hipError_t ferr = workspace ? hipSuccess : hipFreeAsync(ws, s);
@@ -518,10 +526,9 @@ int check_workspace(const void* ws, int64_t rows, int64_t K, int64_t N, const vo
                     int nbufs) {
     if (!ws) return Q4BQ_OK;
     if (!aligned(ws, 16)) return Q4BQ_EINVAL;
-    const size_t need = fused_act_bytes(N, K / kQK);
+    const size_t need = fused_ws_bytes(rows, N, K / kQK);
     for (int i = 0; i < nbufs; ++i)
         if (bufs[i] && overlap(ws, need, bufs[i], sizes[i])) return Q4BQ_EINVAL;
-    (void)rows;
     return Q4BQ_OK;
 }
 
@@ -530,8 +537,9 @@ int check_workspace(const void* ws, int64_t rows, int64_t K, int64_t N, const vo
 extern "C" {
 
 size_t q4bq_fused_workspace_size(int64_t rows, int64_t K, int64_t N) {
-    if (bad_dim(rows) || bad_dim(N) || bad_k(K) || too_big(N, K, 4)) return 0;
-    return fused_act_bytes(N, K / kQK);
+    if (bad_dim(rows) || bad_dim(N) || bad_k(K) || too_big(N, K, 4) || too_big(N, rows, 4 * kPrefillMaxSplits))
+        return 0;
+    return fused_ws_bytes(rows, N, K / kQK);
 }
 
 int mul_mat_q4_0_q8_0_fused(const void* Wq, int64_t rows, int64_t K, const float* X, int64_t N,
