@@ -49,6 +49,11 @@ def test_status_strings(L):
 def test_workspace_size(L):
     assert L.q4bq_workspace_size(4096, 4096, 1) == 128 * 40 + (256 - (128 * 40) % 256) % 256
     assert L.q4bq_workspace_size(14336, 4096, 512) == 512 * 128 * 64
+    # few workgroup tiles (4096 rows x 512 tokens: 19 x 4 < 256): the
+    # activations, then room for up to 4 ranges of fp32 sums of the split K
+    assert L.q4bq_workspace_size(4096, 4096, 512) == 512 * 128 * 64 + 4 * 512 * 4096 * 4
+    # rows of fewer than 32 blocks never split
+    assert L.q4bq_workspace_size(4096, 768, 512) == 512 * 24 * 64
     assert L.q4bq_workspace_size(1, 31, 1) == 0
     assert L.q4bq_workspace_size(0, 32, 1) == 0
     assert L.q4bq_workspace_size(1, 32, 0) == 0
@@ -202,6 +207,8 @@ def test_fused_workspace_size(L):
     assert L.q4bq_fused_workspace_size(14336, 4096, 3) == (3 * 128 * 40 + 255) // 256 * 256
     assert L.q4bq_fused_workspace_size(14336, 4128, 3) == (3 * 129 * 40 + 255) // 256 * 256
     assert L.q4bq_fused_workspace_size(14336, 4096, 512) == 512 * 128 * 64
+    # and the room for the split K's range sums where the grid has few tiles
+    assert L.q4bq_fused_workspace_size(4096, 4096, 512) == 512 * 128 * 64 + 4 * 512 * 4096 * 4
     assert L.q4bq_fused_workspace_size(4, 48, 1) == 0
 
 
